@@ -1,0 +1,139 @@
+"""ctypes binding of libresolvent.so -- argument marshalling only.
+
+Every function here has the name of the C entry point it calls (declared in
+``include/resolvent.h``).  PyTorch supplies device memory and the stream; all
+of the computation happens in the library's HIP kernels.  There is no other
+path: a missing library is an error, never a fallback.
+"""
+import ctypes
+import enum
+import os
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+library_path = os.path.join(PKG, "libresolvent.so")
+
+BF16, F32 = 0, 1
+
+
+class Status(enum.IntEnum):
+    OK = 0
+    NONFINITE = 1
+    BAD_SHAPE = 2
+    BAD_ARG = 3
+    UNSUPPORTED = 4
+    DEVICE_ERROR = 5
+
+
+class ResolventError(RuntimeError):
+    def __init__(self, status):
+        self.status = Status(status) if status in Status._value2member_map_ else status
+        super().__init__(f"resolvent: {resolvent_status_str(int(status))} ({int(status)})")
+
+
+_lib = None
+
+
+def _load():
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(library_path):
+        raise RuntimeError(
+            f"{library_path} is missing: build it first (python -c 'import __graft_entry__ as g; "
+            "g.build()'); there is no fallback implementation")
+    lib = ctypes.CDLL(library_path)
+    i64, i32, vp, dbl = ctypes.c_int64, ctypes.c_int32, ctypes.c_void_p, ctypes.c_double
+    lib.resolvent_workspace_bytes.argtypes = [i64, i64, i64, i64, i32, i32]
+    lib.resolvent_workspace_bytes.restype = ctypes.c_size_t
+    lib.resolvent_forward.argtypes = [vp, vp, vp, vp, vp, dbl, dbl, dbl, i64, i64, i64, i64, i32,
+                                      i32, vp, vp, vp, ctypes.c_size_t, vp, vp]
+    lib.resolvent_forward.restype = i32
+    lib.resolvent_forward_marked.argtypes = lib.resolvent_forward.argtypes + [vp]
+    lib.resolvent_forward_marked.restype = i32
+    lib.resolvent_counters_offset.argtypes = [i64, i64, i64, i64, i32, i32]
+    lib.resolvent_counters_offset.restype = ctypes.c_size_t
+    lib.resolvent_status_str.argtypes = [i32]
+    lib.resolvent_status_str.restype = ctypes.c_char_p
+    _lib = lib
+    return lib
+
+
+def resolvent_status_str(status: int) -> str:
+    return _load().resolvent_status_str(int(status)).decode()
+
+
+def resolvent_workspace_bytes(B, H, n, d, qk_dtype=BF16, v_dtype=BF16) -> int:
+    return int(_load().resolvent_workspace_bytes(B, H, n, d, qk_dtype, v_dtype))
+
+
+def resolvent_counters_offset(B, H, n, d, qk_dtype=BF16, v_dtype=BF16) -> int:
+    return int(_load().resolvent_counters_offset(B, H, n, d, qk_dtype, v_dtype))
+
+
+def _dtype_code(t):
+    import torch
+
+    if t.dtype == torch.bfloat16:
+        return BF16
+    if t.dtype == torch.float32:
+        return F32
+    raise TypeError(f"unsupported dtype {t.dtype}")
+
+
+def resolvent_forward(q, k, u, theta, v, beta, qk, g, *, o_re=None, o_im=None, workspace=None,
+                      status=None, stream=None, check=True, marks=None):
+    """O = readout of the resolvent head: (o_re, o_im), each [B, H, n, d] fp32.
+
+    q, k, v: contiguous [B, H, n, d] device tensors (bf16 or fp32); u, theta:
+    [B, H, n] fp32.  Buffers not given are allocated with torch.  With
+    ``check`` the stream is synchronised and a non-OK device status raises
+    ResolventError; otherwise the caller reads ``status`` itself.  ``marks``
+    (four HIP event handles) selects resolvent_forward_marked."""
+    import torch
+
+    B, H, n, d = q.shape
+    for t in (q, k, v, u, theta):
+        if not t.is_contiguous():
+            raise ValueError("inputs must be contiguous")
+    dev = q.device
+    qk_dt, v_dt = _dtype_code(q), _dtype_code(v)
+    if o_re is None:
+        o_re = torch.empty((B, H, n, d), device=dev, dtype=torch.float32)
+    if o_im is None:
+        o_im = torch.empty((B, H, n, d), device=dev, dtype=torch.float32)
+    ws_bytes = resolvent_workspace_bytes(B, H, n, d, qk_dt, v_dt)
+    if workspace is None:
+        workspace = torch.empty(max(ws_bytes, 1), device=dev, dtype=torch.uint8)
+    if status is None:
+        status = torch.zeros(1, device=dev, dtype=torch.int32)
+    if stream is None:
+        stream = torch.cuda.current_stream(dev)
+    handle = stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
+    args = (q.data_ptr(), k.data_ptr(), u.data_ptr(), theta.data_ptr(), v.data_ptr(),
+            float(beta), float(qk), float(g), B, H, n, d, qk_dt, v_dt, o_re.data_ptr(),
+            o_im.data_ptr(), workspace.data_ptr(), workspace.numel() * workspace.element_size(),
+            status.data_ptr(), handle)
+    if marks is None:
+        rc = _load().resolvent_forward(*args)
+    else:
+        arr = (ctypes.c_void_p * 4)(*marks)
+        rc = _load().resolvent_forward_marked(*args, arr)
+    if rc != Status.OK:
+        raise ResolventError(rc)
+    if check and n > 0 and B > 0 and H > 0:
+        if hasattr(stream, "synchronize"):
+            stream.synchronize()
+        else:
+            torch.cuda.synchronize(dev)
+        st = int(status.item())
+        if st != Status.OK:
+            raise ResolventError(st)
+    return o_re, o_im
+
+
+def forward(q, k, u, theta, v, beta, qk, g, **kw):
+    """resolvent_forward returning one complex tensor (o_re + i o_im)."""
+    import torch
+
+    o_re, o_im = resolvent_forward(q, k, u, theta, v, beta, qk, g, **kw)
+    return torch.complex(o_re, o_im)

@@ -1,0 +1,87 @@
+// layout.h -- tile sizes and the device-workspace layout of the resolvent
+// forward pass (shared by the host entry points and the kernel launchers).
+#pragma once
+
+#include <cstddef>
+#include <cstdint>
+
+namespace resolvent {
+
+// A workgroup owns BQ consecutive queries (NWAVES waves of 32 rows); keys are
+// staged BK at a time.  Gate scans use the same tiling: an inclusive prefix
+// inside each query tile and an exclusive suffix inside each key tile.
+constexpr int NWAVES = 4;
+constexpr int BQ = 32 * NWAVES;
+constexpr int BK = 64;
+static_assert(BQ % BK == 0, "a query tile must hold whole key tiles");
+
+constexpr size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+struct Layout {
+    int64_t BH = 0, n = 0, d = 0;
+    int64_t n_pad = 0, n_qt = 0, n_kt = 0;
+    bool bf16_path = true;
+    // byte offsets into the workspace
+    size_t gate[9] = {};  // a_re a_im a_m | s_re s_im s_m | p_re p_im p_m  (float [BH][n_pad])
+    size_t tile[3] = {};  // A_re A_im A_m per key tile (double [BH][n_kt])
+    size_t qstat = 0, kstat = 0;  // per query tile max |q|, max |k| bits (uint32 [BH][n_qt])
+    size_t counters = 0;  // uint32 [2]: key tiles processed before the query tiles; spare
+    size_t vt = 0;        // bf16 [BH][d][n_pad], keys permuted inside groups of 16
+    size_t total = 0;
+};
+
+inline Layout make_layout(int64_t B, int64_t H, int64_t n, int64_t d, bool bf16_path) {
+    Layout L;
+    L.BH = B * H;
+    L.n = n;
+    L.d = d;
+    L.bf16_path = bf16_path;
+    L.n_pad = (n + BQ - 1) / BQ * BQ;
+    L.n_qt = L.n_pad / BQ;
+    L.n_kt = L.n_pad / BK;
+    size_t off = 0;
+    const size_t per_pos = sizeof(float) * size_t(L.BH) * size_t(L.n_pad);
+    for (int i = 0; i < 9; ++i) {
+        L.gate[i] = off;
+        off = align_up(off + per_pos, 256);
+    }
+    const size_t per_kt = sizeof(double) * size_t(L.BH) * size_t(L.n_kt);
+    for (int i = 0; i < 3; ++i) {
+        L.tile[i] = off;
+        off = align_up(off + per_kt, 256);
+    }
+    const size_t per_qt = sizeof(uint32_t) * size_t(L.BH) * size_t(L.n_qt);
+    L.qstat = off;
+    off = align_up(off + per_qt, 256);
+    L.kstat = off;
+    off = align_up(off + per_qt, 256);
+    L.counters = off;
+    off = align_up(off + 2 * sizeof(uint32_t), 256);
+    L.vt = off;
+    if (bf16_path) off = align_up(off + 2 * size_t(L.BH) * size_t(d) * size_t(L.n_pad), 256);
+    L.total = off;
+    return L;
+}
+
+// Everything a launch needs, in device pointers.
+struct Problem {
+    const void *q, *k, *v;
+    const float *u, *theta;
+    float *o_re, *o_im;
+    int32_t *status;
+    unsigned char *ws;
+    Layout L;
+    double g;
+    float c;            // qk * log2(e) / sqrt(d), the logit scale in log2 units
+    float beta;
+    int beta_mode;      // 0: beta == 0, 1: beta == 1, 2: general
+    bool qk_zero;
+    bool v_f32;         // v stored as float32 (bf16 path converts when staging)
+};
+
+// Kernel launcher (resolvent_kernels.hip).  marks, when not null, are four
+// HIP events recorded on the stream before the first kernel, before the fused
+// forward kernel, after it, and after the last kernel.  Returns a hipError_t.
+int launch_forward(const Problem &P, void *stream, void *const *marks);
+
+}  // namespace resolvent

@@ -1,0 +1,121 @@
+// resolvent_abi.cpp -- the C entry points declared in include/resolvent.h:
+// argument, shape and switch checks (all before any HIP call, so they can be
+// exercised without a GPU), workspace sizing, and the launch.
+#include "resolvent.h"
+
+#include <cfloat>
+#include <cmath>
+#include <cstdint>
+
+#include "layout.h"
+
+using namespace resolvent;
+
+namespace {
+
+bool supported(int64_t d, int32_t qk_dtype, int32_t v_dtype) {
+    if (d != 64 && d != 128) return false;
+    if (qk_dtype == RESOLVENT_BF16) return v_dtype == RESOLVENT_BF16 || v_dtype == RESOLVENT_F32;
+    if (qk_dtype == RESOLVENT_F32) return v_dtype == RESOLVENT_F32;
+    return false;
+}
+
+// Limits that keep every launch grid and in-kernel index in range.
+bool within_limits(int64_t B, int64_t H, int64_t n) {
+    const int64_t maxn = int64_t(1) << 24;
+    if (n > maxn || B > maxn || H > maxn) return false;
+    const int64_t BH = B * H;
+    if (BH > (int64_t(1) << 24)) return false;
+    const int64_t n_pad = (n + BQ - 1) / BQ * BQ;
+    return BH * (n_pad / BK) < (int64_t(1) << 31);
+}
+
+bool aligned(const void *p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+}  // namespace
+
+extern "C" {
+
+size_t resolvent_workspace_bytes(int64_t B, int64_t H, int64_t n, int64_t d, int32_t qk_dtype,
+                                 int32_t v_dtype) {
+    if (B <= 0 || H <= 0 || n <= 0 || d <= 0) return 0;
+    if (!supported(d, qk_dtype, v_dtype) || !within_limits(B, H, n)) return 0;
+    return make_layout(B, H, n, d, qk_dtype == RESOLVENT_BF16).total;
+}
+
+size_t resolvent_counters_offset(int64_t B, int64_t H, int64_t n, int64_t d, int32_t qk_dtype,
+                                 int32_t v_dtype) {
+    if (resolvent_workspace_bytes(B, H, n, d, qk_dtype, v_dtype) == 0) return SIZE_MAX;
+    return make_layout(B, H, n, d, qk_dtype == RESOLVENT_BF16).counters;
+}
+
+int32_t resolvent_forward_marked(const void *q, const void *k, const float *u,
+                                 const float *theta, const void *v, double beta, double qk,
+                                 double g, int64_t B, int64_t H, int64_t n, int64_t d,
+                                 int32_t qk_dtype, int32_t v_dtype, float *o_re, float *o_im,
+                                 void *workspace, size_t workspace_bytes, int32_t *status_dev,
+                                 hipStream_t stream, hipEvent_t *marks) {
+    if (B < 0 || H < 0 || n < 0 || d < 0) return RESOLVENT_BAD_SHAPE;
+    if (B == 0 || H == 0 || n == 0) return RESOLVENT_OK;  // empty in, empty out
+    if (d == 0) return RESOLVENT_BAD_SHAPE;
+    if (!std::isfinite(beta) || !std::isfinite(qk) || !std::isfinite(g))
+        return RESOLVENT_NONFINITE;
+    if (!supported(d, qk_dtype, v_dtype) || !within_limits(B, H, n))
+        return RESOLVENT_UNSUPPORTED;
+    if (!q || !k || !u || !theta || !v || !o_re || !o_im || !status_dev || !workspace)
+        return RESOLVENT_BAD_ARG;
+    if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(o_re, 16) ||
+        !aligned(o_im, 16) || !aligned(u, 4) || !aligned(theta, 4) || !aligned(status_dev, 4) ||
+        !aligned(workspace, 256))
+        return RESOLVENT_BAD_ARG;
+    const Layout L = make_layout(B, H, n, d, qk_dtype == RESOLVENT_BF16);
+    if (workspace_bytes < L.total) return RESOLVENT_BAD_ARG;
+
+    // logit scale in log2 units; the device computes logits in float32
+    const double c = qk * 1.4426950408889634074 / std::sqrt((double)d);
+    if (qk != 0.0 && !(std::fabs(c) <= (double)FLT_MAX)) return RESOLVENT_NONFINITE;
+
+    Problem P;
+    P.q = q;
+    P.k = k;
+    P.v = v;
+    P.u = u;
+    P.theta = theta;
+    P.o_re = o_re;
+    P.o_im = o_im;
+    P.status = status_dev;
+    P.ws = static_cast<unsigned char *>(workspace);
+    P.L = L;
+    P.g = g;
+    P.c = (float)c;
+    P.beta = (float)beta;
+    P.beta_mode = beta == 0.0 ? 0 : (beta == 1.0 ? 1 : 2);
+    P.qk_zero = (qk == 0.0);
+    P.v_f32 = (v_dtype == RESOLVENT_F32);
+    const int err = launch_forward(P, stream, reinterpret_cast<void *const *>(marks));
+    return err == 0 ? RESOLVENT_OK : RESOLVENT_DEVICE_ERROR;
+}
+
+int32_t resolvent_forward(const void *q, const void *k, const float *u, const float *theta,
+                          const void *v, double beta, double qk, double g, int64_t B,
+                          int64_t H, int64_t n, int64_t d, int32_t qk_dtype, int32_t v_dtype,
+                          float *o_re, float *o_im, void *workspace, size_t workspace_bytes,
+                          int32_t *status_dev, hipStream_t stream) {
+    return resolvent_forward_marked(q, k, u, theta, v, beta, qk, g, B, H, n, d, qk_dtype,
+                                    v_dtype, o_re, o_im, workspace, workspace_bytes, status_dev,
+                                    stream, nullptr);
+}
+
+const char *resolvent_status_str(int32_t status) {
+    switch (status) {
+        case RESOLVENT_OK: return "ok";
+        case RESOLVENT_NONFINITE: return "non-finite input refused";
+        case RESOLVENT_BAD_SHAPE: return "bad shape";
+        case RESOLVENT_BAD_ARG: return "bad argument";
+        case RESOLVENT_UNSUPPORTED: return "unsupported head_dim or dtype";
+        case RESOLVENT_DEVICE_ERROR: return "device error";
+        default: return "unknown status";
+    }
+}
+
+}  // extern "C"

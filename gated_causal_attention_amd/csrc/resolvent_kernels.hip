@@ -1,0 +1,910 @@
+// resolvent_kernels.hip -- HIP kernels (gfx950 / CDNA4) of the resolvent
+// operator head forward pass, and their launcher.
+//
+// The head is the one defined on the "Resolvent Operator" page (teerth.dev,
+// Aether-Lang/integrated/resolvent), section "Object"; Z^beta is evaluated in
+// the log domain with a shift by the largest live logit as in its section
+// "Evaluation and refusals".  The path product G_ij = prod_{k=j+1..i} a_k is
+// only ever formed as a product -- never via a logarithm or a division (Lean
+// table of the page, no_prefix_scan_represents_a_zero_gate) -- so a closed
+// gate yields exact zeros.  For a query tile [i0, i0+BQ) and a key tile t that
+// lies wholly before it,
+//     G_ij = S_j * C_t * P_i,
+// with S_j the exclusive suffix product of the gates inside key tile t, C_t
+// the product of every gate between the end of tile t and i0 (carried from
+// tile to tile as the key loop runs backwards), and P_i the inclusive prefix
+// product inside the query tile.  P_i is applied once to the accumulators
+// after the loop; the keys of the query tile itself use G_ij formed explicitly
+// by a running product per row, multiplying a_i, a_{i-1}, ..., a_{j+1} in the
+// order the page's "Rust API" section fixes.
+//
+// Kernels, in launch order on the caller's stream:
+//   vt_kernel / clear_status_kernel  status := OK; (bf16 path) v -> bf16 v^T
+//   gates_kernel                     blend + gate in f64, in-tile scans
+//   fwd_kernel                       the fused forward (MFMA)
+//   logit_check_kernel               exact logit-overflow refusal, only for
+//                                    heads whose |q|,|k| extrema allow one
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdint>
+#include <type_traits>
+
+#include "layout.h"
+
+namespace resolvent {
+namespace {
+
+typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8;
+typedef __attribute__((__vector_size__(16 * sizeof(float)))) float f32x16;
+
+constexpr int32_t kNonFinite = 1;
+constexpr uint32_t kInfBits = 0x7F800000u;
+constexpr int NTHREADS = NWAVES * 64;
+
+// Storage order of keys inside a group of 16: slot p holds key perm16(p)
+// (an involution swapping bits 2 and 3).  With it, the 8 keys that one lane
+// of a 32x32x16 MFMA operand needs are 8 consecutive slots.
+__host__ __device__ constexpr int perm16(int x) {
+    return (x & ~12) | ((x & 4) << 1) | ((x & 8) >> 1);
+}
+__host__ __device__ constexpr int perm64(int x) { return (x & ~15) | perm16(x & 15); }
+
+// |x| of packed bf16 / fp32 values as float bit patterns (monotone in |x|;
+// >= kInfBits means inf or NaN).
+__device__ __forceinline__ uint32_t absbits_bf16x2(uint32_t w) {
+    uint32_t lo = (w & 0x7FFFu) << 16, hi = (w & 0x7FFF0000u);
+    return lo > hi ? lo : hi;
+}
+__device__ __forceinline__ uint32_t absbits_u4_bf16(uint4 v) {
+    uint32_t a = max(absbits_bf16x2(v.x), absbits_bf16x2(v.y));
+    uint32_t b = max(absbits_bf16x2(v.z), absbits_bf16x2(v.w));
+    return max(a, b);
+}
+__device__ __forceinline__ uint32_t absbits_f4(float4 v) {
+    uint32_t a = max(__float_as_uint(v.x) & 0x7FFFFFFFu, __float_as_uint(v.y) & 0x7FFFFFFFu);
+    uint32_t b = max(__float_as_uint(v.z) & 0x7FFFFFFFu, __float_as_uint(v.w) & 0x7FFFFFFFu);
+    return max(a, b);
+}
+
+// --------------------------------------------------------------------------
+// Status and counter clear (fp32 path; the bf16 path clears them in vt_kernel).
+__global__ void clear_status_kernel(int32_t *status, uint32_t *counters) {
+    if (threadIdx.x == 0) status[0] = 0;
+    if (threadIdx.x < 2) counters[threadIdx.x] = 0;
+}
+
+// --------------------------------------------------------------------------
+// v [BH][n][D] (bf16 or fp32) -> v^T [BH][D][n_pad] bf16, keys stored in
+// perm16 order inside each group of 16 and zero past n.  Block 0 also clears
+// the status word and the counters (this kernel runs first on the bf16 path).
+template <int D, bool VF32>
+__global__ __launch_bounds__(256) void vt_kernel(const void *__restrict__ v,
+                                                  uint16_t *__restrict__ vt, int64_t n,
+                                                  int64_t n_pad, int n_kt,
+                                                  int32_t *__restrict__ status,
+                                                  uint32_t *__restrict__ counters) {
+    __shared__ __align__(16) uint16_t tile[D][BK + 8];
+    const int tid = threadIdx.x;
+    if (blockIdx.x == 0 && tid == 0) status[0] = 0;
+    if (blockIdx.x == 0 && tid < 2) counters[tid] = 0;
+    const int64_t bh = blockIdx.x / n_kt;
+    const int64_t kt = blockIdx.x % n_kt;
+    for (int c = tid; c < BK * D / 8; c += 256) {
+        const int key = c / (D / 8), c8 = c % (D / 8);
+        const int64_t p = kt * BK + key;
+        uint16_t vals[8];
+        if (p < n) {
+            if constexpr (VF32) {
+                const float *src = static_cast<const float *>(v) + (bh * n + p) * D + 8 * c8;
+                const float4 f0 = *reinterpret_cast<const float4 *>(src);
+                const float4 f1 = *reinterpret_cast<const float4 *>(src + 4);
+                const float fs[8] = {f0.x, f0.y, f0.z, f0.w, f1.x, f1.y, f1.z, f1.w};
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    __bf16 b = (__bf16)fs[e];
+                    vals[e] = __builtin_bit_cast(uint16_t, b);
+                }
+            } else {
+                const uint16_t *src = static_cast<const uint16_t *>(v) + (bh * n + p) * D + 8 * c8;
+                const uint4 raw = *reinterpret_cast<const uint4 *>(src);
+                const uint32_t ws[4] = {raw.x, raw.y, raw.z, raw.w};
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    vals[2 * e] = uint16_t(ws[e] & 0xFFFFu);
+                    vals[2 * e + 1] = uint16_t(ws[e] >> 16);
+                }
+            }
+        } else {
+#pragma unroll
+            for (int e = 0; e < 8; ++e) vals[e] = 0;
+        }
+        const int slot = perm64(key);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) tile[8 * c8 + e][slot] = vals[e];
+    }
+    __syncthreads();
+    for (int c = tid; c < D * BK / 8; c += 256) {
+        const int d = c / (BK / 8), c8 = c % (BK / 8);
+        const uint4 val = *reinterpret_cast<const uint4 *>(&tile[d][8 * c8]);
+        *reinterpret_cast<uint4 *>(vt + (bh * D + d) * n_pad + kt * BK + 8 * c8) = val;
+    }
+}
+
+// --------------------------------------------------------------------------
+// Gates: blend and gate in f64 (section "Object"; lerp(1,u,g) = (1-g)*1 + g*u
+// without a fused multiply-add, exact at g = 0 and g = 1), the inclusive
+// prefix product inside each query tile, the exclusive suffix product inside
+// each key tile and the product of each key tile, with modulus twins.  One
+// wave per query tile, PPL consecutive positions per lane.  Refuses a
+// non-finite u or theta and an overflowing g*theta (section "Evaluation and
+// refusals").
+struct GatesArgs {
+    const float *u, *theta;
+    double g;
+    int64_t n, n_pad;
+    int n_qt, n_kt;
+    float *a_re, *a_im, *a_m, *s_re, *s_im, *s_m, *p_re, *p_im, *p_m;
+    double *t_re, *t_im, *t_m;
+    int32_t *status;
+};
+
+__device__ __forceinline__ void cmul_d(double xr, double xi, double yr, double yi, double &r,
+                                       double &i) {
+    r = xr * yr - xi * yi;
+    i = xr * yi + xi * yr;
+}
+
+__global__ __launch_bounds__(64) void gates_kernel(GatesArgs A) {
+#pragma clang fp contract(off)
+    constexpr int PPL = BQ / 64;
+    constexpr int SEG = BK / PPL;  // lanes per key tile
+    const int lane = threadIdx.x;
+    const int64_t bh = blockIdx.x / A.n_qt;
+    const int64_t qt = blockIdx.x % A.n_qt;
+    const int64_t p0 = qt * BQ + PPL * lane;
+    double ar[PPL], ai[PPL], am[PPL];
+    bool bad = false;
+#pragma unroll
+    for (int e = 0; e < PPL; ++e) {
+        const int64_t p = p0 + e;
+        if (p < A.n) {
+            const float uu = A.u[bh * A.n + p], tt = A.theta[bh * A.n + p];
+            if (!isfinite(uu) || !isfinite(tt)) bad = true;
+            double l = (1.0 - A.g) * 1.0 + A.g * (double)uu;
+            l = l < 0.0 ? 0.0 : (l > 1.0 ? 1.0 : l);
+            const double tp = A.g * (double)tt;
+            if (!isfinite(tp)) bad = true;
+            ar[e] = l * cos(tp);
+            ai[e] = l * sin(tp);
+            am[e] = l;
+        } else {
+            ar[e] = 1.0;
+            ai[e] = 0.0;
+            am[e] = 1.0;
+        }
+    }
+    if (bad) A.status[0] = kNonFinite;
+
+    // inclusive prefix inside the query tile
+    double lr[PPL], li[PPL], lm[PPL];
+    double cr = 1.0, ci = 0.0, cm = 1.0;
+#pragma unroll
+    for (int e = 0; e < PPL; ++e) {
+        cmul_d(cr, ci, ar[e], ai[e], cr, ci);
+        cm = cm * am[e];
+        lr[e] = cr;
+        li[e] = ci;
+        lm[e] = cm;
+    }
+    double xr = cr, xi = ci, xm = cm;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+        const double yr = __shfl_up(xr, off), yi = __shfl_up(xi, off), ym = __shfl_up(xm, off);
+        if (lane >= off) {
+            cmul_d(yr, yi, xr, xi, xr, xi);
+            xm = ym * xm;
+        }
+    }
+    double er = __shfl_up(xr, 1), ei = __shfl_up(xi, 1), em = __shfl_up(xm, 1);
+    if (lane == 0) {
+        er = 1.0;
+        ei = 0.0;
+        em = 1.0;
+    }
+    const int64_t base = bh * A.n_pad;
+#pragma unroll
+    for (int e = 0; e < PPL; ++e) {
+        double r, i;
+        cmul_d(er, ei, lr[e], li[e], r, i);
+        A.p_re[base + p0 + e] = (float)r;
+        A.p_im[base + p0 + e] = (float)i;
+        A.p_m[base + p0 + e] = (float)(em * lm[e]);
+        A.a_re[base + p0 + e] = (float)ar[e];
+        A.a_im[base + p0 + e] = (float)ai[e];
+        A.a_m[base + p0 + e] = (float)am[e];
+    }
+
+    // exclusive suffix inside each key tile, and the key-tile products
+    double sr[PPL], si[PPL], sm[PPL];
+    double tr = 1.0, ti = 0.0, tm = 1.0;
+#pragma unroll
+    for (int e = PPL - 1; e >= 0; --e) {
+        sr[e] = tr;
+        si[e] = ti;
+        sm[e] = tm;
+        cmul_d(ar[e], ai[e], tr, ti, tr, ti);
+        tm = am[e] * tm;
+    }
+    xr = tr;
+    xi = ti;
+    xm = tm;
+    const int seg_lane = lane % SEG;
+#pragma unroll
+    for (int off = 1; off < SEG; off <<= 1) {
+        const double yr = __shfl_down(xr, off), yi = __shfl_down(xi, off),
+                     ym = __shfl_down(xm, off);
+        if (seg_lane + off < SEG) {
+            cmul_d(xr, xi, yr, yi, xr, xi);
+            xm = xm * ym;
+        }
+    }
+    er = __shfl_down(xr, 1);
+    ei = __shfl_down(xi, 1);
+    em = __shfl_down(xm, 1);
+    if (seg_lane == SEG - 1) {
+        er = 1.0;
+        ei = 0.0;
+        em = 1.0;
+    }
+#pragma unroll
+    for (int e = 0; e < PPL; ++e) {
+        double r, i;
+        cmul_d(sr[e], si[e], er, ei, r, i);
+        A.s_re[base + p0 + e] = (float)r;
+        A.s_im[base + p0 + e] = (float)i;
+        A.s_m[base + p0 + e] = (float)(sm[e] * em);
+    }
+    if (seg_lane == 0) {
+        const int64_t kt = (qt * BQ + PPL * lane) / BK;
+        A.t_re[bh * A.n_kt + kt] = xr;
+        A.t_im[bh * A.n_kt + kt] = xi;
+        A.t_m[bh * A.n_kt + kt] = xm;
+    }
+}
+
+// --------------------------------------------------------------------------
+// Fused forward.
+struct FwdArgs {
+    const void *q, *k, *v;
+    const uint16_t *vt;
+    const float *a_re, *a_im, *a_m, *s_re, *s_im, *s_m, *p_re, *p_im, *p_m;
+    const double *t_re, *t_im, *t_m;
+    float *o_re, *o_im;
+    uint32_t *qstat, *kstat, *counters;
+    int32_t *status;
+    int64_t n, n_pad;
+    int n_qt, n_kt, BH;
+    float c, beta, one_minus_beta;
+    int beta_mode, qk_zero;
+};
+
+// Shared-memory plan.  bf16 path: K tile [BK][D+8], v^T tile [D][BK+8]
+// (bf16); fp32 path: K and V tiles [BK][D+4] (fp32).  Then the per-key carried
+// gate factors T = C*S_j (re, im, modulus), the diagonal gates a_{j+1}, and a
+// few words of flags.
+template <bool F32, int D>
+struct Smem {
+    static constexpr int KS = F32 ? D + 4 : D + 8;
+    static constexpr int VS = F32 ? D + 4 : BK + 8;
+    static constexpr size_t k_bytes = size_t(BK) * KS * (F32 ? 4 : 2);
+    static constexpr size_t v_bytes = F32 ? size_t(BK) * VS * 4 : size_t(D) * VS * 2;
+    static constexpr size_t t_off = k_bytes + v_bytes;
+    static constexpr size_t dg_off = t_off + 3 * BK * sizeof(float);
+    static constexpr size_t misc_off = dg_off + 3 * BK * sizeof(float);
+    static constexpr size_t bytes = misc_off + 8 * sizeof(uint32_t);
+};
+
+template <bool F32, int D>
+struct Frag {
+    using type = typename std::conditional<F32, float, bf16x8>::type;
+    static constexpr int count = F32 ? D / 2 : D / 16;
+};
+
+// Query fragment (B operand of S^T = K Q^T) for the lane's row; returns the
+// largest |q| as float bits.
+template <bool F32, int D>
+__device__ __forceinline__ uint32_t load_q(const FwdArgs &A, int64_t bh, int64_t row, bool row_ok,
+                                           int h, typename Frag<F32, D>::type (&qf)[Frag<F32, D>::count]) {
+    uint32_t bits = 0;
+    if constexpr (!F32) {
+        const uint16_t *qp = static_cast<const uint16_t *>(A.q) + (bh * A.n + row) * D + 8 * h;
+#pragma unroll
+        for (int s = 0; s < D / 16; ++s) {
+            uint4 raw = make_uint4(0, 0, 0, 0);
+            if (row_ok) raw = *reinterpret_cast<const uint4 *>(qp + 16 * s);
+            bits = max(bits, absbits_u4_bf16(raw));
+            qf[s] = __builtin_bit_cast(bf16x8, raw);
+        }
+    } else {
+        const float *qp = static_cast<const float *>(A.q) + (bh * A.n + row) * D + (D / 2) * h;
+#pragma unroll
+        for (int t = 0; t < D / 8; ++t) {
+            float4 f = make_float4(0.f, 0.f, 0.f, 0.f);
+            if (row_ok) f = *reinterpret_cast<const float4 *>(qp + 4 * t);
+            bits = max(bits, absbits_f4(f));
+            qf[4 * t + 0] = f.x;
+            qf[4 * t + 1] = f.y;
+            qf[4 * t + 2] = f.z;
+            qf[4 * t + 3] = f.w;
+        }
+    }
+    return bits;
+}
+
+// Stage key tile t (keys t*BK .. t*BK+BK-1, zero past n) and, unless
+// k_only, the matching value tile.  Returns the largest |k| loaded (float bits).
+template <bool F32, int D>
+__device__ __forceinline__ uint32_t stage_tile(const FwdArgs &A, unsigned char *smem, int64_t bh,
+                                               int64_t t, bool k_only) {
+    using SM = Smem<F32, D>;
+    const int tid = threadIdx.x;
+    uint32_t bits = 0;
+    const int64_t key0 = t * BK;
+    if constexpr (!F32) {
+        uint16_t *Ks = reinterpret_cast<uint16_t *>(smem);
+        const uint16_t *kg = static_cast<const uint16_t *>(A.k) + (bh * A.n + key0) * D;
+        for (int c = tid; c < BK * D / 8; c += NTHREADS) {
+            const int key = c / (D / 8), c8 = c % (D / 8);
+            uint4 val = make_uint4(0, 0, 0, 0);
+            if (key0 + key < A.n) {
+                val = *reinterpret_cast<const uint4 *>(kg + key * D + 8 * c8);
+                bits = max(bits, absbits_u4_bf16(val));
+            }
+            *reinterpret_cast<uint4 *>(Ks + key * SM::KS + 8 * c8) = val;
+        }
+        if (!k_only) {
+            uint16_t *Vs = reinterpret_cast<uint16_t *>(smem + SM::k_bytes);
+            const uint16_t *vg = A.vt + bh * D * A.n_pad + key0;
+            for (int c = tid; c < D * BK / 8; c += NTHREADS) {
+                const int d = c / (BK / 8), c8 = c % (BK / 8);
+                *reinterpret_cast<uint4 *>(Vs + d * SM::VS + 8 * c8) =
+                    *reinterpret_cast<const uint4 *>(vg + d * A.n_pad + 8 * c8);
+            }
+        }
+    } else {
+        float *Ks = reinterpret_cast<float *>(smem);
+        const float *kg = static_cast<const float *>(A.k) + (bh * A.n + key0) * D;
+        for (int c = tid; c < BK * D / 4; c += NTHREADS) {
+            const int key = c / (D / 4), c4 = c % (D / 4);
+            float4 val = make_float4(0.f, 0.f, 0.f, 0.f);
+            if (key0 + key < A.n) {
+                val = *reinterpret_cast<const float4 *>(kg + key * D + 4 * c4);
+                bits = max(bits, absbits_f4(val));
+            }
+            *reinterpret_cast<float4 *>(Ks + key * SM::KS + 4 * c4) = val;
+        }
+        if (!k_only) {
+            float *Vs = reinterpret_cast<float *>(smem + SM::k_bytes);
+            const float *vg = static_cast<const float *>(A.v) + (bh * A.n + key0) * D;
+            for (int c = tid; c < BK * D / 4; c += NTHREADS) {
+                const int key = c / (D / 4), c4 = c % (D / 4);
+                float4 val = make_float4(0.f, 0.f, 0.f, 0.f);
+                if (key0 + key < A.n) val = *reinterpret_cast<const float4 *>(vg + key * D + 4 * c4);
+                *reinterpret_cast<float4 *>(Vs + key * SM::VS + 4 * c4) = val;
+            }
+        }
+    }
+    return bits;
+}
+
+// S^T for keys kb..kb+31 of the staged tile against the wave's 32 queries.
+// Lane (qi, h), register r holds key kb + 8(r/4) + 4h + r%4 of query qi.
+template <bool F32, int D>
+__device__ __forceinline__ f32x16 s_block(const unsigned char *smem, int kb, int qi, int h,
+                                          const typename Frag<F32, D>::type (&qf)[Frag<F32, D>::count]) {
+    using SM = Smem<F32, D>;
+    f32x16 acc;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) acc[r] = 0.f;
+    if constexpr (!F32) {
+        const uint16_t *kp = reinterpret_cast<const uint16_t *>(smem) + (kb + qi) * SM::KS + 8 * h;
+#pragma unroll
+        for (int s = 0; s < D / 16; ++s) {
+            const bf16x8 a = *reinterpret_cast<const bf16x8 *>(kp + 16 * s);
+            acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[s], acc, 0, 0, 0);
+        }
+    } else {
+        const float *kp = reinterpret_cast<const float *>(smem) + (kb + qi) * SM::KS + (D / 2) * h;
+#pragma unroll
+        for (int t = 0; t < D / 8; ++t) {
+            const float4 a = *reinterpret_cast<const float4 *>(kp + 4 * t);
+            acc = __builtin_amdgcn_mfma_f32_32x32x2f32(a.x, qf[4 * t + 0], acc, 0, 0, 0);
+            acc = __builtin_amdgcn_mfma_f32_32x32x2f32(a.y, qf[4 * t + 1], acc, 0, 0, 0);
+            acc = __builtin_amdgcn_mfma_f32_32x32x2f32(a.z, qf[4 * t + 2], acc, 0, 0, 0);
+            acc = __builtin_amdgcn_mfma_f32_32x32x2f32(a.w, qf[4 * t + 3], acc, 0, 0, 0);
+        }
+    }
+    return acc;
+}
+
+// O^T += V^T W~^T for the 16 keys of chunk kc (registers 8kc..8kc+7 of the
+// S^T block at kb): two accumulators, one for Re W~ and one for Im W~, that
+// share the V operand.
+template <bool F32, int D>
+__device__ __forceinline__ void pv_chunk(const unsigned char *smem, int kb, int kc, int qi, int h,
+                                         const float (&wre)[8], const float (&wim)[8],
+                                         f32x16 (&ore)[D / 32], f32x16 (&oim)[D / 32]) {
+    using SM = Smem<F32, D>;
+    if constexpr (!F32) {
+        bf16x8 bre, bim;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            bre[e] = (__bf16)wre[e];
+            bim[e] = (__bf16)wim[e];
+        }
+        const uint16_t *vp = reinterpret_cast<const uint16_t *>(smem + SM::k_bytes) + qi * SM::VS +
+                             kb + 16 * kc + 8 * h;
+#pragma unroll
+        for (int db = 0; db < D / 32; ++db) {
+            const bf16x8 a = *reinterpret_cast<const bf16x8 *>(vp + 32 * db * SM::VS);
+            ore[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, bre, ore[db], 0, 0, 0);
+            oim[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, bim, oim[db], 0, 0, 0);
+        }
+    } else {
+        const float *vs = reinterpret_cast<const float *>(smem + SM::k_bytes);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            const int s = 8 * kc + e;
+            const int key = kb + 8 * (s / 4) + 4 * h + (s % 4);
+#pragma unroll
+            for (int db = 0; db < D / 32; ++db) {
+                const float a = vs[key * SM::VS + 32 * db + qi];
+                ore[db] = __builtin_amdgcn_mfma_f32_32x32x2f32(a, wre[e], ore[db], 0, 0, 0);
+                oim[db] = __builtin_amdgcn_mfma_f32_32x32x2f32(a, wim[e], oim[db], 0, 0, 0);
+            }
+        }
+    }
+}
+
+template <bool F32, int D>
+__global__ __launch_bounds__(NTHREADS) void fwd_kernel(FwdArgs A) {
+    using SM = Smem<F32, D>;
+    using FR = Frag<F32, D>;
+    extern __shared__ __align__(16) unsigned char smem[];
+    float *Tre = reinterpret_cast<float *>(smem + SM::t_off);
+    float *Tim = Tre + BK;
+    float *Tm = Tim + BK;
+    float *Dre = reinterpret_cast<float *>(smem + SM::dg_off);
+    float *Dim = Dre + BK;
+    float *Dm = Dim + BK;
+    uint32_t *misc = reinterpret_cast<uint32_t *>(smem + SM::misc_off);
+    // misc[0], misc[1]: a 32-key block of the staged tile holds a dead column;
+    // misc[2]: largest |q|; misc[3]: largest |k|
+
+    const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, h = lane >> 5, qi = lane & 31;
+    const int L = blockIdx.x;
+    const int64_t qt = A.n_qt - 1 - L / A.BH;  // heaviest query tiles first
+    const int64_t bh = L % A.BH;
+    const int64_t i0 = qt * BQ;
+    const int64_t row = i0 + 32 * w + qi;
+    const bool row_ok = row < A.n;
+    const int64_t gbase = bh * A.n_pad;
+
+    if (tid == 0) {
+        misc[2] = 0;
+        misc[3] = 0;
+    }
+    typename FR::type qf[FR::count];
+    const uint32_t qbits = load_q<F32, D>(A, bh, row, row_ok, h, qf);
+    __syncthreads();
+    atomicMax(&misc[2], qbits);
+
+    // prefix product of the query tile for this row, and its modulus
+    const float Pre = A.p_re[gbase + row], Pim = A.p_im[gbase + row], Pm = A.p_m[gbase + row];
+    const bool row_live = !(Pm == 0.0f);
+    const bool wave_dead_rows = __any(!row_live);
+
+    f32x16 ore[D / 32], oim[D / 32];
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+            ore[db][r] = 0.f;
+            oim[db][r] = 0.f;
+        }
+    float M = -INFINITY;  // running max of live logits (log2 units), same in both halves
+    float z = 0.f;        // this lane's share of the normaliser
+
+    // logits of one S^T block: x = S * c (qk = 0 never forms the product)
+    auto logits = [&](int kb, float (&x)[16]) {
+        if (A.qk_zero) {
+#pragma unroll
+            for (int r = 0; r < 16; ++r) x[r] = 0.f;
+        } else {
+            const f32x16 s = s_block<F32, D>(smem, kb, qi, h, qf);
+            {
+#pragma clang fp contract(off)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) x[r] = s[r] * A.c;
+            }
+        }
+    };
+    // online max over the block; rescales O and z when it grows; returns the
+    // shift to subtract (0 while a row has no live entry yet)
+    auto update_max = [&](const float (&x)[16]) -> float {
+        float t = x[0];
+#pragma unroll
+        for (int r = 1; r < 16; ++r) t = fmaxf(t, x[r]);
+        t = fmaxf(t, __shfl_xor(t, 32));
+        const float Mn = fmaxf(M, t);
+        const bool need = (Mn > M) && (M != -INFINITY);
+        if (__any(need)) {
+            const float alpha = need ? __builtin_amdgcn_exp2f(M - Mn) : 1.0f;
+#pragma unroll
+            for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    ore[db][r] *= alpha;
+                    oim[db][r] *= alpha;
+                }
+            z *= alpha;
+        }
+        M = Mn;
+        return (Mn == -INFINITY) ? 0.0f : Mn;
+    };
+    // exponentials, normaliser and the two W~ V products of one 16-key chunk
+    auto chunk = [&](int kb, int kc, const float (&x)[16], float msub, const float (&fre)[8],
+                     const float (&fim)[8], const float (&fm)[8]) {
+        float wre[8], wim[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            float ex;
+            {
+#pragma clang fp contract(off)
+                ex = __builtin_amdgcn_exp2f(x[8 * kc + e] - msub);
+            }
+            z += ex * fm[e];
+            wre[e] = ex * fre[e];
+            wim[e] = ex * fim[e];
+        }
+        pv_chunk<F32, D>(smem, kb, kc, qi, h, wre, wim, ore, oim);
+    };
+
+    // ---- key tiles wholly before the query tile, last to first ----------
+    double Cre = 1.0, Cim = 0.0, Cm = 1.0;  // gates between the tile's end and i0
+    const int64_t t_first = i0 / BK - 1;
+    uint32_t tiles_done = 0;
+    for (int64_t t = t_first; t >= 0; --t) {
+        // every earlier key is dead once the carried modulus is 0 in float32
+        if ((float)Cm == 0.0f) break;
+        ++tiles_done;
+        __syncthreads();
+        stage_tile<F32, D>(A, smem, bh, t, false);
+        if (tid < BK) {
+            const int64_t pos = gbase + t * BK + tid;
+            const double sre = A.s_re[pos], sim = A.s_im[pos], sm = A.s_m[pos];
+            const int slot = perm64(tid);
+            Tre[slot] = (float)(Cre * sre - Cim * sim);
+            Tim[slot] = (float)(Cre * sim + Cim * sre);
+            const float rt = (float)(Cm * sm);
+            Tm[slot] = rt;
+            const uint64_t dead = __ballot(rt == 0.0f);
+            if (tid == 0) {
+                misc[0] = (uint32_t)(dead & 0xFFFFFFFFull) != 0u;
+                misc[1] = (uint32_t)(dead >> 32) != 0u;
+            }
+        }
+        __syncthreads();
+#pragma unroll
+        for (int blk = 0; blk < 2; ++blk) {
+            const int kb = 32 * blk;
+            float x[16];
+            logits(kb, x);
+            const bool masked = wave_dead_rows || misc[blk] != 0u;
+            if (masked) {
+#pragma unroll
+                for (int kc = 0; kc < 2; ++kc)
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) {
+                        const float rt = Tm[kb + 16 * kc + 8 * h + e];
+                        const int r = 8 * kc + e;
+                        x[r] = (rt > 0.0f && row_live) ? x[r] : -INFINITY;
+                    }
+            }
+            const float msub = update_max(x);
+#pragma unroll
+            for (int kc = 0; kc < 2; ++kc) {
+                float fre[8], fim[8], fm[8];
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    const int slot = kb + 16 * kc + 8 * h + e;
+                    fre[e] = Tre[slot];
+                    fim[e] = Tim[slot];
+                    fm[e] = Tm[slot];
+                }
+                chunk(kb, kc, x, msub, fre, fim, fm);
+            }
+        }
+        // carry: C <- A_t C
+        const int64_t tp = bh * A.n_kt + t;
+        const double are = A.t_re[tp], aim = A.t_im[tp], am = A.t_m[tp];
+        const double nr = are * Cre - aim * Cim, ni = are * Cim + aim * Cre;
+        Cre = nr;
+        Cim = ni;
+        Cm = am * Cm;
+    }
+
+    // rotate the off-diagonal part by the row's prefix product P_i
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+            const float xr = ore[db][r], xi = oim[db][r];
+            ore[db][r] = Pre * xr - Pim * xi;
+            oim[db][r] = Pre * xi + Pim * xr;
+        }
+    z *= Pm;
+
+    // ---- the query tile's own keys: explicit G_ij, last key first --------
+    float gre = 0.f, gim = 0.f, gm = 0.f;  // running G_{row, j}, R_{row, j}
+    uint32_t kbits = 0;
+    for (int dt = BQ / BK - 1; dt >= 0; --dt) {
+        const int64_t t = i0 / BK + dt;
+        __syncthreads();
+        kbits = max(kbits, stage_tile<F32, D>(A, smem, bh, t, false));
+        if (tid < BK) {
+            const int64_t pos = t * BK + 1 + tid;  // a_{j+1} for key j = t*BK + tid
+            const bool ok = pos < A.n;
+            Dre[tid] = ok ? A.a_re[gbase + pos] : 1.0f;
+            Dim[tid] = ok ? A.a_im[gbase + pos] : 0.0f;
+            Dm[tid] = ok ? A.a_m[gbase + pos] : 1.0f;
+        }
+        __syncthreads();
+#pragma unroll
+        for (int blk = 1; blk >= 0; --blk) {
+            const int cidx = (BK / 32) * dt + blk;  // 32-key block index inside the query tile
+            if (cidx > w) continue;                   // wholly above this wave's rows
+            const int kb = 32 * blk;
+            const int64_t j0 = t * BK + kb;
+            float Gre[16], Gim[16], Gm[16];
+#pragma unroll
+            for (int jj = 31; jj >= 0; --jj) {
+                const int64_t j = j0 + jj;
+                const float dr = Dre[kb + jj], di = Dim[kb + jj], dm = Dm[kb + jj];
+                const float nr = gre * dr - gim * di;
+                const float ni = gre * di + gim * dr;
+                const float nm = gm * dm;
+                const bool diag = (j == row);
+                gre = diag ? 1.0f : nr;
+                gim = diag ? 0.0f : ni;
+                gm = diag ? 1.0f : nm;
+                const int r = 4 * (jj >> 3) + (jj & 3);
+                if (h == ((jj >> 2) & 1)) {
+                    Gre[r] = gre;
+                    Gim[r] = gim;
+                    Gm[r] = gm;
+                }
+            }
+            float x[16];
+            logits(kb, x);
+#pragma unroll
+            for (int r = 0; r < 16; ++r) x[r] = (Gm[r] > 0.0f) ? x[r] : -INFINITY;
+            const float msub = update_max(x);
+#pragma unroll
+            for (int kc = 0; kc < 2; ++kc) {
+                float fre[8], fim[8], fm[8];
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    fre[e] = Gre[8 * kc + e];
+                    fim[e] = Gim[8 * kc + e];
+                    fm[e] = Gm[8 * kc + e];
+                }
+                chunk(kb, kc, x, msub, fre, fim, fm);
+            }
+        }
+    }
+    atomicMax(&misc[3], kbits);
+
+    // ---- epilogue: O *= exp2((1-beta) M) z^-beta -------------------------
+    const float zt = z + __shfl_xor(z, 32);
+    float f;
+    if (A.beta_mode == 1)
+        f = 1.0f / zt;
+    else if (A.beta_mode == 0)
+        f = exp2f(M);
+    else
+        f = exp2f(A.one_minus_beta * M - A.beta * log2f(zt));
+    if (row_ok) {
+        float *orp = A.o_re + (bh * A.n + row) * D;
+        float *oip = A.o_im + (bh * A.n + row) * D;
+#pragma unroll
+        for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+            for (int g4 = 0; g4 < 4; ++g4) {
+                const int d0 = 32 * db + 8 * g4 + 4 * h;
+                float4 vr, vi;
+                vr.x = ore[db][4 * g4 + 0] * f;
+                vr.y = ore[db][4 * g4 + 1] * f;
+                vr.z = ore[db][4 * g4 + 2] * f;
+                vr.w = ore[db][4 * g4 + 3] * f;
+                vi.x = oim[db][4 * g4 + 0] * f;
+                vi.y = oim[db][4 * g4 + 1] * f;
+                vi.z = oim[db][4 * g4 + 2] * f;
+                vi.w = oim[db][4 * g4 + 3] * f;
+                *reinterpret_cast<float4 *>(orp + d0) = vr;
+                *reinterpret_cast<float4 *>(oip + d0) = vi;
+            }
+    }
+    __syncthreads();
+    if (tid == 0) {
+        const uint32_t qb = misc[2], kb = misc[3];
+        A.qstat[bh * A.n_qt + qt] = qb;
+        A.kstat[bh * A.n_qt + qt] = kb;
+        if (qb >= kInfBits || kb >= kInfBits) A.status[0] = kNonFinite;
+        atomicAdd(&A.counters[0], tiles_done);
+    }
+}
+
+// --------------------------------------------------------------------------
+// Refusal of an overflowing logit (section "Evaluation and refusals").  The
+// extrema of |q| and |k| that fwd_kernel recorded bound every logit by
+// |c| d max|q| max|k|; only a head where that bound reaches the float32 range
+// recomputes its logits (with the same MFMA code and scale as fwd_kernel) and
+// checks every j <= i.
+template <bool F32, int D>
+__global__ __launch_bounds__(NTHREADS) void logit_check_kernel(FwdArgs A) {
+    using FR = Frag<F32, D>;
+    extern __shared__ __align__(16) unsigned char smem[];
+    __shared__ int go;
+    const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, h = lane >> 5, qi = lane & 31;
+    const int L = blockIdx.x;
+    const int64_t qt = A.n_qt - 1 - L / A.BH;
+    const int64_t bh = L % A.BH;
+    if (tid == 0) {
+        uint32_t qm = 0, km = 0;
+        for (int t = 0; t < A.n_qt; ++t) {
+            qm = max(qm, A.qstat[bh * A.n_qt + t]);
+            km = max(km, A.kstat[bh * A.n_qt + t]);
+        }
+        const double bound = fabs((double)A.c) * (double)D * (double)__uint_as_float(qm) *
+                             (double)__uint_as_float(km) * 1.01;
+        go = !(bound < 3.0e38);
+    }
+    __syncthreads();
+    if (!go) return;
+    const int64_t i0 = qt * BQ;
+    const int64_t row = i0 + 32 * w + qi;
+    const bool row_ok = row < A.n;
+    typename FR::type qf[FR::count];
+    load_q<F32, D>(A, bh, row, row_ok, h, qf);
+    bool bad = false;
+    for (int64_t t = 0; t < (i0 + BQ) / BK; ++t) {
+        __syncthreads();
+        stage_tile<F32, D>(A, smem, bh, t, true);
+        __syncthreads();
+#pragma unroll
+        for (int blk = 0; blk < 2; ++blk) {
+            const f32x16 s = s_block<F32, D>(smem, 32 * blk, qi, h, qf);
+            {
+#pragma clang fp contract(off)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    const int64_t j = t * BK + 32 * blk + 8 * (r / 4) + 4 * h + (r % 4);
+                    const float x = s[r] * A.c;
+                    if (row_ok && j <= row && !isfinite(x)) bad = true;
+                }
+            }
+        }
+    }
+    if (__any(bad) && lane == 0) A.status[0] = kNonFinite;
+}
+
+template <bool F32, int D>
+int launch_typed(const Problem &P, hipStream_t st, hipEvent_t const *marks) {
+    using SM = Smem<F32, D>;
+    const Layout &L = P.L;
+    unsigned char *ws = P.ws;
+    uint32_t *counters = reinterpret_cast<uint32_t *>(ws + L.counters);
+    if (marks) (void)hipEventRecord(marks[0], st);
+    auto fptr = [&](int i) { return reinterpret_cast<float *>(ws + L.gate[i]); };
+    auto dptr = [&](int i) { return reinterpret_cast<double *>(ws + L.tile[i]); };
+    const int BH = (int)L.BH;
+
+    if constexpr (!F32) {
+        uint16_t *vt = reinterpret_cast<uint16_t *>(ws + L.vt);
+        if (P.v_f32)
+            hipLaunchKernelGGL((vt_kernel<D, true>), dim3(BH * L.n_kt), dim3(256), 0, st, P.v, vt,
+                               L.n, L.n_pad, (int)L.n_kt, P.status, counters);
+        else
+            hipLaunchKernelGGL((vt_kernel<D, false>), dim3(BH * L.n_kt), dim3(256), 0, st, P.v, vt,
+                               L.n, L.n_pad, (int)L.n_kt, P.status, counters);
+    } else {
+        hipLaunchKernelGGL(clear_status_kernel, dim3(1), dim3(64), 0, st, P.status, counters);
+    }
+
+    GatesArgs G;
+    G.u = P.u;
+    G.theta = P.theta;
+    G.g = P.g;
+    G.n = L.n;
+    G.n_pad = L.n_pad;
+    G.n_qt = (int)L.n_qt;
+    G.n_kt = (int)L.n_kt;
+    G.a_re = fptr(0);
+    G.a_im = fptr(1);
+    G.a_m = fptr(2);
+    G.s_re = fptr(3);
+    G.s_im = fptr(4);
+    G.s_m = fptr(5);
+    G.p_re = fptr(6);
+    G.p_im = fptr(7);
+    G.p_m = fptr(8);
+    G.t_re = dptr(0);
+    G.t_im = dptr(1);
+    G.t_m = dptr(2);
+    G.status = P.status;
+    hipLaunchKernelGGL(gates_kernel, dim3(BH * L.n_qt), dim3(64), 0, st, G);
+
+    FwdArgs F;
+    F.q = P.q;
+    F.k = P.k;
+    F.v = P.v;
+    F.vt = reinterpret_cast<const uint16_t *>(ws + L.vt);
+    F.a_re = G.a_re;
+    F.a_im = G.a_im;
+    F.a_m = G.a_m;
+    F.s_re = G.s_re;
+    F.s_im = G.s_im;
+    F.s_m = G.s_m;
+    F.p_re = G.p_re;
+    F.p_im = G.p_im;
+    F.p_m = G.p_m;
+    F.t_re = G.t_re;
+    F.t_im = G.t_im;
+    F.t_m = G.t_m;
+    F.o_re = P.o_re;
+    F.o_im = P.o_im;
+    F.qstat = reinterpret_cast<uint32_t *>(ws + L.qstat);
+    F.kstat = reinterpret_cast<uint32_t *>(ws + L.kstat);
+    F.counters = counters;
+    F.status = P.status;
+    F.n = L.n;
+    F.n_pad = L.n_pad;
+    F.n_qt = (int)L.n_qt;
+    F.n_kt = (int)L.n_kt;
+    F.BH = BH;
+    F.c = P.c;
+    F.beta = P.beta;
+    F.one_minus_beta = 1.0f - P.beta;
+    F.beta_mode = P.beta_mode;
+    F.qk_zero = P.qk_zero ? 1 : 0;
+    const size_t shm = SM::bytes;
+    if (shm > 65536) {
+        (void)hipFuncSetAttribute(reinterpret_cast<const void *>(&fwd_kernel<F32, D>),
+                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)shm);
+        (void)hipFuncSetAttribute(reinterpret_cast<const void *>(&logit_check_kernel<F32, D>),
+                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)shm);
+    }
+    if (marks) (void)hipEventRecord(marks[1], st);
+    hipLaunchKernelGGL((fwd_kernel<F32, D>), dim3(BH * L.n_qt), dim3(NTHREADS), shm, st, F);
+    if (marks) (void)hipEventRecord(marks[2], st);
+    if (!P.qk_zero)
+        hipLaunchKernelGGL((logit_check_kernel<F32, D>), dim3(BH * L.n_qt), dim3(NTHREADS), shm,
+                           st, F);
+    if (marks) (void)hipEventRecord(marks[3], st);
+    return (int)hipGetLastError();
+}
+
+}  // namespace
+
+int launch_forward(const Problem &P, void *stream, void *const *marks) {
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    hipEvent_t const *ev = reinterpret_cast<hipEvent_t const *>(marks);
+    const bool f32 = !P.L.bf16_path;
+    if (P.L.d == 64)
+        return f32 ? launch_typed<true, 64>(P, st, ev) : launch_typed<false, 64>(P, st, ev);
+    return f32 ? launch_typed<true, 128>(P, st, ev) : launch_typed<false, 128>(P, st, ev);
+}
+
+}  // namespace resolvent

@@ -1,0 +1,144 @@
+/*
+ * resolvent.h -- C ABI of the MI355X (gfx950) forward pass of the resolvent
+ * operator head.
+ *
+ * The operation is the one the "Resolvent Operator" page (teerth.dev,
+ * Aether-Lang/integrated/resolvent) defines in its section "Object".  For one
+ * causal head of length n, with queries and keys q_i, k_j in R^d, raw gate
+ * magnitudes u_k, phases theta_k, real values V_j and switches (beta, qk, g):
+ *
+ *   s_ij  = <q_i, k_j> / sqrt(d)                      scaled logit
+ *   m_k   = clamp(lerp(1, u_k, g), 0, 1), theta'_k = g theta_k
+ *   a_k   = m_k e^{i theta'_k}                        the gate
+ *   G_ij  = prod_{k=j+1..i} a_k, G_ii = 1             the path product
+ *   R_ij  = prod_{k=j+1..i} m_k = |G_ij|
+ *   Z_i   = sum_{j<=i} R_ij e^{qk s_ij}               the row normaliser
+ *   W_ij  = G_ij e^{qk s_ij} / Z_i^beta  (j <= i),  0 (j > i)
+ *   O_i   = sum_{j<=i} W_ij V_j                       complex readout
+ *
+ * Z_i^beta is evaluated in the log domain with a shift by the largest live
+ * logit (live: R_ij > 0), as in the page's section "Evaluation and refusals".
+ * The corners are softmax attention (1,1,0), the unnormalised exponential
+ * kernel (0,1,0) and the gated-chain path product (0,0,1) (section "The three
+ * corners").  G is formed only as a product of gates -- never through a
+ * logarithm or a division -- so a closed gate (m_k = 0) gives exact zeros
+ * (Lean table, no_prefix_scan_represents_a_zero_gate and pathProd_eq_zero_iff).
+ *
+ * Everything runs on the device, asynchronously, on the caller's stream.  The
+ * library allocates nothing, keeps no state between calls and is thread-safe;
+ * the caller owns every buffer.
+ */
+#ifndef RESOLVENT_H
+#define RESOLVENT_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Status codes: the return value of every call and the device status word. */
+enum resolvent_status {
+    RESOLVENT_OK = 0,
+    RESOLVENT_NONFINITE = 1,   /* refused input ("Evaluation and refusals")  */
+    RESOLVENT_BAD_SHAPE = 2,   /* negative size, or head_dim 0 with n > 0     */
+    RESOLVENT_BAD_ARG = 3,     /* null/misaligned pointer, small workspace    */
+    RESOLVENT_UNSUPPORTED = 4, /* head_dim or dtype pair this build lacks     */
+    RESOLVENT_DEVICE_ERROR = 5 /* a HIP launch failed                         */
+};
+
+/* Storage types of q, k and v. */
+enum resolvent_dtype { RESOLVENT_BF16 = 0, RESOLVENT_F32 = 1 };
+
+/*
+ * resolvent_workspace_bytes -- device workspace that resolvent_forward needs
+ * for this shape and these storage types (0 for an empty problem, and also 0
+ * for an invalid or unsupported one, which resolvent_forward rejects).
+ * The workspace holds the gates, their in-tile scans, the tile products, the
+ * per-tile extrema of q and k and, on the bf16 path, a transposed bf16 copy of
+ * v.  Its contents are scratch between calls.
+ */
+size_t resolvent_workspace_bytes(int64_t B, int64_t H, int64_t n, int64_t d,
+                                 int32_t qk_dtype, int32_t v_dtype);
+
+/*
+ * resolvent_forward -- O = readout of the resolvent head for B*H independent
+ * heads (section "Object" of the page; the Rust API's operator + readout with
+ * value_dim = head_dim).
+ *
+ * Arguments (all device pointers; 16-byte aligned; contiguous row-major):
+ *   q, k        [B, H, n, d] in qk_dtype (RESOLVENT_BF16 or RESOLVENT_F32)
+ *   u, theta    [B, H, n] float32: raw gate magnitudes and phases; u_0 and
+ *               theta_0 are checked although a_0 is never read
+ *   v           [B, H, n, d] in v_dtype
+ *   beta,qk,g   the switches, as the page's Switches (f64)
+ *   d           head_dim; this build supports d = 64 and d = 128
+ *   o_re, o_im  [B, H, n, d] float32 outputs (real and imaginary planes)
+ *   workspace   at least resolvent_workspace_bytes(...) bytes of device memory
+ *   status_dev  one int32 of device memory: the call sets it to RESOLVENT_OK
+ *               and the kernels set it to RESOLVENT_NONFINITE when they refuse
+ *               an input; read it after synchronising the stream
+ *   stream      HIP stream to enqueue on (NULL: the null stream)
+ *
+ * Dtype pairs: (BF16, BF16) and (BF16, F32) run the bf16 MFMA path (an fp32 v
+ * is rounded to bf16 when it is staged); (F32, F32) runs the fp32 MFMA path.
+ *
+ * Returns, before anything is enqueued:
+ *   RESOLVENT_BAD_SHAPE   a negative size; d == 0 with n, B, H > 0
+ *   RESOLVENT_OK          n == 0, B == 0 or H == 0 ("empty in, empty out"):
+ *                         nothing is enqueued and nothing is written
+ *   RESOLVENT_NONFINITE   a non-finite switch, or qk*log2(e)/sqrt(d) not
+ *                         representable in float32
+ *   RESOLVENT_UNSUPPORTED another d or dtype pair
+ *   RESOLVENT_BAD_ARG     a null or misaligned pointer, a small workspace
+ *   RESOLVENT_DEVICE_ERROR a launch failed (status_dev is then unspecified)
+ * and RESOLVENT_OK once the work is enqueued.  On the device the status word
+ * becomes RESOLVENT_NONFINITE for a non-finite q, k, u or theta, an
+ * overflowing g*theta_k (evaluated in f64) or a logit qk*s_ij (j <= i) whose
+ * float32 value overflows; the outputs are then unspecified.  A non-finite v
+ * is not refused (the page refuses operator inputs only) and leaves the
+ * outputs unspecified.  Outside beta = 1, a readout whose true value exceeds
+ * the float32 range is unspecified.
+ */
+int32_t resolvent_forward(const void *q, const void *k, const float *u, const float *theta,
+                          const void *v, double beta, double qk, double g, int64_t B,
+                          int64_t H, int64_t n, int64_t d, int32_t qk_dtype, int32_t v_dtype,
+                          float *o_re, float *o_im, void *workspace, size_t workspace_bytes,
+                          int32_t *status_dev, hipStream_t stream);
+
+/*
+ * resolvent_forward_marked -- resolvent_forward, plus measurement marks: when
+ * marks is not NULL it points to four HIP events (created by the caller, with
+ * timing enabled) that are recorded on the stream before the first kernel,
+ * right before and right after the fused forward kernel, and after the last
+ * kernel, so hipEventElapsedTime brackets each stage.  Same arguments,
+ * checks and return codes as resolvent_forward otherwise.
+ */
+int32_t resolvent_forward_marked(const void *q, const void *k, const float *u,
+                                 const float *theta, const void *v, double beta, double qk,
+                                 double g, int64_t B, int64_t H, int64_t n, int64_t d,
+                                 int32_t qk_dtype, int32_t v_dtype, float *o_re, float *o_im,
+                                 void *workspace, size_t workspace_bytes, int32_t *status_dev,
+                                 hipStream_t stream, hipEvent_t *marks);
+
+/*
+ * resolvent_counters_offset -- byte offset inside the workspace of two uint32
+ * counters that a call leaves behind: [0] the number of (query tile, key tile)
+ * pairs before the diagonal that the fused kernel evaluated (it stops early
+ * once every earlier path product is exactly 0 in float32), [1] reserved.
+ * SIZE_MAX when resolvent_workspace_bytes would return 0.
+ */
+size_t resolvent_counters_offset(int64_t B, int64_t H, int64_t n, int64_t d, int32_t qk_dtype,
+                                 int32_t v_dtype);
+
+/* resolvent_status_str -- a static, human-readable name of a status code. */
+const char *resolvent_status_str(int32_t status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* RESOLVENT_H */

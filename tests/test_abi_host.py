@@ -1,0 +1,94 @@
+"""The C-ABI library loads without a GPU, exports every entry point that
+include/*.h declares, and rejects bad arguments on the host before any HIP
+call (so no compute runs here)."""
+import glob
+import os
+import re
+
+import pytest
+
+from gated_causal_attention_amd import binding
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+S = binding.Status
+FAKE = 1 << 20  # a non-null, aligned address; never dereferenced by these calls
+
+
+def declared_functions():
+    names = []
+    for h in glob.glob(os.path.join(ROOT, "include", "*.h")):
+        text = open(h).read()
+        text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+        names += re.findall(r"\b([a-z_][a-z0-9_]*)\s*\(", text)
+    return sorted({n for n in names if n.startswith("resolvent_")})
+
+
+def test_library_exports_every_declared_symbol():
+    lib = binding._load()
+    names = declared_functions()
+    assert "resolvent_forward" in names and len(names) >= 3
+    for name in names:
+        assert hasattr(lib, name), name
+
+
+def call(B=1, H=1, n=128, d=64, beta=1.0, qk=1.0, g=1.0, qdt=0, vdt=0, ws_bytes=None,
+         ptr=FAKE, ws=FAKE, status=FAKE):
+    lib = binding._load()
+    if ws_bytes is None:
+        ws_bytes = lib.resolvent_workspace_bytes(max(B, 1), max(H, 1), max(n, 1), max(d, 64),
+                                                 qdt, vdt)
+    return lib.resolvent_forward(ptr, ptr, ptr, ptr, ptr, beta, qk, g, B, H, n, d, qdt, vdt, ptr,
+                                 ptr, ws, ws_bytes, status, None)
+
+
+def test_shapes_and_empty():
+    assert call(B=-1) == S.BAD_SHAPE
+    assert call(n=-5) == S.BAD_SHAPE
+    assert call(d=-1) == S.BAD_SHAPE
+    assert call(n=0) == S.OK  # empty in, empty out: nothing enqueued
+    assert call(B=0) == S.OK
+    assert call(H=0, ptr=None) == S.OK
+    assert call(d=0) == S.BAD_SHAPE  # head_dim = 0 with n > 0
+
+
+def test_non_finite_switches():
+    for bad in (float("nan"), float("inf"), -float("inf")):
+        assert call(beta=bad) == S.NONFINITE
+        assert call(qk=bad) == S.NONFINITE
+        assert call(g=bad) == S.NONFINITE
+    assert call(qk=1e300) == S.NONFINITE  # the float32 logit scale overflows
+
+
+def test_unsupported():
+    assert call(d=96) == S.UNSUPPORTED
+    assert call(d=256) == S.UNSUPPORTED
+    assert call(qdt=1, vdt=0) == S.UNSUPPORTED
+    assert call(qdt=7) == S.UNSUPPORTED
+
+
+def test_bad_pointers_and_workspace():
+    assert call(ptr=None) == S.BAD_ARG
+    assert call(ws=None) == S.BAD_ARG
+    assert call(status=None) == S.BAD_ARG
+    assert call(ptr=FAKE + 2) == S.BAD_ARG  # misaligned
+    assert call(ws=FAKE + 16) == S.BAD_ARG
+    assert call(ws_bytes=100) == S.BAD_ARG
+
+
+def test_workspace_sizes():
+    ws = binding.resolvent_workspace_bytes
+    assert ws(0, 1, 10, 64) == 0 and ws(1, 1, 0, 64) == 0
+    assert ws(1, 1, 10, 96) == 0
+    a, b = ws(1, 1, 128, 64), ws(1, 1, 129, 64)
+    assert 0 < a < b
+    assert ws(1, 1, 128, 64, 1, 1) < a  # the fp32 path keeps no v^T copy
+    off = binding.resolvent_counters_offset(4, 16, 8192, 128)
+    assert 0 < off < ws(4, 16, 8192, 128)
+    assert binding.resolvent_counters_offset(1, 1, 0, 64) == 2 ** 64 - 1
+
+
+def test_status_strings():
+    for s in S:
+        text = binding.resolvent_status_str(int(s))
+        assert text and text != "unknown status"
+    assert binding.resolvent_status_str(99) == "unknown status"

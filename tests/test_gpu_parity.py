@@ -1,0 +1,282 @@
+"""Parity of the HIP path (through the C ABI) with the fp64 oracle.
+
+Tolerances are the workloads' own: max |dO| / (max |O| + 1e-6) <= 2e-2 with
+bf16 q,k and <= 1e-4 on the fp32 path.  Small shapes are compared in full
+(several query tiles and a ragged tail); the full-size workloads are compared
+on sampled rows of sampled heads, run in the launch configuration bench.py
+times.  The bitwise tests restate invariants of the "Resolvent Operator" page
+(teerth.dev, Aether-Lang/integrated/resolvent, section "Test evidence") on
+the device.
+"""
+import numpy as np
+import pytest
+import torch
+
+from gated_causal_attention_amd import binding, inputs
+from tests import gpu_util as gu
+
+pytestmark = [pytest.mark.gpu,
+              pytest.mark.skipif(not torch.cuda.is_available(), reason="needs a GPU")]
+
+DEV = "cuda:0"
+
+
+def announce(*a):
+    print("case:", *a, flush=True)
+
+
+# ------------------------------------------------------------ small, in full
+@pytest.mark.parametrize("sw", inputs.CONFIGS[1].switches)
+def test_workload1_fp32_corners(sw):
+    announce("workload 1", sw)
+    inp = inputs.make_config(1, switches=sw)
+    got = gu.gpu_forward(inp, sw)
+    err = gu.compare_full(inp, sw, got)
+    print(f"  rel err {err:.3e}")
+    assert err <= gu.TOL_F32
+
+
+@pytest.mark.parametrize("n", [1, 2, 31, 33, 64, 65, 127, 128, 129, 200, 257, 383, 520])
+@pytest.mark.parametrize("d,qk_dtype,v_dtype", [(64, "bf16", "bf16"), (128, "bf16", "bf16"),
+                                                 (64, "bf16", "f32"), (64, "f32", "f32"),
+                                                 (128, "f32", "f32")])
+def test_ragged_lengths(n, d, qk_dtype, v_dtype):
+    rng = np.random.default_rng(n * 7 + d)
+    sws = [(1, 1, 1), (0.5, 0.7, 0.5), (0, 1, 0), (0, 0, 1), (1, -0.8, 0.9)]
+    sw = sws[int(rng.integers(0, len(sws)))]
+    announce("ragged", n, d, qk_dtype, v_dtype, sw)
+    inp = inputs.draw(2, 2, n, d, seed=1000 + n, qk_dtype=qk_dtype, v_dtype=v_dtype,
+                      qk_scale=0.5 if sw == (0, 1, 0) else 1.0, u_range=(0.3, 1.0),
+                      theta_range=(-2.0, 2.0))
+    got = gu.gpu_forward(inp, sw)
+    err = gu.compare_full(inp, sw, got)
+    print(f"  rel err {err:.3e}")
+    assert err <= gu.tol_for(inp)
+
+
+@pytest.mark.parametrize("sw", [(1, 1, 1), (0.5, 0.7, 0.5), (0, 1, 0), (0, 0, 1), (1, 1, 0),
+                                (0, 0, 0), (1.5, 0.3, 1.3), (0.25, -1.0, 0.7)])
+def test_switch_grid_multi_tile(sw):
+    announce("switch grid", sw)
+    inp = inputs.draw(1, 3, 700, 128, seed=77, qk_scale=0.5, u_range=(0.6, 1.0),
+                      theta_range=(-1.0, 1.0))
+    got = gu.gpu_forward(inp, sw)
+    err = gu.compare_full(inp, sw, got)
+    print(f"  rel err {err:.3e}")
+    assert err <= gu.TOL_BF16
+
+
+def test_workload2_full():
+    for sw in inputs.CONFIGS[2].switches:
+        announce("workload 2", sw)
+        inp = inputs.make_config(2)
+        got = gu.gpu_forward(inp, sw)
+        rng = np.random.default_rng(2)
+        err_full = gu.compare_sampled(inp, sw, got, [(0, 0), (1, 7)], np.arange(inp["n"]))
+        rows = gu.sample_rows(inp["n"], rng)
+        heads = [(b, h) for b in range(2) for h in range(8)]
+        err_s = gu.compare_sampled(inp, sw, got, heads, rows)
+        print(f"  rel err full heads {err_full:.3e}, sampled {err_s:.3e}")
+        assert max(err_full, err_s) <= gu.TOL_BF16
+
+
+# ---------------------------------------------------- full size, sampled rows
+def test_workload3_headline():
+    announce("workload 3 (headline)")
+    inp = inputs.make_config(3)
+    sw = (1, 1, 1)
+    got = gu.gpu_forward(inp, sw)
+    assert np.all(np.isfinite(got))
+    rng = np.random.default_rng(3)
+    heads = [(0, 0), (3, 15), (1, 7), (2, 3)]
+    err = gu.compare_sampled(inp, sw, got, heads, gu.sample_rows(inp["n"], rng))
+    print(f"  rel err {err:.3e}")
+    assert err <= gu.TOL_BF16
+
+
+def test_workload4_zero_gates():
+    announce("workload 4 (bedM gates)")
+    inp = inputs.make_config(4)
+    sw = (1, 1, 1)
+    got = gu.gpu_forward(inp, sw)
+    assert np.all(np.isfinite(got))
+    rng = np.random.default_rng(4)
+    heads = [(0, 0), (0, 9), (0, 15)]
+    err = gu.compare_sampled(inp, sw, got, heads, gu.sample_rows(inp["n"], rng, extra=32))
+    print(f"  rel err {err:.3e}")
+    assert err <= gu.TOL_BF16
+
+
+def test_workload5_switch_sweep():
+    inp = inputs.make_config(5)
+    t = inputs.as_torch(inp, DEV)
+    rng = np.random.default_rng(5)
+    heads = [(0, 0), (7, 31), (3, 12)]
+    rows = gu.sample_rows(inp["n"], rng, extra=12)
+    for sw in inputs.CONFIGS[5].switches:
+        announce("workload 5", sw)
+        o_re, o_im = binding.resolvent_forward(t["q"], t["k"], t["u"], t["theta"], t["v"], *sw)
+        got = o_re.double().cpu().numpy() + 1j * o_im.double().cpu().numpy()
+        err = gu.compare_sampled(inp, sw, got, heads, rows)
+        print(f"  rel err {err:.3e}")
+        assert err <= gu.TOL_BF16, sw
+
+
+# --------------------------------------------------------- bitwise invariants
+def test_bare_row_is_i_plus_one_bitwise():
+    """beta_alone_decides_row_stochasticity: at (0,0,0) row i of a ones
+    channel reads exactly i + 1."""
+    for qk_dtype, n in (("bf16", 1000), ("f32", 300)):
+        inp = inputs.draw(1, 2, n, 64, seed=9, qk_dtype=qk_dtype, v_dtype=qk_dtype)
+        inp["v"][:] = 1.0
+        got = gu.gpu_forward(inp, (0, 0, 0))
+        want = np.arange(1, n + 1, dtype=np.float64)[None, :, None]
+        assert np.array_equal(got.real[0], np.broadcast_to(want, (2, n, 64))[:]), qk_dtype
+        assert np.all(got.imag == 0)
+
+
+def test_closed_gates_leave_identity():
+    """an_empty_sequence_is_empty_and_no_row_is_ever_all_masked: all gates
+    closed at beta = 1 gives W = I, so O = V bitwise (the one live logit of a
+    row is its own maximum, so its weight is exactly 1)."""
+    for qk_dtype in ("bf16", "f32"):
+        inp = inputs.draw(2, 2, 333, 128, seed=11, qk_dtype=qk_dtype, v_dtype=qk_dtype)
+        inp["u"][:] = 0.0
+        got = gu.gpu_forward(inp, (1, 0, 1))
+        assert np.array_equal(got.real, inp["v"].astype(np.float64))
+        assert np.all(got.imag == 0)
+        got = gu.gpu_forward(inp, (1, 1, 1))
+        assert np.array_equal(got.real, inp["v"].astype(np.float64))
+        assert np.all(got.imag == 0)
+
+
+def test_causality_bitwise():
+    """perturbing_the_future_never_moves_the_past: rows <= t are bitwise
+    unchanged when q, k, v, u, theta change after t."""
+    n, t = 900, 437
+    for sw in [(1, 1, 1), (0.5, 0.7, 0.5), (0, 0, 1)]:
+        inp = inputs.draw(1, 2, n, 64, seed=21, u_range=(0.5, 1.0))
+        a = gu.gpu_forward(inp, sw)
+        rng = np.random.default_rng(22)
+        for key in ("q", "k", "v"):
+            inp[key][:, :, t + 1:] = inputs.round_bf16(
+                rng.standard_normal(inp[key][:, :, t + 1:].shape).astype(np.float32))
+        inp["u"][:, :, t + 1:] = rng.uniform(0, 1, inp["u"][:, :, t + 1:].shape)
+        inp["theta"][:, :, t + 1:] = rng.uniform(-3, 3, inp["theta"][:, :, t + 1:].shape)
+        b = gu.gpu_forward(inp, sw)
+        assert np.array_equal(a[:, :, :t + 1], b[:, :, :t + 1]), sw
+
+
+def test_off_switches_bitwise():
+    """an_off_switch_deletes_its_term_exactly: g = 0 makes the output
+    independent of u, theta (and Im O = 0); qk = 0 makes it independent of q,
+    k, even huge ones."""
+    inp = inputs.draw(1, 2, 640, 128, seed=31)
+    a = gu.gpu_forward(inp, (0.5, 0.8, 0))
+    inp2 = dict(inp)
+    rng = np.random.default_rng(32)
+    inp2["u"] = rng.uniform(0, 1, inp["u"].shape).astype(np.float32)
+    inp2["theta"] = rng.uniform(-3, 3, inp["u"].shape).astype(np.float32)
+    b = gu.gpu_forward(inp2, (0.5, 0.8, 0))
+    assert np.array_equal(a, b) and np.all(a.imag == 0)
+    c = gu.gpu_forward(inp, (0.5, 0, 1))
+    inp3 = dict(inp)
+    inp3["q"] = np.full_like(inp["q"], 1e30)
+    inp3["k"] = np.full_like(inp["k"], -3e29)
+    d = gu.gpu_forward(inp3, (0.5, 0, 1))
+    assert np.array_equal(c, d)
+
+
+def test_closed_gate_annihilates_bitwise():
+    """a_closed_gate_annihilates_every_path_through_it_exactly: with m_z = 0,
+    rows >= z do not depend on k, v, u, theta before z."""
+    n, z = 1000, 517
+    for sw in [(1, 1, 1), (0, 1, 1), (0.5, 0.7, 1)]:
+        inp = inputs.draw(1, 2, n, 64, seed=41, u_range=(0.8, 1.0))
+        inp["u"][:, :, z] = 0.0
+        a = gu.gpu_forward(inp, sw)
+        rng = np.random.default_rng(42)
+        for key in ("k", "v"):
+            inp[key][:, :, :z] = inputs.round_bf16(
+                rng.standard_normal(inp[key][:, :, :z].shape).astype(np.float32))
+        inp["u"][:, :, :z] = rng.uniform(0, 1, inp["u"][:, :, :z].shape)
+        inp["theta"][:, :, :z] = rng.uniform(-3, 3, inp["u"][:, :, :z].shape)
+        b = gu.gpu_forward(inp, sw)
+        assert np.array_equal(a[:, :, z:], b[:, :, z:]), sw
+
+
+def test_deterministic():
+    inp = inputs.draw(2, 3, 1500, 128, seed=51, u_range=(0.9, 1.0))
+    a = gu.gpu_forward(inp, (1, 1, 1))
+    b = gu.gpu_forward(inp, (1, 1, 1))
+    assert np.array_equal(a, b)
+
+
+def test_constant_phase_chain_closed_form():
+    """constant_phase_gate_is_rope: unit gates of phase w at (0,0,1) read out a
+    ones channel as the geometric sum (1 - e^{iw(i+1)}) / (1 - e^{iw})."""
+    n, w = 1200, 0.01
+    inp = inputs.draw(1, 1, n, 64, seed=61, qk_dtype="f32", v_dtype="f32")
+    inp["u"][:] = 1.0
+    inp["theta"][:] = np.float32(w)
+    inp["v"][:] = 1.0
+    got = gu.gpu_forward(inp, (0, 0, 1))[0, 0, :, 0]
+    wf = float(np.float32(w))
+    i = np.arange(n)
+    geo = (1 - np.exp(1j * wf * (i + 1))) / (1 - np.exp(1j * wf))
+    assert gu.rel_err(got, geo) <= gu.TOL_F32
+
+
+# ---------------------------------------------------------------- edges
+def test_empty_and_refusals():
+    """Empty in, empty out; device-side refusal of each non-finite input
+    class (section "Evaluation and refusals"), including u_0 and theta_0."""
+    e = torch.empty((1, 2, 0, 64), device=DEV, dtype=torch.bfloat16)
+    eu = torch.empty((1, 2, 0), device=DEV, dtype=torch.float32)
+    o_re, o_im = binding.resolvent_forward(e, e, eu, eu, e, 1, 1, 1)
+    assert o_re.shape == (1, 2, 0, 64)
+    base = inputs.draw(1, 2, 300, 64, seed=71)
+    for key, pos in (("q", 5), ("k", 299), ("u", 0), ("theta", 0), ("u", 150), ("theta", 77)):
+        for bad in (np.nan, np.inf):
+            inp = {kk: (vv.copy() if isinstance(vv, np.ndarray) else vv) for kk, vv in base.items()}
+            arr = inp[key]
+            if arr.ndim == 4:
+                arr[0, 1, pos, 3] = bad
+            else:
+                arr[0, 1, pos] = bad
+            with pytest.raises(binding.ResolventError) as ei:
+                gu.gpu_forward(inp, (1, 1, 1))
+            assert ei.value.status == binding.Status.NONFINITE, (key, pos, bad)
+    with pytest.raises(binding.ResolventError) as ei:
+        inp = dict(base)
+        inp["theta"] = np.full_like(base["theta"], 1e10)
+        gu.gpu_forward(inp, (1, 1, 1e300))
+    assert ei.value.status == binding.Status.NONFINITE
+    inp = dict(base)
+    inp["q"] = np.full_like(base["q"], 1e20)
+    inp["k"] = np.full_like(base["k"], 1e20)
+    with pytest.raises(binding.ResolventError) as ei:
+        gu.gpu_forward(inp, (1, 1, 1))
+    assert ei.value.status == binding.Status.NONFINITE
+    gu.gpu_forward(inp, (1, 0, 1))  # qk = 0 accepts the same q, k
+    with pytest.raises(binding.ResolventError) as ei:
+        gu.gpu_forward(base, (float("nan"), 1, 1))
+    assert ei.value.status == binding.Status.NONFINITE
+
+
+def test_large_logits_fp32_beta_one():
+    """logits_of_ten_thousand_stay_finite_at_beta_one on the fp32 path: rows
+    stay finite and match the oracle.  A float32 logit near 1e4 carries an
+    absolute rounding error near 1e-3, so the bound here is the bf16 one."""
+    inp = inputs.draw(1, 1, 256, 64, seed=81, qk_dtype="f32", v_dtype="f32")
+    inp["q"] *= 50.0
+    inp["k"] *= 50.0
+    sw = (1, 1, 0.5)
+    got = gu.gpu_forward(inp, sw)
+    assert np.all(np.isfinite(got))
+    logits = np.einsum("id,jd->ij", inp["q"][0, 0].astype(np.float64),
+                       inp["k"][0, 0].astype(np.float64)) / 8.0
+    assert np.abs(np.tril(logits)).max() > 1e4
+    err = gu.compare_full(inp, sw, got)
+    print(f"  rel err {err:.3e}")
+    assert err <= gu.TOL_BF16
