@@ -1,0 +1,200 @@
+"""Benchmark of the resolvent-head forward pass on one MI355X.
+
+One step is one resolvent_forward call over the headline workload (B=4, H=16,
+n=8192, d=128, bf16 q,k,v, switches (1,1,1)): status clear + v transpose, gate
+scans, the fused forward kernel and the logit-overflow check, with the inputs
+already resident in HBM.  Prints one JSON line (see the design doc for every field).
+
+  python bench.py [--steps K] [--warmup W] [--gpus 1] [--no-cpu-baseline]
+  python bench.py --copy-bytes N   # a plain copy kernel, for counter calibration
+"""
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2516.6  # MI355X dense bf16 MFMA: 256 CU x 4096 FLOP/clk x 2.4 GHz
+PEAK_HBM_GBS = 8000.0
+BQ, BK = 128, 64  # the library's query and key tiles
+KERNEL_SOURCE = os.path.join(ROOT, "gated_causal_attention_amd", "csrc", "resolvent_kernels.hip")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "fwd_kernel_traffic_headline.json")
+METRIC = "resolvent-head fwd TFLOP/s + Mtokens/s at n=8192,d=128; % bf16 MFMA peak"
+
+
+def kernel_source_sha():
+    with open(KERNEL_SOURCE, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()
+
+
+def measured_traffic(sha):
+    """HBM bytes per fused-kernel launch from the committed rocprofv3 counter
+    runs, if they were taken on this exact kernel source; else None."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            rec = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if rec.get("kernel_source_sha256") != sha:
+        return None
+    return rec.get("traffic_bytes_per_launch")
+
+
+def copy_calibration(nbytes):
+    import torch
+
+    a = torch.empty(nbytes // 4, device="cuda:0", dtype=torch.float32).fill_(1.0)
+    b = torch.empty_like(a)
+    for _ in range(3):
+        b.copy_(a)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_bytes": nbytes, "launches": 3}), flush=True)
+
+
+def cpu_baseline(inp, sw, heads):
+    """The fp64 oracle, as it stands, on whole heads of the same inputs."""
+    import numpy as np
+
+    import oracle
+
+    threads = oracle.default_threads()
+    n, d = inp["n"], inp["d"]
+    rows = np.arange(n)
+    t0 = time.perf_counter()
+    for b, h in heads:
+        st, _ = oracle.forward_rows(inp["q"][b, h], inp["k"][b, h], inp["u"][b, h],
+                                    inp["theta"][b, h], inp["v"][b, h], *sw, rows=rows,
+                                    nthreads=threads)
+        assert st == oracle.OK
+    dt = time.perf_counter() - t0
+    flops = 3.0 * n * (n + 1) * d * len(heads)  # dense-causal MFMA-equivalent FLOPs
+    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
+            "sample": f"{len(heads)} whole heads (b,h) = {heads} of the same workload, all "
+                      f"{n} rows, fp64; {dt:.2f} s; FLOPs counted dense-causal (3 n(n+1) d "
+                      f"per head)",
+            "seconds": dt, "head_tokens_per_s": len(heads) * n / dt}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-bytes", type=int, default=0)
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU: the resolvent head's heads are independent and the "
+              "build has no multi-GPU path (see DESIGN.md, 'Sharding'); run with --gpus 1",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    if args.copy_bytes:
+        copy_calibration(args.copy_bytes)
+        return
+
+    from gated_causal_attention_amd import binding, inputs
+
+    dev = torch.device("cuda:0")
+    sw = (1, 1, 1)
+    inp = inputs.make_config(3)
+    B, H, n, d = inp["B"], inp["H"], inp["n"], inp["d"]
+    t = inputs.as_torch(inp, dev)
+    o_re = torch.empty((B, H, n, d), device=dev, dtype=torch.float32)
+    o_im = torch.empty_like(o_re)
+    ws_bytes = binding.resolvent_workspace_bytes(B, H, n, d, binding.BF16, binding.BF16)
+    ws = torch.empty(ws_bytes, device=dev, dtype=torch.uint8)
+    status = torch.zeros(1, device=dev, dtype=torch.int32)
+    stream = torch.cuda.current_stream(dev)
+    cnt_off = binding.resolvent_counters_offset(B, H, n, d, binding.BF16, binding.BF16)
+
+    def step(marks=None):
+        binding.resolvent_forward(t["q"], t["k"], t["u"], t["theta"], t["v"], *sw, o_re=o_re,
+                                  o_im=o_im, workspace=ws, status=status, stream=stream,
+                                  check=False, marks=marks)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    assert int(status.item()) == 0, binding.resolvent_status_str(int(status.item()))
+
+    K = args.steps
+    marks = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(K)]
+    for ms in marks:  # materialise the HIP events before they are handed to the library
+        for e in ms:
+            e.record(stream)
+    torch.cuda.synchronize()
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    start.record(stream)
+    for i in range(K):
+        step([e.cuda_event for e in marks[i]])
+    end.record(stream)
+    torch.cuda.synchronize()
+    total_ms = start.elapsed_time(end)
+    st = int(status.item())
+    assert st == 0, binding.resolvent_status_str(st)
+    fwd_ms = [m[1].elapsed_time(m[2]) for m in marks]
+    pre_ms = [m[0].elapsed_time(m[1]) for m in marks]
+    post_ms = [m[2].elapsed_time(m[3]) for m in marks]
+    fwd_avg = float(np.mean(fwd_ms))
+    ms_per_step = total_ms / K
+
+    # work: (query, key) pairs the fused kernel evaluated in one launch
+    off_tiles = int(ws[cnt_off:cnt_off + 4].cpu().numpy().view(np.uint32)[0])
+    n_qt = (n + BQ - 1) // BQ
+    diag_pairs = B * H * sum(min(BQ, n - q * BQ) * (min(BQ, n - q * BQ) + 1) // 2
+                             for q in range(n_qt))
+    eval_pairs = off_tiles * BQ * BK + diag_pairs
+    flops_per_pair = 6 * d  # 2d logit + 4d complex readout (two real-by-real products)
+    alg_flops = flops_per_pair * eval_pairs
+    dense_flops = 3.0 * n * (n + 1) * d * B * H
+    diag_blocks_exec = B * H * n_qt * (4 * 5 // 2)  # waves w=0..3 run w+1 blocks of 32x32
+    exec_flops = flops_per_pair * (off_tiles * BQ * BK + diag_blocks_exec * 32 * 32)
+
+    achieved = alg_flops / (fwd_avg * 1e-3) / 1e12
+    sha = kernel_source_sha()
+    traffic = measured_traffic(sha)
+    out = {
+        "metric": METRIC,
+        "value": alg_flops / (ms_per_step * 1e-3) / 1e12,
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": "resolvent head B=4 H=16 n=8192 d=128, bf16 q,k,v ~ N(0,1), "
+                               "u ~ U(0.95,1), theta ~ U(-0.05,0.05), switches (1,1,1), seed 3",
+                   "B": B, "H": H, "n": n, "d": d, "switches": list(sw)},
+        "mtokens_per_s": B * n / (ms_per_step * 1e-3) / 1e6,
+        "head_mtokens_per_s": B * H * n / (ms_per_step * 1e-3) / 1e6,
+        "pct_bf16_mfma_peak": 100.0 * achieved / PEAK_BF16_TFLOPS,
+        "dense_causal_equiv_tflops": dense_flops / (ms_per_step * 1e-3) / 1e12,
+        "evaluated_pair_fraction": eval_pairs * 2.0 / (n * (n + 1) * B * H),
+        "stage_ms": {"prologue": float(np.mean(pre_ms)), "fwd_kernel": fwd_avg,
+                     "logit_check": float(np.mean(post_ms))},
+        "roofline": {"bound": "mfma", "achieved": achieved, "peak": PEAK_BF16_TFLOPS,
+                     "unit": "TFLOP/s", "frac": achieved / PEAK_BF16_TFLOPS,
+                     "traffic": traffic, "kernel": "fwd_kernel<bf16, d=128>",
+                     "flops_per_launch": alg_flops, "executed_mfma_flops": exec_flops,
+                     "executed_mfma_tflops": exec_flops / (fwd_avg * 1e-3) / 1e12},
+    }
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(inp, sw, [(0, 0), (1, 5), (2, 10), (3, 15)])
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

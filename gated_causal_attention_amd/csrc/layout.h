@@ -5,6 +5,12 @@
 #include <cstddef>
 #include <cstdint>
 
+#if defined(__HIPCC__)
+#define RESOLVENT_HD __host__ __device__
+#else
+#define RESOLVENT_HD
+#endif
+
 namespace resolvent {
 
 // A workgroup owns BQ consecutive queries (NWAVES waves of 32 rows); keys are
@@ -61,6 +67,24 @@ inline Layout make_layout(int64_t B, int64_t H, int64_t n, int64_t d, bool bf16_
     if (bf16_path) off = align_up(off + 2 * size_t(L.BH) * size_t(d) * size_t(L.n_pad), 256);
     L.total = off;
     return L;
+}
+
+// Source byte offsets of the direct global->LDS tile copies, relative to the
+// start of the tensor (q/k/v, or the v^T region for the bf16 path).  Slot
+// `slot` of a tile is the 16-byte chunk `slot % slots_per_row` of tile row
+// `slot / slots_per_row`; the last slot of a row is padding and copies chunk
+// 0.  Row `r` of key tile `t` is key t*BK + r, clamped into [0, n-1] so that
+// a tile reaching past the sequence end still reads inside the tensor.
+RESOLVENT_HD inline int64_t tile_row_src(int64_t bh, int64_t n, int64_t t, int r,
+                                         int64_t row_bytes, int chunk) {
+    int64_t key = t * BK + r;
+    key = key < n ? key : n - 1;
+    return (bh * n + key) * row_bytes + int64_t(chunk) * 16;
+}
+// v^T [BH][d][n_pad] bf16: row `dd` of key tile t, chunk `chunk` (8 keys).
+RESOLVENT_HD inline int64_t vt_src(int64_t bh, int64_t d, int64_t n_pad, int64_t t, int dd,
+                                   int chunk) {
+    return ((bh * d + dd) * n_pad + t * BK) * 2 + int64_t(chunk) * 16;
 }
 
 // Everything a launch needs, in device pointers.

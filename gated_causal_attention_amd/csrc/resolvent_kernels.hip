@@ -289,20 +289,31 @@ struct FwdArgs {
     int beta_mode, qk_zero;
 };
 
-// Shared-memory plan.  bf16 path: K tile [BK][D+8], v^T tile [D][BK+8]
-// (bf16); fp32 path: K and V tiles [BK][D+4] (fp32).  Then the per-key carried
-// gate factors T = C*S_j (re, im, modulus), the diagonal gates a_{j+1}, and a
-// few words of flags.
+// Shared-memory plan: two buffers, each holding one key tile K [BK][D], its
+// values (bf16 path: v^T [D][BK] in perm16 key order; fp32 path: V [BK][D]),
+// and per-key side data (the carried gate factor T_j = C*S_j with its modulus
+// for tiles before the query tile; the gates a_{j+1} for the query tile's
+// own keys).  Tiles are written with direct global->LDS loads, 16 bytes per
+// lane and 1 KiB per wave instruction.  Every row carries one 16-byte pad
+// slot (filled with a copy of a real chunk), which keeps the MFMA operand
+// reads free of bank conflicts while every read stays at a fixed immediate
+// offset from one per-lane base address.
 template <bool F32, int D>
 struct Smem {
-    static constexpr int KS = F32 ? D + 4 : D + 8;
-    static constexpr int VS = F32 ? D + 4 : BK + 8;
-    static constexpr size_t k_bytes = size_t(BK) * KS * (F32 ? 4 : 2);
-    static constexpr size_t v_bytes = F32 ? size_t(BK) * VS * 4 : size_t(D) * VS * 2;
-    static constexpr size_t t_off = k_bytes + v_bytes;
-    static constexpr size_t dg_off = t_off + 3 * BK * sizeof(float);
-    static constexpr size_t misc_off = dg_off + 3 * BK * sizeof(float);
+    static constexpr int ESZ = F32 ? 4 : 2;
+    static constexpr int KCH = D * ESZ / 16;    // 16-byte chunks per K (and fp32 V) row
+    static constexpr int KSL = KCH + 1;         // slots per K row, pad included
+    static constexpr int KROW = KSL * 16;       // bytes per K row in LDS
+    static constexpr int VCH = BK * 2 / 16;     // chunks per v^T row (bf16 path)
+    static constexpr int VSL = VCH + 1;
+    static constexpr int VROW = VSL * 16;
+    static constexpr size_t k_bytes = size_t(BK) * KROW;  // a multiple of 1 KiB
+    static constexpr size_t v_bytes = F32 ? size_t(BK) * KROW : size_t(D) * VROW;
+    static constexpr size_t side_off = k_bytes + v_bytes;
+    static constexpr size_t buf_bytes = side_off + 3 * BK * sizeof(float);
+    static constexpr size_t misc_off = 2 * buf_bytes;
     static constexpr size_t bytes = misc_off + 8 * sizeof(uint32_t);
+    static_assert(k_bytes % 1024 == 0 && v_bytes % 1024 == 0, "whole wave copies");
 };
 
 template <bool F32, int D>
@@ -310,6 +321,20 @@ struct Frag {
     using type = typename std::conditional<F32, float, bf16x8>::type;
     static constexpr int count = F32 ? D / 2 : D / 16;
 };
+
+typedef __attribute__((address_space(3))) void lds_void;
+
+// A wave-uniform double kept in scalar registers.
+__device__ __forceinline__ double uniform_f64(double x) {
+    const uint64_t b = __builtin_bit_cast(uint64_t, x);
+    const uint32_t lo = __builtin_amdgcn_readfirstlane(uint32_t(b));
+    const uint32_t hi = __builtin_amdgcn_readfirstlane(uint32_t(b >> 32));
+    return __builtin_bit_cast(double, (uint64_t(hi) << 32) | lo);
+}
+
+__device__ __forceinline__ void g2lds16(const void *g, unsigned char *lds) {
+    __builtin_amdgcn_global_load_lds(g, (lds_void *)(lds), 16, 0, 0);
+}
 
 // Query fragment (B operand of S^T = K Q^T) for the lane's row; returns the
 // largest |q| as float bits.
@@ -342,58 +367,58 @@ __device__ __forceinline__ uint32_t load_q(const FwdArgs &A, int64_t bh, int64_t
     return bits;
 }
 
-// Stage key tile t (keys t*BK .. t*BK+BK-1, zero past n) and, unless
-// k_only, the matching value tile.  Returns the largest |k| loaded (float bits).
+// Start the asynchronous copy of key tile t (K, and the values unless
+// k_only) into buffer buf.  Wave instruction i fills bytes [1024 i, 1024 i +
+// 1024) of a region, lane L the 16 bytes at 16 L, i.e. slot 64 i + L of the
+// padded row layout; a pad slot receives a copy of the row's first chunk.
+// Keys past n repeat key n-1 (their entries are masked).
 template <bool F32, int D>
-__device__ __forceinline__ uint32_t stage_tile(const FwdArgs &A, unsigned char *smem, int64_t bh,
-                                               int64_t t, bool k_only) {
+__device__ __forceinline__ void stage_async(const FwdArgs &A, unsigned char *buf, int64_t bh,
+                                            int64_t t, bool k_only) {
     using SM = Smem<F32, D>;
-    const int tid = threadIdx.x;
-    uint32_t bits = 0;
-    const int64_t key0 = t * BK;
+    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+    constexpr int64_t ROWB = D * SM::ESZ;  // bytes per q/k/v row in memory
+    const unsigned char *kg = static_cast<const unsigned char *>(A.k);
+    for (int i = w; i < int(SM::k_bytes / 1024); i += NWAVES) {
+        const int slot = 64 * i + lane;
+        const int c = slot % SM::KSL;
+        g2lds16(kg + tile_row_src(bh, A.n, t, slot / SM::KSL, ROWB, c < SM::KCH ? c : 0),
+                buf + 1024 * i);
+    }
+    if (k_only) return;
     if constexpr (!F32) {
-        uint16_t *Ks = reinterpret_cast<uint16_t *>(smem);
-        const uint16_t *kg = static_cast<const uint16_t *>(A.k) + (bh * A.n + key0) * D;
-        for (int c = tid; c < BK * D / 8; c += NTHREADS) {
-            const int key = c / (D / 8), c8 = c % (D / 8);
-            uint4 val = make_uint4(0, 0, 0, 0);
-            if (key0 + key < A.n) {
-                val = *reinterpret_cast<const uint4 *>(kg + key * D + 8 * c8);
-                bits = max(bits, absbits_u4_bf16(val));
-            }
-            *reinterpret_cast<uint4 *>(Ks + key * SM::KS + 8 * c8) = val;
-        }
-        if (!k_only) {
-            uint16_t *Vs = reinterpret_cast<uint16_t *>(smem + SM::k_bytes);
-            const uint16_t *vg = A.vt + bh * D * A.n_pad + key0;
-            for (int c = tid; c < D * BK / 8; c += NTHREADS) {
-                const int d = c / (BK / 8), c8 = c % (BK / 8);
-                *reinterpret_cast<uint4 *>(Vs + d * SM::VS + 8 * c8) =
-                    *reinterpret_cast<const uint4 *>(vg + d * A.n_pad + 8 * c8);
-            }
+        const unsigned char *vg = reinterpret_cast<const unsigned char *>(A.vt);
+        for (int i = w; i < int(SM::v_bytes / 1024); i += NWAVES) {
+            const int slot = 64 * i + lane;
+            const int c = slot % SM::VSL;
+            g2lds16(vg + vt_src(bh, D, A.n_pad, t, slot / SM::VSL, c < SM::VCH ? c : 0),
+                    buf + SM::k_bytes + 1024 * i);
         }
     } else {
-        float *Ks = reinterpret_cast<float *>(smem);
-        const float *kg = static_cast<const float *>(A.k) + (bh * A.n + key0) * D;
-        for (int c = tid; c < BK * D / 4; c += NTHREADS) {
-            const int key = c / (D / 4), c4 = c % (D / 4);
-            float4 val = make_float4(0.f, 0.f, 0.f, 0.f);
-            if (key0 + key < A.n) {
-                val = *reinterpret_cast<const float4 *>(kg + key * D + 4 * c4);
-                bits = max(bits, absbits_f4(val));
-            }
-            *reinterpret_cast<float4 *>(Ks + key * SM::KS + 4 * c4) = val;
+        const unsigned char *vg = static_cast<const unsigned char *>(A.v);
+        for (int i = w; i < int(SM::v_bytes / 1024); i += NWAVES) {
+            const int slot = 64 * i + lane;
+            const int c = slot % SM::KSL;
+            g2lds16(vg + tile_row_src(bh, A.n, t, slot / SM::KSL, ROWB, c < SM::KCH ? c : 0),
+                    buf + SM::k_bytes + 1024 * i);
         }
-        if (!k_only) {
-            float *Vs = reinterpret_cast<float *>(smem + SM::k_bytes);
-            const float *vg = static_cast<const float *>(A.v) + (bh * A.n + key0) * D;
-            for (int c = tid; c < BK * D / 4; c += NTHREADS) {
-                const int key = c / (D / 4), c4 = c % (D / 4);
-                float4 val = make_float4(0.f, 0.f, 0.f, 0.f);
-                if (key0 + key < A.n) val = *reinterpret_cast<const float4 *>(vg + key * D + 4 * c4);
-                *reinterpret_cast<float4 *>(Vs + key * SM::VS + 4 * c4) = val;
-            }
-        }
+    }
+}
+
+// Largest |k| over the staged key tile, keys below n only (float bits).
+template <bool F32, int D>
+__device__ __forceinline__ uint32_t tile_kbits(const FwdArgs &A, const unsigned char *buf,
+                                               int64_t t) {
+    using SM = Smem<F32, D>;
+    uint32_t bits = 0;
+    for (int slot = threadIdx.x; slot < BK * SM::KSL; slot += NTHREADS) {
+        const int r = slot / SM::KSL, c = slot % SM::KSL;
+        if (c >= SM::KCH || t * BK + r >= A.n) continue;
+        const uint4 v = *reinterpret_cast<const uint4 *>(buf + slot * 16);
+        if constexpr (F32)
+            bits = max(bits, absbits_f4(__builtin_bit_cast(float4, v)));
+        else
+            bits = max(bits, absbits_u4_bf16(v));
     }
     return bits;
 }
@@ -401,24 +426,24 @@ __device__ __forceinline__ uint32_t stage_tile(const FwdArgs &A, unsigned char *
 // S^T for keys kb..kb+31 of the staged tile against the wave's 32 queries.
 // Lane (qi, h), register r holds key kb + 8(r/4) + 4h + r%4 of query qi.
 template <bool F32, int D>
-__device__ __forceinline__ f32x16 s_block(const unsigned char *smem, int kb, int qi, int h,
+__device__ __forceinline__ f32x16 s_block(const unsigned char *buf, int kb, int qi, int h,
                                           const typename Frag<F32, D>::type (&qf)[Frag<F32, D>::count]) {
     using SM = Smem<F32, D>;
     f32x16 acc;
 #pragma unroll
     for (int r = 0; r < 16; ++r) acc[r] = 0.f;
     if constexpr (!F32) {
-        const uint16_t *kp = reinterpret_cast<const uint16_t *>(smem) + (kb + qi) * SM::KS + 8 * h;
+        const unsigned char *kp = buf + (kb + qi) * SM::KROW + h * 16;
 #pragma unroll
         for (int s = 0; s < D / 16; ++s) {
-            const bf16x8 a = *reinterpret_cast<const bf16x8 *>(kp + 16 * s);
+            const bf16x8 a = *reinterpret_cast<const bf16x8 *>(kp + 32 * s);
             acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[s], acc, 0, 0, 0);
         }
     } else {
-        const float *kp = reinterpret_cast<const float *>(smem) + (kb + qi) * SM::KS + (D / 2) * h;
+        const unsigned char *kp = buf + (kb + qi) * SM::KROW + h * (D / 8) * 16;
 #pragma unroll
         for (int t = 0; t < D / 8; ++t) {
-            const float4 a = *reinterpret_cast<const float4 *>(kp + 4 * t);
+            const float4 a = *reinterpret_cast<const float4 *>(kp + 16 * t);
             acc = __builtin_amdgcn_mfma_f32_32x32x2f32(a.x, qf[4 * t + 0], acc, 0, 0, 0);
             acc = __builtin_amdgcn_mfma_f32_32x32x2f32(a.y, qf[4 * t + 1], acc, 0, 0, 0);
             acc = __builtin_amdgcn_mfma_f32_32x32x2f32(a.z, qf[4 * t + 2], acc, 0, 0, 0);
@@ -432,10 +457,11 @@ __device__ __forceinline__ f32x16 s_block(const unsigned char *smem, int kb, int
 // S^T block at kb): two accumulators, one for Re W~ and one for Im W~, that
 // share the V operand.
 template <bool F32, int D>
-__device__ __forceinline__ void pv_chunk(const unsigned char *smem, int kb, int kc, int qi, int h,
+__device__ __forceinline__ void pv_chunk(const unsigned char *buf, int kb, int kc, int qi, int h,
                                          const float (&wre)[8], const float (&wim)[8],
                                          f32x16 (&ore)[D / 32], f32x16 (&oim)[D / 32]) {
     using SM = Smem<F32, D>;
+    const unsigned char *vb = buf + SM::k_bytes;
     if constexpr (!F32) {
         bf16x8 bre, bim;
 #pragma unroll
@@ -443,23 +469,22 @@ __device__ __forceinline__ void pv_chunk(const unsigned char *smem, int kb, int 
             bre[e] = (__bf16)wre[e];
             bim[e] = (__bf16)wim[e];
         }
-        const uint16_t *vp = reinterpret_cast<const uint16_t *>(smem + SM::k_bytes) + qi * SM::VS +
-                             kb + 16 * kc + 8 * h;
+        const unsigned char *vp = vb + qi * SM::VROW + ((kb >> 3) + 2 * kc + h) * 16;
 #pragma unroll
         for (int db = 0; db < D / 32; ++db) {
-            const bf16x8 a = *reinterpret_cast<const bf16x8 *>(vp + 32 * db * SM::VS);
+            const bf16x8 a = *reinterpret_cast<const bf16x8 *>(vp + 32 * db * SM::VROW);
             ore[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, bre, ore[db], 0, 0, 0);
             oim[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, bim, oim[db], 0, 0, 0);
         }
     } else {
-        const float *vs = reinterpret_cast<const float *>(smem + SM::k_bytes);
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
             const int s = 8 * kc + e;
             const int key = kb + 8 * (s / 4) + 4 * h + (s % 4);
 #pragma unroll
             for (int db = 0; db < D / 32; ++db) {
-                const float a = vs[key * SM::VS + 32 * db + qi];
+                const float a = *reinterpret_cast<const float *>(
+                    vb + key * SM::KROW + (32 * db + qi) * 4);
                 ore[db] = __builtin_amdgcn_mfma_f32_32x32x2f32(a, wre[e], ore[db], 0, 0, 0);
                 oim[db] = __builtin_amdgcn_mfma_f32_32x32x2f32(a, wim[e], oim[db], 0, 0, 0);
             }
@@ -467,20 +492,19 @@ __device__ __forceinline__ void pv_chunk(const unsigned char *smem, int kb, int 
     }
 }
 
+// Lazy rescaling: the shift M only moves when a logit exceeds it by more than
+// this many binary orders (weights stay <= 2^8 in between; the epilogue uses
+// whatever shift was last applied, so the result is the same).
+constexpr float kLazy = 8.0f;
+
 template <bool F32, int D>
-__global__ __launch_bounds__(NTHREADS) void fwd_kernel(FwdArgs A) {
+__global__ __launch_bounds__(NTHREADS, 2) void fwd_kernel(FwdArgs A) {
     using SM = Smem<F32, D>;
     using FR = Frag<F32, D>;
     extern __shared__ __align__(16) unsigned char smem[];
-    float *Tre = reinterpret_cast<float *>(smem + SM::t_off);
-    float *Tim = Tre + BK;
-    float *Tm = Tim + BK;
-    float *Dre = reinterpret_cast<float *>(smem + SM::dg_off);
-    float *Dim = Dre + BK;
-    float *Dm = Dim + BK;
     uint32_t *misc = reinterpret_cast<uint32_t *>(smem + SM::misc_off);
-    // misc[0], misc[1]: a 32-key block of the staged tile holds a dead column;
-    // misc[2]: largest |q|; misc[3]: largest |k|
+    // misc[0..1]: current tile, 32-key block b holds a dead column (off-diagonal)
+    // misc[2]: largest |q|; misc[3]: largest |k|; misc[4..5]: next tile's flags
 
     const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, h = lane >> 5, qi = lane & 31;
     const int L = blockIdx.x;
@@ -490,19 +514,71 @@ __global__ __launch_bounds__(NTHREADS) void fwd_kernel(FwdArgs A) {
     const int64_t row = i0 + 32 * w + qi;
     const bool row_ok = row < A.n;
     const int64_t gbase = bh * A.n_pad;
+    const int64_t t_diag0 = i0 / BK;            // first key tile of the query tile
+    constexpr int NDIAG = BQ / BK;
 
     if (tid == 0) {
         misc[2] = 0;
         misc[3] = 0;
     }
+
+    // ---- the tile schedule: off-diagonal tiles last to first while the
+    // carried modulus is non-zero in float32, then the query tile's own tiles
+    int64_t t_cur = t_diag0 > 0 ? t_diag0 - 1 : t_diag0 + NDIAG - 1;
+    bool off_cur = t_diag0 > 0;
+    double Cre = 1.0, Cim = 0.0, Cm = 1.0;  // carried gates: end of t_cur .. i0-1
+
+    // side data of a tile, written by wave 0 into a buffer: T_j = C S_j
+    // (off-diagonal) or the gates a_{j+1} (the query tile's own keys)
+    auto write_side = [&](unsigned char *buf, int64_t t, bool off, double cr, double ci,
+                          double cm, float g0, float g1, float g2) {
+        float *sd = reinterpret_cast<float *>(buf + SM::side_off);
+        if (off) {
+            const int slot = perm64(tid);
+            sd[slot] = (float)(cr * (double)g0 - ci * (double)g1);
+            sd[BK + slot] = (float)(cr * (double)g1 + ci * (double)g0);
+            const float rt = (float)(cm * (double)g2);
+            sd[2 * BK + slot] = rt;
+            const uint64_t dead = __ballot(rt == 0.0f);
+            if (tid == 0) {
+                misc[4] = (uint32_t)(dead & 0xFFFFFFFFull) != 0u;
+                misc[5] = (uint32_t)(dead >> 32) != 0u;
+            }
+        } else {
+            sd[tid] = g0;
+            sd[BK + tid] = g1;
+            sd[2 * BK + tid] = g2;
+        }
+    };
+    // gate data wave 0 needs for a tile's side data (one key per lane)
+    auto load_side = [&](int64_t t, bool off, float &g0, float &g1, float &g2) {
+        if (off) {
+            const int64_t pos = gbase + t * BK + tid;
+            g0 = A.s_re[pos];
+            g1 = A.s_im[pos];
+            g2 = A.s_m[pos];
+        } else {
+            const int64_t pos = t * BK + 1 + tid;  // a_{j+1} for key j = t*BK + tid
+            const bool ok = pos < A.n;
+            g0 = ok ? A.a_re[gbase + pos] : 1.0f;
+            g1 = ok ? A.a_im[gbase + pos] : 0.0f;
+            g2 = ok ? A.a_m[gbase + pos] : 1.0f;
+        }
+    };
+
+    int cur = 0;
+    stage_async<F32, D>(A, smem, bh, t_cur, false);
+    if (tid < BK) {
+        float g0, g1, g2;
+        load_side(t_cur, off_cur, g0, g1, g2);
+        write_side(smem, t_cur, off_cur, Cre, Cim, Cm, g0, g1, g2);
+    }
     typename FR::type qf[FR::count];
     const uint32_t qbits = load_q<F32, D>(A, bh, row, row_ok, h, qf);
-    __syncthreads();
-    atomicMax(&misc[2], qbits);
 
-    // prefix product of the query tile for this row, and its modulus
-    const float Pre = A.p_re[gbase + row], Pim = A.p_im[gbase + row], Pm = A.p_m[gbase + row];
-    const bool row_live = !(Pm == 0.0f);
+    // the modulus of the query tile's prefix product for this row: a row whose
+    // prefix holds a closed gate sees no key before the query tile
+    const bool row_live = !(A.p_m[gbase + row] == 0.0f);
     const bool wave_dead_rows = __any(!row_live);
 
     f32x16 ore[D / 32], oim[D / 32];
@@ -513,16 +589,26 @@ __global__ __launch_bounds__(NTHREADS) void fwd_kernel(FwdArgs A) {
             ore[db][r] = 0.f;
             oim[db][r] = 0.f;
         }
-    float M = -INFINITY;  // running max of live logits (log2 units), same in both halves
+    float M = -INFINITY;  // shift of the live logits (log2 units), same in both halves
     float z = 0.f;        // this lane's share of the normaliser
+    uint32_t tiles_done = 0;
+
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    if (tid == 0) {
+        misc[0] = misc[4];
+        misc[1] = misc[5];
+    }
+    atomicMax(&misc[2], qbits);
+    __syncthreads();
 
     // logits of one S^T block: x = S * c (qk = 0 never forms the product)
-    auto logits = [&](int kb, float (&x)[16]) {
+    auto logits = [&](const unsigned char *buf, int kb, float (&x)[16]) {
         if (A.qk_zero) {
 #pragma unroll
             for (int r = 0; r < 16; ++r) x[r] = 0.f;
         } else {
-            const f32x16 s = s_block<F32, D>(smem, kb, qi, h, qf);
+            const f32x16 s = s_block<F32, D>(buf, kb, qi, h, qf);
             {
 #pragma clang fp contract(off)
 #pragma unroll
@@ -530,17 +616,16 @@ __global__ __launch_bounds__(NTHREADS) void fwd_kernel(FwdArgs A) {
             }
         }
     };
-    // online max over the block; rescales O and z when it grows; returns the
+    // online max over the block with lazy rescaling of O and z; returns the
     // shift to subtract (0 while a row has no live entry yet)
     auto update_max = [&](const float (&x)[16]) -> float {
         float t = x[0];
 #pragma unroll
         for (int r = 1; r < 16; ++r) t = fmaxf(t, x[r]);
         t = fmaxf(t, __shfl_xor(t, 32));
-        const float Mn = fmaxf(M, t);
-        const bool need = (Mn > M) && (M != -INFINITY);
-        if (__any(need)) {
-            const float alpha = need ? __builtin_amdgcn_exp2f(M - Mn) : 1.0f;
+        const bool grow = t > M + kLazy || (M == -INFINITY && t > M);
+        if (__any(grow && M != -INFINITY)) {
+            const float alpha = (grow && M != -INFINITY) ? __builtin_amdgcn_exp2f(M - t) : 1.0f;
 #pragma unroll
             for (int db = 0; db < D / 32; ++db)
 #pragma unroll
@@ -550,12 +635,12 @@ __global__ __launch_bounds__(NTHREADS) void fwd_kernel(FwdArgs A) {
                 }
             z *= alpha;
         }
-        M = Mn;
-        return (Mn == -INFINITY) ? 0.0f : Mn;
+        M = grow ? t : M;
+        return (M == -INFINITY) ? 0.0f : M;
     };
     // exponentials, normaliser and the two W~ V products of one 16-key chunk
-    auto chunk = [&](int kb, int kc, const float (&x)[16], float msub, const float (&fre)[8],
-                     const float (&fim)[8], const float (&fm)[8]) {
+    auto chunk = [&](const unsigned char *buf, int kb, int kc, const float (&x)[16], float msub,
+                     const float (&fre)[8], const float (&fim)[8], const float (&fm)[8]) {
         float wre[8], wim[8];
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
@@ -568,141 +653,159 @@ __global__ __launch_bounds__(NTHREADS) void fwd_kernel(FwdArgs A) {
             wre[e] = ex * fre[e];
             wim[e] = ex * fim[e];
         }
-        pv_chunk<F32, D>(smem, kb, kc, qi, h, wre, wim, ore, oim);
+        pv_chunk<F32, D>(buf, kb, kc, qi, h, wre, wim, ore, oim);
     };
 
-    // ---- key tiles wholly before the query tile, last to first ----------
-    double Cre = 1.0, Cim = 0.0, Cm = 1.0;  // gates between the tile's end and i0
-    const int64_t t_first = i0 / BK - 1;
-    uint32_t tiles_done = 0;
-    for (int64_t t = t_first; t >= 0; --t) {
+    // ---- key tiles wholly before the query tile: G = S_j C_t P_i ----------
+    while (off_cur) {
+        unsigned char *buf = smem + cur * SM::buf_bytes;
+        unsigned char *nbuf = smem + (cur ^ 1) * SM::buf_bytes;
+        const float *side = reinterpret_cast<const float *>(buf + SM::side_off);
+        // the next tile, and its asynchronous copy
+        const int64_t tp = bh * A.n_kt + t_cur;
+        const double are = A.t_re[tp], aim = A.t_im[tp], am = A.t_m[tp];
+        const double nCre = uniform_f64(are * Cre - aim * Cim);
+        const double nCim = uniform_f64(are * Cim + aim * Cre);
+        const double nCm = uniform_f64(am * Cm);
         // every earlier key is dead once the carried modulus is 0 in float32
-        if ((float)Cm == 0.0f) break;
+        const bool off_nxt = t_cur > 0 && (float)nCm != 0.0f;
+        const int64_t t_nxt = off_nxt ? t_cur - 1 : t_diag0 + NDIAG - 1;
+        stage_async<F32, D>(A, nbuf, bh, t_nxt, false);
+        float g0 = 0.f, g1 = 0.f, g2 = 0.f;
+        if (tid < BK) load_side(t_nxt, off_nxt, g0, g1, g2);
+
         ++tiles_done;
-        __syncthreads();
-        stage_tile<F32, D>(A, smem, bh, t, false);
-        if (tid < BK) {
-            const int64_t pos = gbase + t * BK + tid;
-            const double sre = A.s_re[pos], sim = A.s_im[pos], sm = A.s_m[pos];
-            const int slot = perm64(tid);
-            Tre[slot] = (float)(Cre * sre - Cim * sim);
-            Tim[slot] = (float)(Cre * sim + Cim * sre);
-            const float rt = (float)(Cm * sm);
-            Tm[slot] = rt;
-            const uint64_t dead = __ballot(rt == 0.0f);
-            if (tid == 0) {
-                misc[0] = (uint32_t)(dead & 0xFFFFFFFFull) != 0u;
-                misc[1] = (uint32_t)(dead >> 32) != 0u;
-            }
-        }
-        __syncthreads();
 #pragma unroll
         for (int blk = 0; blk < 2; ++blk) {
             const int kb = 32 * blk;
             float x[16];
-            logits(kb, x);
-            const bool masked = wave_dead_rows || misc[blk] != 0u;
-            if (masked) {
+            logits(buf, kb, x);
+            if (wave_dead_rows || misc[blk] != 0u) {
 #pragma unroll
-                for (int kc = 0; kc < 2; ++kc)
+                for (int kc = 0; kc < 2; ++kc) {
+                    const float4 m0 =
+                        *reinterpret_cast<const float4 *>(side + 2 * BK + kb + 16 * kc + 8 * h);
+                    const float4 m1 =
+                        *reinterpret_cast<const float4 *>(side + 2 * BK + kb + 16 * kc + 8 * h + 4);
+                    const float mm[8] = {m0.x, m0.y, m0.z, m0.w, m1.x, m1.y, m1.z, m1.w};
 #pragma unroll
-                    for (int e = 0; e < 8; ++e) {
-                        const float rt = Tm[kb + 16 * kc + 8 * h + e];
-                        const int r = 8 * kc + e;
-                        x[r] = (rt > 0.0f && row_live) ? x[r] : -INFINITY;
-                    }
+                    for (int e = 0; e < 8; ++e)
+                        x[8 * kc + e] = (mm[e] > 0.0f && row_live) ? x[8 * kc + e] : -INFINITY;
+                }
             }
             const float msub = update_max(x);
 #pragma unroll
             for (int kc = 0; kc < 2; ++kc) {
                 float fre[8], fim[8], fm[8];
+                const int s0 = kb + 16 * kc + 8 * h;
 #pragma unroll
-                for (int e = 0; e < 8; ++e) {
-                    const int slot = kb + 16 * kc + 8 * h + e;
-                    fre[e] = Tre[slot];
-                    fim[e] = Tim[slot];
-                    fm[e] = Tm[slot];
+                for (int e = 0; e < 8; e += 4) {
+                    const float4 a = *reinterpret_cast<const float4 *>(side + s0 + e);
+                    const float4 b = *reinterpret_cast<const float4 *>(side + BK + s0 + e);
+                    const float4 c = *reinterpret_cast<const float4 *>(side + 2 * BK + s0 + e);
+                    fre[e] = a.x; fre[e + 1] = a.y; fre[e + 2] = a.z; fre[e + 3] = a.w;
+                    fim[e] = b.x; fim[e + 1] = b.y; fim[e + 2] = b.z; fim[e + 3] = b.w;
+                    fm[e] = c.x; fm[e + 1] = c.y; fm[e + 2] = c.z; fm[e + 3] = c.w;
                 }
-                chunk(kb, kc, x, msub, fre, fim, fm);
+                chunk(buf, kb, kc, x, msub, fre, fim, fm);
             }
         }
-        // carry: C <- A_t C
-        const int64_t tp = bh * A.n_kt + t;
-        const double are = A.t_re[tp], aim = A.t_im[tp], am = A.t_m[tp];
-        const double nr = are * Cre - aim * Cim, ni = are * Cim + aim * Cre;
-        Cre = nr;
-        Cim = ni;
-        Cm = am * Cm;
+
+        if (tid < BK) write_side(nbuf, t_nxt, off_nxt, nCre, nCim, nCm, g0, g1, g2);
+        __builtin_amdgcn_s_waitcnt(0);
+        __syncthreads();
+        if (tid == 0) {
+            misc[0] = misc[4];
+            misc[1] = misc[5];
+        }
+        __syncthreads();
+        Cre = nCre;
+        Cim = nCim;
+        Cm = nCm;
+        t_cur = t_nxt;
+        off_cur = off_nxt;
+        cur ^= 1;
+        if (!off_cur) {
+            // leaving the off-diagonal tiles: rotate by the prefix product P_i
+            const float Pre = A.p_re[gbase + row], Pim = A.p_im[gbase + row];
+            const float Pm = A.p_m[gbase + row];
+#pragma unroll
+            for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    const float xr = ore[db][r], xi = oim[db][r];
+                    ore[db][r] = Pre * xr - Pim * xi;
+                    oim[db][r] = Pre * xi + Pim * xr;
+                }
+            z *= Pm;
+        }
     }
 
-    // rotate the off-diagonal part by the row's prefix product P_i
-#pragma unroll
-    for (int db = 0; db < D / 32; ++db)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-            const float xr = ore[db][r], xi = oim[db][r];
-            ore[db][r] = Pre * xr - Pim * xi;
-            oim[db][r] = Pre * xi + Pim * xr;
-        }
-    z *= Pm;
-
-    // ---- the query tile's own keys: explicit G_ij, last key first --------
-    float gre = 0.f, gim = 0.f, gm = 0.f;  // running G_{row, j}, R_{row, j}
+    // ---- the query tile's own keys: explicit G_ij, last key first ---------
+    float gre = 0.f, gim = 0.f, gm = 0.f;  // running G_{row,j}, R_{row,j}
     uint32_t kbits = 0;
-    for (int dt = BQ / BK - 1; dt >= 0; --dt) {
-        const int64_t t = i0 / BK + dt;
-        __syncthreads();
-        kbits = max(kbits, stage_tile<F32, D>(A, smem, bh, t, false));
-        if (tid < BK) {
-            const int64_t pos = t * BK + 1 + tid;  // a_{j+1} for key j = t*BK + tid
-            const bool ok = pos < A.n;
-            Dre[tid] = ok ? A.a_re[gbase + pos] : 1.0f;
-            Dim[tid] = ok ? A.a_im[gbase + pos] : 0.0f;
-            Dm[tid] = ok ? A.a_m[gbase + pos] : 1.0f;
+    while (true) {
+        unsigned char *buf = smem + cur * SM::buf_bytes;
+        unsigned char *nbuf = smem + (cur ^ 1) * SM::buf_bytes;
+        const float *side = reinterpret_cast<const float *>(buf + SM::side_off);
+        const bool more = t_cur > t_diag0;
+        float g0 = 0.f, g1 = 0.f, g2 = 0.f;
+        if (more) {
+            stage_async<F32, D>(A, nbuf, bh, t_cur - 1, false);
+            if (tid < BK) load_side(t_cur - 1, false, g0, g1, g2);
         }
-        __syncthreads();
+        kbits = max(kbits, tile_kbits<F32, D>(A, buf, t_cur));
 #pragma unroll
         for (int blk = 1; blk >= 0; --blk) {
-            const int cidx = (BK / 32) * dt + blk;  // 32-key block index inside the query tile
-            if (cidx > w) continue;                   // wholly above this wave's rows
+            const int cidx = int((t_cur - t_diag0) * (BK / 32)) + blk;
+            if (cidx > w) continue;  // wholly above this wave's rows
             const int kb = 32 * blk;
-            const int64_t j0 = t * BK + kb;
-            float Gre[16], Gim[16], Gm[16];
+            const int dpos = int(row - (t_cur * BK + kb));  // 0..31 on the block's diagonal
+            // pass 1: modulus R_{row,j} of the 16 keys this lane holds
+            float Gm[16];
+            const float gre0 = gre, gim0 = gim;
 #pragma unroll
             for (int jj = 31; jj >= 0; --jj) {
-                const int64_t j = j0 + jj;
-                const float dr = Dre[kb + jj], di = Dim[kb + jj], dm = Dm[kb + jj];
-                const float nr = gre * dr - gim * di;
-                const float ni = gre * di + gim * dr;
-                const float nm = gm * dm;
-                const bool diag = (j == row);
-                gre = diag ? 1.0f : nr;
-                gim = diag ? 0.0f : ni;
-                gm = diag ? 1.0f : nm;
-                const int r = 4 * (jj >> 3) + (jj & 3);
-                if (h == ((jj >> 2) & 1)) {
-                    Gre[r] = gre;
-                    Gim[r] = gim;
-                    Gm[r] = gm;
-                }
+                const float nm = gm * side[2 * BK + kb + jj];
+                gm = (jj == dpos) ? 1.0f : nm;
+                if (h == ((jj >> 2) & 1)) Gm[4 * (jj >> 3) + (jj & 3)] = gm;
             }
             float x[16];
-            logits(kb, x);
+            logits(buf, kb, x);
 #pragma unroll
             for (int r = 0; r < 16; ++r) x[r] = (Gm[r] > 0.0f) ? x[r] : -INFINITY;
             const float msub = update_max(x);
+            // pass 2: G_{row,j} chunk by chunk, keys 31..16 then 15..0
+            gre = gre0;
+            gim = gim0;
 #pragma unroll
-            for (int kc = 0; kc < 2; ++kc) {
+            for (int kc = 1; kc >= 0; --kc) {
                 float fre[8], fim[8], fm[8];
 #pragma unroll
-                for (int e = 0; e < 8; ++e) {
-                    fre[e] = Gre[8 * kc + e];
-                    fim[e] = Gim[8 * kc + e];
-                    fm[e] = Gm[8 * kc + e];
+                for (int jj = 16 * kc + 15; jj >= 16 * kc; --jj) {
+                    const float dr = side[kb + jj], di = side[BK + kb + jj];
+                    const float nr = gre * dr - gim * di;
+                    const float ni = gre * di + gim * dr;
+                    const bool diag = (jj == dpos);
+                    gre = diag ? 1.0f : nr;
+                    gim = diag ? 0.0f : ni;
+                    if (h == ((jj >> 2) & 1)) {
+                        const int e = 4 * ((jj - 16 * kc) >> 3) + (jj & 3);
+                        fre[e] = gre;
+                        fim[e] = gim;
+                    }
                 }
-                chunk(kb, kc, x, msub, fre, fim, fm);
+#pragma unroll
+                for (int e = 0; e < 8; ++e) fm[e] = Gm[8 * kc + e];
+                chunk(buf, kb, kc, x, msub, fre, fim, fm);
             }
         }
+        if (!more) break;
+        if (tid < BK) write_side(nbuf, t_cur - 1, false, 0.0, 0.0, 0.0, g0, g1, g2);
+        __builtin_amdgcn_s_waitcnt(0);
+        __syncthreads();
+        t_cur -= 1;
+        cur ^= 1;
     }
     atomicMax(&misc[3], kbits);
 
@@ -781,7 +884,8 @@ __global__ __launch_bounds__(NTHREADS) void logit_check_kernel(FwdArgs A) {
     bool bad = false;
     for (int64_t t = 0; t < (i0 + BQ) / BK; ++t) {
         __syncthreads();
-        stage_tile<F32, D>(A, smem, bh, t, true);
+        stage_async<F32, D>(A, smem, bh, t, true);
+        __builtin_amdgcn_s_waitcnt(0);
         __syncthreads();
 #pragma unroll
         for (int blk = 0; blk < 2; ++blk) {
@@ -792,7 +896,7 @@ __global__ __launch_bounds__(NTHREADS) void logit_check_kernel(FwdArgs A) {
                 for (int r = 0; r < 16; ++r) {
                     const int64_t j = t * BK + 32 * blk + 8 * (r / 4) + 4 * h + (r % 4);
                     const float x = s[r] * A.c;
-                    if (row_ok && j <= row && !isfinite(x)) bad = true;
+                    if (row_ok && j <= row && j < A.n && !isfinite(x)) bad = true;
                 }
             }
         }

@@ -61,7 +61,11 @@ def _ptr(a):
 
 
 def default_threads() -> int:
-    return len(os.sched_getaffinity(0))
+    """Threads for the oracle: OMP_NUM_THREADS when set (the host's CPU share),
+    else every core this process may run on."""
+    env = os.environ.get("OMP_NUM_THREADS", "")
+    cores = len(os.sched_getaffinity(0))
+    return min(int(env), cores) if env.isdigit() and int(env) > 0 else cores
 
 
 def blend(u, theta, g):
