@@ -70,11 +70,10 @@ inline Layout make_layout(int64_t B, int64_t H, int64_t n, int64_t d, bool bf16_
 }
 
 // Source byte offsets of the direct global->LDS tile copies, relative to the
-// start of the tensor (q/k/v, or the v^T region for the bf16 path).  Slot
-// `slot` of a tile is the 16-byte chunk `slot % slots_per_row` of tile row
-// `slot / slots_per_row`; the last slot of a row is padding and copies chunk
-// 0.  Row `r` of key tile `t` is key t*BK + r, clamped into [0, n-1] so that
-// a tile reaching past the sequence end still reads inside the tensor.
+// start of the tensor (q/k/v, or the v^T region for the bf16 path).  Row `r`
+// of key tile `t` is key t*BK + r, clamped into [0, n-1] so that a tile
+// reaching past the sequence end still reads inside the tensor; `chunk` is a
+// 16-byte chunk of that row.
 RESOLVENT_HD inline int64_t tile_row_src(int64_t bh, int64_t n, int64_t t, int r,
                                          int64_t row_bytes, int chunk) {
     int64_t key = t * BK + r;

@@ -20,10 +20,11 @@ bool supported(int64_t d, int32_t qk_dtype, int32_t v_dtype) {
     return false;
 }
 
-// Limits that keep every launch grid and in-kernel index in range.
+// Limits that keep every launch grid and in-kernel index in range (the tile
+// copies address a head with 32-bit offsets: n * d * 4 bytes < 2^31).
 bool within_limits(int64_t B, int64_t H, int64_t n) {
-    const int64_t maxn = int64_t(1) << 24;
-    if (n > maxn || B > maxn || H > maxn) return false;
+    const int64_t maxn = int64_t(1) << 22;
+    if (n > maxn || B > (int64_t(1) << 24) || H > (int64_t(1) << 24)) return false;
     const int64_t BH = B * H;
     if (BH > (int64_t(1) << 24)) return false;
     const int64_t n_pad = (n + BQ - 1) / BQ * BQ;

@@ -293,27 +293,23 @@ struct FwdArgs {
 // values (bf16 path: v^T [D][BK] in perm16 key order; fp32 path: V [BK][D]),
 // and per-key side data (the carried gate factor T_j = C*S_j with its modulus
 // for tiles before the query tile; the gates a_{j+1} for the query tile's
-// own keys).  Tiles are written with direct global->LDS loads, 16 bytes per
-// lane and 1 KiB per wave instruction.  Every row carries one 16-byte pad
-// slot (filled with a copy of a real chunk), which keeps the MFMA operand
-// reads free of bank conflicts while every read stays at a fixed immediate
-// offset from one per-lane base address.
+// own keys).  Tiles are stored 16-byte-chunk-major: chunk c of row r sits at
+// (c * rows + r) * 16.  One direct global->LDS wave instruction then copies
+// one chunk of 64 consecutive rows (lane L -> row L), and each half-wave of
+// an MFMA operand read touches 512 contiguous bytes (no bank conflicts), at
+// an immediate offset from one per-lane base address.
 template <bool F32, int D>
 struct Smem {
     static constexpr int ESZ = F32 ? 4 : 2;
     static constexpr int KCH = D * ESZ / 16;    // 16-byte chunks per K (and fp32 V) row
-    static constexpr int KSL = KCH + 1;         // slots per K row, pad included
-    static constexpr int KROW = KSL * 16;       // bytes per K row in LDS
     static constexpr int VCH = BK * 2 / 16;     // chunks per v^T row (bf16 path)
-    static constexpr int VSL = VCH + 1;
-    static constexpr int VROW = VSL * 16;
-    static constexpr size_t k_bytes = size_t(BK) * KROW;  // a multiple of 1 KiB
-    static constexpr size_t v_bytes = F32 ? size_t(BK) * KROW : size_t(D) * VROW;
+    static constexpr size_t k_bytes = size_t(KCH) * BK * 16;
+    static constexpr size_t v_bytes = F32 ? size_t(KCH) * BK * 16 : size_t(VCH) * D * 16;
     static constexpr size_t side_off = k_bytes + v_bytes;
     static constexpr size_t buf_bytes = side_off + 3 * BK * sizeof(float);
     static constexpr size_t misc_off = 2 * buf_bytes;
     static constexpr size_t bytes = misc_off + 8 * sizeof(uint32_t);
-    static_assert(k_bytes % 1024 == 0 && v_bytes % 1024 == 0, "whole wave copies");
+    static_assert(KCH % NWAVES == 0 && (VCH * D / 64) % NWAVES == 0, "whole wave copies");
 };
 
 template <bool F32, int D>
@@ -368,39 +364,46 @@ __device__ __forceinline__ uint32_t load_q(const FwdArgs &A, int64_t bh, int64_t
 }
 
 // Start the asynchronous copy of key tile t (K, and the values unless
-// k_only) into buffer buf.  Wave instruction i fills bytes [1024 i, 1024 i +
-// 1024) of a region, lane L the 16 bytes at 16 L, i.e. slot 64 i + L of the
-// padded row layout; a pad slot receives a copy of the row's first chunk.
-// Keys past n repeat key n-1 (their entries are masked).
+// k_only) into buffer buf.  Wave w copies chunks w, w+NWAVES, ...: lane L
+// fetches 16 bytes of row L.  Keys past n repeat key n-1 (their entries are
+// masked); the v^T copy is zero there.
 template <bool F32, int D>
 __device__ __forceinline__ void stage_async(const FwdArgs &A, unsigned char *buf, int64_t bh,
                                             int64_t t, bool k_only) {
     using SM = Smem<F32, D>;
-    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+    const int lane = threadIdx.x & 63;
+    const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     constexpr int64_t ROWB = D * SM::ESZ;  // bytes per q/k/v row in memory
-    const unsigned char *kg = static_cast<const unsigned char *>(A.k);
-    for (int i = w; i < int(SM::k_bytes / 1024); i += NWAVES) {
-        const int slot = 64 * i + lane;
-        const int c = slot % SM::KSL;
-        g2lds16(kg + tile_row_src(bh, A.n, t, slot / SM::KSL, ROWB, c < SM::KCH ? c : 0),
-                buf + 1024 * i);
+    // head base (uniform) + 32-bit offset of row `lane` of the tile (clamped)
+    const int64_t hbase = bh * A.n * ROWB;
+    const uint32_t koff = uint32_t(tile_row_src(bh, A.n, t, lane, ROWB, 0) - hbase);
+    const unsigned char *kh = static_cast<const unsigned char *>(A.k) + hbase;
+#pragma unroll
+    for (int i = 0; i < SM::KCH / NWAVES; ++i) {
+        const int c = w + NWAVES * i;
+        g2lds16(kh + (koff + uint32_t(c * 16)), buf + c * 1024);
     }
     if (k_only) return;
     if constexpr (!F32) {
-        const unsigned char *vg = reinterpret_cast<const unsigned char *>(A.vt);
-        for (int i = w; i < int(SM::v_bytes / 1024); i += NWAVES) {
-            const int slot = 64 * i + lane;
-            const int c = slot % SM::VSL;
-            g2lds16(vg + vt_src(bh, D, A.n_pad, t, slot / SM::VSL, c < SM::VCH ? c : 0),
-                    buf + SM::k_bytes + 1024 * i);
+        // v^T rows d = lane + 64 grp, chunks of 8 keys
+        const int64_t vbase = bh * D * A.n_pad * 2;
+        const uint32_t voff = uint32_t(vt_src(bh, D, A.n_pad, t, lane, 0) - vbase);
+        const uint32_t row64 = uint32_t(64 * A.n_pad * 2);
+        const unsigned char *vh = reinterpret_cast<const unsigned char *>(A.vt) + vbase;
+        constexpr int NI = SM::VCH * D / 64 / NWAVES;
+#pragma unroll
+        for (int i = 0; i < NI; ++i) {
+            const int idx = w + NWAVES * i;  // (chunk, 64-row group)
+            const int c = idx % SM::VCH, grp = idx / SM::VCH;
+            g2lds16(vh + (voff + uint32_t(grp) * row64 + uint32_t(c * 16)),
+                    buf + SM::k_bytes + (c * D + 64 * grp) * 16);
         }
     } else {
-        const unsigned char *vg = static_cast<const unsigned char *>(A.v);
-        for (int i = w; i < int(SM::v_bytes / 1024); i += NWAVES) {
-            const int slot = 64 * i + lane;
-            const int c = slot % SM::KSL;
-            g2lds16(vg + tile_row_src(bh, A.n, t, slot / SM::KSL, ROWB, c < SM::KCH ? c : 0),
-                    buf + SM::k_bytes + 1024 * i);
+        const unsigned char *vh = static_cast<const unsigned char *>(A.v) + hbase;
+#pragma unroll
+        for (int i = 0; i < SM::KCH / NWAVES; ++i) {
+            const int c = w + NWAVES * i;
+            g2lds16(vh + (koff + uint32_t(c * 16)), buf + SM::k_bytes + c * 1024);
         }
     }
 }
@@ -411,10 +414,9 @@ __device__ __forceinline__ uint32_t tile_kbits(const FwdArgs &A, const unsigned 
                                                int64_t t) {
     using SM = Smem<F32, D>;
     uint32_t bits = 0;
-    for (int slot = threadIdx.x; slot < BK * SM::KSL; slot += NTHREADS) {
-        const int r = slot / SM::KSL, c = slot % SM::KSL;
-        if (c >= SM::KCH || t * BK + r >= A.n) continue;
-        const uint4 v = *reinterpret_cast<const uint4 *>(buf + slot * 16);
+    for (int u = threadIdx.x; u < SM::KCH * BK; u += NTHREADS) {
+        if (t * BK + (u % BK) >= A.n) continue;
+        const uint4 v = *reinterpret_cast<const uint4 *>(buf + u * 16);
         if constexpr (F32)
             bits = max(bits, absbits_f4(__builtin_bit_cast(float4, v)));
         else
@@ -433,17 +435,17 @@ __device__ __forceinline__ f32x16 s_block(const unsigned char *buf, int kb, int 
 #pragma unroll
     for (int r = 0; r < 16; ++r) acc[r] = 0.f;
     if constexpr (!F32) {
-        const unsigned char *kp = buf + (kb + qi) * SM::KROW + h * 16;
+        const unsigned char *kp = buf + (h * BK + kb + qi) * 16;  // chunk 2s+h of row kb+qi
 #pragma unroll
         for (int s = 0; s < D / 16; ++s) {
-            const bf16x8 a = *reinterpret_cast<const bf16x8 *>(kp + 32 * s);
+            const bf16x8 a = *reinterpret_cast<const bf16x8 *>(kp + 2 * s * BK * 16);
             acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[s], acc, 0, 0, 0);
         }
     } else {
-        const unsigned char *kp = buf + (kb + qi) * SM::KROW + h * (D / 8) * 16;
+        const unsigned char *kp = buf + (h * (D / 8) * BK + kb + qi) * 16;
 #pragma unroll
         for (int t = 0; t < D / 8; ++t) {
-            const float4 a = *reinterpret_cast<const float4 *>(kp + 16 * t);
+            const float4 a = *reinterpret_cast<const float4 *>(kp + t * BK * 16);
             acc = __builtin_amdgcn_mfma_f32_32x32x2f32(a.x, qf[4 * t + 0], acc, 0, 0, 0);
             acc = __builtin_amdgcn_mfma_f32_32x32x2f32(a.y, qf[4 * t + 1], acc, 0, 0, 0);
             acc = __builtin_amdgcn_mfma_f32_32x32x2f32(a.z, qf[4 * t + 2], acc, 0, 0, 0);
@@ -469,10 +471,11 @@ __device__ __forceinline__ void pv_chunk(const unsigned char *buf, int kb, int k
             bre[e] = (__bf16)wre[e];
             bim[e] = (__bf16)wim[e];
         }
-        const unsigned char *vp = vb + qi * SM::VROW + ((kb >> 3) + 2 * kc + h) * 16;
+        // chunk (kb/8 + 2kc + h) of v^T row 32db + qi
+        const unsigned char *vp = vb + (((kb >> 3) + 2 * kc + h) * D + qi) * 16;
 #pragma unroll
         for (int db = 0; db < D / 32; ++db) {
-            const bf16x8 a = *reinterpret_cast<const bf16x8 *>(vp + 32 * db * SM::VROW);
+            const bf16x8 a = *reinterpret_cast<const bf16x8 *>(vp + 32 * db * 16);
             ore[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, bre, ore[db], 0, 0, 0);
             oim[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, bim, oim[db], 0, 0, 0);
         }
@@ -483,8 +486,9 @@ __device__ __forceinline__ void pv_chunk(const unsigned char *buf, int kb, int k
             const int key = kb + 8 * (s / 4) + 4 * h + (s % 4);
 #pragma unroll
             for (int db = 0; db < D / 32; ++db) {
+                const int d = 32 * db + qi;
                 const float a = *reinterpret_cast<const float *>(
-                    vb + key * SM::KROW + (32 * db + qi) * 4);
+                    vb + ((d >> 2) * BK + key) * 16 + (d & 3) * 4);
                 ore[db] = __builtin_amdgcn_mfma_f32_32x32x2f32(a, wre[e], ore[db], 0, 0, 0);
                 oim[db] = __builtin_amdgcn_mfma_f32_32x32x2f32(a, wim[e], oim[db], 0, 0, 0);
             }
@@ -497,8 +501,8 @@ __device__ __forceinline__ void pv_chunk(const unsigned char *buf, int kb, int k
 // whatever shift was last applied, so the result is the same).
 constexpr float kLazy = 8.0f;
 
-template <bool F32, int D>
-__global__ __launch_bounds__(NTHREADS, 2) void fwd_kernel(FwdArgs A) {
+template <bool F32, int D, bool QKZ>
+__global__ __launch_bounds__(NTHREADS, F32 ? 1 : 2) void fwd_kernel(FwdArgs A) {
     using SM = Smem<F32, D>;
     using FR = Frag<F32, D>;
     extern __shared__ __align__(16) unsigned char smem[];
@@ -580,6 +584,7 @@ __global__ __launch_bounds__(NTHREADS, 2) void fwd_kernel(FwdArgs A) {
     // prefix holds a closed gate sees no key before the query tile
     const bool row_live = !(A.p_m[gbase + row] == 0.0f);
     const bool wave_dead_rows = __any(!row_live);
+    bool row_live_cur = row_live;  // rows gate the off-diagonal tiles only
 
     f32x16 ore[D / 32], oim[D / 32];
 #pragma unroll
@@ -589,7 +594,9 @@ __global__ __launch_bounds__(NTHREADS, 2) void fwd_kernel(FwdArgs A) {
             ore[db][r] = 0.f;
             oim[db][r] = 0.f;
         }
-    float M = -INFINITY;  // shift of the live logits (log2 units), same in both halves
+    // shift of the live logits (log2 units), same in both halves; with qk = 0
+    // every live logit is 0 and the shift is 0 throughout
+    float M = QKZ ? 0.0f : -INFINITY;
     float z = 0.f;        // this lane's share of the normaliser
     uint32_t tiles_done = 0;
 
@@ -602,53 +609,70 @@ __global__ __launch_bounds__(NTHREADS, 2) void fwd_kernel(FwdArgs A) {
     atomicMax(&misc[2], qbits);
     __syncthreads();
 
-    // logits of one S^T block: x = S * c (qk = 0 never forms the product)
-    auto logits = [&](const unsigned char *buf, int kb, float (&x)[16]) {
-        if (A.qk_zero) {
+    // Raw scores S of one S^T block (QKZ: qk = 0 never forms the product).
+    // Logits are c*S in log2 units; c = qk log2(e)/sqrt(d) may be negative.
+    const bool cpos = A.c > 0.0f;
+    const float dead_s = cpos ? -INFINITY : INFINITY;  // a score whose logit is -inf
+    auto scores = [&](const unsigned char *buf, int kb, float (&x)[16]) {
+        if constexpr (!QKZ) {
+            const f32x16 sc = s_block<F32, D>(buf, kb, qi, h, qf);
 #pragma unroll
-            for (int r = 0; r < 16; ++r) x[r] = 0.f;
+            for (int r = 0; r < 16; ++r) x[r] = sc[r];
+        }
+    };
+    // online max of the block's live logits, with lazy rescaling of O and z;
+    // returns the shift to subtract (0 while a row has no live entry yet)
+    auto update_max = [&](const float (&x)[16]) -> float {
+        if constexpr (QKZ) {
+            return 0.0f;  // every live logit is 0: the shift stays 0
         } else {
-            const f32x16 s = s_block<F32, D>(buf, kb, qi, h, qf);
+            float ts;
+            if (cpos) {
+                ts = x[0];
+#pragma unroll
+                for (int r = 1; r < 16; ++r) ts = fmaxf(ts, x[r]);
+                ts = fmaxf(ts, __shfl_xor(ts, 32));
+            } else {
+                ts = x[0];
+#pragma unroll
+                for (int r = 1; r < 16; ++r) ts = fminf(ts, x[r]);
+                ts = fminf(ts, __shfl_xor(ts, 32));
+            }
+            float t;
             {
 #pragma clang fp contract(off)
-#pragma unroll
-                for (int r = 0; r < 16; ++r) x[r] = s[r] * A.c;
+                t = ts * A.c;  // the block's largest logit (-inf if none is live)
             }
+            const bool grow = t > M + kLazy || (M == -INFINITY && t > M);
+            if (__any(grow && M != -INFINITY)) {
+                const float alpha =
+                    (grow && M != -INFINITY) ? __builtin_amdgcn_exp2f(M - t) : 1.0f;
+#pragma unroll
+                for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) {
+                        ore[db][r] *= alpha;
+                        oim[db][r] *= alpha;
+                    }
+                z *= alpha;
+            }
+            M = grow ? t : M;
+            return (M == -INFINITY) ? 0.0f : M;
         }
     };
-    // online max over the block with lazy rescaling of O and z; returns the
-    // shift to subtract (0 while a row has no live entry yet)
-    auto update_max = [&](const float (&x)[16]) -> float {
-        float t = x[0];
-#pragma unroll
-        for (int r = 1; r < 16; ++r) t = fmaxf(t, x[r]);
-        t = fmaxf(t, __shfl_xor(t, 32));
-        const bool grow = t > M + kLazy || (M == -INFINITY && t > M);
-        if (__any(grow && M != -INFINITY)) {
-            const float alpha = (grow && M != -INFINITY) ? __builtin_amdgcn_exp2f(M - t) : 1.0f;
-#pragma unroll
-            for (int db = 0; db < D / 32; ++db)
-#pragma unroll
-                for (int r = 0; r < 16; ++r) {
-                    ore[db][r] *= alpha;
-                    oim[db][r] *= alpha;
-                }
-            z *= alpha;
-        }
-        M = grow ? t : M;
-        return (M == -INFINITY) ? 0.0f : M;
-    };
-    // exponentials, normaliser and the two W~ V products of one 16-key chunk
+    // exponentials e = 2^(c S - M), normaliser and the two W~ V products of
+    // one 16-key chunk; `live` (QKZ only) marks the entries that are not masked
     auto chunk = [&](const unsigned char *buf, int kb, int kc, const float (&x)[16], float msub,
-                     const float (&fre)[8], const float (&fim)[8], const float (&fm)[8]) {
+                     const float (&fre)[8], const float (&fim)[8], const float (&fm)[8],
+                     bool all_live) {
         float wre[8], wim[8];
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
             float ex;
-            {
-#pragma clang fp contract(off)
-                ex = __builtin_amdgcn_exp2f(x[8 * kc + e] - msub);
-            }
+            if constexpr (QKZ)
+                ex = (all_live || (fm[e] > 0.0f && row_live_cur)) ? 1.0f : 0.0f;
+            else
+                ex = __builtin_amdgcn_exp2f(fmaf(x[8 * kc + e], A.c, -msub));
             z += ex * fm[e];
             wre[e] = ex * fre[e];
             wim[e] = ex * fim[e];
@@ -679,8 +703,9 @@ __global__ __launch_bounds__(NTHREADS, 2) void fwd_kernel(FwdArgs A) {
         for (int blk = 0; blk < 2; ++blk) {
             const int kb = 32 * blk;
             float x[16];
-            logits(buf, kb, x);
-            if (wave_dead_rows || misc[blk] != 0u) {
+            scores(buf, kb, x);
+            const bool masked = wave_dead_rows || misc[blk] != 0u;
+            if (!QKZ && masked) {
 #pragma unroll
                 for (int kc = 0; kc < 2; ++kc) {
                     const float4 m0 =
@@ -690,7 +715,7 @@ __global__ __launch_bounds__(NTHREADS, 2) void fwd_kernel(FwdArgs A) {
                     const float mm[8] = {m0.x, m0.y, m0.z, m0.w, m1.x, m1.y, m1.z, m1.w};
 #pragma unroll
                     for (int e = 0; e < 8; ++e)
-                        x[8 * kc + e] = (mm[e] > 0.0f && row_live) ? x[8 * kc + e] : -INFINITY;
+                        x[8 * kc + e] = (mm[e] > 0.0f && row_live) ? x[8 * kc + e] : dead_s;
                 }
             }
             const float msub = update_max(x);
@@ -707,7 +732,7 @@ __global__ __launch_bounds__(NTHREADS, 2) void fwd_kernel(FwdArgs A) {
                     fim[e] = b.x; fim[e + 1] = b.y; fim[e + 2] = b.z; fim[e + 3] = b.w;
                     fm[e] = c.x; fm[e + 1] = c.y; fm[e + 2] = c.z; fm[e + 3] = c.w;
                 }
-                chunk(buf, kb, kc, x, msub, fre, fim, fm);
+                chunk(buf, kb, kc, x, msub, fre, fim, fm, !masked);
             }
         }
 
@@ -742,6 +767,7 @@ __global__ __launch_bounds__(NTHREADS, 2) void fwd_kernel(FwdArgs A) {
     }
 
     // ---- the query tile's own keys: explicit G_ij, last key first ---------
+    row_live_cur = true;
     float gre = 0.f, gim = 0.f, gm = 0.f;  // running G_{row,j}, R_{row,j}
     uint32_t kbits = 0;
     while (true) {
@@ -771,9 +797,11 @@ __global__ __launch_bounds__(NTHREADS, 2) void fwd_kernel(FwdArgs A) {
                 if (h == ((jj >> 2) & 1)) Gm[4 * (jj >> 3) + (jj & 3)] = gm;
             }
             float x[16];
-            logits(buf, kb, x);
+            scores(buf, kb, x);
+            if constexpr (!QKZ) {
 #pragma unroll
-            for (int r = 0; r < 16; ++r) x[r] = (Gm[r] > 0.0f) ? x[r] : -INFINITY;
+                for (int r = 0; r < 16; ++r) x[r] = (Gm[r] > 0.0f) ? x[r] : dead_s;
+            }
             const float msub = update_max(x);
             // pass 2: G_{row,j} chunk by chunk, keys 31..16 then 15..0
             gre = gre0;
@@ -797,7 +825,7 @@ __global__ __launch_bounds__(NTHREADS, 2) void fwd_kernel(FwdArgs A) {
                 }
 #pragma unroll
                 for (int e = 0; e < 8; ++e) fm[e] = Gm[8 * kc + e];
-                chunk(buf, kb, kc, x, msub, fre, fim, fm);
+                chunk(buf, kb, kc, x, msub, fre, fim, fm, false);
             }
         }
         if (!more) break;
@@ -985,13 +1013,20 @@ int launch_typed(const Problem &P, hipStream_t st, hipEvent_t const *marks) {
     F.qk_zero = P.qk_zero ? 1 : 0;
     const size_t shm = SM::bytes;
     if (shm > 65536) {
-        (void)hipFuncSetAttribute(reinterpret_cast<const void *>(&fwd_kernel<F32, D>),
+        (void)hipFuncSetAttribute(reinterpret_cast<const void *>(&fwd_kernel<F32, D, false>),
+                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)shm);
+        (void)hipFuncSetAttribute(reinterpret_cast<const void *>(&fwd_kernel<F32, D, true>),
                             hipFuncAttributeMaxDynamicSharedMemorySize, (int)shm);
         (void)hipFuncSetAttribute(reinterpret_cast<const void *>(&logit_check_kernel<F32, D>),
                             hipFuncAttributeMaxDynamicSharedMemorySize, (int)shm);
     }
     if (marks) (void)hipEventRecord(marks[1], st);
-    hipLaunchKernelGGL((fwd_kernel<F32, D>), dim3(BH * L.n_qt), dim3(NTHREADS), shm, st, F);
+    if (P.qk_zero)
+        hipLaunchKernelGGL((fwd_kernel<F32, D, true>), dim3(BH * L.n_qt), dim3(NTHREADS), shm, st,
+                           F);
+    else
+        hipLaunchKernelGGL((fwd_kernel<F32, D, false>), dim3(BH * L.n_qt), dim3(NTHREADS), shm,
+                           st, F);
     if (marks) (void)hipEventRecord(marks[2], st);
     if (!P.qk_zero)
         hipLaunchKernelGGL((logit_check_kernel<F32, D>), dim3(BH * L.n_qt), dim3(NTHREADS), shm,

@@ -1,8 +1,8 @@
 // Host check of the fused kernel's direct global->LDS copies: every 16-byte
 // source range that a workgroup can ask for lies inside its tensor.  It walks
 // every key tile of every shape given on the command line (all tiles a
-// workgroup of any query tile stages, the logit check included) and every
-// slot of the padded LDS row layout, using the same helpers as the kernel.
+// workgroup of any query tile stages, the logit check included), every row
+// and every 16-byte chunk, using the same helpers as the kernel.
 #include <cstdio>
 #include <cstdlib>
 
@@ -13,21 +13,21 @@ using namespace resolvent;
 static int check(int64_t B, int64_t H, int64_t n, int64_t d, int esz, bool bf16_path) {
     const Layout L = make_layout(B, H, n, d, bf16_path);
     const int64_t row_bytes = d * esz;
-    const int kch = int(row_bytes / 16), ksl = kch + 1;
+    const int kch = int(row_bytes / 16);
     const int64_t tensor = L.BH * n * row_bytes;
     const int64_t vt_bytes = L.BH * d * L.n_pad * 2;
     int bad = 0;
     for (int64_t bh = 0; bh < L.BH; bh += (L.BH > 2 ? L.BH - 1 : 1))
         for (int64_t t = 0; t < L.n_kt; ++t) {
-            for (int slot = 0; slot < BK * ksl; ++slot) {
-                const int c = slot % ksl;
-                const int64_t off = tile_row_src(bh, n, t, slot / ksl, row_bytes, c < kch ? c : 0);
-                if (off < 0 || off + 16 > tensor) {
-                    if (bad++ < 5)
-                        std::printf("k/v out of range: n=%lld d=%lld t=%lld slot=%d off=%lld\n",
-                                    (long long)n, (long long)d, (long long)t, slot, (long long)off);
+            for (int r = 0; r < BK; ++r)
+                for (int c = 0; c < kch; ++c) {
+                    const int64_t off = tile_row_src(bh, n, t, r, row_bytes, c);
+                    if (off < 0 || off + 16 > tensor) {
+                        if (bad++ < 5)
+                            std::printf("k/v out of range: n=%lld d=%lld t=%lld r=%d off=%lld\n",
+                                        (long long)n, (long long)d, (long long)t, r, (long long)off);
+                    }
                 }
-            }
             if (bf16_path)
                 for (int dd = 0; dd < d; ++dd)
                     for (int c = 0; c < BK * 2 / 16; ++c) {

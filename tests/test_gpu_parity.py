@@ -137,8 +137,8 @@ def test_bare_row_is_i_plus_one_bitwise():
 
 def test_closed_gates_leave_identity():
     """an_empty_sequence_is_empty_and_no_row_is_ever_all_masked: all gates
-    closed at beta = 1 gives W = I, so O = V bitwise (the one live logit of a
-    row is its own maximum, so its weight is exactly 1)."""
+    closed at beta = 1 gives W = I: O = V bitwise at qk = 0 (every weight is
+    exactly 1), and within float32 rounding of the exponent at qk = 1."""
     for qk_dtype in ("bf16", "f32"):
         inp = inputs.draw(2, 2, 333, 128, seed=11, qk_dtype=qk_dtype, v_dtype=qk_dtype)
         inp["u"][:] = 0.0
@@ -146,7 +146,7 @@ def test_closed_gates_leave_identity():
         assert np.array_equal(got.real, inp["v"].astype(np.float64))
         assert np.all(got.imag == 0)
         got = gu.gpu_forward(inp, (1, 1, 1))
-        assert np.array_equal(got.real, inp["v"].astype(np.float64))
+        assert np.abs(got.real - inp["v"]).max() <= 1e-6 * np.abs(inp["v"]).max()
         assert np.all(got.imag == 0)
 
 
