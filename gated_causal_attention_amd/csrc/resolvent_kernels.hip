@@ -306,7 +306,10 @@ struct Smem {
     static constexpr size_t k_bytes = size_t(KCH) * BK * 16;
     static constexpr size_t v_bytes = F32 ? size_t(KCH) * BK * 16 : size_t(VCH) * D * 16;
     static constexpr size_t side_off = k_bytes + v_bytes;
-    static constexpr size_t buf_bytes = side_off + 3 * BK * sizeof(float);
+    // side data: 3 x BK floats, then 2 flag words (32-key block b of the
+    // staged tile holds a dead column)
+    static constexpr size_t flag_off = side_off + 3 * BK * sizeof(float);
+    static constexpr size_t buf_bytes = flag_off + 16;
     static constexpr size_t misc_off = 2 * buf_bytes;
     static constexpr size_t bytes = misc_off + 8 * sizeof(uint32_t);
     static_assert(KCH % NWAVES == 0 && (VCH * D / 64) % NWAVES == 0, "whole wave copies");
@@ -502,18 +505,32 @@ __device__ __forceinline__ void pv_chunk(const unsigned char *buf, int kb, int k
 constexpr float kLazy = 8.0f;
 
 template <bool F32, int D, bool QKZ>
-__global__ __launch_bounds__(NTHREADS, F32 ? 1 : 2) void fwd_kernel(FwdArgs A) {
+__global__ __launch_bounds__(NTHREADS, F32 ? 1 : 2) void fwd_kernel(
+    FwdArgs A, const double *__restrict__ tre, const double *__restrict__ tim,
+    const double *__restrict__ tmm) {
+    // (the key-tile products come as separate read-only arguments so that
+    // their wave-uniform loads go through the scalar cache)
     using SM = Smem<F32, D>;
     using FR = Frag<F32, D>;
     extern __shared__ __align__(16) unsigned char smem[];
     uint32_t *misc = reinterpret_cast<uint32_t *>(smem + SM::misc_off);
-    // misc[0..1]: current tile, 32-key block b holds a dead column (off-diagonal)
-    // misc[2]: largest |q|; misc[3]: largest |k|; misc[4..5]: next tile's flags
+    // misc[2]: largest |q|; misc[3]: largest |k|
 
     const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, h = lane >> 5, qi = lane & 31;
+    // Work item of this workgroup.  Workgroups go round-robin to the 8 XCDs
+    // (L mod 8); when the heads split evenly, XCD x takes heads x, x+8, ...
+    // one at a time (its L2 then holds one head's keys and values), each
+    // head's query tiles heaviest first.
     const int L = blockIdx.x;
-    const int64_t qt = A.n_qt - 1 - L / A.BH;  // heaviest query tiles first
-    const int64_t bh = L % A.BH;
+    int64_t qt, bh;
+    if ((A.BH & 7) == 0) {
+        const int x = L & 7, j = L >> 3;
+        bh = x + 8 * (j / A.n_qt);
+        qt = A.n_qt - 1 - (j % A.n_qt);
+    } else {
+        qt = A.n_qt - 1 - L / A.BH;
+        bh = L % A.BH;
+    }
     const int64_t i0 = qt * BQ;
     const int64_t row = i0 + 32 * w + qi;
     const bool row_ok = row < A.n;
@@ -544,9 +561,10 @@ __global__ __launch_bounds__(NTHREADS, F32 ? 1 : 2) void fwd_kernel(FwdArgs A) {
             const float rt = (float)(cm * (double)g2);
             sd[2 * BK + slot] = rt;
             const uint64_t dead = __ballot(rt == 0.0f);
+            uint32_t *fl = reinterpret_cast<uint32_t *>(buf + SM::flag_off);
             if (tid == 0) {
-                misc[4] = (uint32_t)(dead & 0xFFFFFFFFull) != 0u;
-                misc[5] = (uint32_t)(dead >> 32) != 0u;
+                fl[0] = (uint32_t)(dead & 0xFFFFFFFFull) != 0u;
+                fl[1] = (uint32_t)(dead >> 32) != 0u;
             }
         } else {
             sd[tid] = g0;
@@ -602,12 +620,7 @@ __global__ __launch_bounds__(NTHREADS, F32 ? 1 : 2) void fwd_kernel(FwdArgs A) {
 
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
-    if (tid == 0) {
-        misc[0] = misc[4];
-        misc[1] = misc[5];
-    }
     atomicMax(&misc[2], qbits);
-    __syncthreads();
 
     // Raw scores S of one S^T block (QKZ: qk = 0 never forms the product).
     // Logits are c*S in log2 units; c = qk log2(e)/sqrt(d) may be negative.
@@ -687,7 +700,7 @@ __global__ __launch_bounds__(NTHREADS, F32 ? 1 : 2) void fwd_kernel(FwdArgs A) {
         const float *side = reinterpret_cast<const float *>(buf + SM::side_off);
         // the next tile, and its asynchronous copy
         const int64_t tp = bh * A.n_kt + t_cur;
-        const double are = A.t_re[tp], aim = A.t_im[tp], am = A.t_m[tp];
+        const double are = tre[tp], aim = tim[tp], am = tmm[tp];
         const double nCre = uniform_f64(are * Cre - aim * Cim);
         const double nCim = uniform_f64(are * Cim + aim * Cre);
         const double nCm = uniform_f64(am * Cm);
@@ -704,7 +717,8 @@ __global__ __launch_bounds__(NTHREADS, F32 ? 1 : 2) void fwd_kernel(FwdArgs A) {
             const int kb = 32 * blk;
             float x[16];
             scores(buf, kb, x);
-            const bool masked = wave_dead_rows || misc[blk] != 0u;
+            const bool masked = wave_dead_rows ||
+                                reinterpret_cast<const uint32_t *>(buf + SM::flag_off)[blk] != 0u;
             if (!QKZ && masked) {
 #pragma unroll
                 for (int kc = 0; kc < 2; ++kc) {
@@ -738,11 +752,6 @@ __global__ __launch_bounds__(NTHREADS, F32 ? 1 : 2) void fwd_kernel(FwdArgs A) {
 
         if (tid < BK) write_side(nbuf, t_nxt, off_nxt, nCre, nCim, nCm, g0, g1, g2);
         __builtin_amdgcn_s_waitcnt(0);
-        __syncthreads();
-        if (tid == 0) {
-            misc[0] = misc[4];
-            misc[1] = misc[5];
-        }
         __syncthreads();
         Cre = nCre;
         Cim = nCim;
@@ -1023,10 +1032,10 @@ int launch_typed(const Problem &P, hipStream_t st, hipEvent_t const *marks) {
     if (marks) (void)hipEventRecord(marks[1], st);
     if (P.qk_zero)
         hipLaunchKernelGGL((fwd_kernel<F32, D, true>), dim3(BH * L.n_qt), dim3(NTHREADS), shm, st,
-                           F);
+                           F, G.t_re, G.t_im, G.t_m);
     else
         hipLaunchKernelGGL((fwd_kernel<F32, D, false>), dim3(BH * L.n_qt), dim3(NTHREADS), shm,
-                           st, F);
+                           st, F, G.t_re, G.t_im, G.t_m);
     if (marks) (void)hipEventRecord(marks[2], st);
     if (!P.qk_zero)
         hipLaunchKernelGGL((logit_check_kernel<F32, D>), dim3(BH * L.n_qt), dim3(NTHREADS), shm,
