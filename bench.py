@@ -20,7 +20,6 @@ sys.path.insert(0, ROOT)
 
 PEAK_BF16_TFLOPS = 2516.6  # MI355X dense bf16 MFMA: 256 CU x 4096 FLOP/clk x 2.4 GHz
 PEAK_HBM_GBS = 8000.0
-BQ, BK = 128, 64  # the library's query and key tiles
 KERNEL_SOURCE = os.path.join(ROOT, "gated_causal_attention_amd", "csrc", "resolvent_kernels.hip")
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "fwd_kernel_traffic_headline.json")
 METRIC = "resolvent-head fwd TFLOP/s + Mtokens/s at n=8192,d=128; % bf16 MFMA peak"
@@ -148,6 +147,7 @@ def main():
     ms_per_step = total_ms / K
 
     # work: (query, key) pairs the fused kernel evaluated in one launch
+    BQ, BK = binding.resolvent_tile_shape()
     off_tiles = int(ws[cnt_off:cnt_off + 4].cpu().numpy().view(np.uint32)[0])
     n_qt = (n + BQ - 1) // BQ
     diag_pairs = B * H * sum(min(BQ, n - q * BQ) * (min(BQ, n - q * BQ) + 1) // 2
@@ -156,7 +156,8 @@ def main():
     flops_per_pair = 6 * d  # 2d logit + 4d complex readout (two real-by-real products)
     alg_flops = flops_per_pair * eval_pairs
     dense_flops = 3.0 * n * (n + 1) * d * B * H
-    diag_blocks_exec = B * H * n_qt * (4 * 5 // 2)  # waves w=0..3 run w+1 blocks of 32x32
+    nw = BQ // 32  # waves per query tile; wave w runs w+1 blocks of 32x32 on the diagonal
+    diag_blocks_exec = B * H * n_qt * (nw * (nw + 1) // 2)
     exec_flops = flops_per_pair * (off_tiles * BQ * BK + diag_blocks_exec * 32 * 32)
 
     achieved = alg_flops / (fwd_avg * 1e-3) / 1e12

@@ -52,6 +52,8 @@ def _load():
     lib.resolvent_forward_marked.restype = i32
     lib.resolvent_counters_offset.argtypes = [i64, i64, i64, i64, i32, i32]
     lib.resolvent_counters_offset.restype = ctypes.c_size_t
+    lib.resolvent_tile_shape.argtypes = [ctypes.POINTER(i32), ctypes.POINTER(i32)]
+    lib.resolvent_tile_shape.restype = None
     lib.resolvent_status_str.argtypes = [i32]
     lib.resolvent_status_str.restype = ctypes.c_char_p
     _lib = lib
@@ -68,6 +70,13 @@ def resolvent_workspace_bytes(B, H, n, d, qk_dtype=BF16, v_dtype=BF16) -> int:
 
 def resolvent_counters_offset(B, H, n, d, qk_dtype=BF16, v_dtype=BF16) -> int:
     return int(_load().resolvent_counters_offset(B, H, n, d, qk_dtype, v_dtype))
+
+
+def resolvent_tile_shape() -> tuple:
+    """(query rows per query tile, keys per key tile) of the library's tiling."""
+    bq, bk = ctypes.c_int32(), ctypes.c_int32()
+    _load().resolvent_tile_shape(ctypes.byref(bq), ctypes.byref(bk))
+    return bq.value, bk.value
 
 
 def _dtype_code(t):

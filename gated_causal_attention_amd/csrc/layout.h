@@ -86,6 +86,27 @@ RESOLVENT_HD inline int64_t vt_src(int64_t bh, int64_t d, int64_t n_pad, int64_t
     return ((bh * d + dd) * n_pad + t * BK) * 2 + int64_t(chunk) * 16;
 }
 
+// The same as 32-bit offsets inside one head (the kernels add them to a
+// wave-uniform head base; every offset fits 32 bits for n <= 2^22, d <= 128).
+RESOLVENT_HD inline uint32_t tile_row_off(int64_t n, int64_t t, int r, int64_t row_bytes) {
+    int64_t key = t * BK + r;
+    key = key < n ? key : n - 1;
+    return uint32_t(key * row_bytes);
+}
+RESOLVENT_HD inline uint32_t vt_row_off(int64_t n_pad, int64_t t, int dd) {
+    return uint32_t((dd * n_pad + t * BK) * 2);
+}
+
+// Float index, inside a gate plane [BH][n_pad], of the datum lane `lane`
+// copies for key tile t: S_j of key t*BK + lane (a tile before the query
+// tile), or a_{j+1} (own) -- one past the head's last position this is the
+// first entry of the next row, or of the next plane for the last head, still
+// inside the workspace and only ever multiplied into an entry above the
+// diagonal.
+RESOLVENT_HD inline int64_t gate_src(int64_t bh, int64_t n_pad, int64_t t, int lane, bool own) {
+    return bh * n_pad + t * BK + lane + (own ? 1 : 0);
+}
+
 // Everything a launch needs, in device pointers.
 struct Problem {
     const void *q, *k, *v;

@@ -50,6 +50,11 @@ size_t resolvent_counters_offset(int64_t B, int64_t H, int64_t n, int64_t d, int
     return make_layout(B, H, n, d, qk_dtype == RESOLVENT_BF16).counters;
 }
 
+void resolvent_tile_shape(int32_t *bq, int32_t *bk) {
+    if (bq) *bq = BQ;
+    if (bk) *bk = BK;
+}
+
 int32_t resolvent_forward_marked(const void *q, const void *k, const float *u,
                                  const float *theta, const void *v, double beta, double qk,
                                  double g, int64_t B, int64_t H, int64_t n, int64_t d,

@@ -134,6 +134,14 @@ int32_t resolvent_forward_marked(const void *q, const void *k, const float *u,
 size_t resolvent_counters_offset(int64_t B, int64_t H, int64_t n, int64_t d, int32_t qk_dtype,
                                  int32_t v_dtype);
 
+/*
+ * resolvent_tile_shape -- the tiling the counters above refer to: *bq query
+ * rows per query tile, *bk keys per key tile.  A counted (query tile, key
+ * tile) pair stands for bq * bk (query, key) entries.  Either pointer may be
+ * NULL.
+ */
+void resolvent_tile_shape(int32_t *bq, int32_t *bk);
+
 /* resolvent_status_str -- a static, human-readable name of a status code. */
 const char *resolvent_status_str(int32_t status);
 

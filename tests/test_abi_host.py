@@ -79,9 +79,11 @@ def test_workspace_sizes():
     ws = binding.resolvent_workspace_bytes
     assert ws(0, 1, 10, 64) == 0 and ws(1, 1, 0, 64) == 0
     assert ws(1, 1, 10, 96) == 0
-    a, b = ws(1, 1, 128, 64), ws(1, 1, 129, 64)
+    bq, bk = binding.resolvent_tile_shape()
+    assert bq % bk == 0 and bq % 32 == 0 and bk % 32 == 0
+    a, b = ws(1, 1, bq, 64), ws(1, 1, bq + 1, 64)  # one more query tile
     assert 0 < a < b
-    assert ws(1, 1, 128, 64, 1, 1) < a  # the fp32 path keeps no v^T copy
+    assert ws(1, 1, bq, 64, 1, 1) < a  # the fp32 path keeps no v^T copy
     off = binding.resolvent_counters_offset(4, 16, 8192, 128)
     assert 0 < off < ws(4, 16, 8192, 128)
     assert binding.resolvent_counters_offset(1, 1, 0, 64) == 2 ** 64 - 1
