@@ -16,12 +16,16 @@ namespace resolvent {
 // A workgroup owns BQ consecutive queries (NWAVES waves of 32 rows); keys are
 // staged BK at a time.  Gate scans use the same tiling: an inclusive prefix
 // inside each query tile and an exclusive suffix inside each key tile.
-constexpr int NWAVES = 4;
+constexpr int NWAVES = 8;
 constexpr int BQ = 32 * NWAVES;
 constexpr int BK = 64;
 static_assert(BQ % BK == 0, "a query tile must hold whole key tiles");
 
 constexpr size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+// Carry-table entries of the query tiles before query tile qt (query tile q
+// visits at most q*BQ/BK key tiles before itself).
+RESOLVENT_HD constexpr int64_t ctab_entries(int64_t qt) { return (BQ / BK) * qt * (qt - 1) / 2; }
 
 struct Layout {
     int64_t BH = 0, n = 0, d = 0;
@@ -30,7 +34,13 @@ struct Layout {
     // byte offsets into the workspace
     size_t gate[9] = {};  // a_re a_im a_m | s_re s_im s_m | p_re p_im p_m  (float [BH][n_pad])
     size_t tile[3] = {};  // A_re A_im A_m per key tile (double [BH][n_kt])
+    // per query tile qt and each key tile it visits before itself (visit s =
+    // key tile qt*BQ/BK - 1 - s): the carried gate product C from the end of
+    // that tile to the query tile, rounded to float, as (C_re, C_im, C_m, 0)
+    // (float4 [BH][ctab_entries(n_qt)], query tile qt from ctab_entries(qt))
+    size_t ctab = 0;
     size_t qstat = 0, kstat = 0;  // per query tile max |q|, max |k| bits (uint32 [BH][n_qt])
+    size_t noff = 0;  // per query tile: key tiles before it that the forward visits (int32 [BH][n_qt])
     size_t counters = 0;  // uint32 [2]: key tiles processed before the query tiles; spare
     size_t vt = 0;        // bf16 [BH][d][n_pad], keys permuted inside groups of 16
     size_t total = 0;
@@ -56,10 +66,14 @@ inline Layout make_layout(int64_t B, int64_t H, int64_t n, int64_t d, bool bf16_
         L.tile[i] = off;
         off = align_up(off + per_kt, 256);
     }
+    L.ctab = off;
+    off = align_up(off + 16 * size_t(L.BH) * size_t(ctab_entries(L.n_qt)), 256);
     const size_t per_qt = sizeof(uint32_t) * size_t(L.BH) * size_t(L.n_qt);
     L.qstat = off;
     off = align_up(off + per_qt, 256);
     L.kstat = off;
+    off = align_up(off + per_qt, 256);
+    L.noff = off;
     off = align_up(off + per_qt, 256);
     L.counters = off;
     off = align_up(off + 2 * sizeof(uint32_t), 256);
@@ -95,6 +109,71 @@ RESOLVENT_HD inline uint32_t tile_row_off(int64_t n, int64_t t, int r, int64_t r
 }
 RESOLVENT_HD inline uint32_t vt_row_off(int64_t n_pad, int64_t t, int dd) {
     return uint32_t((dd * n_pad + t * BK) * 2);
+}
+
+// bf16-path tiles in LDS are row-major -- K: BK rows of 2d bytes; v^T: d
+// rows of 2BK bytes -- with the 16-byte chunks of row r stored in the order
+// c ^ chunk_swz(r).  With CPR chunks per row (8 or 16), any 16 consecutive
+// rows then hold a given chunk in 16 different 16-byte bank groups of the
+// 256-byte bank cycle, so a half-wave reading one chunk of 16 rows has no
+// bank conflict, while one direct global->LDS wave instruction still copies
+// 1 KiB of whole, consecutive rows (lane L writes 16 bytes at 16 L).
+template <int CPR>
+RESOLVENT_HD constexpr int chunk_swz(int r) {
+    static_assert(CPR == 8 || CPR == 16, "8 or 16 chunks per row");
+    return (r >> (CPR == 16 ? 0 : 1)) & (CPR - 1);
+}
+// Copy instruction j of a tile with CPR chunks per row: lane `lane` fetches
+// chunk copy_chunk of row copy_row (and writes LDS offset 1024 j + 16 lane).
+template <int CPR>
+RESOLVENT_HD constexpr int copy_row(int j, int lane) {
+    return (64 / CPR) * j + lane / CPR;
+}
+template <int CPR>
+RESOLVENT_HD constexpr int copy_chunk(int j, int lane) {
+    return (lane % CPR) ^ chunk_swz<CPR>(copy_row<CPR>(j, lane));
+}
+// Source offsets (inside one head, 32 bits) of copy instruction j, lane
+// `lane`, of key tile t: the K copy (row_bytes = 16 CPR, rows past n clamped
+// to key n-1) and the v^T copy (8 chunks of 8 keys per row).
+template <int CPR>
+RESOLVENT_HD inline uint32_t k_copy_off(int64_t n, int64_t t, int j, int lane) {
+    return tile_row_off(n, t, copy_row<CPR>(j, lane), 16 * CPR) +
+           uint32_t(16 * copy_chunk<CPR>(j, lane));
+}
+RESOLVENT_HD inline uint32_t vt_copy_off(int64_t n_pad, int64_t t, int j, int lane) {
+    return vt_row_off(n_pad, t, copy_row<8>(j, lane)) + uint32_t(16 * copy_chunk<8>(j, lane));
+}
+// The per-lane parts of those offsets for copy instruction j (wave-uniform
+// parts excluded).  A wave that issues instructions j0, j0 + NC, j0 + 2 NC,
+// ... (NC a multiple of 4 rows' worth of instructions, so that every step
+// moves 16 rows and keeps the swizzle) adds only uniform terms:
+//   k_copy_off(n, t, j0 + NC i, lane)
+//       = t BK 16 CPR + 1024 NC i + k_lane_off(j0, lane)   (tile t inside n)
+//   vt_copy_off(n_pad, t, j0 + NC i, lane)
+//       = 2 BK t + 16 NC n_pad i + vt_lane_off(n_pad, j0, lane)
+template <int CPR>
+RESOLVENT_HD constexpr uint32_t k_lane_off(int j, int lane) {
+    return uint32_t(copy_row<CPR>(j, lane) * 16 * CPR + 16 * copy_chunk<CPR>(j, lane));
+}
+RESOLVENT_HD inline uint32_t vt_lane_off(int64_t n_pad, int j, int lane) {
+    return uint32_t(copy_row<8>(j, lane) * n_pad * 2 + 16 * copy_chunk<8>(j, lane));
+}
+// Byte offset inside a tile of the 16-byte chunk `c` of row `r`.
+template <int CPR>
+RESOLVENT_HD constexpr int tile_chunk_off(int r, int c) {
+    return r * CPR * 16 + 16 * (c ^ chunk_swz<CPR>(r));
+}
+// Matrix-operand reads.  Lane (qi, h) of a 32x32x16 bf16 product reads, for
+// step s, chunk 2s+h of K row kb+qi (kb a multiple of 32); its offset is
+// kfrag_base ^ (32 s).  For v^T it reads chunk kb/8 + 2kc + h of row
+// 32db + qi: offset (vfrag_base ^ (2kb + 32kc)) + 4096 db.
+template <int CPR>
+RESOLVENT_HD constexpr int kfrag_base(int kb, int qi, int h) {
+    return (kb + qi) * CPR * 16 + 16 * (h ^ chunk_swz<CPR>(qi));
+}
+RESOLVENT_HD constexpr int vfrag_base(int qi, int h) {
+    return qi * 128 + 16 * (h ^ chunk_swz<8>(qi));
 }
 
 // Float index, inside a gate plane [BH][n_pad], of the datum lane `lane`

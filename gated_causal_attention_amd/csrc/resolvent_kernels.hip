@@ -11,16 +11,19 @@
 // lies wholly before it,
 //     G_ij = S_j * C_t * P_i,
 // with S_j the exclusive suffix product of the gates inside key tile t, C_t
-// the product of every gate between the end of tile t and i0 (carried from
-// tile to tile as the key loop runs backwards), and P_i the inclusive prefix
-// product inside the query tile.  P_i is applied once to the accumulators
-// after the loop; the keys of the query tile itself use G_ij formed explicitly
+// the product of every gate between the end of tile t and i0 (the product of
+// the whole-tile products, accumulated in f64 as the key tiles are visited
+// backwards from the diagonal), and P_i the inclusive prefix product inside
+// the query tile.  P_i is applied once to the accumulators when the loop
+// reaches the query tile's own keys; those keys use G_ij formed explicitly
 // by a running product per row, multiplying a_i, a_{i-1}, ..., a_{j+1} in the
 // order the page's "Rust API" section fixes.
 //
 // Kernels, in launch order on the caller's stream:
 //   vt_kernel / clear_status_kernel  status := OK; (bf16 path) v -> bf16 v^T
 //   gates_kernel                     blend + gate in f64, in-tile scans
+//   schedule_kernel                  key tiles each query tile visits, and
+//                                    the carried product C_t of each visit
 //   fwd_kernel                       the fused forward (MFMA)
 //   logit_check_kernel               exact logit-overflow refusal, only for
 //                                    heads whose |q|,|k| extrema allow one
@@ -41,6 +44,9 @@ typedef __attribute__((__vector_size__(16 * sizeof(float)))) float f32x16;
 constexpr int32_t kNonFinite = 1;
 constexpr uint32_t kInfBits = 0x7F800000u;
 constexpr int NTHREADS = NWAVES * 64;
+// Waves 0 .. NCOPY-1 issue the tile copies (all of them: each wave's share
+// of a tile is small enough to fit the slack after its matrix step).
+constexpr int NCOPY = NWAVES;
 
 // Storage order of keys inside a group of 16: slot p holds key perm16(p)
 // (an involution swapping bits 2 and 3).  With it, the 8 keys that one lane
@@ -280,8 +286,13 @@ struct FwdArgs {
     const uint16_t *vt;
     const float *a_re, *a_im, *a_m, *s_re, *s_im, *s_m, *p_re, *p_im, *p_m;
     const double *t_re, *t_im, *t_m;
+    const float *ctab;    // carried gate products of the visited key tiles
+    int64_t ctab_head;    // entries per head
+    const float *gates;   // gate plane 0; plane k starts `plane` floats later
+    int64_t plane;
     float *o_re, *o_im;
     uint32_t *qstat, *kstat, *counters;
+    const int32_t *noff;
     int32_t *status;
     int64_t n, n_pad;
     int n_qt, n_kt, BH;
@@ -289,15 +300,17 @@ struct FwdArgs {
     int beta_mode, qk_zero;
 };
 
-// Shared-memory plan: two buffers, each holding one key tile K [BK][D], its
+// Shared-memory plan: NBUF buffers, each holding one key tile K [BK][D], its
 // values (bf16 path: v^T [D][BK] in perm16 key order; fp32 path: V [BK][D]),
-// and per-key side data (the carried gate factor T_j = C*S_j with its modulus
+// per-key side data (the carried gate factor T_j = C*S_j with its modulus
 // for tiles before the query tile; the gates a_{j+1} for the query tile's
-// own keys).  Tiles are stored 16-byte-chunk-major: chunk c of row r sits at
-// (c * rows + r) * 16.  One direct global->LDS wave instruction then copies
-// one chunk of 64 consecutive rows (lane L -> row L), and each half-wave of
-// an MFMA operand read touches 512 contiguous bytes (no bank conflicts), at
-// an immediate offset from one per-lane base address.
+// own keys) and the raw in-tile suffix products S_j it is formed from.
+// bf16 tiles are row-major with the 16-byte chunks of each row in a
+// row-dependent XOR order (chunk_swz): a direct global->LDS wave instruction
+// copies 1 KiB of whole consecutive rows (8 cache lines) and the MFMA
+// operand reads stay free of bank conflicts.  fp32 tiles are 16-byte-chunk-
+// major: chunk c of row r sits at (c * rows + r) * 16 (one wave instruction
+// copies one chunk of 64 rows).  Buffers start on 256-byte boundaries.
 template <bool F32, int D>
 struct Smem {
     static constexpr int ESZ = F32 ? 4 : 2;
@@ -306,13 +319,19 @@ struct Smem {
     static constexpr size_t k_bytes = size_t(KCH) * BK * 16;
     static constexpr size_t v_bytes = F32 ? size_t(KCH) * BK * 16 : size_t(VCH) * D * 16;
     static constexpr size_t side_off = k_bytes + v_bytes;
-    // side data: 3 x BK floats, then 2 flag words (32-key block b of the
-    // staged tile holds a dead column)
-    static constexpr size_t flag_off = side_off + 3 * BK * sizeof(float);
-    static constexpr size_t buf_bytes = flag_off + 16;
-    static constexpr size_t misc_off = 2 * buf_bytes;
+    // side data: 3 x BK floats; raw: S_j as 3 x BK floats and the tile's
+    // carried product C (C_re, C_im, C_m, 0) as floats; then 2 flag words
+    // (32-key block b of the staged tile holds a dead column)
+    static constexpr size_t raw_off = side_off + 3 * BK * sizeof(float);
+    static constexpr size_t carry_off = raw_off + 3 * BK * sizeof(float);
+    static constexpr size_t flag_off = carry_off + 4 * sizeof(float);
+    static constexpr size_t buf_bytes = (flag_off + 16 + 255) / 256 * 256;
+    // four buffers keep two tiles in flight while two are read; the fp32
+    // d=128 tiles only fit twice into the 160 KB of LDS
+    static constexpr int NBUF = (F32 && D == 128) ? 2 : 4;
+    static constexpr size_t misc_off = NBUF * buf_bytes;
     static constexpr size_t bytes = misc_off + 8 * sizeof(uint32_t);
-    static_assert(KCH % NWAVES == 0 && (VCH * D / 64) % NWAVES == 0, "whole wave copies");
+    static_assert(KCH % NCOPY == 0 && (VCH * D / 64) % NCOPY == 0, "whole wave copies");
 };
 
 template <bool F32, int D>
@@ -323,16 +342,111 @@ struct Frag {
 
 typedef __attribute__((address_space(3))) void lds_void;
 
-// A wave-uniform double kept in scalar registers.
-__device__ __forceinline__ double uniform_f64(double x) {
-    const uint64_t b = __builtin_bit_cast(uint64_t, x);
+// A wave-uniform pointer kept in scalar registers (also keeps the compiler
+// from folding a per-lane offset into it and hoisting 64-bit lane addresses).
+template <typename T>
+__device__ __forceinline__ const T *uniform_ptr(const T *p) {
+    const uint64_t b = reinterpret_cast<uint64_t>(p);
     const uint32_t lo = __builtin_amdgcn_readfirstlane(uint32_t(b));
     const uint32_t hi = __builtin_amdgcn_readfirstlane(uint32_t(b >> 32));
-    return __builtin_bit_cast(double, (uint64_t(hi) << 32) | lo);
+    return reinterpret_cast<const T *>((uint64_t(hi) << 32) | lo);
 }
 
-__device__ __forceinline__ void g2lds16(const void *g, unsigned char *lds) {
-    __builtin_amdgcn_global_load_lds(g, (lds_void *)(lds), 16, 0, 0);
+// The lane index, computed where it is used: the compiler can neither hoist
+// nor merge the asm statement, so per-lane copy offsets derived from it are
+// recomputed inside the loop instead of held in registers across it.
+__device__ __forceinline__ int fresh_lane() {
+    int l;
+    asm volatile("v_mbcnt_lo_u32_b32 %0, -1, 0\n\tv_mbcnt_hi_u32_b32 %0, -1, %0" : "=v"(l));
+    return l;
+}
+
+// LDS byte address of a pointer into the workgroup's shared memory.
+__device__ __forceinline__ uint32_t lds_addr(const unsigned char *p) {
+    return (uint32_t)(uintptr_t)(lds_void *)(p);
+}
+
+// Direct global->LDS copy of 16 bytes per lane: lane L reads base + off and
+// writes LDS address lds + 16 L; base and lds (a byte address) are
+// wave-uniform.  Written as
+// inline assembly so that the compiler does not track it as an LDS store: its
+// aliasing rules would otherwise hold every later LDS read of any buffer until
+// the copy lands.  Readers wait for the copy explicitly (wait_vmcnt() and a
+// barrier).  m0 carries the LDS address and is restored afterwards.
+__device__ __forceinline__ void g2lds16(const unsigned char *base, uint32_t off, uint32_t lds) {
+    const uint32_t la = __builtin_amdgcn_readfirstlane(lds);
+    uint32_t saved;
+    asm volatile(
+        "s_mov_b32 %0, m0\n\t"
+        "s_mov_b32 m0, %3\n\t"
+        "s_nop 0\n\t"
+        "global_load_lds_dwordx4 %1, %2\n\t"
+        "s_mov_b32 m0, %0"
+        : "=&s"(saved)
+        : "v"(off), "s"(base), "s"(la)
+        : "memory");
+}
+
+// The same for 4 bytes per lane (lane L writes lds + 4 L).
+__device__ __forceinline__ void g2lds4(const unsigned char *base, uint32_t off, uint32_t lds) {
+    const uint32_t la = __builtin_amdgcn_readfirstlane(lds);
+    uint32_t saved;
+    asm volatile(
+        "s_mov_b32 %0, m0\n\t"
+        "s_mov_b32 m0, %3\n\t"
+        "s_nop 0\n\t"
+        "global_load_lds_dword %1, %2\n\t"
+        "s_mov_b32 m0, %0"
+        : "=&s"(saved)
+        : "v"(off), "s"(base), "s"(la)
+        : "memory");
+}
+
+// 16 bytes in lane 0 only (lane 0 reads base + off and writes lds; the other
+// lanes are masked off for the one instruction and restored).
+__device__ __forceinline__ void g2lds16x1(const unsigned char *base, uint32_t off, uint32_t lds) {
+    const uint32_t la = __builtin_amdgcn_readfirstlane(lds);
+    uint32_t saved;
+    uint64_t ex;
+    asm volatile(
+        "s_mov_b64 %1, exec\n\t"
+        "s_mov_b64 exec, 1\n\t"
+        "s_mov_b32 %0, m0\n\t"
+        "s_mov_b32 m0, %4\n\t"
+        "s_nop 0\n\t"
+        "global_load_lds_dwordx4 %2, %3\n\t"
+        "s_mov_b32 m0, %0\n\t"
+        "s_mov_b64 exec, %1"
+        : "=&s"(saved), "=&s"(ex)
+        : "v"(off), "s"(base), "s"(la)
+        : "memory");
+}
+
+// s_waitcnt vmcnt(N) for a compile-time N (gfx9 encoding: low bits 3:0,
+// high bits 15:14; expcnt and lgkmcnt left at their maxima).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
+
+// Workgroup barrier that waits for the wave's own LDS operations only, not
+// for its copies in flight (the __syncthreads() of HIP also waits on vmcnt).
+// Keeps the computation of v before this point: the empty asm statement reads
+// it, and volatile asm statements keep their order.  (lds_barrier orders
+// memory operations only; arithmetic whose result is first used after a
+// barrier may otherwise be sunk past it, into the next phase.)
+template <typename T>
+__device__ __forceinline__ void settle(const T &v) {
+    asm volatile("" ::"v"(v));
+}
+
+__device__ __forceinline__ void lds_barrier() {
+    __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+    __builtin_amdgcn_s_barrier();
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
 }
 
 // Query fragment (B operand of S^T = K Q^T) for the lane's row; returns the
@@ -367,63 +481,83 @@ __device__ __forceinline__ uint32_t load_q(const FwdArgs &A, int64_t bh, int64_t
 }
 
 // Start the asynchronous copy of key tile t (K, and the values unless
-// k_only) into buffer buf.  Wave w copies chunks w, w+NWAVES, ...: lane L
-// fetches 16 bytes of row L.  Keys past n repeat key n-1 (their entries are
-// masked); the v^T copy is zero there.
+// k_only) into buffer buf (an LDS byte address).  Wave w < NCOPY copies
+// chunks w, w+NCOPY, ...: lane L fetches 16 bytes of row L; other waves copy
+// nothing.  Keys past n repeat key n-1 (their entries are
+// masked); the v^T copy is zero there.  kh, vh: this head's rows of k and of
+// v^T (bf16 path) or v (fp32 path), wave-uniform.
 template <bool F32, int D>
-__device__ __forceinline__ void stage_async(const FwdArgs &A, unsigned char *buf, int64_t bh,
-                                            int64_t t, bool k_only) {
+__device__ __forceinline__ void stage_async(const FwdArgs &A, uint32_t buf,
+                                            const unsigned char *kh, const unsigned char *vh,
+                                            int t, bool k_only, int w) {
     using SM = Smem<F32, D>;
-    const int lane = threadIdx.x & 63;
-    const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    constexpr int64_t ROWB = D * SM::ESZ;  // bytes per q/k/v row in memory
-    // head base (uniform) + 32-bit offset of row `lane` of the tile (clamped)
-    const int64_t hbase = bh * A.n * ROWB;
-    const uint32_t koff = uint32_t(tile_row_src(bh, A.n, t, lane, ROWB, 0) - hbase);
-    const unsigned char *kh = static_cast<const unsigned char *>(A.k) + hbase;
-#pragma unroll
-    for (int i = 0; i < SM::KCH / NWAVES; ++i) {
-        const int c = w + NWAVES * i;
-        g2lds16(kh + (koff + uint32_t(c * 16)), buf + c * 1024);
-    }
-    if (k_only) return;
+    const int lane = fresh_lane();
+    if (w >= NCOPY) return;
+    constexpr int ROWB = D * SM::ESZ;  // bytes per q/k/v row in memory
     if constexpr (!F32) {
-        // v^T rows d = lane + 64 grp, chunks of 8 keys
-        const int64_t vbase = bh * D * A.n_pad * 2;
-        const uint32_t voff = uint32_t(vt_src(bh, D, A.n_pad, t, lane, 0) - vbase);
-        const uint32_t row64 = uint32_t(64 * A.n_pad * 2);
-        const unsigned char *vh = reinterpret_cast<const unsigned char *>(A.vt) + vbase;
-        constexpr int NI = SM::VCH * D / 64 / NWAVES;
+        // K: instruction j copies whole rows (64/CPR) j, ... of the tile
+        constexpr int CPR = D / 8;
+#pragma unroll
+        for (int i = 0; i < SM::KCH / NCOPY; ++i) {
+            const int j = w + NCOPY * i;
+            g2lds16(kh, k_copy_off<CPR>(A.n, t, j, lane), buf + uint32_t(j * 1024));
+        }
+        if (k_only) return;
+        // v^T: instruction j copies rows d = 8 j, ..., 8 j + 7 (keys of tile t)
+        constexpr int NI = SM::VCH * D / 64 / NCOPY;
 #pragma unroll
         for (int i = 0; i < NI; ++i) {
-            const int idx = w + NWAVES * i;  // (chunk, 64-row group)
-            const int c = idx % SM::VCH, grp = idx / SM::VCH;
-            g2lds16(vh + (voff + uint32_t(grp) * row64 + uint32_t(c * 16)),
-                    buf + SM::k_bytes + (c * D + 64 * grp) * 16);
+            const int j = w + NCOPY * i;
+            g2lds16(vh, vt_copy_off(A.n_pad, t, j, lane),
+                    buf + uint32_t(SM::k_bytes + j * 1024));
         }
     } else {
-        const unsigned char *vh = static_cast<const unsigned char *>(A.v) + hbase;
+        const uint32_t koff = tile_row_off(A.n, t, lane, ROWB);
 #pragma unroll
-        for (int i = 0; i < SM::KCH / NWAVES; ++i) {
-            const int c = w + NWAVES * i;
-            g2lds16(vh + (koff + uint32_t(c * 16)), buf + SM::k_bytes + c * 1024);
+        for (int i = 0; i < SM::KCH / NCOPY; ++i) {
+            const int c = w + NCOPY * i;
+            g2lds16(kh, koff + uint32_t(c * 16), buf + uint32_t(c * 1024));
+        }
+        if (k_only) return;
+#pragma unroll
+        for (int i = 0; i < SM::KCH / NCOPY; ++i) {
+            const int c = w + NCOPY * i;
+            g2lds16(vh, koff + uint32_t(c * 16), buf + uint32_t(SM::k_bytes + c * 1024));
         }
     }
 }
 
-// Largest |k| over the staged key tile, keys below n only (float bits).
+// Head bases of the tile copies (wave-uniform).
 template <bool F32, int D>
-__device__ __forceinline__ uint32_t tile_kbits(const FwdArgs &A, const unsigned char *buf,
-                                               int64_t t) {
+__device__ __forceinline__ void head_bases(const FwdArgs &A, int64_t bh, const unsigned char *&kh,
+                                           const unsigned char *&vh) {
+    constexpr int64_t ROWB = D * Smem<F32, D>::ESZ;
+    kh = uniform_ptr(static_cast<const unsigned char *>(A.k) + bh * A.n * ROWB);
+    if constexpr (!F32)
+        vh = uniform_ptr(reinterpret_cast<const unsigned char *>(A.vt) + bh * D * A.n_pad * 2);
+    else
+        vh = uniform_ptr(static_cast<const unsigned char *>(A.v) + bh * A.n * ROWB);
+}
+
+// Largest |k| (float bits) over the K bytes of key tile t that wave w copied
+// itself (stage_async: its copy instructions j = w, w+NCOPY, ... wrote LDS
+// offset 1024 j + 16 lane).  A row past the sequence end holds a copy of key
+// n-1.  Valid once the wave's own copies have landed.
+template <bool F32, int D>
+__device__ __forceinline__ uint32_t own_kbits(const FwdArgs &A, const unsigned char *buf,
+                                              int64_t t, int w) {
     using SM = Smem<F32, D>;
     uint32_t bits = 0;
-    for (int u = threadIdx.x; u < SM::KCH * BK; u += NTHREADS) {
-        if (t * BK + (u % BK) >= A.n) continue;
-        const uint4 v = *reinterpret_cast<const uint4 *>(buf + u * 16);
-        if constexpr (F32)
-            bits = max(bits, absbits_f4(__builtin_bit_cast(float4, v)));
-        else
-            bits = max(bits, absbits_u4_bf16(v));
+    if (w < NCOPY) {
+#pragma unroll
+        for (int i = 0; i < SM::KCH / NCOPY; ++i) {
+            const int j = w + NCOPY * i;
+            const uint4 v = *reinterpret_cast<const uint4 *>(buf + (j * 64 + fresh_lane()) * 16);
+            if constexpr (F32)
+                bits = max(bits, absbits_f4(__builtin_bit_cast(float4, v)));
+            else
+                bits = max(bits, absbits_u4_bf16(v));
+        }
     }
     return bits;
 }
@@ -433,15 +567,14 @@ __device__ __forceinline__ uint32_t tile_kbits(const FwdArgs &A, const unsigned 
 template <bool F32, int D>
 __device__ __forceinline__ f32x16 s_block(const unsigned char *buf, int kb, int qi, int h,
                                           const typename Frag<F32, D>::type (&qf)[Frag<F32, D>::count]) {
-    using SM = Smem<F32, D>;
     f32x16 acc;
 #pragma unroll
     for (int r = 0; r < 16; ++r) acc[r] = 0.f;
     if constexpr (!F32) {
-        const unsigned char *kp = buf + (h * BK + kb + qi) * 16;  // chunk 2s+h of row kb+qi
+        const int kf = kfrag_base<D / 8>(kb, qi, h);  // chunk 2s+h of row kb+qi: kf ^ 32s
 #pragma unroll
         for (int s = 0; s < D / 16; ++s) {
-            const bf16x8 a = *reinterpret_cast<const bf16x8 *>(kp + 2 * s * BK * 16);
+            const bf16x8 a = *reinterpret_cast<const bf16x8 *>(buf + (kf ^ (32 * s)));
             acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[s], acc, 0, 0, 0);
         }
     } else {
@@ -458,45 +591,121 @@ __device__ __forceinline__ f32x16 s_block(const unsigned char *buf, int kb, int 
     return acc;
 }
 
-// O^T += V^T W~^T for the 16 keys of chunk kc (registers 8kc..8kc+7 of the
-// S^T block at kb): two accumulators, one for Re W~ and one for Im W~, that
-// share the V operand.
-template <bool F32, int D>
-__device__ __forceinline__ void pv_chunk(const unsigned char *buf, int kb, int kc, int qi, int h,
-                                         const float (&wre)[8], const float (&wim)[8],
-                                         f32x16 (&ore)[D / 32], f32x16 (&oim)[D / 32]) {
-    using SM = Smem<F32, D>;
-    const unsigned char *vb = buf + SM::k_bytes;
-    if constexpr (!F32) {
-        bf16x8 bre, bim;
+// O^T += V^T W~^T for one 32-key block at kb (bf16 path), W~ packed per
+// 16-key chunk kc as the B operand (registers 8kc..8kc+7 of the S^T block):
+// two accumulators, one for Re W~ and one for Im W~, share the V operand.
+template <int D>
+__device__ __forceinline__ void pv_block_bf16(const unsigned char *buf, int kb, int qi, int h,
+                                              const bf16x8 (&wr)[2], const bf16x8 (&wi)[2],
+                                              f32x16 (&ore)[D / 32], f32x16 (&oim)[D / 32]) {
+    const unsigned char *vb = buf + Smem<false, D>::k_bytes;
+    const int vf = vfrag_base(qi, h);
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-            bre[e] = (__bf16)wre[e];
-            bim[e] = (__bf16)wim[e];
-        }
+    for (int kc = 0; kc < 2; ++kc) {
         // chunk (kb/8 + 2kc + h) of v^T row 32db + qi
-        const unsigned char *vp = vb + (((kb >> 3) + 2 * kc + h) * D + qi) * 16;
+        const unsigned char *vp = vb + (vf ^ (2 * kb + 32 * kc));
 #pragma unroll
         for (int db = 0; db < D / 32; ++db) {
-            const bf16x8 a = *reinterpret_cast<const bf16x8 *>(vp + 32 * db * 16);
-            ore[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, bre, ore[db], 0, 0, 0);
-            oim[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, bim, oim[db], 0, 0, 0);
-        }
-    } else {
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-            const int s = 8 * kc + e;
-            const int key = kb + 8 * (s / 4) + 4 * h + (s % 4);
-#pragma unroll
-            for (int db = 0; db < D / 32; ++db) {
-                const int d = 32 * db + qi;
-                const float a = *reinterpret_cast<const float *>(
-                    vb + ((d >> 2) * BK + key) * 16 + (d & 3) * 4);
-                ore[db] = __builtin_amdgcn_mfma_f32_32x32x2f32(a, wre[e], ore[db], 0, 0, 0);
-                oim[db] = __builtin_amdgcn_mfma_f32_32x32x2f32(a, wim[e], oim[db], 0, 0, 0);
-            }
+            const bf16x8 a = *reinterpret_cast<const bf16x8 *>(vp + 32 * db * 128);
+            ore[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, wr[kc], ore[db], 0, 0, 0);
+            oim[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, wi[kc], oim[db], 0, 0, 0);
         }
     }
+}
+
+// The same for the 16 keys of chunk kc on the fp32 path (fp32 V rows).
+template <int D>
+__device__ __forceinline__ void pv_chunk_f32(const unsigned char *buf, int kb, int kc, int qi,
+                                             int h, const float (&wre)[8], const float (&wim)[8],
+                                             f32x16 (&ore)[D / 32], f32x16 (&oim)[D / 32]) {
+    const unsigned char *vb = buf + Smem<true, D>::k_bytes;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+        const int s = 8 * kc + e;
+        const int key = kb + 8 * (s / 4) + 4 * h + (s % 4);
+#pragma unroll
+        for (int db = 0; db < D / 32; ++db) {
+            const int d = 32 * db + qi;
+            const float a =
+                *reinterpret_cast<const float *>(vb + ((d >> 2) * BK + key) * 16 + (d & 3) * 4);
+            ore[db] = __builtin_amdgcn_mfma_f32_32x32x2f32(a, wre[e], ore[db], 0, 0, 0);
+            oim[db] = __builtin_amdgcn_mfma_f32_32x32x2f32(a, wim[e], oim[db], 0, 0, 0);
+        }
+    }
+}
+
+// Matrix step of the bf16 path: O^T += V^T W~^T for the block at (bv, kbv)
+// (PV) and S^T = K Q^T for the block at (bs, kbs) into sacc (S).  The S
+// products form one accumulation chain, so each sits between two W~ V
+// products (a dependent matrix instruction then never waits on the one
+// before).  K and v^T fragments stream through four-deep pipelines (LDS
+// latency under load is a few hundred cycles); scheduling fences keep the
+// order.
+constexpr int MDEPTH = 4;
+struct MPrefetch {
+    bf16x8 vf[MDEPTH], kf[MDEPTH];
+};
+template <int D>
+__device__ __forceinline__ bf16x8 mstep_vload(const unsigned char *bv, int vf, int kbv, int i) {
+    // chunk (kbv/8 + 2kc + h) of v^T row 32db + qi, fragment i = (kc, db)
+    const int kc = i / (D / 32), db = i % (D / 32);
+    return *reinterpret_cast<const bf16x8 *>(bv + Smem<false, D>::k_bytes + 4096 * db +
+                                             (vf ^ (2 * kbv + 32 * kc)));
+}
+__device__ __forceinline__ bf16x8 mstep_kload(const unsigned char *bs, int kf, int i) {
+    // chunk 2i+h of K row kbs+qi
+    return *reinterpret_cast<const bf16x8 *>(bs + (kf ^ (32 * i)));
+}
+// Operand fragments [I0, I1) of each kind of a matrix step (mstep_bf16 with
+// NPRE = I1 then starts from the first NPRE of them).
+template <int D, bool PV, bool S, int I0, int I1>
+__device__ __forceinline__ void mstep_prefetch(const unsigned char *bv, int kbv,
+                                               const unsigned char *bs, int kbs, int qi, int h,
+                                               MPrefetch &pf) {
+    constexpr int NV = PV ? 2 * (D / 32) : 0;
+    constexpr int NK = S ? D / 16 : 0;
+    const int vf = vfrag_base(qi, h);
+    const int kf = kfrag_base<D / 8>(kbs, qi, h);
+#pragma unroll
+    for (int i = I0; i < I1; ++i) {
+        if (i < NV) pf.vf[i] = mstep_vload<D>(bv, vf, kbv, i);
+        if (i < NK) pf.kf[i] = mstep_kload(bs, kf, i);
+    }
+}
+template <int D, bool PV, bool S, int NPRE>
+__device__ __forceinline__ void mstep_bf16(const unsigned char *bv, int kbv,
+                                           const unsigned char *bs, int kbs, int qi, int h,
+                                           MPrefetch &pf, const bf16x8 (&wr)[2],
+                                           const bf16x8 (&wi)[2], const bf16x8 (&qf)[D / 16],
+                                           f32x16 (&ore)[D / 32], f32x16 (&oim)[D / 32],
+                                           f32x16 &sacc) {
+    constexpr int NDB = D / 32;
+    constexpr int NV = PV ? 2 * NDB : 0;  // v^T fragments: chunk kc, row block db
+    constexpr int NK = S ? D / 16 : 0;    // K fragments
+    constexpr int NSTEP = NV > NK ? NV : NK;
+    const int vf = vfrag_base(qi, h);
+    const int kf = kfrag_base<D / 8>(kbs, qi, h);
+    mstep_prefetch<D, PV, S, NPRE, MDEPTH>(bv, kbv, bs, kbs, qi, h, pf);
+    if constexpr (S) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) sacc[r] = 0.f;
+    }
+#pragma unroll
+    for (int i = 0; i < NSTEP; ++i) {
+        __builtin_amdgcn_sched_barrier(0);
+        if (i < NV) {
+            const int kc = i / NDB, db = i % NDB;
+            const bf16x8 a = pf.vf[i % MDEPTH];
+            ore[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, wr[kc], ore[db], 0, 0, 0);
+            oim[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, wi[kc], oim[db], 0, 0, 0);
+            if (i + MDEPTH < NV) pf.vf[i % MDEPTH] = mstep_vload<D>(bv, vf, kbv, i + MDEPTH);
+        }
+        if (i < NK) {
+            sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(pf.kf[i % MDEPTH], qf[i], sacc, 0, 0, 0);
+            if (i + MDEPTH < NK) pf.kf[i % MDEPTH] = mstep_kload(bs, kf, i + MDEPTH);
+        }
+    }
+    __builtin_amdgcn_sched_barrier(0);
 }
 
 // Lazy rescaling: the shift M only moves when a logit exceeds it by more than
@@ -504,19 +713,141 @@ __device__ __forceinline__ void pv_chunk(const unsigned char *buf, int kb, int k
 // whatever shift was last applied, so the result is the same).
 constexpr float kLazy = 8.0f;
 
+// --------------------------------------------------------------------------
+// Visit count and carried gate products per query tile.  The key tiles before
+// query tile qt are visited last to first; visit s carries
+//     C_s = A_{t0-1} A_{t0-2} ... A_{t0-s}   (C_0 = 1; A_t the whole-tile
+// product of key tile t, t0 the query tile's first key tile), the gate
+// product from the end of the visited tile up to the query tile.  C is
+// accumulated in f64 in visiting order and stored rounded to float; the
+// visits stop after the tile whose product makes the modulus of C zero in
+// float32: every key before it sits behind a closed gate (section "Object")
+// and is exactly dead.  One wave per query tile: the lanes fetch 64 tile
+// products at a time and the product is accumulated in order.
+__global__ __launch_bounds__(64) void schedule_kernel(const double *__restrict__ tre,
+                                                      const double *__restrict__ tim,
+                                                      const double *__restrict__ tmm, int n_kt,
+                                                      int n_qt, int32_t *__restrict__ noff,
+                                                      float *__restrict__ ctab,
+                                                      int64_t ctab_head) {
+#pragma clang fp contract(off)
+    const int L = blockIdx.x;
+    const int64_t bh = L / n_qt;
+    const int qt = L % n_qt;
+    const int lane = threadIdx.x;
+    const int t0 = qt * (BQ / BK);  // first key tile of the query tile
+    const double *pr = tre + bh * n_kt, *pi = tim + bh * n_kt, *pm = tmm + bh * n_kt;
+    float *cq = ctab + 4 * (bh * ctab_head + ctab_entries(qt));
+    double cr = 1.0, ci = 0.0, cm = 1.0;
+    int result = t0;  // every tile before the query tile
+    auto lane_f64 = [](double x, int s) {
+        const uint64_t bits = __builtin_bit_cast(uint64_t, x);
+        const uint32_t lo = __builtin_amdgcn_readlane(uint32_t(bits), s);
+        const uint32_t hi = __builtin_amdgcn_readlane(uint32_t(bits >> 32), s);
+        return __builtin_bit_cast(double, (uint64_t(hi) << 32) | lo);
+    };
+    for (int base = 0; base < t0; base += 64) {
+        const bool valid = base + lane < t0;
+        const int t = t0 - 1 - (base + lane);
+        const double ar = valid ? pr[t] : 1.0, ai = valid ? pi[t] : 0.0,
+                     am = valid ? pm[t] : 1.0;
+        const int cnt = min(64, t0 - base);
+        float mr = 0.f, mi = 0.f, mm = 0.f;  // C of this lane's visit
+        int found = -1;
+        for (int s = 0; s < cnt; ++s) {
+            if (lane == s) {
+                mr = (float)cr;
+                mi = (float)ci;
+                mm = (float)cm;
+            }
+            const double xr = lane_f64(ar, s), xi = lane_f64(ai, s), xm = lane_f64(am, s);
+            const double nr = xr * cr - xi * ci;
+            const double ni = xr * ci + xi * cr;
+            cm = xm * cm;
+            cr = nr;
+            ci = ni;
+            if (base + s == t0 - 1 || (float)cm == 0.0f) {
+                found = base + s + 1;
+                break;
+            }
+        }
+        if (valid && (found < 0 || base + lane < found)) {
+            float4 e;
+            e.x = mr;
+            e.y = mi;
+            e.z = mm;
+            e.w = 0.f;
+            reinterpret_cast<float4 *>(cq)[base + lane] = e;
+        }
+        if (found >= 0) {
+            result = found;
+            break;
+        }
+    }
+    if (lane == 0) noff[L] = result;
+}
+
+// Weights W~ of one 32-key block as the B operand of O^T += V^T W~^T, per
+// 16-key chunk kc (bf16: packed; fp32: 8 floats per lane).
+template <bool F32>
+struct BlockW {
+    bf16x8 r[2], i[2];
+};
+template <>
+struct BlockW<true> {
+    float r[2][8], i[2][8];
+};
+
+// O^T += V^T W~^T for the 32-key block at kb of a staged tile.
+template <bool F32, int D>
+__device__ __forceinline__ void pv_block(const unsigned char *buf, int kb, int qi, int h,
+                                         const BlockW<F32> &wb, f32x16 (&ore)[D / 32],
+                                         f32x16 (&oim)[D / 32]) {
+    if constexpr (F32) {
+#pragma unroll
+        for (int kc = 0; kc < 2; ++kc) pv_chunk_f32<D>(buf, kb, kc, qi, h, wb.r[kc], wb.i[kc], ore, oim);
+    } else {
+        pv_block_bf16<D>(buf, kb, qi, h, wb.r, wb.i, ore, oim);
+    }
+}
+
+// Fused forward.  A workgroup owns the BQ queries [i0, i0+BQ) of one head;
+// wave w owns rows i0+32w .. i0+32w+31.  Keys go in 32-key blocks, tile by
+// tile: the n_off key tiles before the query tile that the visit count
+// allows, last to first, then the query tile's own NDIAG tiles, last to first.
+//
+// Each block k passes through two steps of a wave:
+//   M(k)  matrix step: O += W~(k-1) V(k-1) and S(k) = K(k) Q^T;
+//   V(k)  vector step: masks, shift, exponentials and gate factors of block
+//         k, giving W~(k) packed as the next B operand (the fp32 path adds
+//         W~(k) V(k) right there).
+// The workgroup advances in phases separated by LDS-only barriers.  Waves
+// 0..3 run step p in phase p and waves 4..7 one phase later, so the two
+// waves that share a SIMD (w and w+4) alternate between matrix and vector
+// work.  Key tiles, and the gate data of their side data, are copied
+// asynchronously into NBUF rotating LDS buffers phases ahead of use; what is
+// copied and landed in a phase is a function of the phase number alone, and
+// every vector-memory operation in the phase loops is such a copy, waited
+// for with exact counts.
 template <bool F32, int D, bool QKZ>
-__global__ __launch_bounds__(NTHREADS, F32 ? 1 : 2) void fwd_kernel(
-    FwdArgs A, const double *__restrict__ tre, const double *__restrict__ tim,
-    const double *__restrict__ tmm) {
-    // (the key-tile products come as separate read-only arguments so that
-    // their wave-uniform loads go through the scalar cache)
+__global__ __launch_bounds__(NTHREADS, 1) void fwd_kernel(FwdArgs A) {
     using SM = Smem<F32, D>;
     using FR = Frag<F32, D>;
+    using WB = BlockW<F32>;
+    constexpr int NBUF = SM::NBUF;
+    constexpr int NDIAG = BQ / BK;    // key tiles inside the query tile
+    constexpr int NDB = 2 * NDIAG;    // 32-key blocks inside the query tile
+    // copies a leading wave issues per tile: its K and V chunks (wave 0 also
+    // the three gate planes of the side data and the tile's product)
+    constexpr int VM_TILE = SM::KCH / NCOPY + (F32 ? SM::KCH / NCOPY : SM::VCH * D / 64 / NCOPY);
+    static_assert(VM_TILE + 4 < 64, "vmcnt range");
     extern __shared__ __align__(16) unsigned char smem[];
     uint32_t *misc = reinterpret_cast<uint32_t *>(smem + SM::misc_off);
     // misc[2]: largest |q|; misc[3]: largest |k|
 
-    const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, h = lane >> 5, qi = lane & 31;
+    const int tid = threadIdx.x, lane = tid & 63, h = lane >> 5, qi = lane & 31;
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int lag = w / (NWAVES / 2);  // 0: leading waves, 1: trailing waves
     // Work item of this workgroup.  Workgroups go round-robin to the 8 XCDs
     // (L mod 8); when the heads split evenly, XCD x takes heads x, x+8, ...
     // one at a time (its L2 then holds one head's keys and values), each
@@ -535,74 +866,195 @@ __global__ __launch_bounds__(NTHREADS, F32 ? 1 : 2) void fwd_kernel(
     const int64_t row = i0 + 32 * w + qi;
     const bool row_ok = row < A.n;
     const int64_t gbase = bh * A.n_pad;
-    const int64_t t_diag0 = i0 / BK;            // first key tile of the query tile
-    constexpr int NDIAG = BQ / BK;
+    const int t_diag0 = int(i0 / BK);  // first key tile of the query tile
+    const int n_off = __builtin_amdgcn_readfirstlane(A.noff[bh * A.n_qt + qt]);
+    const int n_tiles = n_off + NDIAG;
+    const unsigned char *kh, *vh;
+    head_bases<F32, D>(A, bh, kh, vh);
 
     if (tid == 0) {
         misc[2] = 0;
         misc[3] = 0;
     }
 
-    // ---- the tile schedule: off-diagonal tiles last to first while the
-    // carried modulus is non-zero in float32, then the query tile's own tiles
-    int64_t t_cur = t_diag0 > 0 ? t_diag0 - 1 : t_diag0 + NDIAG - 1;
-    bool off_cur = t_diag0 > 0;
-    double Cre = 1.0, Cim = 0.0, Cm = 1.0;  // carried gates: end of t_cur .. i0-1
+    // key tile visited at schedule position sg, and its buffer
+    auto tile_of = [&](int sg) __attribute__((always_inline)) {
+        return sg < n_off ? t_diag0 - 1 - sg : t_diag0 + NDIAG - 1 - (sg - n_off);
+    };
+    auto tile_buf = [&](int sg) __attribute__((always_inline)) {
+        return smem + (sg % NBUF) * SM::buf_bytes;
+    };
 
-    // side data of a tile, written by wave 0 into a buffer: T_j = C S_j
-    // (off-diagonal) or the gates a_{j+1} (the query tile's own keys)
-    auto write_side = [&](unsigned char *buf, int64_t t, bool off, double cr, double ci,
-                          double cm, float g0, float g1, float g2) {
-        float *sd = reinterpret_cast<float *>(buf + SM::side_off);
-        if (off) {
-            const int slot = perm64(tid);
-            sd[slot] = (float)(cr * (double)g0 - ci * (double)g1);
-            sd[BK + slot] = (float)(cr * (double)g1 + ci * (double)g0);
-            const float rt = (float)(cm * (double)g2);
-            sd[2 * BK + slot] = rt;
-            const uint64_t dead = __ballot(rt == 0.0f);
-            uint32_t *fl = reinterpret_cast<uint32_t *>(buf + SM::flag_off);
-            if (tid == 0) {
-                fl[0] = (uint32_t)(dead & 0xFFFFFFFFull) != 0u;
-                fl[1] = (uint32_t)(dead >> 32) != 0u;
+    // ---- copies.  issue(sg) starts the copy of tile sg: K and V, and (wave
+    // 0) three gate planes of its 64 keys -- S_j (re, im, modulus) into the
+    // raw area for a tile before the query tile, a_{j+1} straight into the
+    // side area for an own tile (the gate planes hold the identity gate past
+    // n, and a_{j+1} past the head's last position is only ever multiplied
+    // into an entry above the diagonal) -- and the tile's product.  On the
+    // bf16 path every copy of a tile inside the sequence adds only uniform
+    // terms to the wave's two per-lane offsets (recomputed per tile rather
+    // than held in registers through the loop); the ragged last tile (rows
+    // clamped to key n-1) takes the general K copy.
+    const uint32_t smem_lds = lds_addr(smem);
+    static_assert(F32 || (64 / (D / 8)) * NCOPY % 16 == 0, "a copy step keeps the swizzle");
+    const int n32 = int(A.n);  // n <= 2^22 (checked on the host)
+    uint32_t k_lane = 0, v_lane = 0;
+    if constexpr (!F32) {
+        k_lane = k_lane_off<D / 8>(w, lane);
+        v_lane = vt_lane_off(A.n_pad, w, lane);
+    }
+    // this head's S_j planes, a_{j+1} planes and the query tile's carry entries
+    const float *gS = uniform_ptr(A.gates + 3 * A.plane + bh * A.n_pad);
+    const float *gA = uniform_ptr(A.gates + bh * A.n_pad + 1);
+    const float *cq = uniform_ptr(A.ctab + 4 * (bh * A.ctab_head + ctab_entries(qt)));
+    auto issue = [&](int sg) __attribute__((always_inline)) {
+        if (sg >= n_tiles) return;
+        const int t = tile_of(sg);
+        const uint32_t buf = smem_lds + uint32_t((sg % NBUF) * SM::buf_bytes);
+        if constexpr (!F32) {
+            if (w < NCOPY) {
+                if ((t + 1) * BK <= n32) {
+                    const unsigned char *kt = kh + int64_t(t) * (BK * D * 2);
+#pragma unroll
+                    for (int i = 0; i < SM::KCH / NCOPY; ++i)
+                        g2lds16(kt + 1024 * NCOPY * i, k_lane,
+                                buf + uint32_t((w + NCOPY * i) * 1024));
+                } else {
+                    stage_async<F32, D>(A, buf, kh, vh, t, true, w);
+                }
+                const unsigned char *vt = vh + int64_t(t) * (BK * 2);
+#pragma unroll
+                for (int i = 0; i < SM::VCH * D / 64 / NCOPY; ++i)
+                    g2lds16(vt + int64_t(16 * NCOPY * i) * A.n_pad, v_lane,
+                            buf + uint32_t(SM::k_bytes + (w + NCOPY * i) * 1024));
             }
         } else {
-            sd[tid] = g0;
-            sd[BK + tid] = g1;
-            sd[2 * BK + tid] = g2;
+            stage_async<F32, D>(A, buf, kh, vh, t, false, w);
+        }
+        if (w == 0) {
+            const bool off = sg < n_off;
+            const uint32_t lo = uint32_t(fresh_lane() * 4);
+            // (gate_src(bh, n_pad, t, lane, !off) of plane 3 or 0)
+            const float *g = (off ? gS : gA) + t * BK;
+            const uint32_t dst = buf + uint32_t(off ? SM::raw_off : SM::side_off);
+            g2lds4(reinterpret_cast<const unsigned char *>(g), lo, dst);
+            g2lds4(reinterpret_cast<const unsigned char *>(g + A.plane), lo, dst + BK * 4);
+            g2lds4(reinterpret_cast<const unsigned char *>(g + 2 * A.plane), lo, dst + 2 * BK * 4);
+            // the carried product of the visit (16 bytes, lane 0); an own
+            // tile copies 16 bytes of its gates instead (unused), so that
+            // every tile costs wave 0 the same copies
+            const float *cs = off ? cq + 4 * sg : g;
+            g2lds16x1(reinterpret_cast<const unsigned char *>(cs), 0u,
+                      buf + uint32_t(SM::carry_off));
         }
     };
-    // gate data wave 0 needs for a tile's side data (one key per lane)
-    auto load_side = [&](int64_t t, bool off, float &g0, float &g1, float &g2) {
-        if (off) {
-            const int64_t pos = gbase + t * BK + tid;
-            g0 = A.s_re[pos];
-            g1 = A.s_im[pos];
-            g2 = A.s_m[pos];
+    uint32_t kbits = 0;
+    // Landing of tile sg, once this wave's copies of it are in.  Wave 0 forms
+    // T_j = C S_j of its 64 keys (C the visit's carried product, rounded to
+    // float; one float rounding per product, far below the bf16 rounding of
+    // the weights) with the dead flags.  For an own tile every copying wave
+    // takes the largest |k| of the K bytes it copied.
+    auto land = [&](int sg) __attribute__((always_inline)) {
+        if (sg >= n_tiles) return;
+        unsigned char *buf = tile_buf(sg);
+        if (sg < n_off) {
+            if (w == 0) {
+                const float *raw = reinterpret_cast<const float *>(buf + SM::raw_off);
+                float *sd = reinterpret_cast<float *>(buf + SM::side_off);
+                const int ln = fresh_lane();
+                const float g0 = raw[ln], g1 = raw[BK + ln], g2 = raw[2 * BK + ln];
+                const float4 cc = *reinterpret_cast<const float4 *>(buf + SM::carry_off);
+                const float rt = cc.z * g2;
+                const int slot = perm64(ln);
+                sd[slot] = cc.x * g0 - cc.y * g1;
+                sd[BK + slot] = cc.x * g1 + cc.y * g0;
+                sd[2 * BK + slot] = rt;
+                const uint64_t dead = __ballot(rt == 0.0f);
+                if (ln == 0) {
+                    uint32_t *fl = reinterpret_cast<uint32_t *>(buf + SM::flag_off);
+                    fl[0] = (uint32_t)(dead & 0xFFFFFFFFull) != 0u;
+                    fl[1] = (uint32_t)(dead >> 32) != 0u;
+                }
+            }
         } else {
-            const int64_t pos = t * BK + 1 + tid;  // a_{j+1} for key j = t*BK + tid
-            const bool ok = pos < A.n;
-            g0 = ok ? A.a_re[gbase + pos] : 1.0f;
-            g1 = ok ? A.a_im[gbase + pos] : 0.0f;
-            g2 = ok ? A.a_m[gbase + pos] : 1.0f;
+            kbits = max(kbits, own_kbits<F32, D>(A, buf, tile_of(sg), w));
+        }
+    };
+    // wait until this wave's copies of the tile landing now are in, leaving
+    // those of the one tile after it (if started) in flight
+    auto wait_landing = [&](bool newer_in_flight) __attribute__((always_inline)) {
+        if (!newer_in_flight)
+            wait_vmcnt<0>();
+        else if (w == 0)
+            wait_vmcnt<VM_TILE + 4>();
+        else
+            wait_vmcnt<VM_TILE>();
+    };
+    // Copies, around the steps of block k (tile m = k/2; the matrix step of
+    // block k runs in phase 2k + lag, its vector step in phase 2k + 1 + lag).
+    // Four buffers: every wave starts its share of tile m+2 right after its
+    // matrix step of block 2m (phase 4m for the leading waves, 4m+1 for the
+    // trailing ones; the buffer is tile m-2's, last read in phase 4m-3), and
+    // waits for its share of tile m+1 in phase 4m+2 -- the leading waves
+    // after their matrix step of block 2m+1, where wave 0 also lands the tile,
+    // the trailing ones after their vector step of block 2m -- so that the
+    // barrier closing phase 4m+2 publishes tile m+1.  A matrix step ends a
+    // little before its partner's vector step: the copy work fills that
+    // slack.  Two buffers (fp32 d = 128): tile m+1 is started in phase 4m+2
+    // (the buffer of tile m-1, last read in phase 4m+1) and landed in phase
+    // 4m+3.
+    auto land_wait = [&](int m) __attribute__((always_inline)) {
+        wait_landing(m + 2 < n_tiles);
+        land(m + 1);
+    };
+    auto after_m = [&](int k) __attribute__((always_inline)) {
+        const int m = k >> 1;
+        if constexpr (NBUF == 4) {
+            if ((k & 1) == 0)
+                issue(m + 2);
+            else if (!lag)
+                land_wait(m);
+        } else {
+            static_assert(NBUF == 2, "two or four buffers");
+            if (k & 1) {
+                if (!lag) {
+                    issue(m + 1);
+                } else {
+                    wait_vmcnt<0>();
+                    land(m + 1);
+                }
+            }
+        }
+    };
+    auto after_v = [&](int k) __attribute__((always_inline)) {
+        const int m = k >> 1;
+        if constexpr (NBUF == 4) {
+            if (lag && (k & 1) == 0) land_wait(m);
+        } else {
+            if (!lag && (k & 1)) {
+                wait_vmcnt<0>();
+                land(m + 1);
+            } else if (lag && (k & 1) == 0) {
+                issue(m + 1);
+            }
         }
     };
 
-    int cur = 0;
-    stage_async<F32, D>(A, smem, bh, t_cur, false);
-    if (tid < BK) {
-        float g0, g1, g2;
-        load_side(t_cur, off_cur, g0, g1, g2);
-        write_side(smem, t_cur, off_cur, Cre, Cim, Cm, g0, g1, g2);
-    }
+    // ---- prologue: Q, the row's prefix product, the first tiles
     typename FR::type qf[FR::count];
     const uint32_t qbits = load_q<F32, D>(A, bh, row, row_ok, h, qf);
-
-    // the modulus of the query tile's prefix product for this row: a row whose
-    // prefix holds a closed gate sees no key before the query tile
-    const bool row_live = !(A.p_m[gbase + row] == 0.0f);
+    // a row whose prefix inside the query tile holds a closed gate sees no
+    // key before the query tile
+    const float prow_re = A.p_re[gbase + row], prow_im = A.p_im[gbase + row];
+    const float prow_m = A.p_m[gbase + row];
+    const bool row_live = !(prow_m == 0.0f);
     const bool wave_dead_rows = __any(!row_live);
-    bool row_live_cur = row_live;  // rows gate the off-diagonal tiles only
+#pragma unroll
+    for (int sg = 0; sg < NBUF / 2; ++sg) issue(sg);
+    wait_vmcnt<0>();
+    land(0);
+    lds_barrier();
+    atomicMax(&misc[2], qbits);
 
     f32x16 ore[D / 32], oim[D / 32];
 #pragma unroll
@@ -615,51 +1067,49 @@ __global__ __launch_bounds__(NTHREADS, F32 ? 1 : 2) void fwd_kernel(
     // shift of the live logits (log2 units), same in both halves; with qk = 0
     // every live logit is 0 and the shift is 0 throughout
     float M = QKZ ? 0.0f : -INFINITY;
-    float z = 0.f;        // this lane's share of the normaliser
-    uint32_t tiles_done = 0;
-
-    __builtin_amdgcn_s_waitcnt(0);
-    __syncthreads();
-    atomicMax(&misc[2], qbits);
-
-    // Raw scores S of one S^T block (QKZ: qk = 0 never forms the product).
+    float z = 0.f;                         // this lane's share of the normaliser
+    float gre = 0.f, gim = 0.f, gm = 0.f;  // running G_{row,j}, R_{row,j} (own tiles)
+    f32x16 x;                              // scores of the block between M and V
+#pragma unroll
+    for (int r = 0; r < 16; ++r) x[r] = 0.f;
+    WB wk;  // W~ of the block between V and M (bf16 path)
     // Logits are c*S in log2 units; c = qk log2(e)/sqrt(d) may be negative.
     const bool cpos = A.c > 0.0f;
     const float dead_s = cpos ? -INFINITY : INFINITY;  // a score whose logit is -inf
-    auto scores = [&](const unsigned char *buf, int kb, float (&x)[16]) {
-        if constexpr (!QKZ) {
-            const f32x16 sc = s_block<F32, D>(buf, kb, qi, h, qf);
-#pragma unroll
-            for (int r = 0; r < 16; ++r) x[r] = sc[r];
-        }
-    };
-    // online max of the block's live logits, with lazy rescaling of O and z;
-    // returns the shift to subtract (0 while a row has no live entry yet)
-    auto update_max = [&](const float (&x)[16]) -> float {
+
+    // New shift of block k from its (masked) scores, with the lazy rescale
+    // of O and z (O then holds every block before k); returns the shift the
+    // block's exponentials use (0 while a row has no live entry yet).
+    // (the row's two halves meet through v_permlane32_swap of ts with itself:
+    // its first result carries the lower half's values into both halves, its
+    // second the upper half's)
+    auto block_shift = [&]() __attribute__((always_inline)) -> float {
         if constexpr (QKZ) {
             return 0.0f;  // every live logit is 0: the shift stays 0
         } else {
-            float ts;
+            float ts = x[0];
             if (cpos) {
-                ts = x[0];
 #pragma unroll
                 for (int r = 1; r < 16; ++r) ts = fmaxf(ts, x[r]);
-                ts = fmaxf(ts, __shfl_xor(ts, 32));
+                const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(ts),
+                                                                 __float_as_uint(ts), false, false);
+                ts = fmaxf(ts, fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1])));
             } else {
-                ts = x[0];
 #pragma unroll
                 for (int r = 1; r < 16; ++r) ts = fminf(ts, x[r]);
-                ts = fminf(ts, __shfl_xor(ts, 32));
+                const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(ts),
+                                                                 __float_as_uint(ts), false, false);
+                ts = fminf(ts, fminf(__uint_as_float(sw[0]), __uint_as_float(sw[1])));
             }
             float t;
             {
 #pragma clang fp contract(off)
                 t = ts * A.c;  // the block's largest logit (-inf if none is live)
             }
-            const bool grow = t > M + kLazy || (M == -INFINITY && t > M);
-            if (__any(grow && M != -INFINITY)) {
-                const float alpha =
-                    (grow && M != -INFINITY) ? __builtin_amdgcn_exp2f(M - t) : 1.0f;
+            const bool grow = (t > M + kLazy) | ((M == -INFINITY) & (t > M));
+            const bool resc = grow & (M != -INFINITY);
+            if (__any(resc)) {
+                const float alpha = resc ? __builtin_amdgcn_exp2f(M - t) : 1.0f;
 #pragma unroll
                 for (int db = 0; db < D / 32; ++db)
 #pragma unroll
@@ -673,177 +1123,253 @@ __global__ __launch_bounds__(NTHREADS, F32 ? 1 : 2) void fwd_kernel(
             return (M == -INFINITY) ? 0.0f : M;
         }
     };
-    // exponentials e = 2^(c S - M), normaliser and the two W~ V products of
-    // one 16-key chunk; `live` (QKZ only) marks the entries that are not masked
-    auto chunk = [&](const unsigned char *buf, int kb, int kc, const float (&x)[16], float msub,
-                     const float (&fre)[8], const float (&fim)[8], const float (&fm)[8],
-                     bool all_live) {
+    // exponentials e = 2^(c S - M) of one 16-key chunk, the normaliser, and
+    // W~ = e * gate factor: packed for the next matrix step (bf16 path) or
+    // multiplied into O right away (fp32 path).  QKZ: e is 1 on live entries
+    // (all_live, or a non-zero modulus on a live row), else 0.
+    auto weights = [&](const unsigned char *buf, int kb, int kc, float msub, const float (&fre)[8],
+                       const float (&fim)[8], const float (&fm)[8], bool all_live,
+                       bool rlive) __attribute__((always_inline)) {
         float wre[8], wim[8];
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
             float ex;
             if constexpr (QKZ)
-                ex = (all_live || (fm[e] > 0.0f && row_live_cur)) ? 1.0f : 0.0f;
+                ex = (all_live || (fm[e] > 0.0f && rlive)) ? 1.0f : 0.0f;
             else
                 ex = __builtin_amdgcn_exp2f(fmaf(x[8 * kc + e], A.c, -msub));
             z += ex * fm[e];
             wre[e] = ex * fre[e];
             wim[e] = ex * fim[e];
         }
-        pv_chunk<F32, D>(buf, kb, kc, qi, h, wre, wim, ore, oim);
-    };
-
-    // ---- key tiles wholly before the query tile: G = S_j C_t P_i ----------
-    while (off_cur) {
-        unsigned char *buf = smem + cur * SM::buf_bytes;
-        unsigned char *nbuf = smem + (cur ^ 1) * SM::buf_bytes;
-        const float *side = reinterpret_cast<const float *>(buf + SM::side_off);
-        // the next tile, and its asynchronous copy
-        const int64_t tp = bh * A.n_kt + t_cur;
-        const double are = tre[tp], aim = tim[tp], am = tmm[tp];
-        const double nCre = uniform_f64(are * Cre - aim * Cim);
-        const double nCim = uniform_f64(are * Cim + aim * Cre);
-        const double nCm = uniform_f64(am * Cm);
-        // every earlier key is dead once the carried modulus is 0 in float32
-        const bool off_nxt = t_cur > 0 && (float)nCm != 0.0f;
-        const int64_t t_nxt = off_nxt ? t_cur - 1 : t_diag0 + NDIAG - 1;
-        stage_async<F32, D>(A, nbuf, bh, t_nxt, false);
-        float g0 = 0.f, g1 = 0.f, g2 = 0.f;
-        if (tid < BK) load_side(t_nxt, off_nxt, g0, g1, g2);
-
-        ++tiles_done;
+        if constexpr (F32) {
+            pv_chunk_f32<D>(buf, kb, kc, qi, h, wre, wim, ore, oim);
+        } else {
 #pragma unroll
-        for (int blk = 0; blk < 2; ++blk) {
-            const int kb = 32 * blk;
-            float x[16];
-            scores(buf, kb, x);
-            const bool masked = wave_dead_rows ||
-                                reinterpret_cast<const uint32_t *>(buf + SM::flag_off)[blk] != 0u;
-            if (!QKZ && masked) {
-#pragma unroll
-                for (int kc = 0; kc < 2; ++kc) {
-                    const float4 m0 =
-                        *reinterpret_cast<const float4 *>(side + 2 * BK + kb + 16 * kc + 8 * h);
-                    const float4 m1 =
-                        *reinterpret_cast<const float4 *>(side + 2 * BK + kb + 16 * kc + 8 * h + 4);
-                    const float mm[8] = {m0.x, m0.y, m0.z, m0.w, m1.x, m1.y, m1.z, m1.w};
-#pragma unroll
-                    for (int e = 0; e < 8; ++e)
-                        x[8 * kc + e] = (mm[e] > 0.0f && row_live) ? x[8 * kc + e] : dead_s;
-                }
-            }
-            const float msub = update_max(x);
-#pragma unroll
-            for (int kc = 0; kc < 2; ++kc) {
-                float fre[8], fim[8], fm[8];
-                const int s0 = kb + 16 * kc + 8 * h;
-#pragma unroll
-                for (int e = 0; e < 8; e += 4) {
-                    const float4 a = *reinterpret_cast<const float4 *>(side + s0 + e);
-                    const float4 b = *reinterpret_cast<const float4 *>(side + BK + s0 + e);
-                    const float4 c = *reinterpret_cast<const float4 *>(side + 2 * BK + s0 + e);
-                    fre[e] = a.x; fre[e + 1] = a.y; fre[e + 2] = a.z; fre[e + 3] = a.w;
-                    fim[e] = b.x; fim[e + 1] = b.y; fim[e + 2] = b.z; fim[e + 3] = b.w;
-                    fm[e] = c.x; fm[e + 1] = c.y; fm[e + 2] = c.z; fm[e + 3] = c.w;
-                }
-                chunk(buf, kb, kc, x, msub, fre, fim, fm, !masked);
+            for (int e = 0; e < 8; ++e) {
+                wk.r[kc][e] = (__bf16)wre[e];
+                wk.i[kc][e] = (__bf16)wim[e];
             }
         }
+    };
+    // vector step of a block of a tile before the query tile: G = S_j C_t P_i
+    // (P_i applied to O once, when the query tile's own keys begin); masked:
+    // the block holds a dead column or the wave a dead row
+    auto vstep_off = [&](const unsigned char *buf, int kb, bool masked) __attribute__((always_inline)) {
+        const float *side = reinterpret_cast<const float *>(buf + SM::side_off);
+        if (!QKZ && masked) {
+#pragma unroll
+            for (int kc = 0; kc < 2; ++kc) {
+                const float4 m0 =
+                    *reinterpret_cast<const float4 *>(side + 2 * BK + kb + 16 * kc + 8 * h);
+                const float4 m1 =
+                    *reinterpret_cast<const float4 *>(side + 2 * BK + kb + 16 * kc + 8 * h + 4);
+                const float mm[8] = {m0.x, m0.y, m0.z, m0.w, m1.x, m1.y, m1.z, m1.w};
+#pragma unroll
+                for (int e = 0; e < 8; ++e)
+                    x[8 * kc + e] = (mm[e] > 0.0f && row_live) ? x[8 * kc + e] : dead_s;
+            }
+        }
+        const float msub = block_shift();
+#pragma unroll
+        for (int kc = 0; kc < 2; ++kc) {
+            float fre[8], fim[8], fm[8];
+            const int s0 = kb + 16 * kc + 8 * h;
+#pragma unroll
+            for (int e = 0; e < 8; e += 4) {
+                const float4 a = *reinterpret_cast<const float4 *>(side + s0 + e);
+                const float4 b = *reinterpret_cast<const float4 *>(side + BK + s0 + e);
+                const float4 c = *reinterpret_cast<const float4 *>(side + 2 * BK + s0 + e);
+                fre[e] = a.x; fre[e + 1] = a.y; fre[e + 2] = a.z; fre[e + 3] = a.w;
+                fim[e] = b.x; fim[e + 1] = b.y; fim[e + 2] = b.z; fim[e + 3] = b.w;
+                fm[e] = c.x; fm[e + 1] = c.y; fm[e + 2] = c.z; fm[e + 3] = c.w;
+            }
+            weights(buf, kb, kc, msub, fre, fim, fm, !masked, row_live);
+            __builtin_amdgcn_sched_barrier(0);  // one chunk's side data at a time
+        }
+    };
+    // vector step of a block of the query tile's own keys: explicit G_ij by a
+    // running product per row, a_i a_{i-1} ... a_{j+1}, last key first; the
+    // product restarts at 1 on the diagonal and is 0 above it
+    auto vstep_own = [&](const unsigned char *buf, int kb, int dpos) __attribute__((always_inline)) {
+        const float *side = reinterpret_cast<const float *>(buf + SM::side_off);
+        // pass 1: modulus R_{row,j} of the 16 keys this lane holds
+        float Gm[16];
+        const float gre0 = gre, gim0 = gim;
+        // (fences every four keys keep few side values live at a time)
+#pragma unroll
+        for (int jj = 31; jj >= 0; --jj) {
+            const float nm = gm * side[2 * BK + kb + jj];
+            gm = (jj == dpos) ? 1.0f : nm;
+            if (h == ((jj >> 2) & 1)) Gm[4 * (jj >> 3) + (jj & 3)] = gm;
+            if ((jj & 3) == 0) __builtin_amdgcn_sched_barrier(0);
+        }
+        if constexpr (!QKZ) {
+#pragma unroll
+            for (int r = 0; r < 16; ++r) x[r] = (Gm[r] > 0.0f) ? x[r] : dead_s;
+        }
+        const float msub = block_shift();
+        // pass 2: G_{row,j} chunk by chunk, keys 31..16 then 15..0
+        gre = gre0;
+        gim = gim0;
+#pragma unroll
+        for (int kc = 1; kc >= 0; --kc) {
+            float fre[8], fim[8], fm[8];
+#pragma unroll
+            for (int jj = 16 * kc + 15; jj >= 16 * kc; --jj) {
+                const float dr = side[kb + jj], di = side[BK + kb + jj];
+                const float nr = gre * dr - gim * di;
+                const float ni = gre * di + gim * dr;
+                const bool diag = (jj == dpos);
+                gre = diag ? 1.0f : nr;
+                gim = diag ? 0.0f : ni;
+                if (h == ((jj >> 2) & 1)) {
+                    const int e = 4 * ((jj - 16 * kc) >> 3) + (jj & 3);
+                    fre[e] = gre;
+                    fim[e] = gim;
+                }
+                if ((jj & 3) == 0) __builtin_amdgcn_sched_barrier(0);
+            }
+#pragma unroll
+            for (int e = 0; e < 8; ++e) fm[e] = Gm[8 * kc + e];
+            weights(buf, kb, kc, msub, fre, fim, fm, false, true);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+    };
 
-        if (tid < BK) write_side(nbuf, t_nxt, off_nxt, nCre, nCim, nCm, g0, g1, g2);
-        __builtin_amdgcn_s_waitcnt(0);
-        __syncthreads();
-        Cre = nCre;
-        Cim = nCim;
-        Cm = nCm;
-        t_cur = t_nxt;
-        off_cur = off_nxt;
-        cur ^= 1;
-        if (!off_cur) {
-            // leaving the off-diagonal tiles: rotate by the prefix product P_i
-            const float Pre = A.p_re[gbase + row], Pim = A.p_im[gbase + row];
-            const float Pm = A.p_m[gbase + row];
+    auto block_buf = [&](int k) __attribute__((always_inline)) { return tile_buf(k >> 1); };
+    // key offset of block k inside its tile: ascending in the tiles before
+    // the query tile, descending in its own tiles
+    auto block_kb = [&](int k, bool off) __attribute__((always_inline)) {
+        return off ? 32 * (k & 1) : 32 * (1 - (k & 1));
+    };
+    // an own-tile block wholly above this wave's rows is skipped
+    auto block_active = [&](int k, bool off) __attribute__((always_inline)) {
+        return off || k - 2 * n_off >= NDB - 1 - w;
+    };
+    // dead-column flag of block k (read during its matrix step, where the LDS
+    // latency hides behind the matrix instructions)
+    uint32_t kflag = 0;
+    // matrix step of block k when blocks k-1 and k both lie before the query
+    // tile (bf16 path: its first operands were requested by m_prefetch_off at
+    // the end of the vector step of block k-1)
+    MPrefetch pf;
+    constexpr int NPRE_OFF = 2;  // fragments of each kind requested early
+    auto m_prefetch_off = [&](int k) __attribute__((always_inline)) {
+        if constexpr (!F32)
+            mstep_prefetch<D, true, !QKZ, 0, NPRE_OFF>(block_buf(k - 1), block_kb(k - 1, true),
+                                                      block_buf(k), block_kb(k, true), qi, h, pf);
+    };
+    auto m_step_off = [&](int k) __attribute__((always_inline)) {
+        kflag = reinterpret_cast<const uint32_t *>(block_buf(k) + SM::flag_off)[k & 1];
+        if constexpr (!F32) {
+            if (k >= 1)
+                mstep_bf16<D, true, !QKZ, NPRE_OFF>(block_buf(k - 1), block_kb(k - 1, true),
+                                                block_buf(k), block_kb(k, true), qi, h, pf, wk.r,
+                                                wk.i, qf, ore, oim, x);
+            else
+                mstep_bf16<D, false, !QKZ, 0>(block_buf(k), 0, block_buf(k),
+                                                  block_kb(k, true), qi, h, pf, wk.r, wk.i, qf, ore,
+                                                  oim, x);
+        } else if constexpr (!QKZ) {
+            x = s_block<F32, D>(block_buf(k), block_kb(k, true), qi, h, qf);
+        }
+    };
+    auto m_step = [&](int k) __attribute__((always_inline)) {
+        if constexpr (!F32) {
+            if (k >= 1) {
+                const int kp = k - 1;
+                const bool offp = (kp >> 1) < n_off;
+                if (block_active(kp, offp))
+                    pv_block<F32, D>(block_buf(kp), block_kb(kp, offp), qi, h, wk, ore, oim);
+            }
+        }
+        if constexpr (!QKZ) {
+            if ((k >> 1) < n_tiles) {
+                const bool off = (k >> 1) < n_off;
+                if (block_active(k, off)) x = s_block<F32, D>(block_buf(k), block_kb(k, off), qi, h, qf);
+            }
+        }
+    };
+    // the vector step's results stay in its own phase (the bf16 path's W~ is
+    // first used by the next matrix step, after a barrier)
+    auto settle_weights = [&]() __attribute__((always_inline)) {
+        if constexpr (!F32) {
+            settle(wk.r[0]);
+            settle(wk.r[1]);
+            settle(wk.i[0]);
+            settle(wk.i[1]);
+        }
+        settle(z);
+    };
+    // vector step of block k of a tile before the query tile; block k+1 is
+    // one too when k + 1 < 2 n_off, and its matrix step's first operands are
+    // requested here (the vector step ends well before its partner's matrix
+    // step, so the LDS latency hides in the wait at the barrier).  Block k+1's
+    // tile has landed: the landing of a tile is two phases before the first
+    // vector step that reaches it.
+    auto v_step_off = [&](int k) __attribute__((always_inline)) {
+        vstep_off(block_buf(k), block_kb(k, true),
+                  wave_dead_rows || __builtin_amdgcn_readfirstlane(kflag) != 0u);
+        settle_weights();
+        if (k + 1 < 2 * n_off) m_prefetch_off(k + 1);
+    };
+    // vector step of block k of the query tile's own tiles
+    auto v_step_own = [&](int k) __attribute__((always_inline)) {
+        if (n_off > 0 && k == 2 * n_off) {
+            // the last block before the query tile is in O: rotate by P_i
 #pragma unroll
             for (int db = 0; db < D / 32; ++db)
 #pragma unroll
                 for (int r = 0; r < 16; ++r) {
                     const float xr = ore[db][r], xi = oim[db][r];
-                    ore[db][r] = Pre * xr - Pim * xi;
-                    oim[db][r] = Pre * xi + Pim * xr;
+                    ore[db][r] = prow_re * xr - prow_im * xi;
+                    oim[db][r] = prow_re * xi + prow_im * xr;
                 }
-            z *= Pm;
+            z *= prow_m;
         }
-    }
+        if (!block_active(k, false)) return;
+        const int kb = block_kb(k, false);
+        const int tl = NDIAG - 1 - ((k >> 1) - n_off);  // key tile, counted from t_diag0
+        vstep_own(block_buf(k), kb, 32 * w + qi - (tl * BK + kb));  // 0..31 on the block's diagonal
+        settle_weights();
+    };
 
-    // ---- the query tile's own keys: explicit G_ij, last key first ---------
-    row_live_cur = true;
-    float gre = 0.f, gim = 0.f, gm = 0.f;  // running G_{row,j}, R_{row,j}
-    uint32_t kbits = 0;
-    while (true) {
-        unsigned char *buf = smem + cur * SM::buf_bytes;
-        unsigned char *nbuf = smem + (cur ^ 1) * SM::buf_bytes;
-        const float *side = reinterpret_cast<const float *>(buf + SM::side_off);
-        const bool more = t_cur > t_diag0;
-        float g0 = 0.f, g1 = 0.f, g2 = 0.f;
-        if (more) {
-            stage_async<F32, D>(A, nbuf, bh, t_cur - 1, false);
-            if (tid < BK) load_side(t_cur - 1, false, g0, g1, g2);
-        }
-        kbits = max(kbits, tile_kbits<F32, D>(A, buf, t_cur));
-#pragma unroll
-        for (int blk = 1; blk >= 0; --blk) {
-            const int cidx = int((t_cur - t_diag0) * (BK / 32)) + blk;
-            if (cidx > w) continue;  // wholly above this wave's rows
-            const int kb = 32 * blk;
-            const int dpos = int(row - (t_cur * BK + kb));  // 0..31 on the block's diagonal
-            // pass 1: modulus R_{row,j} of the 16 keys this lane holds
-            float Gm[16];
-            const float gre0 = gre, gim0 = gim;
-#pragma unroll
-            for (int jj = 31; jj >= 0; --jj) {
-                const float nm = gm * side[2 * BK + kb + jj];
-                gm = (jj == dpos) ? 1.0f : nm;
-                if (h == ((jj >> 2) & 1)) Gm[4 * (jj >> 3) + (jj & 3)] = gm;
-            }
-            float x[16];
-            scores(buf, kb, x);
-            if constexpr (!QKZ) {
-#pragma unroll
-                for (int r = 0; r < 16; ++r) x[r] = (Gm[r] > 0.0f) ? x[r] : dead_s;
-            }
-            const float msub = update_max(x);
-            // pass 2: G_{row,j} chunk by chunk, keys 31..16 then 15..0
-            gre = gre0;
-            gim = gim0;
-#pragma unroll
-            for (int kc = 1; kc >= 0; --kc) {
-                float fre[8], fim[8], fm[8];
-#pragma unroll
-                for (int jj = 16 * kc + 15; jj >= 16 * kc; --jj) {
-                    const float dr = side[kb + jj], di = side[BK + kb + jj];
-                    const float nr = gre * dr - gim * di;
-                    const float ni = gre * di + gim * dr;
-                    const bool diag = (jj == dpos);
-                    gre = diag ? 1.0f : nr;
-                    gim = diag ? 0.0f : ni;
-                    if (h == ((jj >> 2) & 1)) {
-                        const int e = 4 * ((jj - 16 * kc) >> 3) + (jj & 3);
-                        fre[e] = gre;
-                        fim[e] = gim;
-                    }
-                }
-#pragma unroll
-                for (int e = 0; e < 8; ++e) fm[e] = Gm[8 * kc + e];
-                chunk(buf, kb, kc, x, msub, fre, fim, fm, false);
-            }
-        }
-        if (!more) break;
-        if (tid < BK) write_side(nbuf, t_cur - 1, false, 0.0, 0.0, 0.0, g0, g1, g2);
-        __builtin_amdgcn_s_waitcnt(0);
-        __syncthreads();
-        t_cur -= 1;
-        cur ^= 1;
+    // ---- the phases.  Block k has its matrix step in phase 2k + lag and its
+    // vector step in phase 2k + 1 + lag; a barrier ends every phase, and the
+    // trailing waves pass one extra barrier first, the leading ones one last.
+    // The copies of a phase (leading waves only) run around its step.
+    // A wave in its matrix step takes issue priority over its SIMD partner in
+    // its vector step, so that the partner's vector instructions fill the
+    // cycles between matrix instructions instead of delaying them.
+    if (lag) lds_barrier();
+    int k = 0;
+    for (; k < 2 * n_off; ++k) {
+        __builtin_amdgcn_s_setprio(2);
+        m_step_off(k);
+        after_m(k);
+        lds_barrier();
+        __builtin_amdgcn_s_setprio(0);
+        v_step_off(k);
+        after_v(k);
+        lds_barrier();
     }
+    for (; k < 2 * n_tiles; ++k) {
+        __builtin_amdgcn_s_setprio(2);
+        m_step(k);
+        after_m(k);
+        lds_barrier();
+        __builtin_amdgcn_s_setprio(0);
+        v_step_own(k);
+        after_v(k);
+        lds_barrier();
+    }
+    __builtin_amdgcn_s_setprio(2);
+    m_step(k);  // the last block's W~ V
+    after_m(k);
+    lds_barrier();
+    __builtin_amdgcn_s_setprio(0);
+    if (!lag) lds_barrier();
     atomicMax(&misc[3], kbits);
 
     // ---- epilogue: O *= exp2((1-beta) M) z^-beta -------------------------
@@ -882,7 +1408,7 @@ __global__ __launch_bounds__(NTHREADS, F32 ? 1 : 2) void fwd_kernel(
         A.qstat[bh * A.n_qt + qt] = qb;
         A.kstat[bh * A.n_qt + qt] = kb;
         if (qb >= kInfBits || kb >= kInfBits) A.status[0] = kNonFinite;
-        atomicAdd(&A.counters[0], tiles_done);
+        atomicAdd(&A.counters[0], uint32_t(n_off));
     }
 }
 
@@ -918,10 +1444,13 @@ __global__ __launch_bounds__(NTHREADS) void logit_check_kernel(FwdArgs A) {
     const bool row_ok = row < A.n;
     typename FR::type qf[FR::count];
     load_q<F32, D>(A, bh, row, row_ok, h, qf);
+    const unsigned char *kh, *vh;
+    head_bases<F32, D>(A, bh, kh, vh);
     bool bad = false;
     for (int64_t t = 0; t < (i0 + BQ) / BK; ++t) {
         __syncthreads();
-        stage_async<F32, D>(A, smem, bh, t, true);
+        stage_async<F32, D>(A, lds_addr(smem), kh, vh, int(t), true,
+                            __builtin_amdgcn_readfirstlane(w));
         __builtin_amdgcn_s_waitcnt(0);
         __syncthreads();
 #pragma unroll
@@ -986,6 +1515,10 @@ int launch_typed(const Problem &P, hipStream_t st, hipEvent_t const *marks) {
     G.t_m = dptr(2);
     G.status = P.status;
     hipLaunchKernelGGL(gates_kernel, dim3(BH * L.n_qt), dim3(64), 0, st, G);
+    int32_t *noff = reinterpret_cast<int32_t *>(ws + L.noff);
+    float *ctab = reinterpret_cast<float *>(ws + L.ctab);
+    hipLaunchKernelGGL(schedule_kernel, dim3(BH * L.n_qt), dim3(64), 0, st, G.t_re, G.t_im,
+                       G.t_m, (int)L.n_kt, (int)L.n_qt, noff, ctab, ctab_entries(L.n_qt));
 
     FwdArgs F;
     F.q = P.q;
@@ -1004,11 +1537,16 @@ int launch_typed(const Problem &P, hipStream_t st, hipEvent_t const *marks) {
     F.t_re = G.t_re;
     F.t_im = G.t_im;
     F.t_m = G.t_m;
+    F.ctab = ctab;
+    F.ctab_head = ctab_entries(L.n_qt);
+    F.gates = G.a_re;
+    F.plane = int64_t(L.gate[1] - L.gate[0]) / int64_t(sizeof(float));
     F.o_re = P.o_re;
     F.o_im = P.o_im;
     F.qstat = reinterpret_cast<uint32_t *>(ws + L.qstat);
     F.kstat = reinterpret_cast<uint32_t *>(ws + L.kstat);
     F.counters = counters;
+    F.noff = noff;
     F.status = P.status;
     F.n = L.n;
     F.n_pad = L.n_pad;
@@ -1032,10 +1570,10 @@ int launch_typed(const Problem &P, hipStream_t st, hipEvent_t const *marks) {
     if (marks) (void)hipEventRecord(marks[1], st);
     if (P.qk_zero)
         hipLaunchKernelGGL((fwd_kernel<F32, D, true>), dim3(BH * L.n_qt), dim3(NTHREADS), shm, st,
-                           F, G.t_re, G.t_im, G.t_m);
+                           F);
     else
         hipLaunchKernelGGL((fwd_kernel<F32, D, false>), dim3(BH * L.n_qt), dim3(NTHREADS), shm,
-                           st, F, G.t_re, G.t_im, G.t_m);
+                           st, F);
     if (marks) (void)hipEventRecord(marks[2], st);
     if (!P.qk_zero)
         hipLaunchKernelGGL((logit_check_kernel<F32, D>), dim3(BH * L.n_qt), dim3(NTHREADS), shm,

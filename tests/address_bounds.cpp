@@ -3,9 +3,14 @@
 // inside the workspace (the gate planes).  It walks
 // every key tile of every shape given on the command line (all tiles a
 // workgroup of any query tile stages, the logit check included), every row
-// and every 16-byte chunk, using the same helpers as the kernel.
+// and every 16-byte chunk, using the same helpers as the kernel.  For the
+// bf16 tiles it also walks the copy instructions lane by lane: each reads a
+// chunk inside the tensor, each (row, chunk) of a tile is copied once, into
+// the LDS slot where the matrix-operand reads look for it, and a 16-lane
+// group of an operand read touches 16 different bank groups.
 #include <cstdio>
 #include <cstdlib>
+#include <vector>
 
 #include "layout.h"
 
@@ -50,6 +55,52 @@ static int check(int64_t B, int64_t H, int64_t n, int64_t d, int esz, bool bf16_
                                             (long long)n, (long long)t, dd, c);
                         }
                     }
+            // the bf16 copy instructions, lane by lane (kernel helpers)
+            if (bf16_path) {
+                const int64_t head_k = bh * n * row_bytes, head_vt = bh * d * L.n_pad * 2;
+                for (int j = 0; j < kch; ++j)
+                    for (int lane = 0; lane < 64; ++lane) {
+                        const int64_t ko = head_k + int64_t(d == 128 ? k_copy_off<16>(n, t, j, lane)
+                                                                     : k_copy_off<8>(n, t, j, lane));
+                        if ((ko < head_k || ko + 16 > head_k + n * row_bytes) && bad++ < 5)
+                            std::printf("k copy out of the head: n=%lld t=%lld j=%d lane=%d\n",
+                                        (long long)n, (long long)t, j, lane);
+                    }
+                // the kernels' split into per-lane and uniform parts (NC copy waves)
+                const bool inside = (t + 1) * BK <= n;
+                for (int NC = 4; NC <= 8; NC += 4) {
+                    for (int j = 0; j < kch; ++j)
+                        for (int lane = 0; lane < 64; ++lane) {
+                            const int j0 = j % NC, i = j / NC;
+                            const uint32_t full = d == 128 ? k_copy_off<16>(n, t, j, lane)
+                                                           : k_copy_off<8>(n, t, j, lane);
+                            const uint32_t split = uint32_t(t * BK * 2 * d) +
+                                                   uint32_t(1024 * NC * i) +
+                                                   (d == 128 ? k_lane_off<16>(j0, lane)
+                                                             : k_lane_off<8>(j0, lane));
+                            if (inside && full != split && bad++ < 5)
+                                std::printf("k copy split mismatch: n=%lld t=%lld j=%d lane=%d\n",
+                                            (long long)n, (long long)t, j, lane);
+                        }
+                    for (int j = 0; j < int(d) / 8; ++j)
+                        for (int lane = 0; lane < 64; ++lane) {
+                            const int j0 = j % NC, i = j / NC;
+                            const uint32_t split = uint32_t(2 * BK * t) +
+                                                   uint32_t(16 * NC * L.n_pad * i) +
+                                                   vt_lane_off(L.n_pad, j0, lane);
+                            if (split != vt_copy_off(L.n_pad, t, j, lane) && bad++ < 5)
+                                std::printf("v^T copy split mismatch: n=%lld t=%lld j=%d lane=%d\n",
+                                            (long long)n, (long long)t, j, lane);
+                        }
+                }
+                for (int j = 0; j < int(d) / 8; ++j)
+                    for (int lane = 0; lane < 64; ++lane) {
+                        const int64_t vo = head_vt + int64_t(vt_copy_off(L.n_pad, t, j, lane));
+                        if ((vo < head_vt || vo + 16 > head_vt + d * L.n_pad * 2) && bad++ < 5)
+                            std::printf("v^T copy out of the head: n=%lld t=%lld j=%d lane=%d\n",
+                                        (long long)n, (long long)t, j, lane);
+                    }
+            }
             // gate planes: S_j (planes 3..5) and a_{j+1} (planes 0..2), 4 bytes a lane
             for (int own = 0; own < 2; ++own)
                 for (int p = own ? 0 : 3; p < (own ? 3 : 6); ++p)
@@ -63,11 +114,106 @@ static int check(int64_t B, int64_t H, int64_t n, int64_t d, int esz, bool bf16_
                         }
                     }
         }
+    // the carried-product copies: visit s < qt*BQ/BK of query tile qt, 16 bytes
+    for (int64_t bh = 0; bh < L.BH; bh += (L.BH > 2 ? L.BH - 1 : 1))
+        for (int64_t qt = 0; qt < L.n_qt; ++qt)
+            for (int64_t sg = 0; sg < qt * (BQ / BK); ++sg) {
+                const int64_t e = bh * ctab_entries(L.n_qt) + ctab_entries(qt) + sg;
+                const int64_t off = int64_t(L.ctab) + 16 * e;
+                const bool own_head = e >= bh * ctab_entries(L.n_qt) &&
+                                      e < (bh + 1) * ctab_entries(L.n_qt);
+                const bool own_tile = sg < ctab_entries(qt + 1) - ctab_entries(qt);
+                if ((!own_head || !own_tile || off + 16 > int64_t(L.total)) && bad++ < 5)
+                    std::printf("carry entry out of range: n=%lld qt=%lld s=%lld\n",
+                                (long long)n, (long long)qt, (long long)sg);
+            }
+    return bad;
+}
+
+// The swizzled bf16 tile layout with CPR chunks per row (K: CPR = d/8;
+// v^T: CPR = 8), independent of the shape.
+template <int CPR>
+static int check_tile_layout(const char *what) {
+    int bad = 0;
+    // copies: instruction j, lane -> LDS offset 1024 j + 16 lane holds chunk
+    // copy_chunk of row copy_row.  CPR 16: the K tile of d = 128 (64 rows);
+    // CPR 8: the v^T tile of d = 128 (128 rows; its first 64 are the K tile of
+    // d = 64 and the v^T tile of d = 64).
+    const int rows = (CPR == 16) ? 64 : 128;
+    std::vector<int> seen(size_t(rows) * CPR, 0);
+    for (int j = 0; j < rows * CPR / 64; ++j)
+        for (int lane = 0; lane < 64; ++lane) {
+            const int r = copy_row<CPR>(j, lane), c = copy_chunk<CPR>(j, lane);
+            if (r < 0 || r >= rows || c < 0 || c >= CPR) {
+                if (bad++ < 5) std::printf("%s: copy j=%d lane=%d out of tile\n", what, j, lane);
+                continue;
+            }
+            ++seen[size_t(r) * CPR + c];
+            if (tile_chunk_off<CPR>(r, c) != 1024 * j + 16 * lane && bad++ < 5)
+                std::printf("%s: chunk (%d,%d) copied to %d, read at %d\n", what, r, c,
+                            1024 * j + 16 * lane, tile_chunk_off<CPR>(r, c));
+        }
+    for (size_t i = 0; i < seen.size(); ++i)
+        if (seen[i] != 1 && bad++ < 5)
+            std::printf("%s: (row %zu, chunk %zu) copied %d times\n", what, i / CPR, i % CPR,
+                        seen[i]);
+    return bad;
+}
+
+// Operand reads of the bf16 matrix steps: lane (qi, h), step s reads chunk
+// 2s+h of K row kb+qi; PV reads chunk kb/8+2kc+h of v^T row 32db+qi.
+template <int CPR>
+static int check_operand_reads() {
+    int bad = 0;
+    for (int kb = 0; kb < 64; kb += 32)
+        for (int s = 0; s < CPR / 2; ++s)
+            for (int g = 0; g < 4; ++g) {  // 16-lane groups: (h, qi / 16)
+                const int h = g >> 1;
+                unsigned used = 0;
+                for (int q = 0; q < 16; ++q) {
+                    const int qi = 16 * (g & 1) + q;
+                    const int off = kfrag_base<CPR>(kb, qi, h) ^ (32 * s);
+                    if (off != tile_chunk_off<CPR>(kb + qi, 2 * s + h) && bad++ < 5)
+                        std::printf("K read (kb %d s %d qi %d h %d) at %d, chunk at %d\n", kb, s,
+                                    qi, h, off, tile_chunk_off<CPR>(kb + qi, 2 * s + h));
+                    used |= 1u << ((off % 256) / 16);
+                }
+                if (used != 0xFFFFu && bad++ < 5)
+                    std::printf("K read (CPR %d kb %d s %d group %d): bank groups %04x\n", CPR, kb,
+                                s, g, used);
+            }
+    return bad;
+}
+
+static int check_v_reads(int d) {
+    int bad = 0;
+    for (int kb = 0; kb < 64; kb += 32)
+        for (int kc = 0; kc < 2; ++kc)
+            for (int db = 0; db < d / 32; ++db)
+                for (int g = 0; g < 4; ++g) {
+                    const int h = g >> 1;
+                    unsigned used = 0;
+                    for (int q = 0; q < 16; ++q) {
+                        const int qi = 16 * (g & 1) + q;
+                        const int off = 4096 * db + (vfrag_base(qi, h) ^ (2 * kb + 32 * kc));
+                        const int want = tile_chunk_off<8>(32 * db + qi, kb / 8 + 2 * kc + h);
+                        if (off != want && bad++ < 5)
+                            std::printf("v^T read (kb %d kc %d db %d qi %d h %d) at %d, chunk at %d\n",
+                                        kb, kc, db, qi, h, off, want);
+                        used |= 1u << ((off % 256) / 16);
+                    }
+                    if (used != 0xFFFFu && bad++ < 5)
+                        std::printf("v^T read (kb %d kc %d db %d group %d): bank groups %04x\n", kb,
+                                    kc, db, g, used);
+                }
     return bad;
 }
 
 int main(int argc, char **argv) {
-    int bad = 0, cases = 0;
+    int bad = check_tile_layout<16>("K d=128") + check_tile_layout<8>("K d=64 / v^T") +
+              check_operand_reads<16>() + check_operand_reads<8>() + check_v_reads(64) +
+              check_v_reads(128);
+    int cases = 0;
     for (int a = 1; a + 3 < argc; a += 4) {
         const int64_t B = std::atoll(argv[a]), H = std::atoll(argv[a + 1]);
         const int64_t n = std::atoll(argv[a + 2]), d = std::atoll(argv[a + 3]);
@@ -75,6 +221,6 @@ int main(int argc, char **argv) {
         bad += check(B, H, n, d, 4, false);  // fp32 q, k, v
         ++cases;
     }
-    std::printf("%d shapes, %d out-of-range ranges\n", cases, bad);
+    std::printf("%d shapes, %d problems\n", cases, bad);
     return bad ? 1 : 0;
 }
