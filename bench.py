@@ -54,6 +54,59 @@ def copy_calibration(nbytes):
     print(json.dumps({"copy_bytes": nbytes, "launches": 3}), flush=True)
 
 
+def counter_per_dispatch(run_dir, counter, name_filter):
+    """Mean value of one rocprofv3 counter over the dispatches whose kernel name
+    contains name_filter, from the CSV files under run_dir."""
+    import csv
+    import glob
+
+    vals = []
+    for f in glob.glob(os.path.join(run_dir, "**", "*counter_collection.csv"), recursive=True):
+        with open(f) as fh:
+            for r in csv.DictReader(fh):
+                if name_filter in r["Kernel_Name"] and r["Counter_Name"] == counter:
+                    vals.append(float(r["Counter_Value"]))
+    if not vals:
+        raise SystemExit(f"no {counter} rows for '{name_filter}' under {run_dir}")
+    return sum(vals) / len(vals), len(vals)
+
+
+def summarize_traffic(fetch_dir, write_dir, copy_fetch_dir, copy_write_dir, copy_bytes):
+    """HBM bytes per fused-kernel launch: FETCH_SIZE and WRITE_SIZE (KiB per
+    dispatch), each divided by what the same counter reads per byte of a plain
+    device copy of copy_bytes (torch copy_ of one device tensor into another: the
+    runtime's copyBuffer kernel, which reads and writes copy_bytes)."""
+    kf, nkf = counter_per_dispatch(fetch_dir, "FETCH_SIZE", "fwd_kernel")
+    kw, nkw = counter_per_dispatch(write_dir, "WRITE_SIZE", "fwd_kernel")
+    cf, _ = counter_per_dispatch(copy_fetch_dir, "FETCH_SIZE", "copyBuffer")
+    cw, _ = counter_per_dispatch(copy_write_dir, "WRITE_SIZE", "copyBuffer")
+    f_fac = cf * 1024.0 / copy_bytes
+    w_fac = cw * 1024.0 / copy_bytes
+    fetch = kf * 1024.0 / f_fac
+    write = kw * 1024.0 / w_fac
+    return {
+        "kernel": "fwd_kernel<bf16, d=128> (headline workload, switches (1,1,1))",
+        "kernel_source_sha256": kernel_source_sha(),
+        "fetch_size_kib_per_dispatch": kf, "write_size_kib_per_dispatch": kw,
+        "dispatches": [nkf, nkw],
+        "copy_bytes": copy_bytes,
+        "copy_fetch_size_kib": cf, "copy_write_size_kib": cw,
+        "fetch_factor": f_fac, "write_factor": w_fac,
+        "hbm_read_bytes_per_launch": fetch, "hbm_write_bytes_per_launch": write,
+        "traffic_bytes_per_launch": fetch + write,
+        "commands": [
+            "rocprofv3 --pmc FETCH_SIZE -d F -o run --output-format csv -- python3 bench.py "
+            "--steps 2 --warmup 1 --no-cpu-baseline",
+            "rocprofv3 --pmc WRITE_SIZE -d W -o run --output-format csv -- python3 bench.py "
+            "--steps 2 --warmup 1 --no-cpu-baseline",
+            f"rocprofv3 --pmc FETCH_SIZE -d CF -o run --output-format csv -- python3 bench.py "
+            f"--copy-bytes {copy_bytes}",
+            f"rocprofv3 --pmc WRITE_SIZE -d CW -o run --output-format csv -- python3 bench.py "
+            f"--copy-bytes {copy_bytes}",
+            f"python3 bench.py --summarize-traffic F W CF CW --copy-bytes {copy_bytes}"],
+    }
+
+
 def cpu_baseline(inp, sw, heads):
     """The fp64 oracle, as it stands, on whole heads of the same inputs."""
     import numpy as np
@@ -85,7 +138,12 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-bytes", type=int, default=0)
+    ap.add_argument("--summarize-traffic", nargs=4, metavar=("FETCH", "WRITE", "COPY_FETCH",
+                                                              "COPY_WRITE"))
     args = ap.parse_args()
+    if args.summarize_traffic:
+        print(json.dumps(summarize_traffic(*args.summarize_traffic, args.copy_bytes), indent=1))
+        return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU: the resolvent head's heads are independent and the "
               "build has no multi-GPU path (see DESIGN.md, 'Sharding'); run with --gpus 1",
@@ -95,7 +153,7 @@ def main():
     import numpy as np
     import torch
 
-    if args.copy_bytes:
+    if args.copy_bytes:  # the calibration copy of the traffic counters
         copy_calibration(args.copy_bytes)
         return
 
