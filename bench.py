@@ -131,6 +131,100 @@ def cpu_baseline(inp, sw, heads):
             "seconds": dt, "head_tokens_per_s": len(heads) * n / dt}
 
 
+def chain_cpu_baseline(inp, g, heads):
+    """The oracle's gated chain, as it stands, on whole heads of the same inputs."""
+    import numpy as np
+
+    import oracle
+
+    dv = inp["v"].shape[-1]
+    n = inp["n"]
+    t0 = time.perf_counter()
+    for b, h in heads:
+        st, a = oracle.gates(inp["u"][b, h], inp["theta"][b, h], g)
+        assert st == oracle.OK
+        for c in range(dv):
+            oracle.chain(a, inp["v"][b, h, :, c], y0_from_b0=True)
+    dt = time.perf_counter() - t0
+    nbytes = len(heads) * n * (8 + 2 * dv + 8 * dv)
+    return {"value": nbytes / dt / 1e9, "unit": "GB/s", "cores": 1, "kind": "oracle",
+            "sample": f"{len(heads)} whole heads of the same inputs, all {dv} channels, fp64, "
+                      f"one thread; {dt:.2f} s; bytes counted as on the device (u, theta, "
+                      f"bf16 v in, fp32 O out)",
+            "seconds": dt}
+
+
+def bench_chain(args):
+    """The chain-corner scan (resolvent_chain) on the headline inputs."""
+    import numpy as np
+    import torch
+
+    from gated_causal_attention_amd import binding, inputs
+
+    dev = torch.device("cuda:0")
+    g = 1.0
+    inp = inputs.make_config(3)
+    B, H, n = inp["B"], inp["H"], inp["n"]
+    dv = inp["v"].shape[-1]
+    t = inputs.as_torch(inp, dev)
+    o_re = torch.empty((B, H, n, dv), device=dev, dtype=torch.float32)
+    o_im = torch.empty_like(o_re)
+    ws = torch.empty(binding.resolvent_chain_workspace_bytes(B, H, n, dv), device=dev,
+                     dtype=torch.uint8)
+    status = torch.zeros(1, device=dev, dtype=torch.int32)
+    stream = torch.cuda.current_stream(dev)
+
+    def step():
+        binding.resolvent_chain(t["u"], t["theta"], t["v"], g, o_re=o_re, o_im=o_im,
+                                workspace=ws, status=status, stream=stream, check=False)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    assert int(status.item()) == 0
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(args.steps)]
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    start.record(stream)
+    for a, b in ev:
+        a.record(stream)
+        step()
+        b.record(stream)
+    end.record(stream)
+    torch.cuda.synchronize()
+    assert int(status.item()) == 0
+    ms_per_step = start.elapsed_time(end) / args.steps
+    call_ms = float(np.mean([a.elapsed_time(b) for a, b in ev]))
+    # algorithmic HBM bytes: u, theta in; bf16 v in; O_re, O_im out
+    alg = B * H * n * (8 + 2 * dv + 8 * dv)
+    achieved = alg / (call_ms * 1e-3) / 1e9
+    out = {
+        "metric": "chain-corner scan (resolvent_chain): GB/s of algorithmic HBM traffic",
+        "value": alg / (ms_per_step * 1e-3) / 1e9,
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": "chain corner O_i = sum_j G_ij V_j at g = 1 on the headline "
+                               "inputs: B=4 H=16 n=8192 dv=128, bf16 v ~ N(0,1), "
+                               "u ~ U(0.95,1), theta ~ U(-0.05,0.05), seed 3",
+                   "B": B, "H": H, "n": n, "dv": dv, "g": g},
+        "roofline": {"bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                     "frac": achieved / PEAK_HBM_GBS, "traffic": None,
+                     "kernel": "resolvent_chain (gates + three scan kernels, one call)",
+                     "bytes_per_launch": alg},
+    }
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = chain_cpu_baseline(inp, g, [(0, 0), (1, 5), (2, 10), (3, 15)])
+    print(json.dumps(out), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -138,6 +232,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-bytes", type=int, default=0)
+    ap.add_argument("--path", choices=("forward", "chain"), default="forward",
+                    help="forward: the head (the headline line); chain: the chain-corner scan")
     ap.add_argument("--summarize-traffic", nargs=4, metavar=("FETCH", "WRITE", "COPY_FETCH",
                                                               "COPY_WRITE"))
     args = ap.parse_args()
@@ -155,6 +251,10 @@ def main():
 
     if args.copy_bytes:  # the calibration copy of the traffic counters
         copy_calibration(args.copy_bytes)
+        return
+
+    if args.path == "chain":
+        bench_chain(args)
         return
 
     from gated_causal_attention_amd import binding, inputs

@@ -54,6 +54,11 @@ def _load():
     lib.resolvent_counters_offset.restype = ctypes.c_size_t
     lib.resolvent_tile_shape.argtypes = [ctypes.POINTER(i32), ctypes.POINTER(i32)]
     lib.resolvent_tile_shape.restype = None
+    lib.resolvent_chain_workspace_bytes.argtypes = [i64, i64, i64, i64]
+    lib.resolvent_chain_workspace_bytes.restype = ctypes.c_size_t
+    lib.resolvent_chain.argtypes = [vp, vp, vp, dbl, i64, i64, i64, i64, i32, vp, vp, vp,
+                                    ctypes.c_size_t, vp, vp]
+    lib.resolvent_chain.restype = i32
     lib.resolvent_status_str.argtypes = [i32]
     lib.resolvent_status_str.restype = ctypes.c_char_p
     _lib = lib
@@ -127,6 +132,53 @@ def resolvent_forward(q, k, u, theta, v, beta, qk, g, *, o_re=None, o_im=None, w
     else:
         arr = (ctypes.c_void_p * 4)(*marks)
         rc = _load().resolvent_forward_marked(*args, arr)
+    if rc != Status.OK:
+        raise ResolventError(rc)
+    if check and n > 0 and B > 0 and H > 0:
+        if hasattr(stream, "synchronize"):
+            stream.synchronize()
+        else:
+            torch.cuda.synchronize(dev)
+        st = int(status.item())
+        if st != Status.OK:
+            raise ResolventError(st)
+    return o_re, o_im
+
+
+def resolvent_chain_workspace_bytes(B, H, n, dv) -> int:
+    return int(_load().resolvent_chain_workspace_bytes(B, H, n, dv))
+
+
+def resolvent_chain(u, theta, v, g, *, o_re=None, o_im=None, workspace=None, status=None,
+                    stream=None, check=True):
+    """The path-product corner: O_i = sum_{j<=i} G_ij V_j as the gated chain,
+    (o_re, o_im) each [B, H, n, dv] fp32.  u, theta: [B, H, n] fp32 device
+    tensors; v: [B, H, n, dv] bf16 or fp32.  Buffers not given are allocated
+    with torch; ``check`` synchronises and raises on a non-OK device status."""
+    import torch
+
+    B, H, n, dv = v.shape
+    for t in (u, theta, v):
+        if not t.is_contiguous():
+            raise ValueError("inputs must be contiguous")
+    dev = v.device
+    if o_re is None:
+        o_re = torch.empty((B, H, n, dv), device=dev, dtype=torch.float32)
+    if o_im is None:
+        o_im = torch.empty((B, H, n, dv), device=dev, dtype=torch.float32)
+    ws_bytes = resolvent_chain_workspace_bytes(B, H, n, dv)
+    if workspace is None:
+        workspace = torch.empty(max(ws_bytes, 1), device=dev, dtype=torch.uint8)
+    if status is None:
+        status = torch.zeros(1, device=dev, dtype=torch.int32)
+    if stream is None:
+        stream = torch.cuda.current_stream(dev)
+    handle = stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
+    rc = _load().resolvent_chain(u.data_ptr(), theta.data_ptr(), v.data_ptr(), float(g), B, H,
+                                 n, dv, _dtype_code(v), o_re.data_ptr(), o_im.data_ptr(),
+                                 workspace.data_ptr(),
+                                 workspace.numel() * workspace.element_size(), status.data_ptr(),
+                                 handle)
     if rc != Status.OK:
         raise ResolventError(rc)
     if check and n > 0 and B > 0 and H > 0:

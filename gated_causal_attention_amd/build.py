@@ -31,15 +31,17 @@ def build_library(verbose: bool = False) -> str:
     """Compile every source for gfx950 and link the shared library."""
     os.makedirs(BUILD, exist_ok=True)
     hipcc = _hipcc()
-    kobj = os.path.join(BUILD, "resolvent_kernels.o")
+    kobjs = []
+    for src in ("resolvent_kernels", "chain_kernels"):
+        kobjs.append(os.path.join(BUILD, src + ".o"))
+        _run([hipcc, f"--offload-arch={ARCH}", *COMMON, *DEVICE_FLAGS, "-c",
+              os.path.join(CSRC, src + ".hip"), "-o", kobjs[-1]], verbose)
     aobj = os.path.join(BUILD, "resolvent_abi.o")
-    _run([hipcc, f"--offload-arch={ARCH}", *COMMON, *DEVICE_FLAGS, "-c",
-          os.path.join(CSRC, "resolvent_kernels.hip"), "-o", kobj], verbose)
     rocm_inc = os.path.join(os.path.dirname(os.path.dirname(os.path.realpath(hipcc))), "include")
     _run([hipcc, *COMMON, "-D__HIP_PLATFORM_AMD__", "-I", rocm_inc, "-x", "c++", "-c",
           os.path.join(CSRC, "resolvent_abi.cpp"), "-o", aobj], verbose)
     tmp = LIBRARY + ".tmp"
-    _run([hipcc, f"--offload-arch={ARCH}", "-shared", "-fPIC", kobj, aobj, "-o", tmp], verbose)
+    _run([hipcc, f"--offload-arch={ARCH}", "-shared", "-fPIC", *kobjs, aobj, "-o", tmp], verbose)
     os.replace(tmp, LIBRARY)
     return LIBRARY
 

@@ -83,6 +83,30 @@ inline Layout make_layout(int64_t B, int64_t H, int64_t n, int64_t d, bool bf16_
     return L;
 }
 
+// Workspace of the chain-corner scan (resolvent_chain): the gate planes and
+// tile products of make_layout, then per (head, 64-position tile, channel)
+// the tile's own scan end with a zero carry-in (agg) and the carry into the
+// tile (carry), both complex float (float2) [BH][n_kt][dv].
+struct ChainLayout {
+    Layout g;
+    int64_t dv = 0;
+    size_t agg = 0, carry = 0, total = 0;
+};
+
+inline ChainLayout make_chain_layout(int64_t B, int64_t H, int64_t n, int64_t dv) {
+    ChainLayout C;
+    C.g = make_layout(B, H, n, dv, false);
+    C.dv = dv;
+    const size_t per = 8 * size_t(C.g.BH) * size_t(C.g.n_kt) * size_t(dv);
+    size_t off = C.g.total;
+    C.agg = off;
+    off = align_up(off + per, 256);
+    C.carry = off;
+    off = align_up(off + per, 256);
+    C.total = off;
+    return C;
+}
+
 // Source byte offsets of the direct global->LDS tile copies, relative to the
 // start of the tensor (q/k/v, or the v^T region for the bf16 path).  Row `r`
 // of key tile `t` is key t*BK + r, clamped into [0, n-1] so that a tile
@@ -201,6 +225,18 @@ struct Problem {
     bool qk_zero;
     bool v_f32;         // v stored as float32 (bf16 path converts when staging)
 };
+
+// Status := OK, then the gates and their in-tile scans of make_layout into
+// the workspace (resolvent_kernels.hip).  Returns a hipError_t.
+int launch_gates(const Layout &L, const float *u, const float *theta, double g,
+                 unsigned char *ws, int32_t *status, void *stream);
+
+// The chain-corner scan (chain_kernels.hip): the gates, then the three scan
+// kernels.  v is [BH][n][dv] bf16 (v_f32 false) or float32.  Returns a
+// hipError_t.
+int launch_chain(const ChainLayout &C, const float *u, const float *theta, const void *v,
+                 bool v_f32, double g, float *o_re, float *o_im, unsigned char *ws,
+                 int32_t *status, void *stream);
 
 // Kernel launcher (resolvent_kernels.hip).  marks, when not null, are four
 // HIP events recorded on the stream before the first kernel, before the fused

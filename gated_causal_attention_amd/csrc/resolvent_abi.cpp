@@ -112,6 +112,35 @@ int32_t resolvent_forward(const void *q, const void *k, const float *u, const fl
                                     stream, nullptr);
 }
 
+size_t resolvent_chain_workspace_bytes(int64_t B, int64_t H, int64_t n, int64_t dv) {
+    if (B <= 0 || H <= 0 || n <= 0 || dv <= 0) return 0;
+    if (dv % 64 != 0 || dv > 4096 || !within_limits(B, H, n)) return 0;
+    return make_chain_layout(B, H, n, dv).total;
+}
+
+int32_t resolvent_chain(const float *u, const float *theta, const void *v, double g, int64_t B,
+                        int64_t H, int64_t n, int64_t dv, int32_t v_dtype, float *o_re,
+                        float *o_im, void *workspace, size_t workspace_bytes,
+                        int32_t *status_dev, hipStream_t stream) {
+    if (B < 0 || H < 0 || n < 0 || dv < 0) return RESOLVENT_BAD_SHAPE;
+    if (B == 0 || H == 0 || n == 0) return RESOLVENT_OK;  // empty in, empty out
+    if (dv == 0) return RESOLVENT_BAD_SHAPE;
+    if (!std::isfinite(g)) return RESOLVENT_NONFINITE;
+    if (dv % 64 != 0 || dv > 4096 || !within_limits(B, H, n) ||
+        (v_dtype != RESOLVENT_BF16 && v_dtype != RESOLVENT_F32))
+        return RESOLVENT_UNSUPPORTED;
+    if (!u || !theta || !v || !o_re || !o_im || !status_dev || !workspace) return RESOLVENT_BAD_ARG;
+    if (!aligned(u, 4) || !aligned(theta, 4) || !aligned(v, v_dtype == RESOLVENT_F32 ? 4 : 2) ||
+        !aligned(o_re, 4) || !aligned(o_im, 4) || !aligned(status_dev, 4) ||
+        !aligned(workspace, 256))
+        return RESOLVENT_BAD_ARG;
+    const ChainLayout C = make_chain_layout(B, H, n, dv);
+    if (workspace_bytes < C.total) return RESOLVENT_BAD_ARG;
+    const int err = launch_chain(C, u, theta, v, v_dtype == RESOLVENT_F32, g, o_re, o_im,
+                                 static_cast<unsigned char *>(workspace), status_dev, stream);
+    return err == 0 ? RESOLVENT_OK : RESOLVENT_DEVICE_ERROR;
+}
+
 const char *resolvent_status_str(int32_t status) {
     switch (status) {
         case RESOLVENT_OK: return "ok";

@@ -1470,33 +1470,14 @@ __global__ __launch_bounds__(NTHREADS) void logit_check_kernel(FwdArgs A) {
     if (__any(bad) && lane == 0) A.status[0] = kNonFinite;
 }
 
-template <bool F32, int D>
-int launch_typed(const Problem &P, hipStream_t st, hipEvent_t const *marks) {
-    using SM = Smem<F32, D>;
-    const Layout &L = P.L;
-    unsigned char *ws = P.ws;
-    uint32_t *counters = reinterpret_cast<uint32_t *>(ws + L.counters);
-    if (marks) (void)hipEventRecord(marks[0], st);
+GatesArgs gates_args(const Layout &L, const float *u, const float *theta, double g,
+                     unsigned char *ws, int32_t *status) {
     auto fptr = [&](int i) { return reinterpret_cast<float *>(ws + L.gate[i]); };
     auto dptr = [&](int i) { return reinterpret_cast<double *>(ws + L.tile[i]); };
-    const int BH = (int)L.BH;
-
-    if constexpr (!F32) {
-        uint16_t *vt = reinterpret_cast<uint16_t *>(ws + L.vt);
-        if (P.v_f32)
-            hipLaunchKernelGGL((vt_kernel<D, true>), dim3(BH * L.n_kt), dim3(256), 0, st, P.v, vt,
-                               L.n, L.n_pad, (int)L.n_kt, P.status, counters);
-        else
-            hipLaunchKernelGGL((vt_kernel<D, false>), dim3(BH * L.n_kt), dim3(256), 0, st, P.v, vt,
-                               L.n, L.n_pad, (int)L.n_kt, P.status, counters);
-    } else {
-        hipLaunchKernelGGL(clear_status_kernel, dim3(1), dim3(64), 0, st, P.status, counters);
-    }
-
     GatesArgs G;
-    G.u = P.u;
-    G.theta = P.theta;
-    G.g = P.g;
+    G.u = u;
+    G.theta = theta;
+    G.g = g;
     G.n = L.n;
     G.n_pad = L.n_pad;
     G.n_qt = (int)L.n_qt;
@@ -1513,7 +1494,32 @@ int launch_typed(const Problem &P, hipStream_t st, hipEvent_t const *marks) {
     G.t_re = dptr(0);
     G.t_im = dptr(1);
     G.t_m = dptr(2);
-    G.status = P.status;
+    G.status = status;
+    return G;
+}
+
+template <bool F32, int D>
+int launch_typed(const Problem &P, hipStream_t st, hipEvent_t const *marks) {
+    using SM = Smem<F32, D>;
+    const Layout &L = P.L;
+    unsigned char *ws = P.ws;
+    uint32_t *counters = reinterpret_cast<uint32_t *>(ws + L.counters);
+    if (marks) (void)hipEventRecord(marks[0], st);
+    const int BH = (int)L.BH;
+
+    if constexpr (!F32) {
+        uint16_t *vt = reinterpret_cast<uint16_t *>(ws + L.vt);
+        if (P.v_f32)
+            hipLaunchKernelGGL((vt_kernel<D, true>), dim3(BH * L.n_kt), dim3(256), 0, st, P.v, vt,
+                               L.n, L.n_pad, (int)L.n_kt, P.status, counters);
+        else
+            hipLaunchKernelGGL((vt_kernel<D, false>), dim3(BH * L.n_kt), dim3(256), 0, st, P.v, vt,
+                               L.n, L.n_pad, (int)L.n_kt, P.status, counters);
+    } else {
+        hipLaunchKernelGGL(clear_status_kernel, dim3(1), dim3(64), 0, st, P.status, counters);
+    }
+
+    const GatesArgs G = gates_args(L, P.u, P.theta, P.g, ws, P.status);
     hipLaunchKernelGGL(gates_kernel, dim3(BH * L.n_qt), dim3(64), 0, st, G);
     int32_t *noff = reinterpret_cast<int32_t *>(ws + L.noff);
     float *ctab = reinterpret_cast<float *>(ws + L.ctab);
@@ -1583,6 +1589,16 @@ int launch_typed(const Problem &P, hipStream_t st, hipEvent_t const *marks) {
 }
 
 }  // namespace
+
+int launch_gates(const Layout &L, const float *u, const float *theta, double g,
+                 unsigned char *ws, int32_t *status, void *stream) {
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    uint32_t *counters = reinterpret_cast<uint32_t *>(ws + L.counters);
+    hipLaunchKernelGGL(clear_status_kernel, dim3(1), dim3(64), 0, st, status, counters);
+    const GatesArgs G = gates_args(L, u, theta, g, ws, status);
+    hipLaunchKernelGGL(gates_kernel, dim3(L.BH * L.n_qt), dim3(64), 0, st, G);
+    return (int)hipGetLastError();
+}
 
 int launch_forward(const Problem &P, void *stream, void *const *marks) {
     hipStream_t st = static_cast<hipStream_t>(stream);

@@ -142,7 +142,55 @@ size_t resolvent_counters_offset(int64_t B, int64_t H, int64_t n, int64_t d, int
  */
 void resolvent_tile_shape(int32_t *bq, int32_t *bk);
 
-/* resolvent_status_str -- a static, human-readable name of a status code. */
+/*
+ * resolvent_chain_workspace_bytes -- device workspace that resolvent_chain
+ * needs (0 for an empty problem, and also 0 for an invalid or unsupported
+ * one, which resolvent_chain rejects).  It holds the gates, their in-tile
+ * scans and tile products, and two complex floats per (head, 64-position
+ * tile, value channel).  Its contents are scratch between calls.
+ */
+size_t resolvent_chain_workspace_bytes(int64_t B, int64_t H, int64_t n, int64_t dv);
+
+/*
+ * resolvent_chain -- the path-product corner of the head (the page's section
+ * "The path-product corner is a resolvent"): O_i = sum_{j<=i} G_ij V_j, the
+ * readout at switches (beta, qk, g) = (0, 0, g), computed as the gated chain
+ * y_i = a_i y_{i-1} + V_i, y_0 = V_0, per value channel (O(n dv) work; q and k
+ * play no part at qk = 0).  For a given g its result equals resolvent_forward
+ * at (0, 0, g) up to rounding.
+ *
+ * Arguments (device pointers; contiguous row-major):
+ *   u, theta    [B, H, n] float32 raw gate magnitudes and phases, 4-byte
+ *               aligned; every entry is checked although a_0 is never read
+ *   v           [B, H, n, dv] in v_dtype (RESOLVENT_BF16 or RESOLVENT_F32),
+ *               aligned to its element size
+ *   g           the gate switch (f64)
+ *   dv          value channels: a multiple of 64, at most 4096
+ *   o_re, o_im  [B, H, n, dv] float32 outputs, 4-byte aligned
+ *   workspace   at least resolvent_chain_workspace_bytes(...) bytes, 256-byte
+ *               aligned
+ *   status_dev  one int32 of device memory, as for resolvent_forward
+ *   stream      HIP stream to enqueue on (NULL: the null stream)
+ *
+ * Returns, before anything is enqueued: RESOLVENT_BAD_SHAPE for a negative
+ * size or dv == 0 with n, B, H > 0; RESOLVENT_OK with nothing enqueued when
+ * n, B or H is 0; RESOLVENT_NONFINITE for a non-finite g; RESOLVENT_UNSUPPORTED
+ * for a dv that is not a multiple of 64 or exceeds 4096, another dtype, or a
+ * size past the limits of resolvent_forward; RESOLVENT_BAD_ARG for a null or
+ * misaligned pointer or a small workspace; RESOLVENT_DEVICE_ERROR when a
+ * launch fails; RESOLVENT_OK once the work is enqueued.  On the device the
+ * status word becomes RESOLVENT_NONFINITE for a non-finite u or theta or an
+ * overflowing g*theta_k; the outputs are then unspecified.  A non-finite v is
+ * not refused and leaves the outputs unspecified.
+ */
+int32_t resolvent_chain(const float *u, const float *theta, const void *v, double g, int64_t B,
+                        int64_t H, int64_t n, int64_t dv, int32_t v_dtype, float *o_re,
+                        float *o_im, void *workspace, size_t workspace_bytes,
+                        int32_t *status_dev, hipStream_t stream);
+
+/*
+ * resolvent_status_str -- a static, human-readable name of a status code.
+ */
 const char *resolvent_status_str(int32_t status);
 
 #ifdef __cplusplus

@@ -35,6 +35,8 @@ def _load():
     d, i64, i32 = ctypes.c_double, ctypes.c_int64, ctypes.c_int32
     lib.oracle_blend.argtypes = [d, d, d, _dp, _dp]
     lib.oracle_gate.argtypes = [d, d, _dp, _dp]
+    lib.oracle_gates.argtypes = [_dp, _dp, ctypes.c_int64, d, _dp, _dp]
+    lib.oracle_gates.restype = ctypes.c_int
     lib.oracle_path_product.argtypes = [_dp, _dp, i64, _dp, _dp]
     lib.oracle_modulus.argtypes = [_dp, i64, _dp]
     lib.oracle_chain.argtypes = [_dp, _dp, _dp, i64, i32, _dp, _dp]
@@ -80,6 +82,16 @@ def gate(m, theta_p):
     re, im = ctypes.c_double(), ctypes.c_double()
     _load().oracle_gate(float(m), float(theta_p), ctypes.byref(re), ctypes.byref(im))
     return complex(re.value, im.value)
+
+
+def gates(u, theta, g):
+    """Gates a [n] (complex) of one head: gate(blend(u_k, theta_k, g)) for every
+    k.  Returns (status, a)."""
+    u, theta = _f64(u), _f64(theta)
+    n = u.shape[0]
+    ar, ai = np.zeros(n), np.zeros(n)
+    st = _load().oracle_gates(_ptr(u), _ptr(theta), n, float(g), _ptr(ar), _ptr(ai))
+    return st, ar + 1j * ai
 
 
 def path_product(a):

@@ -64,6 +64,21 @@ void oracle_gate(double m, double theta_p, double *re, double *im) {
     *im = m * sin(theta_p);
 }
 
+/* gates(u, theta, g) -> a [n]: blend then gate at every position, as the
+ * head's validation does; returns ORACLE_NONFINITE at the first non-finite
+ * u, theta or g*theta (a is then partly written). */
+int oracle_gates(const double *u, const double *theta, int64_t n, double g, double *a_re,
+                 double *a_im) {
+    for (int64_t k = 0; k < n; ++k) {
+        double m, tp;
+        if (!isfinite(u[k]) || !isfinite(theta[k])) return ORACLE_NONFINITE;
+        oracle_blend(u[k], theta[k], g, &m, &tp);
+        if (!isfinite(tp)) return ORACLE_NONFINITE;
+        oracle_gate(m, tp, &a_re[k], &a_im[k]);
+    }
+    return ORACLE_OK;
+}
+
 /* Complex product x * a, textbook form. */
 static inline void cmul(double xr, double xi, double ar, double ai, double *r, double *i) {
     *r = xr * ar - xi * ai;

@@ -94,3 +94,38 @@ def test_status_strings():
         text = binding.resolvent_status_str(int(s))
         assert text and text != "unknown status"
     assert binding.resolvent_status_str(99) == "unknown status"
+
+
+def chain_call(B=1, H=1, n=128, dv=64, g=1.0, vdt=0, ws_bytes=None, ptr=FAKE, ws=FAKE,
+               status=FAKE):
+    lib = binding._load()
+    if ws_bytes is None:
+        ws_bytes = lib.resolvent_chain_workspace_bytes(max(B, 1), max(H, 1), max(n, 1),
+                                                       max(dv, 64))
+    return lib.resolvent_chain(ptr, ptr, ptr, g, B, H, n, dv, vdt, ptr, ptr, ws, ws_bytes,
+                               status, None)
+
+
+def test_chain_host_checks():
+    assert chain_call(B=-1) == S.BAD_SHAPE
+    assert chain_call(dv=-64) == S.BAD_SHAPE
+    assert chain_call(n=0, ptr=None) == S.OK  # empty in, empty out
+    assert chain_call(dv=0) == S.BAD_SHAPE
+    for bad in (float("nan"), float("inf")):
+        assert chain_call(g=bad) == S.NONFINITE
+    assert chain_call(dv=96) == S.UNSUPPORTED
+    assert chain_call(dv=8192) == S.UNSUPPORTED
+    assert chain_call(vdt=5) == S.UNSUPPORTED
+    assert chain_call(ptr=None) == S.BAD_ARG
+    assert chain_call(ptr=FAKE + 1) == S.BAD_ARG  # v misaligned for bf16
+    assert chain_call(ws=FAKE + 16) == S.BAD_ARG
+    assert chain_call(ws_bytes=100) == S.BAD_ARG
+
+
+def test_chain_workspace_sizes():
+    ws = binding.resolvent_chain_workspace_bytes
+    assert ws(0, 1, 10, 64) == 0 and ws(1, 1, 10, 96) == 0
+    a, b = ws(1, 1, 64, 64), ws(1, 1, 64, 128)
+    assert 0 < a < b  # the tile carries grow with the channels
+    bq, _ = binding.resolvent_tile_shape()
+    assert ws(1, 1, bq + 1, 64) > ws(1, 1, bq, 64)  # sized on n rounded up to bq

@@ -236,6 +236,25 @@ def test_bedm_values(page_values):
         assert abs(a.imag) <= pv["imag_bound"]
 
 
+def test_vector_gates_hold_the_page_values(page_values):
+    """oracle.gates over a whole head: the bedM gates -1, 0, +1 (exact real
+    parts, sin(pi) residue below 1.3e-16), the identity gate 1 at g = 0
+    ("g = 0 removes the gates exactly"), and the refusal of a non-finite u,
+    theta or g*theta."""
+    pv = page_values["bedm"]
+    us = [m for m, _, _ in pv["gates_m_theta_value"]] * 3
+    ths = [math.pi if th == "pi" else th for _, th, _ in pv["gates_m_theta_value"]] * 3
+    st, a = oracle.gates(us, ths, 1.0)
+    assert st == oracle.OK
+    assert list(a.real) == [val for _, _, val in pv["gates_m_theta_value"]] * 3
+    assert np.abs(a.imag).max() <= pv["imag_bound"]
+    st, a = oracle.gates(np.linspace(0, 1, 7), np.linspace(-3, 3, 7), 0.0)
+    assert st == oracle.OK and np.all(a == 1.0)
+    assert oracle.gates([0.5, float("nan")], [0.0, 0.0], 1.0)[0] == oracle.NONFINITE
+    assert oracle.gates([0.5, 0.5], [0.0, float("inf")], 1.0)[0] == oracle.NONFINITE
+    assert oracle.gates([0.5], [1e308], 1e10)[0] == oracle.NONFINITE  # g*theta overflows
+
+
 def test_constant_phase_is_rope_kernel(page_values):
     """constant_phase_gate_is_rope / cumulative_phase_is_separable: unit gates of
     constant phase w give G_ij = e^{i w (i-j)} (Toeplitz, 1e-13); the readout
