@@ -225,6 +225,103 @@ def bench_chain(args):
     print(json.dumps(out), flush=True)
 
 
+def bench_grouped(args):
+    """resolvent_forward_grouped on a grouped workload: 16 query heads sharing
+    2 k/v heads per batch entry, value width 64."""
+    import numpy as np
+    import torch
+
+    from gated_causal_attention_amd import binding, inputs
+
+    dev = torch.device("cuda:0")
+    sw = (1, 1, 1)
+    B, H, Hkv, n, d, dv = 4, 16, 2, 8192, 128, 64
+    inp = inputs.draw(B, H, n, d, 7, dv=dv, u_range=(0.95, 1.0), theta_range=(-0.05, 0.05))
+    inp["k"] = np.ascontiguousarray(inp["k"][:, :Hkv])
+    inp["v"] = np.ascontiguousarray(inp["v"][:, :Hkv])
+    t = inputs.as_torch(inp, dev)
+    o_re = torch.empty((B, H, n, dv), device=dev, dtype=torch.float32)
+    o_im = torch.empty_like(o_re)
+    ws = torch.empty(binding.resolvent_workspace_bytes_grouped(B, H, Hkv, n, d, dv), device=dev,
+                     dtype=torch.uint8)
+    status = torch.zeros(1, device=dev, dtype=torch.int32)
+    stream = torch.cuda.current_stream(dev)
+    cnt_off = binding.resolvent_counters_offset(B, H, n, d)
+
+    def step():
+        binding.resolvent_forward_grouped(t["q"], t["k"], t["u"], t["theta"], t["v"], *sw,
+                                          o_re=o_re, o_im=o_im, workspace=ws, status=status,
+                                          stream=stream, check=False)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    assert int(status.item()) == 0
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(args.steps)]
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    start.record(stream)
+    for a, b in ev:
+        a.record(stream)
+        step()
+        b.record(stream)
+    end.record(stream)
+    torch.cuda.synchronize()
+    assert int(status.item()) == 0
+    ms_per_step = start.elapsed_time(end) / args.steps
+    call_ms = float(np.mean([a.elapsed_time(b) for a, b in ev]))
+    BQ, BK = binding.resolvent_tile_shape()
+    off_tiles = int(ws[cnt_off:cnt_off + 4].cpu().numpy().view(np.uint32)[0])
+    n_qt = (n + BQ - 1) // BQ
+    diag_pairs = B * H * sum(min(BQ, n - q * BQ) * (min(BQ, n - q * BQ) + 1) // 2
+                             for q in range(n_qt))
+    eval_pairs = off_tiles * BQ * BK + diag_pairs
+    alg_flops = (2 * d + 4 * dv) * eval_pairs
+    achieved = alg_flops / (call_ms * 1e-3) / 1e12
+    out = {
+        "metric": "grouped resolvent head (resolvent_forward_grouped): TFLOP/s",
+        "value": alg_flops / (ms_per_step * 1e-3) / 1e12,
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": "grouped head B=4 H=16 Hkv=2 n=8192 d=128 dv=64, bf16 q,k,v "
+                               "~ N(0,1), u ~ U(0.95,1), theta ~ U(-0.05,0.05), switches "
+                               "(1,1,1), seed 7",
+                   "B": B, "H": H, "Hkv": Hkv, "n": n, "d": d, "dv": dv},
+        "mtokens_per_s": B * n / (ms_per_step * 1e-3) / 1e6,
+        "evaluated_pair_fraction": eval_pairs * 2.0 / (n * (n + 1) * B * H),
+        "roofline": {"bound": "mfma", "achieved": achieved, "peak": PEAK_BF16_TFLOPS,
+                     "unit": "TFLOP/s", "frac": achieved / PEAK_BF16_TFLOPS, "traffic": None,
+                     "kernel": "resolvent_forward_grouped (whole call)",
+                     "flops_per_launch": alg_flops},
+    }
+    if not args.no_cpu_baseline:
+        heads = [(0, 0), (1, 9)]
+        import oracle
+
+        t0 = time.perf_counter()
+        for b, h in heads:
+            st, _ = oracle.forward_rows(inp["q"][b, h], inp["k"][b, h // (H // Hkv)],
+                                        inp["u"][b, h], inp["theta"][b, h],
+                                        inp["v"][b, h // (H // Hkv)], *sw, rows=np.arange(n),
+                                        nthreads=oracle.default_threads())
+            assert st == oracle.OK
+        dt = time.perf_counter() - t0
+        flops = (d + 2 * dv) * n * (n + 1) * len(heads)
+        out["cpu_baseline"] = {"value": flops / dt / 1e12, "unit": "TFLOP/s",
+                               "cores": oracle.default_threads(), "kind": "oracle",
+                               "sample": f"{len(heads)} whole heads {heads}, all {n} rows, fp64; "
+                                         f"{dt:.2f} s; FLOPs counted dense-causal"}
+    print(json.dumps(out), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -232,8 +329,9 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-bytes", type=int, default=0)
-    ap.add_argument("--path", choices=("forward", "chain"), default="forward",
-                    help="forward: the head (the headline line); chain: the chain-corner scan")
+    ap.add_argument("--path", choices=("forward", "chain", "grouped"), default="forward",
+                    help="forward: the head (the headline line); chain: the chain-corner "
+                         "scan; grouped: shared k/v heads and another value width")
     ap.add_argument("--summarize-traffic", nargs=4, metavar=("FETCH", "WRITE", "COPY_FETCH",
                                                               "COPY_WRITE"))
     args = ap.parse_args()
@@ -255,6 +353,9 @@ def main():
 
     if args.path == "chain":
         bench_chain(args)
+        return
+    if args.path == "grouped":
+        bench_grouped(args)
         return
 
     from gated_causal_attention_amd import binding, inputs

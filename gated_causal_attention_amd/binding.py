@@ -54,6 +54,12 @@ def _load():
     lib.resolvent_counters_offset.restype = ctypes.c_size_t
     lib.resolvent_tile_shape.argtypes = [ctypes.POINTER(i32), ctypes.POINTER(i32)]
     lib.resolvent_tile_shape.restype = None
+    lib.resolvent_workspace_bytes_grouped.argtypes = [i64, i64, i64, i64, i64, i64, i32, i32]
+    lib.resolvent_workspace_bytes_grouped.restype = ctypes.c_size_t
+    lib.resolvent_forward_grouped.argtypes = [vp, vp, vp, vp, vp, dbl, dbl, dbl, i64, i64, i64,
+                                              i64, i64, i64, i32, i32, vp, vp, vp,
+                                              ctypes.c_size_t, vp, vp]
+    lib.resolvent_forward_grouped.restype = i32
     lib.resolvent_chain_workspace_bytes.argtypes = [i64, i64, i64, i64]
     lib.resolvent_chain_workspace_bytes.restype = ctypes.c_size_t
     lib.resolvent_chain.argtypes = [vp, vp, vp, dbl, i64, i64, i64, i64, i32, vp, vp, vp,
@@ -132,6 +138,54 @@ def resolvent_forward(q, k, u, theta, v, beta, qk, g, *, o_re=None, o_im=None, w
     else:
         arr = (ctypes.c_void_p * 4)(*marks)
         rc = _load().resolvent_forward_marked(*args, arr)
+    if rc != Status.OK:
+        raise ResolventError(rc)
+    if check and n > 0 and B > 0 and H > 0:
+        if hasattr(stream, "synchronize"):
+            stream.synchronize()
+        else:
+            torch.cuda.synchronize(dev)
+        st = int(status.item())
+        if st != Status.OK:
+            raise ResolventError(st)
+    return o_re, o_im
+
+
+def resolvent_workspace_bytes_grouped(B, H, Hkv, n, d, dv, qk_dtype=BF16, v_dtype=BF16) -> int:
+    return int(_load().resolvent_workspace_bytes_grouped(B, H, Hkv, n, d, dv, qk_dtype, v_dtype))
+
+
+def resolvent_forward_grouped(q, k, u, theta, v, beta, qk, g, *, o_re=None, o_im=None,
+                              workspace=None, status=None, stream=None, check=True):
+    """Grouped k/v heads and free value width: q [B, H, n, d]; k [B, Hkv, n, d];
+    v [B, Hkv, n, dv]; u, theta [B, H, n].  Returns (o_re, o_im), each
+    [B, H, n, dv] fp32."""
+    import torch
+
+    B, H, n, d = q.shape
+    Hkv, dv = k.shape[1], v.shape[-1]
+    for t in (q, k, v, u, theta):
+        if not t.is_contiguous():
+            raise ValueError("inputs must be contiguous")
+    dev = q.device
+    qk_dt, v_dt = _dtype_code(q), _dtype_code(v)
+    if o_re is None:
+        o_re = torch.empty((B, H, n, dv), device=dev, dtype=torch.float32)
+    if o_im is None:
+        o_im = torch.empty((B, H, n, dv), device=dev, dtype=torch.float32)
+    ws_bytes = resolvent_workspace_bytes_grouped(B, H, Hkv, n, d, dv, qk_dt, v_dt)
+    if workspace is None:
+        workspace = torch.empty(max(ws_bytes, 1), device=dev, dtype=torch.uint8)
+    if status is None:
+        status = torch.zeros(1, device=dev, dtype=torch.int32)
+    if stream is None:
+        stream = torch.cuda.current_stream(dev)
+    handle = stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
+    rc = _load().resolvent_forward_grouped(
+        q.data_ptr(), k.data_ptr(), u.data_ptr(), theta.data_ptr(), v.data_ptr(), float(beta),
+        float(qk), float(g), B, H, Hkv, n, d, dv, qk_dt, v_dt, o_re.data_ptr(), o_im.data_ptr(),
+        workspace.data_ptr(), workspace.numel() * workspace.element_size(), status.data_ptr(),
+        handle)
     if rc != Status.OK:
         raise ResolventError(rc)
     if check and n > 0 and B > 0 and H > 0:

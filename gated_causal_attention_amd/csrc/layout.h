@@ -29,6 +29,8 @@ RESOLVENT_HD constexpr int64_t ctab_entries(int64_t qt) { return (BQ / BK) * qt 
 
 struct Layout {
     int64_t BH = 0, n = 0, d = 0;
+    int64_t H = 0, Hkv = 0, BHkv = 0, dv = 0;  // query heads per batch entry; k/v heads;
+                                               // k/v heads in all; value channels
     int64_t n_pad = 0, n_qt = 0, n_kt = 0;
     bool bf16_path = true;
     // byte offsets into the workspace
@@ -42,15 +44,22 @@ struct Layout {
     size_t qstat = 0, kstat = 0;  // per query tile max |q|, max |k| bits (uint32 [BH][n_qt])
     size_t noff = 0;  // per query tile: key tiles before it that the forward visits (int32 [BH][n_qt])
     size_t counters = 0;  // uint32 [2]: key tiles processed before the query tiles; spare
-    size_t vt = 0;        // bf16 [BH][d][n_pad], keys permuted inside groups of 16
+    size_t vt = 0;        // bf16 [BHkv][dv][n_pad], keys permuted inside groups of 16
     size_t total = 0;
 };
 
-inline Layout make_layout(int64_t B, int64_t H, int64_t n, int64_t d, bool bf16_path) {
+// Hkv k/v heads (each shared by H/Hkv query heads) and dv value channels;
+// 0 means Hkv = H and dv = d.
+inline Layout make_layout(int64_t B, int64_t H, int64_t n, int64_t d, bool bf16_path,
+                          int64_t Hkv = 0, int64_t dv = 0) {
     Layout L;
     L.BH = B * H;
     L.n = n;
     L.d = d;
+    L.H = H;
+    L.Hkv = Hkv > 0 ? Hkv : H;
+    L.BHkv = B * L.Hkv;
+    L.dv = dv > 0 ? dv : d;
     L.bf16_path = bf16_path;
     L.n_pad = (n + BQ - 1) / BQ * BQ;
     L.n_qt = L.n_pad / BQ;
@@ -78,7 +87,7 @@ inline Layout make_layout(int64_t B, int64_t H, int64_t n, int64_t d, bool bf16_
     L.counters = off;
     off = align_up(off + 2 * sizeof(uint32_t), 256);
     L.vt = off;
-    if (bf16_path) off = align_up(off + 2 * size_t(L.BH) * size_t(d) * size_t(L.n_pad), 256);
+    if (bf16_path) off = align_up(off + 2 * size_t(L.BHkv) * size_t(L.dv) * size_t(L.n_pad), 256);
     L.total = off;
     return L;
 }

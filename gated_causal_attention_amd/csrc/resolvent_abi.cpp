@@ -33,6 +33,63 @@ bool within_limits(int64_t B, int64_t H, int64_t n) {
 
 bool aligned(const void *p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
 
+bool supported_dv(int64_t dv) { return dv == 64 || dv == 128; }
+
+size_t workspace_grouped(int64_t B, int64_t H, int64_t Hkv, int64_t n, int64_t d, int64_t dv,
+                         int32_t qk_dtype, int32_t v_dtype) {
+    if (B <= 0 || H <= 0 || Hkv <= 0 || n <= 0 || d <= 0 || dv <= 0 || H % Hkv != 0) return 0;
+    if (!supported(d, qk_dtype, v_dtype) || !supported_dv(dv) || !within_limits(B, H, n))
+        return 0;
+    return make_layout(B, H, n, d, qk_dtype == RESOLVENT_BF16, Hkv, dv).total;
+}
+
+int32_t forward_impl(const void *q, const void *k, const float *u, const float *theta,
+                     const void *v, double beta, double qk, double g, int64_t B, int64_t H,
+                     int64_t Hkv, int64_t n, int64_t d, int64_t dv, int32_t qk_dtype,
+                     int32_t v_dtype, float *o_re, float *o_im, void *workspace,
+                     size_t workspace_bytes, int32_t *status_dev, hipStream_t stream,
+                     hipEvent_t *marks) {
+    if (B < 0 || H < 0 || Hkv < 0 || n < 0 || d < 0 || dv < 0) return RESOLVENT_BAD_SHAPE;
+    if (B == 0 || H == 0 || n == 0) return RESOLVENT_OK;  // empty in, empty out
+    if (d == 0 || dv == 0 || Hkv == 0 || H % Hkv != 0) return RESOLVENT_BAD_SHAPE;
+    if (!std::isfinite(beta) || !std::isfinite(qk) || !std::isfinite(g))
+        return RESOLVENT_NONFINITE;
+    if (!supported(d, qk_dtype, v_dtype) || !supported_dv(dv) || !within_limits(B, H, n))
+        return RESOLVENT_UNSUPPORTED;
+    if (!q || !k || !u || !theta || !v || !o_re || !o_im || !status_dev || !workspace)
+        return RESOLVENT_BAD_ARG;
+    if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(o_re, 16) ||
+        !aligned(o_im, 16) || !aligned(u, 4) || !aligned(theta, 4) || !aligned(status_dev, 4) ||
+        !aligned(workspace, 256))
+        return RESOLVENT_BAD_ARG;
+    const Layout L = make_layout(B, H, n, d, qk_dtype == RESOLVENT_BF16, Hkv, dv);
+    if (workspace_bytes < L.total) return RESOLVENT_BAD_ARG;
+
+    // logit scale in log2 units; the device computes logits in float32
+    const double c = qk * 1.4426950408889634074 / std::sqrt((double)d);
+    if (qk != 0.0 && !(std::fabs(c) <= (double)FLT_MAX)) return RESOLVENT_NONFINITE;
+
+    Problem P;
+    P.q = q;
+    P.k = k;
+    P.v = v;
+    P.u = u;
+    P.theta = theta;
+    P.o_re = o_re;
+    P.o_im = o_im;
+    P.status = status_dev;
+    P.ws = static_cast<unsigned char *>(workspace);
+    P.L = L;
+    P.g = g;
+    P.c = (float)c;
+    P.beta = (float)beta;
+    P.beta_mode = beta == 0.0 ? 0 : (beta == 1.0 ? 1 : 2);
+    P.qk_zero = (qk == 0.0);
+    P.v_f32 = (v_dtype == RESOLVENT_F32);
+    const int err = launch_forward(P, stream, reinterpret_cast<void *const *>(marks));
+    return err == 0 ? RESOLVENT_OK : RESOLVENT_DEVICE_ERROR;
+}
+
 }  // namespace
 
 extern "C" {
@@ -61,45 +118,25 @@ int32_t resolvent_forward_marked(const void *q, const void *k, const float *u,
                                  int32_t qk_dtype, int32_t v_dtype, float *o_re, float *o_im,
                                  void *workspace, size_t workspace_bytes, int32_t *status_dev,
                                  hipStream_t stream, hipEvent_t *marks) {
-    if (B < 0 || H < 0 || n < 0 || d < 0) return RESOLVENT_BAD_SHAPE;
-    if (B == 0 || H == 0 || n == 0) return RESOLVENT_OK;  // empty in, empty out
-    if (d == 0) return RESOLVENT_BAD_SHAPE;
-    if (!std::isfinite(beta) || !std::isfinite(qk) || !std::isfinite(g))
-        return RESOLVENT_NONFINITE;
-    if (!supported(d, qk_dtype, v_dtype) || !within_limits(B, H, n))
-        return RESOLVENT_UNSUPPORTED;
-    if (!q || !k || !u || !theta || !v || !o_re || !o_im || !status_dev || !workspace)
-        return RESOLVENT_BAD_ARG;
-    if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(o_re, 16) ||
-        !aligned(o_im, 16) || !aligned(u, 4) || !aligned(theta, 4) || !aligned(status_dev, 4) ||
-        !aligned(workspace, 256))
-        return RESOLVENT_BAD_ARG;
-    const Layout L = make_layout(B, H, n, d, qk_dtype == RESOLVENT_BF16);
-    if (workspace_bytes < L.total) return RESOLVENT_BAD_ARG;
+    return forward_impl(q, k, u, theta, v, beta, qk, g, B, H, H, n, d, d, qk_dtype, v_dtype,
+                        o_re, o_im, workspace, workspace_bytes, status_dev, stream, marks);
+}
 
-    // logit scale in log2 units; the device computes logits in float32
-    const double c = qk * 1.4426950408889634074 / std::sqrt((double)d);
-    if (qk != 0.0 && !(std::fabs(c) <= (double)FLT_MAX)) return RESOLVENT_NONFINITE;
+size_t resolvent_workspace_bytes_grouped(int64_t B, int64_t H, int64_t Hkv, int64_t n,
+                                         int64_t d, int64_t dv, int32_t qk_dtype,
+                                         int32_t v_dtype) {
+    return workspace_grouped(B, H, Hkv, n, d, dv, qk_dtype, v_dtype);
+}
 
-    Problem P;
-    P.q = q;
-    P.k = k;
-    P.v = v;
-    P.u = u;
-    P.theta = theta;
-    P.o_re = o_re;
-    P.o_im = o_im;
-    P.status = status_dev;
-    P.ws = static_cast<unsigned char *>(workspace);
-    P.L = L;
-    P.g = g;
-    P.c = (float)c;
-    P.beta = (float)beta;
-    P.beta_mode = beta == 0.0 ? 0 : (beta == 1.0 ? 1 : 2);
-    P.qk_zero = (qk == 0.0);
-    P.v_f32 = (v_dtype == RESOLVENT_F32);
-    const int err = launch_forward(P, stream, reinterpret_cast<void *const *>(marks));
-    return err == 0 ? RESOLVENT_OK : RESOLVENT_DEVICE_ERROR;
+int32_t resolvent_forward_grouped(const void *q, const void *k, const float *u,
+                                  const float *theta, const void *v, double beta, double qk,
+                                  double g, int64_t B, int64_t H, int64_t Hkv, int64_t n,
+                                  int64_t d, int64_t dv, int32_t qk_dtype, int32_t v_dtype,
+                                  float *o_re, float *o_im, void *workspace,
+                                  size_t workspace_bytes, int32_t *status_dev,
+                                  hipStream_t stream) {
+    return forward_impl(q, k, u, theta, v, beta, qk, g, B, H, Hkv, n, d, dv, qk_dtype, v_dtype,
+                        o_re, o_im, workspace, workspace_bytes, status_dev, stream, nullptr);
 }
 
 int32_t resolvent_forward(const void *q, const void *k, const float *u, const float *theta,

@@ -296,12 +296,18 @@ struct FwdArgs {
     int32_t *status;
     int64_t n, n_pad;
     int n_qt, n_kt, BH;
+    int H, group;  // query heads per batch entry; query heads per k/v head
     float c, beta, one_minus_beta;
     int beta_mode, qk_zero;
 };
 
+// The k/v head that query head bh (= b H + h) reads: b H/group + h/group.
+__device__ __forceinline__ int64_t kv_head(const FwdArgs &A, int64_t bh) {
+    return (bh / A.H) * (A.H / A.group) + (bh % A.H) / A.group;
+}
+
 // Shared-memory plan: NBUF buffers, each holding one key tile K [BK][D], its
-// values (bf16 path: v^T [D][BK] in perm16 key order; fp32 path: V [BK][D]),
+// values (bf16 path: v^T [DV][BK] in perm16 key order; fp32 path: V [BK][DV]),
 // per-key side data (the carried gate factor T_j = C*S_j with its modulus
 // for tiles before the query tile; the gates a_{j+1} for the query tile's
 // own keys) and the raw in-tile suffix products S_j it is formed from.
@@ -311,13 +317,15 @@ struct FwdArgs {
 // operand reads stay free of bank conflicts.  fp32 tiles are 16-byte-chunk-
 // major: chunk c of row r sits at (c * rows + r) * 16 (one wave instruction
 // copies one chunk of 64 rows).  Buffers start on 256-byte boundaries.
-template <bool F32, int D>
+template <bool F32, int D, int DV = D>
 struct Smem {
     static constexpr int ESZ = F32 ? 4 : 2;
-    static constexpr int KCH = D * ESZ / 16;    // 16-byte chunks per K (and fp32 V) row
+    static constexpr int KCH = D * ESZ / 16;    // 16-byte chunks per K row
+    static constexpr int VKCH = DV * 4 / 16;    // chunks per V row (fp32 path)
     static constexpr int VCH = BK * 2 / 16;     // chunks per v^T row (bf16 path)
+    static constexpr int VINS = F32 ? VKCH : VCH * DV / 64;  // V copy instructions per tile
     static constexpr size_t k_bytes = size_t(KCH) * BK * 16;
-    static constexpr size_t v_bytes = F32 ? size_t(KCH) * BK * 16 : size_t(VCH) * D * 16;
+    static constexpr size_t v_bytes = F32 ? size_t(VKCH) * BK * 16 : size_t(VCH) * DV * 16;
     static constexpr size_t side_off = k_bytes + v_bytes;
     // side data: 3 x BK floats; raw: S_j as 3 x BK floats and the tile's
     // carried product C (C_re, C_im, C_m, 0) as floats; then 2 flag words
@@ -326,12 +334,12 @@ struct Smem {
     static constexpr size_t carry_off = raw_off + 3 * BK * sizeof(float);
     static constexpr size_t flag_off = carry_off + 4 * sizeof(float);
     static constexpr size_t buf_bytes = (flag_off + 16 + 255) / 256 * 256;
-    // four buffers keep two tiles in flight while two are read; the fp32
-    // d=128 tiles only fit twice into the 160 KB of LDS
-    static constexpr int NBUF = (F32 && D == 128) ? 2 : 4;
+    // four buffers keep two tiles in flight while two are read, when they
+    // fit into the 160 KB of LDS (not the larger fp32 tiles)
+    static constexpr int NBUF = 4 * buf_bytes + 64 <= 160 * 1024 ? 4 : 2;
     static constexpr size_t misc_off = NBUF * buf_bytes;
     static constexpr size_t bytes = misc_off + 8 * sizeof(uint32_t);
-    static_assert(KCH % NCOPY == 0 && (VCH * D / 64) % NCOPY == 0, "whole wave copies");
+    static_assert(KCH % NCOPY == 0 && VINS % NCOPY == 0, "whole wave copies");
 };
 
 template <bool F32, int D>
@@ -486,11 +494,11 @@ __device__ __forceinline__ uint32_t load_q(const FwdArgs &A, int64_t bh, int64_t
 // nothing.  Keys past n repeat key n-1 (their entries are
 // masked); the v^T copy is zero there.  kh, vh: this head's rows of k and of
 // v^T (bf16 path) or v (fp32 path), wave-uniform.
-template <bool F32, int D>
+template <bool F32, int D, int DV>
 __device__ __forceinline__ void stage_async(const FwdArgs &A, uint32_t buf,
                                             const unsigned char *kh, const unsigned char *vh,
                                             int t, bool k_only, int w) {
-    using SM = Smem<F32, D>;
+    using SM = Smem<F32, D, DV>;
     const int lane = fresh_lane();
     if (w >= NCOPY) return;
     constexpr int ROWB = D * SM::ESZ;  // bytes per q/k/v row in memory
@@ -504,7 +512,7 @@ __device__ __forceinline__ void stage_async(const FwdArgs &A, uint32_t buf,
         }
         if (k_only) return;
         // v^T: instruction j copies rows d = 8 j, ..., 8 j + 7 (keys of tile t)
-        constexpr int NI = SM::VCH * D / 64 / NCOPY;
+        constexpr int NI = SM::VINS / NCOPY;
 #pragma unroll
         for (int i = 0; i < NI; ++i) {
             const int j = w + NCOPY * i;
@@ -519,24 +527,26 @@ __device__ __forceinline__ void stage_async(const FwdArgs &A, uint32_t buf,
             g2lds16(kh, koff + uint32_t(c * 16), buf + uint32_t(c * 1024));
         }
         if (k_only) return;
+        const uint32_t voff = tile_row_off(A.n, t, lane, DV * 4);
 #pragma unroll
-        for (int i = 0; i < SM::KCH / NCOPY; ++i) {
+        for (int i = 0; i < SM::VINS / NCOPY; ++i) {
             const int c = w + NCOPY * i;
-            g2lds16(vh, koff + uint32_t(c * 16), buf + uint32_t(SM::k_bytes + c * 1024));
+            g2lds16(vh, voff + uint32_t(c * 16), buf + uint32_t(SM::k_bytes + c * 1024));
         }
     }
 }
 
-// Head bases of the tile copies (wave-uniform).
-template <bool F32, int D>
-__device__ __forceinline__ void head_bases(const FwdArgs &A, int64_t bh, const unsigned char *&kh,
-                                           const unsigned char *&vh) {
+// Bases of the tile copies for k/v head kvh (wave-uniform): its rows of k,
+// and of v^T (bf16 path) or v (fp32 path).
+template <bool F32, int D, int DV>
+__device__ __forceinline__ void head_bases(const FwdArgs &A, int64_t kvh,
+                                           const unsigned char *&kh, const unsigned char *&vh) {
     constexpr int64_t ROWB = D * Smem<F32, D>::ESZ;
-    kh = uniform_ptr(static_cast<const unsigned char *>(A.k) + bh * A.n * ROWB);
+    kh = uniform_ptr(static_cast<const unsigned char *>(A.k) + kvh * A.n * ROWB);
     if constexpr (!F32)
-        vh = uniform_ptr(reinterpret_cast<const unsigned char *>(A.vt) + bh * D * A.n_pad * 2);
+        vh = uniform_ptr(reinterpret_cast<const unsigned char *>(A.vt) + kvh * DV * A.n_pad * 2);
     else
-        vh = uniform_ptr(static_cast<const unsigned char *>(A.v) + bh * A.n * ROWB);
+        vh = uniform_ptr(static_cast<const unsigned char *>(A.v) + kvh * A.n * (DV * 4));
 }
 
 // Largest |k| (float bits) over the K bytes of key tile t that wave w copied
@@ -594,10 +604,10 @@ __device__ __forceinline__ f32x16 s_block(const unsigned char *buf, int kb, int 
 // O^T += V^T W~^T for one 32-key block at kb (bf16 path), W~ packed per
 // 16-key chunk kc as the B operand (registers 8kc..8kc+7 of the S^T block):
 // two accumulators, one for Re W~ and one for Im W~, share the V operand.
-template <int D>
+template <int D, int DV>
 __device__ __forceinline__ void pv_block_bf16(const unsigned char *buf, int kb, int qi, int h,
                                               const bf16x8 (&wr)[2], const bf16x8 (&wi)[2],
-                                              f32x16 (&ore)[D / 32], f32x16 (&oim)[D / 32]) {
+                                              f32x16 (&ore)[DV / 32], f32x16 (&oim)[DV / 32]) {
     const unsigned char *vb = buf + Smem<false, D>::k_bytes;
     const int vf = vfrag_base(qi, h);
 #pragma unroll
@@ -605,7 +615,7 @@ __device__ __forceinline__ void pv_block_bf16(const unsigned char *buf, int kb, 
         // chunk (kb/8 + 2kc + h) of v^T row 32db + qi
         const unsigned char *vp = vb + (vf ^ (2 * kb + 32 * kc));
 #pragma unroll
-        for (int db = 0; db < D / 32; ++db) {
+        for (int db = 0; db < DV / 32; ++db) {
             const bf16x8 a = *reinterpret_cast<const bf16x8 *>(vp + 32 * db * 128);
             ore[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, wr[kc], ore[db], 0, 0, 0);
             oim[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, wi[kc], oim[db], 0, 0, 0);
@@ -614,17 +624,17 @@ __device__ __forceinline__ void pv_block_bf16(const unsigned char *buf, int kb, 
 }
 
 // The same for the 16 keys of chunk kc on the fp32 path (fp32 V rows).
-template <int D>
+template <int D, int DV>
 __device__ __forceinline__ void pv_chunk_f32(const unsigned char *buf, int kb, int kc, int qi,
                                              int h, const float (&wre)[8], const float (&wim)[8],
-                                             f32x16 (&ore)[D / 32], f32x16 (&oim)[D / 32]) {
+                                             f32x16 (&ore)[DV / 32], f32x16 (&oim)[DV / 32]) {
     const unsigned char *vb = buf + Smem<true, D>::k_bytes;
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
         const int s = 8 * kc + e;
         const int key = kb + 8 * (s / 4) + 4 * h + (s % 4);
 #pragma unroll
-        for (int db = 0; db < D / 32; ++db) {
+        for (int db = 0; db < DV / 32; ++db) {
             const int d = 32 * db + qi;
             const float a =
                 *reinterpret_cast<const float *>(vb + ((d >> 2) * BK + key) * 16 + (d & 3) * 4);
@@ -645,10 +655,10 @@ constexpr int MDEPTH = 4;
 struct MPrefetch {
     bf16x8 vf[MDEPTH], kf[MDEPTH];
 };
-template <int D>
+template <int D, int DV>
 __device__ __forceinline__ bf16x8 mstep_vload(const unsigned char *bv, int vf, int kbv, int i) {
     // chunk (kbv/8 + 2kc + h) of v^T row 32db + qi, fragment i = (kc, db)
-    const int kc = i / (D / 32), db = i % (D / 32);
+    const int kc = i / (DV / 32), db = i % (DV / 32);
     return *reinterpret_cast<const bf16x8 *>(bv + Smem<false, D>::k_bytes + 4096 * db +
                                              (vf ^ (2 * kbv + 32 * kc)));
 }
@@ -658,34 +668,34 @@ __device__ __forceinline__ bf16x8 mstep_kload(const unsigned char *bs, int kf, i
 }
 // Operand fragments [I0, I1) of each kind of a matrix step (mstep_bf16 with
 // NPRE = I1 then starts from the first NPRE of them).
-template <int D, bool PV, bool S, int I0, int I1>
+template <int D, int DV, bool PV, bool S, int I0, int I1>
 __device__ __forceinline__ void mstep_prefetch(const unsigned char *bv, int kbv,
                                                const unsigned char *bs, int kbs, int qi, int h,
                                                MPrefetch &pf) {
-    constexpr int NV = PV ? 2 * (D / 32) : 0;
+    constexpr int NV = PV ? 2 * (DV / 32) : 0;
     constexpr int NK = S ? D / 16 : 0;
     const int vf = vfrag_base(qi, h);
     const int kf = kfrag_base<D / 8>(kbs, qi, h);
 #pragma unroll
     for (int i = I0; i < I1; ++i) {
-        if (i < NV) pf.vf[i] = mstep_vload<D>(bv, vf, kbv, i);
+        if (i < NV) pf.vf[i] = mstep_vload<D, DV>(bv, vf, kbv, i);
         if (i < NK) pf.kf[i] = mstep_kload(bs, kf, i);
     }
 }
-template <int D, bool PV, bool S, int NPRE>
+template <int D, int DV, bool PV, bool S, int NPRE>
 __device__ __forceinline__ void mstep_bf16(const unsigned char *bv, int kbv,
                                            const unsigned char *bs, int kbs, int qi, int h,
                                            MPrefetch &pf, const bf16x8 (&wr)[2],
                                            const bf16x8 (&wi)[2], const bf16x8 (&qf)[D / 16],
-                                           f32x16 (&ore)[D / 32], f32x16 (&oim)[D / 32],
+                                           f32x16 (&ore)[DV / 32], f32x16 (&oim)[DV / 32],
                                            f32x16 &sacc) {
-    constexpr int NDB = D / 32;
+    constexpr int NDB = DV / 32;
     constexpr int NV = PV ? 2 * NDB : 0;  // v^T fragments: chunk kc, row block db
     constexpr int NK = S ? D / 16 : 0;    // K fragments
     constexpr int NSTEP = NV > NK ? NV : NK;
     const int vf = vfrag_base(qi, h);
     const int kf = kfrag_base<D / 8>(kbs, qi, h);
-    mstep_prefetch<D, PV, S, NPRE, MDEPTH>(bv, kbv, bs, kbs, qi, h, pf);
+    mstep_prefetch<D, DV, PV, S, NPRE, MDEPTH>(bv, kbv, bs, kbs, qi, h, pf);
     if constexpr (S) {
 #pragma unroll
         for (int r = 0; r < 16; ++r) sacc[r] = 0.f;
@@ -698,7 +708,7 @@ __device__ __forceinline__ void mstep_bf16(const unsigned char *bv, int kbv,
             const bf16x8 a = pf.vf[i % MDEPTH];
             ore[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, wr[kc], ore[db], 0, 0, 0);
             oim[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, wi[kc], oim[db], 0, 0, 0);
-            if (i + MDEPTH < NV) pf.vf[i % MDEPTH] = mstep_vload<D>(bv, vf, kbv, i + MDEPTH);
+            if (i + MDEPTH < NV) pf.vf[i % MDEPTH] = mstep_vload<D, DV>(bv, vf, kbv, i + MDEPTH);
         }
         if (i < NK) {
             sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(pf.kf[i % MDEPTH], qf[i], sacc, 0, 0, 0);
@@ -799,15 +809,16 @@ struct BlockW<true> {
 };
 
 // O^T += V^T W~^T for the 32-key block at kb of a staged tile.
-template <bool F32, int D>
+template <bool F32, int D, int DV>
 __device__ __forceinline__ void pv_block(const unsigned char *buf, int kb, int qi, int h,
-                                         const BlockW<F32> &wb, f32x16 (&ore)[D / 32],
-                                         f32x16 (&oim)[D / 32]) {
+                                         const BlockW<F32> &wb, f32x16 (&ore)[DV / 32],
+                                         f32x16 (&oim)[DV / 32]) {
     if constexpr (F32) {
 #pragma unroll
-        for (int kc = 0; kc < 2; ++kc) pv_chunk_f32<D>(buf, kb, kc, qi, h, wb.r[kc], wb.i[kc], ore, oim);
+        for (int kc = 0; kc < 2; ++kc)
+            pv_chunk_f32<D, DV>(buf, kb, kc, qi, h, wb.r[kc], wb.i[kc], ore, oim);
     } else {
-        pv_block_bf16<D>(buf, kb, qi, h, wb.r, wb.i, ore, oim);
+        pv_block_bf16<D, DV>(buf, kb, qi, h, wb.r, wb.i, ore, oim);
     }
 }
 
@@ -829,9 +840,9 @@ __device__ __forceinline__ void pv_block(const unsigned char *buf, int kb, int q
 // copied and landed in a phase is a function of the phase number alone, and
 // every vector-memory operation in the phase loops is such a copy, waited
 // for with exact counts.
-template <bool F32, int D, bool QKZ>
+template <bool F32, int D, int DV, bool QKZ>
 __global__ __launch_bounds__(NTHREADS, 1) void fwd_kernel(FwdArgs A) {
-    using SM = Smem<F32, D>;
+    using SM = Smem<F32, D, DV>;
     using FR = Frag<F32, D>;
     using WB = BlockW<F32>;
     constexpr int NBUF = SM::NBUF;
@@ -839,7 +850,7 @@ __global__ __launch_bounds__(NTHREADS, 1) void fwd_kernel(FwdArgs A) {
     constexpr int NDB = 2 * NDIAG;    // 32-key blocks inside the query tile
     // copies a leading wave issues per tile: its K and V chunks (wave 0 also
     // the three gate planes of the side data and the tile's product)
-    constexpr int VM_TILE = SM::KCH / NCOPY + (F32 ? SM::KCH / NCOPY : SM::VCH * D / 64 / NCOPY);
+    constexpr int VM_TILE = SM::KCH / NCOPY + SM::VINS / NCOPY;
     static_assert(VM_TILE + 4 < 64, "vmcnt range");
     extern __shared__ __align__(16) unsigned char smem[];
     uint32_t *misc = reinterpret_cast<uint32_t *>(smem + SM::misc_off);
@@ -870,7 +881,7 @@ __global__ __launch_bounds__(NTHREADS, 1) void fwd_kernel(FwdArgs A) {
     const int n_off = __builtin_amdgcn_readfirstlane(A.noff[bh * A.n_qt + qt]);
     const int n_tiles = n_off + NDIAG;
     const unsigned char *kh, *vh;
-    head_bases<F32, D>(A, bh, kh, vh);
+    head_bases<F32, D, DV>(A, kv_head(A, bh), kh, vh);
 
     if (tid == 0) {
         misc[2] = 0;
@@ -920,16 +931,16 @@ __global__ __launch_bounds__(NTHREADS, 1) void fwd_kernel(FwdArgs A) {
                         g2lds16(kt + 1024 * NCOPY * i, k_lane,
                                 buf + uint32_t((w + NCOPY * i) * 1024));
                 } else {
-                    stage_async<F32, D>(A, buf, kh, vh, t, true, w);
+                    stage_async<F32, D, DV>(A, buf, kh, vh, t, true, w);
                 }
                 const unsigned char *vt = vh + int64_t(t) * (BK * 2);
 #pragma unroll
-                for (int i = 0; i < SM::VCH * D / 64 / NCOPY; ++i)
+                for (int i = 0; i < SM::VINS / NCOPY; ++i)
                     g2lds16(vt + int64_t(16 * NCOPY * i) * A.n_pad, v_lane,
                             buf + uint32_t(SM::k_bytes + (w + NCOPY * i) * 1024));
             }
         } else {
-            stage_async<F32, D>(A, buf, kh, vh, t, false, w);
+            stage_async<F32, D, DV>(A, buf, kh, vh, t, false, w);
         }
         if (w == 0) {
             const bool off = sg < n_off;
@@ -1056,9 +1067,9 @@ __global__ __launch_bounds__(NTHREADS, 1) void fwd_kernel(FwdArgs A) {
     lds_barrier();
     atomicMax(&misc[2], qbits);
 
-    f32x16 ore[D / 32], oim[D / 32];
+    f32x16 ore[DV / 32], oim[DV / 32];
 #pragma unroll
-    for (int db = 0; db < D / 32; ++db)
+    for (int db = 0; db < DV / 32; ++db)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
             ore[db][r] = 0.f;
@@ -1111,7 +1122,7 @@ __global__ __launch_bounds__(NTHREADS, 1) void fwd_kernel(FwdArgs A) {
             if (__any(resc)) {
                 const float alpha = resc ? __builtin_amdgcn_exp2f(M - t) : 1.0f;
 #pragma unroll
-                for (int db = 0; db < D / 32; ++db)
+                for (int db = 0; db < DV / 32; ++db)
 #pragma unroll
                     for (int r = 0; r < 16; ++r) {
                         ore[db][r] *= alpha;
@@ -1143,7 +1154,7 @@ __global__ __launch_bounds__(NTHREADS, 1) void fwd_kernel(FwdArgs A) {
             wim[e] = ex * fim[e];
         }
         if constexpr (F32) {
-            pv_chunk_f32<D>(buf, kb, kc, qi, h, wre, wim, ore, oim);
+            pv_chunk_f32<D, DV>(buf, kb, kc, qi, h, wre, wim, ore, oim);
         } else {
 #pragma unroll
             for (int e = 0; e < 8; ++e) {
@@ -1257,18 +1268,18 @@ __global__ __launch_bounds__(NTHREADS, 1) void fwd_kernel(FwdArgs A) {
     constexpr int NPRE_OFF = 2;  // fragments of each kind requested early
     auto m_prefetch_off = [&](int k) __attribute__((always_inline)) {
         if constexpr (!F32)
-            mstep_prefetch<D, true, !QKZ, 0, NPRE_OFF>(block_buf(k - 1), block_kb(k - 1, true),
+            mstep_prefetch<D, DV, true, !QKZ, 0, NPRE_OFF>(block_buf(k - 1), block_kb(k - 1, true),
                                                       block_buf(k), block_kb(k, true), qi, h, pf);
     };
     auto m_step_off = [&](int k) __attribute__((always_inline)) {
         kflag = reinterpret_cast<const uint32_t *>(block_buf(k) + SM::flag_off)[k & 1];
         if constexpr (!F32) {
             if (k >= 1)
-                mstep_bf16<D, true, !QKZ, NPRE_OFF>(block_buf(k - 1), block_kb(k - 1, true),
+                mstep_bf16<D, DV, true, !QKZ, NPRE_OFF>(block_buf(k - 1), block_kb(k - 1, true),
                                                 block_buf(k), block_kb(k, true), qi, h, pf, wk.r,
                                                 wk.i, qf, ore, oim, x);
             else
-                mstep_bf16<D, false, !QKZ, 0>(block_buf(k), 0, block_buf(k),
+                mstep_bf16<D, DV, false, !QKZ, 0>(block_buf(k), 0, block_buf(k),
                                                   block_kb(k, true), qi, h, pf, wk.r, wk.i, qf, ore,
                                                   oim, x);
         } else if constexpr (!QKZ) {
@@ -1281,7 +1292,7 @@ __global__ __launch_bounds__(NTHREADS, 1) void fwd_kernel(FwdArgs A) {
                 const int kp = k - 1;
                 const bool offp = (kp >> 1) < n_off;
                 if (block_active(kp, offp))
-                    pv_block<F32, D>(block_buf(kp), block_kb(kp, offp), qi, h, wk, ore, oim);
+                    pv_block<F32, D, DV>(block_buf(kp), block_kb(kp, offp), qi, h, wk, ore, oim);
             }
         }
         if constexpr (!QKZ) {
@@ -1319,7 +1330,7 @@ __global__ __launch_bounds__(NTHREADS, 1) void fwd_kernel(FwdArgs A) {
         if (n_off > 0 && k == 2 * n_off) {
             // the last block before the query tile is in O: rotate by P_i
 #pragma unroll
-            for (int db = 0; db < D / 32; ++db)
+            for (int db = 0; db < DV / 32; ++db)
 #pragma unroll
                 for (int r = 0; r < 16; ++r) {
                     const float xr = ore[db][r], xi = oim[db][r];
@@ -1382,10 +1393,10 @@ __global__ __launch_bounds__(NTHREADS, 1) void fwd_kernel(FwdArgs A) {
     else
         f = exp2f(A.one_minus_beta * M - A.beta * log2f(zt));
     if (row_ok) {
-        float *orp = A.o_re + (bh * A.n + row) * D;
-        float *oip = A.o_im + (bh * A.n + row) * D;
+        float *orp = A.o_re + (bh * A.n + row) * DV;
+        float *oip = A.o_im + (bh * A.n + row) * DV;
 #pragma unroll
-        for (int db = 0; db < D / 32; ++db)
+        for (int db = 0; db < DV / 32; ++db)
 #pragma unroll
             for (int g4 = 0; g4 < 4; ++g4) {
                 const int d0 = 32 * db + 8 * g4 + 4 * h;
@@ -1445,11 +1456,11 @@ __global__ __launch_bounds__(NTHREADS) void logit_check_kernel(FwdArgs A) {
     typename FR::type qf[FR::count];
     load_q<F32, D>(A, bh, row, row_ok, h, qf);
     const unsigned char *kh, *vh;
-    head_bases<F32, D>(A, bh, kh, vh);
+    head_bases<F32, D, D>(A, kv_head(A, bh), kh, vh);
     bool bad = false;
     for (int64_t t = 0; t < (i0 + BQ) / BK; ++t) {
         __syncthreads();
-        stage_async<F32, D>(A, lds_addr(smem), kh, vh, int(t), true,
+        stage_async<F32, D, D>(A, lds_addr(smem), kh, vh, int(t), true,
                             __builtin_amdgcn_readfirstlane(w));
         __builtin_amdgcn_s_waitcnt(0);
         __syncthreads();
@@ -1498,9 +1509,9 @@ GatesArgs gates_args(const Layout &L, const float *u, const float *theta, double
     return G;
 }
 
-template <bool F32, int D>
+template <bool F32, int D, int DV>
 int launch_typed(const Problem &P, hipStream_t st, hipEvent_t const *marks) {
-    using SM = Smem<F32, D>;
+    using SM = Smem<F32, D, DV>;
     const Layout &L = P.L;
     unsigned char *ws = P.ws;
     uint32_t *counters = reinterpret_cast<uint32_t *>(ws + L.counters);
@@ -1509,11 +1520,12 @@ int launch_typed(const Problem &P, hipStream_t st, hipEvent_t const *marks) {
 
     if constexpr (!F32) {
         uint16_t *vt = reinterpret_cast<uint16_t *>(ws + L.vt);
+        const unsigned vblocks = (unsigned)(L.BHkv * L.n_kt);  // one per k/v head and key tile
         if (P.v_f32)
-            hipLaunchKernelGGL((vt_kernel<D, true>), dim3(BH * L.n_kt), dim3(256), 0, st, P.v, vt,
+            hipLaunchKernelGGL((vt_kernel<DV, true>), dim3(vblocks), dim3(256), 0, st, P.v, vt,
                                L.n, L.n_pad, (int)L.n_kt, P.status, counters);
         else
-            hipLaunchKernelGGL((vt_kernel<D, false>), dim3(BH * L.n_kt), dim3(256), 0, st, P.v, vt,
+            hipLaunchKernelGGL((vt_kernel<DV, false>), dim3(vblocks), dim3(256), 0, st, P.v, vt,
                                L.n, L.n_pad, (int)L.n_kt, P.status, counters);
     } else {
         hipLaunchKernelGGL(clear_status_kernel, dim3(1), dim3(64), 0, st, P.status, counters);
@@ -1559,6 +1571,8 @@ int launch_typed(const Problem &P, hipStream_t st, hipEvent_t const *marks) {
     F.n_qt = (int)L.n_qt;
     F.n_kt = (int)L.n_kt;
     F.BH = BH;
+    F.H = (int)L.H;
+    F.group = (int)(L.H / L.Hkv);
     F.c = P.c;
     F.beta = P.beta;
     F.one_minus_beta = 1.0f - P.beta;
@@ -1566,20 +1580,20 @@ int launch_typed(const Problem &P, hipStream_t st, hipEvent_t const *marks) {
     F.qk_zero = P.qk_zero ? 1 : 0;
     const size_t shm = SM::bytes;
     if (shm > 65536) {
-        (void)hipFuncSetAttribute(reinterpret_cast<const void *>(&fwd_kernel<F32, D, false>),
+        (void)hipFuncSetAttribute(reinterpret_cast<const void *>(&fwd_kernel<F32, D, DV, false>),
                             hipFuncAttributeMaxDynamicSharedMemorySize, (int)shm);
-        (void)hipFuncSetAttribute(reinterpret_cast<const void *>(&fwd_kernel<F32, D, true>),
+        (void)hipFuncSetAttribute(reinterpret_cast<const void *>(&fwd_kernel<F32, D, DV, true>),
                             hipFuncAttributeMaxDynamicSharedMemorySize, (int)shm);
         (void)hipFuncSetAttribute(reinterpret_cast<const void *>(&logit_check_kernel<F32, D>),
                             hipFuncAttributeMaxDynamicSharedMemorySize, (int)shm);
     }
     if (marks) (void)hipEventRecord(marks[1], st);
     if (P.qk_zero)
-        hipLaunchKernelGGL((fwd_kernel<F32, D, true>), dim3(BH * L.n_qt), dim3(NTHREADS), shm, st,
-                           F);
-    else
-        hipLaunchKernelGGL((fwd_kernel<F32, D, false>), dim3(BH * L.n_qt), dim3(NTHREADS), shm,
+        hipLaunchKernelGGL((fwd_kernel<F32, D, DV, true>), dim3(BH * L.n_qt), dim3(NTHREADS), shm,
                            st, F);
+    else
+        hipLaunchKernelGGL((fwd_kernel<F32, D, DV, false>), dim3(BH * L.n_qt), dim3(NTHREADS),
+                           shm, st, F);
     if (marks) (void)hipEventRecord(marks[2], st);
     if (!P.qk_zero)
         hipLaunchKernelGGL((logit_check_kernel<F32, D>), dim3(BH * L.n_qt), dim3(NTHREADS), shm,
@@ -1604,9 +1618,17 @@ int launch_forward(const Problem &P, void *stream, void *const *marks) {
     hipStream_t st = static_cast<hipStream_t>(stream);
     hipEvent_t const *ev = reinterpret_cast<hipEvent_t const *>(marks);
     const bool f32 = !P.L.bf16_path;
-    if (P.L.d == 64)
-        return f32 ? launch_typed<true, 64>(P, st, ev) : launch_typed<false, 64>(P, st, ev);
-    return f32 ? launch_typed<true, 128>(P, st, ev) : launch_typed<false, 128>(P, st, ev);
+    const int64_t d = P.L.d, dv = P.L.dv;
+    if (d == 64 && dv == 64)
+        return f32 ? launch_typed<true, 64, 64>(P, st, ev) : launch_typed<false, 64, 64>(P, st, ev);
+    if (d == 64 && dv == 128)
+        return f32 ? launch_typed<true, 64, 128>(P, st, ev)
+                   : launch_typed<false, 64, 128>(P, st, ev);
+    if (d == 128 && dv == 64)
+        return f32 ? launch_typed<true, 128, 64>(P, st, ev)
+                   : launch_typed<false, 128, 64>(P, st, ev);
+    return f32 ? launch_typed<true, 128, 128>(P, st, ev)
+               : launch_typed<false, 128, 128>(P, st, ev);
 }
 
 }  // namespace resolvent

@@ -125,6 +125,46 @@ int32_t resolvent_forward_marked(const void *q, const void *k, const float *u,
                                  hipStream_t stream, hipEvent_t *marks);
 
 /*
+ * resolvent_workspace_bytes_grouped -- device workspace for
+ * resolvent_forward_grouped (0 for an empty, invalid or unsupported
+ * problem, which resolvent_forward_grouped rejects).
+ */
+size_t resolvent_workspace_bytes_grouped(int64_t B, int64_t H, int64_t Hkv, int64_t n,
+                                         int64_t d, int64_t dv, int32_t qk_dtype,
+                                         int32_t v_dtype);
+
+/*
+ * resolvent_forward_grouped -- resolvent_forward with the page's value_dim
+ * free (section "Rust API": the readout takes V as [seq, value_dim]) and with
+ * keys and values shared by groups of heads: H query heads read Hkv k/v heads,
+ * query head h of batch entry b using k/v head h / (H / Hkv) of that entry.
+ * Each query head keeps its own gates (u, theta) and its own operator; only k
+ * and v are shared.  resolvent_forward(..., H, n, d, ...) is
+ * resolvent_forward_grouped(..., H, H, n, d, d, ...).
+ *
+ * Arguments as for resolvent_forward, except:
+ *   q           [B, H, n, d]
+ *   k           [B, Hkv, n, d]
+ *   v           [B, Hkv, n, dv]
+ *   u, theta    [B, H, n]
+ *   Hkv         k/v heads: 1 <= Hkv, H a multiple of Hkv
+ *   dv          value channels: 64 or 128 (d is 64 or 128 as well)
+ *   o_re, o_im  [B, H, n, dv]
+ *   workspace   at least resolvent_workspace_bytes_grouped(...) bytes
+ *
+ * Returns as resolvent_forward, with RESOLVENT_BAD_SHAPE also for Hkv <= 0
+ * or H not a multiple of Hkv (when n, B, H > 0), and RESOLVENT_UNSUPPORTED
+ * for another dv.
+ */
+int32_t resolvent_forward_grouped(const void *q, const void *k, const float *u,
+                                  const float *theta, const void *v, double beta, double qk,
+                                  double g, int64_t B, int64_t H, int64_t Hkv, int64_t n,
+                                  int64_t d, int64_t dv, int32_t qk_dtype, int32_t v_dtype,
+                                  float *o_re, float *o_im, void *workspace,
+                                  size_t workspace_bytes, int32_t *status_dev,
+                                  hipStream_t stream);
+
+/*
  * resolvent_counters_offset -- byte offset inside the workspace of two uint32
  * counters that a call leaves behind: [0] the number of (query tile, key tile)
  * pairs before the diagonal that the fused kernel evaluated (it stops early

@@ -16,14 +16,27 @@
 
 using namespace resolvent;
 
-static int check(int64_t B, int64_t H, int64_t n, int64_t d, int esz, bool bf16_path) {
-    const Layout L = make_layout(B, H, n, d, bf16_path);
+// Every k/v head the kernels address (bh below runs over k/v heads: the
+// query heads' kv_head()), with Hkv k/v heads and dv value channels.
+static int check(int64_t B, int64_t H, int64_t n, int64_t d, int esz, bool bf16_path,
+                 int64_t Hkv, int64_t dv) {
+    const Layout L = make_layout(B, H, n, d, bf16_path, Hkv, dv);
     const int64_t row_bytes = d * esz;
     const int kch = int(row_bytes / 16);
-    const int64_t tensor = L.BH * n * row_bytes;
-    const int64_t vt_bytes = L.BH * d * L.n_pad * 2;
+    const int64_t tensor = L.BHkv * n * row_bytes;
+    const int64_t vt_bytes = L.BHkv * dv * L.n_pad * 2;
+    const int64_t vrow_bytes = dv * esz;
+    const int64_t vtensor = L.BHkv * n * vrow_bytes;
     int bad = 0;
-    for (int64_t bh = 0; bh < L.BH; bh += (L.BH > 2 ? L.BH - 1 : 1))
+    // the query heads map onto k/v heads inside the batch entry
+    for (int64_t b = 0; b < B; ++b)
+        for (int64_t h = 0; h < H; ++h) {
+            const int64_t kv = b * L.Hkv + h / (H / L.Hkv);
+            if ((kv < 0 || kv >= L.BHkv) && bad++ < 5)
+                std::printf("query head (%lld,%lld) maps to k/v head %lld of %lld\n",
+                            (long long)b, (long long)h, (long long)kv, (long long)L.BHkv);
+        }
+    for (int64_t bh = 0; bh < L.BHkv; bh += (L.BHkv > 2 ? L.BHkv - 1 : 1))
         for (int64_t t = 0; t < L.n_kt; ++t) {
             for (int r = 0; r < BK; ++r)
                 for (int c = 0; c < kch; ++c) {
@@ -40,12 +53,21 @@ static int check(int64_t B, int64_t H, int64_t n, int64_t d, int esz, bool bf16_
                                         (long long)n, (long long)d, (long long)t, r, (long long)off);
                     }
                 }
+            if (!bf16_path)  // fp32 V rows of dv channels
+                for (int r = 0; r < BK; ++r)
+                    for (int c = 0; c < int(vrow_bytes / 16); ++c) {
+                        const int64_t off = bh * n * vrow_bytes +
+                                            int64_t(tile_row_off(n, t, r, vrow_bytes)) + 16 * c;
+                        if ((off < 0 || off + 16 > vtensor) && bad++ < 5)
+                            std::printf("v out of range: n=%lld dv=%lld t=%lld r=%d\n",
+                                        (long long)n, (long long)dv, (long long)t, r);
+                    }
             if (bf16_path)
-                for (int dd = 0; dd < d; ++dd)
+                for (int dd = 0; dd < dv; ++dd)
                     for (int c = 0; c < BK * 2 / 16; ++c) {
-                        const int64_t off = vt_src(bh, d, L.n_pad, t, dd, c);
+                        const int64_t off = vt_src(bh, dv, L.n_pad, t, dd, c);
                         const int64_t alt =
-                            bh * d * L.n_pad * 2 + int64_t(vt_row_off(L.n_pad, t, dd)) + 16 * c;
+                            bh * dv * L.n_pad * 2 + int64_t(vt_row_off(L.n_pad, t, dd)) + 16 * c;
                         if (alt != off && bad++ < 5)
                             std::printf("v^T 32-bit offset mismatch: n=%lld t=%lld d=%d\n",
                                         (long long)n, (long long)t, dd);
@@ -57,7 +79,7 @@ static int check(int64_t B, int64_t H, int64_t n, int64_t d, int esz, bool bf16_
                     }
             // the bf16 copy instructions, lane by lane (kernel helpers)
             if (bf16_path) {
-                const int64_t head_k = bh * n * row_bytes, head_vt = bh * d * L.n_pad * 2;
+                const int64_t head_k = bh * n * row_bytes, head_vt = bh * dv * L.n_pad * 2;
                 for (int j = 0; j < kch; ++j)
                     for (int lane = 0; lane < 64; ++lane) {
                         const int64_t ko = head_k + int64_t(d == 128 ? k_copy_off<16>(n, t, j, lane)
@@ -82,7 +104,7 @@ static int check(int64_t B, int64_t H, int64_t n, int64_t d, int esz, bool bf16_
                                 std::printf("k copy split mismatch: n=%lld t=%lld j=%d lane=%d\n",
                                             (long long)n, (long long)t, j, lane);
                         }
-                    for (int j = 0; j < int(d) / 8; ++j)
+                    for (int j = 0; j < int(dv) / 8; ++j)
                         for (int lane = 0; lane < 64; ++lane) {
                             const int j0 = j % NC, i = j / NC;
                             const uint32_t split = uint32_t(2 * BK * t) +
@@ -93,15 +115,19 @@ static int check(int64_t B, int64_t H, int64_t n, int64_t d, int esz, bool bf16_
                                             (long long)n, (long long)t, j, lane);
                         }
                 }
-                for (int j = 0; j < int(d) / 8; ++j)
+                for (int j = 0; j < int(dv) / 8; ++j)
                     for (int lane = 0; lane < 64; ++lane) {
                         const int64_t vo = head_vt + int64_t(vt_copy_off(L.n_pad, t, j, lane));
-                        if ((vo < head_vt || vo + 16 > head_vt + d * L.n_pad * 2) && bad++ < 5)
+                        if ((vo < head_vt || vo + 16 > head_vt + dv * L.n_pad * 2) && bad++ < 5)
                             std::printf("v^T copy out of the head: n=%lld t=%lld j=%d lane=%d\n",
                                         (long long)n, (long long)t, j, lane);
                     }
             }
-            // gate planes: S_j (planes 3..5) and a_{j+1} (planes 0..2), 4 bytes a lane
+        }
+    // gate planes of every query head: S_j (planes 3..5) and a_{j+1} (planes
+    // 0..2), 4 bytes a lane
+    for (int64_t bh = 0; bh < L.BH; bh += (L.BH > 2 ? L.BH - 1 : 1))
+        for (int64_t t = 0; t < L.n_kt; ++t)
             for (int own = 0; own < 2; ++own)
                 for (int p = own ? 0 : 3; p < (own ? 3 : 6); ++p)
                     for (int lane = 0; lane < BK; ++lane) {
@@ -113,7 +139,6 @@ static int check(int64_t B, int64_t H, int64_t n, int64_t d, int esz, bool bf16_
                                             p, (long long)n, (long long)t, lane);
                         }
                     }
-        }
     // the carried-product copies: visit s < qt*BQ/BK of query tile qt, 16 bytes
     for (int64_t bh = 0; bh < L.BH; bh += (L.BH > 2 ? L.BH - 1 : 1))
         for (int64_t qt = 0; qt < L.n_qt; ++qt)
@@ -217,8 +242,11 @@ int main(int argc, char **argv) {
     for (int a = 1; a + 3 < argc; a += 4) {
         const int64_t B = std::atoll(argv[a]), H = std::atoll(argv[a + 1]);
         const int64_t n = std::atoll(argv[a + 2]), d = std::atoll(argv[a + 3]);
-        bad += check(B, H, n, d, 2, true);   // bf16 q, k; bf16 v^T copy
-        bad += check(B, H, n, d, 4, false);  // fp32 q, k, v
+        for (int64_t dv = 64; dv <= 128; dv += 64)
+            for (int64_t Hkv : {H, int64_t(1)}) {
+                bad += check(B, H, n, d, 2, true, Hkv, dv);   // bf16 q, k; bf16 v^T copy
+                bad += check(B, H, n, d, 4, false, Hkv, dv);  // fp32 q, k, v
+            }
         ++cases;
     }
     std::printf("%d shapes, %d problems\n", cases, bad);

@@ -129,3 +129,29 @@ def test_chain_workspace_sizes():
     assert 0 < a < b  # the tile carries grow with the channels
     bq, _ = binding.resolvent_tile_shape()
     assert ws(1, 1, bq + 1, 64) > ws(1, 1, bq, 64)  # sized on n rounded up to bq
+
+
+def grouped_call(B=1, H=4, Hkv=2, n=128, d=64, dv=128, qdt=0, vdt=0, ws_bytes=None, ptr=FAKE):
+    lib = binding._load()
+    if ws_bytes is None:
+        ws_bytes = lib.resolvent_workspace_bytes_grouped(1, 4, 2, 128, 64, 128, qdt, vdt)
+    return lib.resolvent_forward_grouped(ptr, ptr, ptr, ptr, ptr, 1.0, 1.0, 1.0, B, H, Hkv, n,
+                                         d, dv, qdt, vdt, ptr, ptr, FAKE, ws_bytes, FAKE, None)
+
+
+def test_grouped_host_checks():
+    assert grouped_call(Hkv=3) == S.BAD_SHAPE  # 4 query heads cannot share 3 k/v heads
+    assert grouped_call(Hkv=0) == S.BAD_SHAPE
+    assert grouped_call(Hkv=-1) == S.BAD_SHAPE
+    assert grouped_call(dv=0) == S.BAD_SHAPE
+    assert grouped_call(dv=96) == S.UNSUPPORTED
+    assert grouped_call(dv=256) == S.UNSUPPORTED
+    assert grouped_call(n=0, ptr=None) == S.OK
+    assert grouped_call(ptr=None) == S.BAD_ARG
+    assert grouped_call(ws_bytes=64) == S.BAD_ARG
+    ws = binding.resolvent_workspace_bytes_grouped
+    assert ws(1, 4, 3, 128, 64, 64) == 0 and ws(1, 4, 2, 128, 64, 96) == 0
+    # fewer k/v heads: a smaller v^T copy; the same call as resolvent_forward at Hkv = H, dv = d
+    assert ws(2, 8, 2, 512, 128, 128) < ws(2, 8, 8, 512, 128, 128)
+    assert ws(2, 8, 8, 512, 128, 128) == binding.resolvent_workspace_bytes(2, 8, 512, 128)
+    assert ws(1, 2, 2, 256, 64, 128) > ws(1, 2, 2, 256, 64, 64)
