@@ -322,6 +322,101 @@ def bench_grouped(args):
     print(json.dumps(out), flush=True)
 
 
+def bench_decode(args):
+    """One decode step (resolvent_decode) on the headline inputs: the readout
+    of position n-1 of every head against caches of n = 8192 positions."""
+    import numpy as np
+    import torch
+
+    from gated_causal_attention_amd import binding, inputs
+
+    dev = torch.device("cuda:0")
+    sw = (1, 1, 1)
+    inp = inputs.make_config(3)
+    B, H, n, d = inp["B"], inp["H"], inp["n"], inp["d"]
+    dv = inp["v"].shape[-1]
+    t = inputs.as_torch(inp, dev)
+    q = t["q"][:, :, n - 1].contiguous()
+    o_re = torch.empty((B, H, dv), device=dev, dtype=torch.float32)
+    o_im = torch.empty_like(o_re)
+    ws = torch.empty(binding.resolvent_decode_workspace_bytes(B, H, H, n, d, dv), device=dev,
+                     dtype=torch.uint8)
+    status = torch.zeros(1, device=dev, dtype=torch.int32)
+    stream = torch.cuda.current_stream(dev)
+
+    def step():
+        binding.resolvent_decode(q, t["k"], t["u"], t["theta"], t["v"], *sw, o_re=o_re,
+                                 o_im=o_im, workspace=ws, status=status, stream=stream,
+                                 check=False)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    assert int(status.item()) == 0
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(args.steps)]
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    start.record(stream)
+    for a, b in ev:
+        a.record(stream)
+        step()
+        b.record(stream)
+    end.record(stream)
+    torch.cuda.synchronize()
+    assert int(status.item()) == 0
+    ms_per_step = start.elapsed_time(end) / args.steps
+    call_ms = float(np.mean([a.elapsed_time(b) for a, b in ev]))
+    # algorithmic HBM bytes of a step: the bf16 caches k, v and the fp32 u, theta
+    # of n positions, the query in, the complex fp32 readout out
+    per_head = n * (2 * d + 2 * dv + 8) + 2 * d + 8 * dv
+    alg = B * H * per_head
+    achieved = alg / (call_ms * 1e-3) / 1e9
+    out = {
+        "metric": "decode step (resolvent_decode): GB/s of algorithmic HBM traffic",
+        "value": alg / (ms_per_step * 1e-3) / 1e9,
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": "decode step: the readout of position n-1 of every head, "
+                               "headline inputs B=4 H=16 n=8192 d=128 dv=128, bf16 q,k,v "
+                               "~ N(0,1), u ~ U(0.95,1), theta ~ U(-0.05,0.05), switches "
+                               "(1,1,1), seed 3, query = q[:, :, n-1]",
+                   "B": B, "H": H, "n": n, "d": d, "dv": dv},
+        "decode_steps_per_s": 1e3 / ms_per_step,
+        "roofline": {"bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                     "frac": achieved / PEAK_HBM_GBS, "traffic": None,
+                     "kernel": "resolvent_decode (part and merge kernels: one call)",
+                     "bytes_per_launch": alg},
+    }
+    if not args.no_cpu_baseline:
+        import oracle
+
+        heads = [(b, h) for b in range(B) for h in range(H)]
+        t0 = time.perf_counter()
+        done = 0
+        while time.perf_counter() - t0 < 10.0 and done < 40 * len(heads):
+            b, h = heads[done % len(heads)]
+            st, _ = oracle.forward_rows(inp["q"][b, h], inp["k"][b, h], inp["u"][b, h],
+                                        inp["theta"][b, h], inp["v"][b, h], *sw,
+                                        rows=[n - 1], nthreads=1)
+            assert st == oracle.OK
+            done += 1
+        dt = time.perf_counter() - t0
+        out["cpu_baseline"] = {"value": done * per_head / dt / 1e9, "unit": "GB/s", "cores": 1,
+                               "kind": "oracle",
+                               "sample": f"{done} head decode steps (row n-1 of the same "
+                                         f"heads, cycled), fp64, one thread; {dt:.2f} s; "
+                                         f"bytes counted as on the device"}
+    print(json.dumps(out), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -329,9 +424,11 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-bytes", type=int, default=0)
-    ap.add_argument("--path", choices=("forward", "chain", "grouped"), default="forward",
+    ap.add_argument("--path", choices=("forward", "chain", "grouped", "decode"),
+                    default="forward",
                     help="forward: the head (the headline line); chain: the chain-corner "
-                         "scan; grouped: shared k/v heads and another value width")
+                         "scan; grouped: shared k/v heads and another value width; decode: "
+                         "one decode step against an n-position cache")
     ap.add_argument("--summarize-traffic", nargs=4, metavar=("FETCH", "WRITE", "COPY_FETCH",
                                                               "COPY_WRITE"))
     args = ap.parse_args()
@@ -356,6 +453,9 @@ def main():
         return
     if args.path == "grouped":
         bench_grouped(args)
+        return
+    if args.path == "decode":
+        bench_decode(args)
         return
 
     from gated_causal_attention_amd import binding, inputs

@@ -65,6 +65,13 @@ def _load():
     lib.resolvent_chain.argtypes = [vp, vp, vp, dbl, i64, i64, i64, i64, i32, vp, vp, vp,
                                     ctypes.c_size_t, vp, vp]
     lib.resolvent_chain.restype = i32
+    lib.resolvent_decode_workspace_bytes.argtypes = [i64, i64, i64, i64, i64, i64, i32, i32]
+    lib.resolvent_decode_workspace_bytes.restype = ctypes.c_size_t
+    lib.resolvent_decode.argtypes = [vp, vp, vp, vp, vp, dbl, dbl, dbl, i64, i64, i64, i64, i64,
+                                     i64, i64, i32, i32, vp, vp, vp, ctypes.c_size_t, vp, vp]
+    lib.resolvent_decode.restype = i32
+    lib.resolvent_chain_step.argtypes = [vp, vp, vp, vp, vp, dbl, i64, i64, i64, i32, vp, vp]
+    lib.resolvent_chain_step.restype = i32
     lib.resolvent_status_str.argtypes = [i32]
     lib.resolvent_status_str.restype = ctypes.c_char_p
     _lib = lib
@@ -244,6 +251,92 @@ def resolvent_chain(u, theta, v, g, *, o_re=None, o_im=None, workspace=None, sta
         if st != Status.OK:
             raise ResolventError(st)
     return o_re, o_im
+
+
+def _stream_handle(stream, dev):
+    import torch
+
+    if stream is None:
+        stream = torch.cuda.current_stream(dev)
+    return stream, (stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream))
+
+
+def _finish(rc, stream, dev, status, check):
+    """Raise on a refused call; with ``check``, wait and raise on a refused
+    device status."""
+    import torch
+
+    if rc != Status.OK:
+        raise ResolventError(rc)
+    if check:
+        if hasattr(stream, "synchronize"):
+            stream.synchronize()
+        else:
+            torch.cuda.synchronize(dev)
+        st = int(status.item())
+        if st != Status.OK:
+            raise ResolventError(st)
+
+
+def resolvent_decode_workspace_bytes(B, H, Hkv, n, d, dv, qk_dtype=BF16, v_dtype=BF16) -> int:
+    return int(_load().resolvent_decode_workspace_bytes(B, H, Hkv, n, d, dv, qk_dtype, v_dtype))
+
+
+def resolvent_decode(q, k, u, theta, v, beta, qk, g, *, n=None, o_re=None, o_im=None,
+                     workspace=None, status=None, stream=None, check=True):
+    """One decode step: the readout of position n-1 for the query q [B, H, d]
+    against the caches k [B, Hkv, cap, d], v [B, Hkv, cap, dv] and the gate
+    inputs u, theta [B, H, cap], of which positions 0..n-1 are read (n
+    defaults to cap).  Returns (o_re, o_im), each [B, H, dv] fp32."""
+    import torch
+
+    B, H, d = q.shape
+    Hkv, cap, dv = k.shape[1], k.shape[2], v.shape[-1]
+    n = cap if n is None else int(n)
+    for t in (q, k, v, u, theta):
+        if not t.is_contiguous():
+            raise ValueError("inputs must be contiguous")
+    dev = q.device
+    qk_dt, v_dt = _dtype_code(q), _dtype_code(v)
+    if o_re is None:
+        o_re = torch.empty((B, H, dv), device=dev, dtype=torch.float32)
+    if o_im is None:
+        o_im = torch.empty((B, H, dv), device=dev, dtype=torch.float32)
+    ws_bytes = resolvent_decode_workspace_bytes(B, H, Hkv, n, d, dv, qk_dt, v_dt)
+    if workspace is None:
+        workspace = torch.empty(max(ws_bytes, 1), device=dev, dtype=torch.uint8)
+    if status is None:
+        status = torch.zeros(1, device=dev, dtype=torch.int32)
+    stream, handle = _stream_handle(stream, dev)
+    rc = _load().resolvent_decode(
+        q.data_ptr(), k.data_ptr(), u.data_ptr(), theta.data_ptr(), v.data_ptr(), float(beta),
+        float(qk), float(g), B, H, Hkv, n, cap, d, dv, qk_dt, v_dt, o_re.data_ptr(),
+        o_im.data_ptr(),
+        workspace.data_ptr(), workspace.numel() * workspace.element_size(), status.data_ptr(),
+        handle)
+    _finish(rc, stream, dev, status, check and n > 0 and B > 0 and H > 0)
+    return o_re, o_im
+
+
+def resolvent_chain_step(y_re, y_im, u, theta, v, g, *, status=None, stream=None, check=True):
+    """One step of the chain corner, in place: y <- a y + v with
+    a = gate(u, theta, g); y_re, y_im [B, H, dv] fp32, u, theta [B, H] fp32,
+    v [B, H, dv] bf16 or fp32.  Returns (y_re, y_im)."""
+    import torch
+
+    B, H, dv = v.shape
+    for t in (y_re, y_im, u, theta, v):
+        if not t.is_contiguous():
+            raise ValueError("inputs must be contiguous")
+    dev = v.device
+    if status is None:
+        status = torch.zeros(1, device=dev, dtype=torch.int32)
+    stream, handle = _stream_handle(stream, dev)
+    rc = _load().resolvent_chain_step(y_re.data_ptr(), y_im.data_ptr(), u.data_ptr(),
+                                      theta.data_ptr(), v.data_ptr(), float(g), B, H, dv,
+                                      _dtype_code(v), status.data_ptr(), handle)
+    _finish(rc, stream, dev, status, check and B > 0 and H > 0 and dv > 0)
+    return y_re, y_im
 
 
 def forward(q, k, u, theta, v, beta, qk, g, **kw):

@@ -116,6 +116,43 @@ inline ChainLayout make_chain_layout(int64_t B, int64_t H, int64_t n, int64_t dv
     return C;
 }
 
+// Workspace of a decode step (resolvent_decode).  Positions are grouped in
+// chunks of DEC_CT key tiles (DEC_CT BK = 256 positions): per chunk its gate
+// product P, f64 (double [3][BH][n_ch]: re, im, modulus), the merge's scale of
+// the chunk, C 2^(M_c - M) with C the gates from the chunk's end to the newest
+// position (float4 [BH][n_ch]: re, im, modulus, 0), and one partial
+// (M, z, refused, 0, O_re[dv], O_im[dv]) relative to the chunk's end (float
+// [BH][n_ch][4 + 2 dv]; the header is padded so that O starts on 16 bytes).
+constexpr int DEC_CT = 4;
+constexpr int64_t DEC_CHUNK = DEC_CT * BK;
+constexpr int64_t dec_part_floats(int64_t dv) { return 4 + 2 * dv; }
+struct DecodeLayout {
+    int64_t BH = 0, H = 0, Hkv = 0, n = 0, d = 0, dv = 0, n_ch = 0;
+    size_t prod = 0, scale = 0, part = 0, total = 0;
+};
+
+inline DecodeLayout make_decode_layout(int64_t B, int64_t H, int64_t Hkv, int64_t n, int64_t d,
+                                       int64_t dv) {
+    DecodeLayout D;
+    D.BH = B * H;
+    D.H = H;
+    D.Hkv = Hkv;
+    D.n = n;
+    D.d = d;
+    D.dv = dv;
+    D.n_ch = (n + DEC_CHUNK - 1) / DEC_CHUNK;
+    const size_t per = 3 * sizeof(double) * size_t(D.BH) * size_t(D.n_ch);
+    size_t off = 0;
+    D.prod = off;
+    off = align_up(off + per, 256);
+    D.scale = off;
+    off = align_up(off + 16 * size_t(D.BH) * size_t(D.n_ch), 256);
+    D.part = off;
+    off = align_up(off + 4 * size_t(D.BH) * size_t(D.n_ch) * size_t(dec_part_floats(dv)), 256);
+    D.total = off;
+    return D;
+}
+
 // Source byte offsets of the direct global->LDS tile copies, relative to the
 // start of the tensor (q/k/v, or the v^T region for the bf16 path).  Row `r`
 // of key tile `t` is key t*BK + r, clamped into [0, n-1] so that a tile
@@ -236,9 +273,10 @@ struct Problem {
 };
 
 // Status := OK, then the gates and their in-tile scans of make_layout into
-// the workspace (resolvent_kernels.hip).  Returns a hipError_t.
+// the workspace (resolvent_kernels.hip).  u, theta hold ldu positions per head
+// (0: L.n).  Returns a hipError_t.
 int launch_gates(const Layout &L, const float *u, const float *theta, double g,
-                 unsigned char *ws, int32_t *status, void *stream);
+                 unsigned char *ws, int32_t *status, void *stream, int64_t ldu = 0);
 
 // The chain-corner scan (chain_kernels.hip): the gates, then the three scan
 // kernels.  v is [BH][n][dv] bf16 (v_f32 false) or float32.  Returns a
@@ -246,6 +284,18 @@ int launch_gates(const Layout &L, const float *u, const float *theta, double g,
 int launch_chain(const ChainLayout &C, const float *u, const float *theta, const void *v,
                  bool v_f32, double g, float *o_re, float *o_im, unsigned char *ws,
                  int32_t *status, void *stream);
+
+// One decode step (decode_kernels.hip): the chunk partials (with their
+// gates) and their merge.  c is the logit scale qk log2(e)/sqrt(d).
+// Returns a hipError_t.
+int launch_decode(const DecodeLayout &DL, const void *q, const void *k, const float *u,
+                  const float *theta, const void *v, int64_t cap, bool qk_f32, bool v_f32,
+                  double g, float c, float beta, int beta_mode, bool qk_zero, float *o_re,
+                  float *o_im, unsigned char *ws, int32_t *status, void *stream);
+// One step of the gated chain per (head, channel), in place (decode_kernels.hip).
+int launch_chain_step(float *y_re, float *y_im, const float *u, const float *theta,
+                      const void *v, bool v_f32, double g, int64_t BH, int64_t dv,
+                      int32_t *status, void *stream);
 
 // Kernel launcher (resolvent_kernels.hip).  marks, when not null, are four
 // HIP events recorded on the stream before the first kernel, before the fused

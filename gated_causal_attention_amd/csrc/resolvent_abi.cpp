@@ -178,6 +178,64 @@ int32_t resolvent_chain(const float *u, const float *theta, const void *v, doubl
     return err == 0 ? RESOLVENT_OK : RESOLVENT_DEVICE_ERROR;
 }
 
+size_t resolvent_decode_workspace_bytes(int64_t B, int64_t H, int64_t Hkv, int64_t n, int64_t d,
+                                        int64_t dv, int32_t qk_dtype, int32_t v_dtype) {
+    if (B <= 0 || H <= 0 || Hkv <= 0 || n <= 0 || d <= 0 || dv <= 0 || H % Hkv != 0) return 0;
+    if (!supported(d, qk_dtype, v_dtype) || !supported_dv(dv) || !within_limits(B, H, n))
+        return 0;
+    return make_decode_layout(B, H, Hkv, n, d, dv).total;
+}
+
+int32_t resolvent_decode(const void *q, const void *k, const float *u, const float *theta,
+                         const void *v, double beta, double qk, double g, int64_t B, int64_t H,
+                         int64_t Hkv, int64_t n, int64_t cap, int64_t d, int64_t dv,
+                         int32_t qk_dtype, int32_t v_dtype, float *o_re, float *o_im,
+                         void *workspace, size_t workspace_bytes, int32_t *status_dev,
+                         hipStream_t stream) {
+    if (B < 0 || H < 0 || Hkv < 0 || n < 0 || cap < n || d < 0 || dv < 0)
+        return RESOLVENT_BAD_SHAPE;
+    if (B == 0 || H == 0 || n == 0) return RESOLVENT_OK;  // no position, no readout
+    if (d == 0 || dv == 0 || Hkv == 0 || H % Hkv != 0) return RESOLVENT_BAD_SHAPE;
+    if (!std::isfinite(beta) || !std::isfinite(qk) || !std::isfinite(g))
+        return RESOLVENT_NONFINITE;
+    if (!supported(d, qk_dtype, v_dtype) || !supported_dv(dv) || !within_limits(B, H, n) ||
+        !within_limits(B, H, cap))
+        return RESOLVENT_UNSUPPORTED;
+    if (!q || !k || !u || !theta || !v || !o_re || !o_im || !status_dev || !workspace)
+        return RESOLVENT_BAD_ARG;
+    if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(o_re, 4) ||
+        !aligned(o_im, 4) || !aligned(u, 4) || !aligned(theta, 4) || !aligned(status_dev, 4) ||
+        !aligned(workspace, 256))
+        return RESOLVENT_BAD_ARG;
+    const DecodeLayout DL = make_decode_layout(B, H, Hkv, n, d, dv);
+    if (workspace_bytes < DL.total) return RESOLVENT_BAD_ARG;
+    const double c = qk * 1.4426950408889634074 / std::sqrt((double)d);
+    if (qk != 0.0 && !(std::fabs(c) <= (double)FLT_MAX)) return RESOLVENT_NONFINITE;
+    const int err = launch_decode(DL, q, k, u, theta, v, cap, qk_dtype == RESOLVENT_F32,
+                                  v_dtype == RESOLVENT_F32, g, (float)c, (float)beta,
+                                  beta == 0.0 ? 0 : (beta == 1.0 ? 1 : 2), qk == 0.0, o_re, o_im,
+                                  static_cast<unsigned char *>(workspace), status_dev, stream);
+    return err == 0 ? RESOLVENT_OK : RESOLVENT_DEVICE_ERROR;
+}
+
+int32_t resolvent_chain_step(float *y_re, float *y_im, const float *u, const float *theta,
+                             const void *v, double g, int64_t B, int64_t H, int64_t dv,
+                             int32_t v_dtype, int32_t *status_dev, hipStream_t stream) {
+    if (B < 0 || H < 0 || dv < 0) return RESOLVENT_BAD_SHAPE;
+    if (B == 0 || H == 0 || dv == 0) return RESOLVENT_OK;
+    if (!std::isfinite(g)) return RESOLVENT_NONFINITE;
+    if ((v_dtype != RESOLVENT_BF16 && v_dtype != RESOLVENT_F32) || B * H > (int64_t(1) << 24) ||
+        dv > 4096)
+        return RESOLVENT_UNSUPPORTED;
+    if (!y_re || !y_im || !u || !theta || !v || !status_dev) return RESOLVENT_BAD_ARG;
+    if (!aligned(y_re, 4) || !aligned(y_im, 4) || !aligned(u, 4) || !aligned(theta, 4) ||
+        !aligned(v, v_dtype == RESOLVENT_F32 ? 4 : 2) || !aligned(status_dev, 4))
+        return RESOLVENT_BAD_ARG;
+    const int err = launch_chain_step(y_re, y_im, u, theta, v, v_dtype == RESOLVENT_F32, g, B * H,
+                                      dv, status_dev, stream);
+    return err == 0 ? RESOLVENT_OK : RESOLVENT_DEVICE_ERROR;
+}
+
 const char *resolvent_status_str(int32_t status) {
     switch (status) {
         case RESOLVENT_OK: return "ok";

@@ -149,6 +149,7 @@ struct GatesArgs {
     const float *u, *theta;
     double g;
     int64_t n, n_pad;
+    int64_t ldu;  // positions between heads in u, theta (>= n)
     int n_qt, n_kt;
     float *a_re, *a_im, *a_m, *s_re, *s_im, *s_m, *p_re, *p_im, *p_m;
     double *t_re, *t_im, *t_m;
@@ -175,7 +176,7 @@ __global__ __launch_bounds__(64) void gates_kernel(GatesArgs A) {
     for (int e = 0; e < PPL; ++e) {
         const int64_t p = p0 + e;
         if (p < A.n) {
-            const float uu = A.u[bh * A.n + p], tt = A.theta[bh * A.n + p];
+            const float uu = A.u[bh * A.ldu + p], tt = A.theta[bh * A.ldu + p];
             if (!isfinite(uu) || !isfinite(tt)) bad = true;
             double l = (1.0 - A.g) * 1.0 + A.g * (double)uu;
             l = l < 0.0 ? 0.0 : (l > 1.0 ? 1.0 : l);
@@ -1491,6 +1492,7 @@ GatesArgs gates_args(const Layout &L, const float *u, const float *theta, double
     G.g = g;
     G.n = L.n;
     G.n_pad = L.n_pad;
+    G.ldu = L.n;
     G.n_qt = (int)L.n_qt;
     G.n_kt = (int)L.n_kt;
     G.a_re = fptr(0);
@@ -1605,11 +1607,12 @@ int launch_typed(const Problem &P, hipStream_t st, hipEvent_t const *marks) {
 }  // namespace
 
 int launch_gates(const Layout &L, const float *u, const float *theta, double g,
-                 unsigned char *ws, int32_t *status, void *stream) {
+                 unsigned char *ws, int32_t *status, void *stream, int64_t ldu) {
     hipStream_t st = static_cast<hipStream_t>(stream);
     uint32_t *counters = reinterpret_cast<uint32_t *>(ws + L.counters);
     hipLaunchKernelGGL(clear_status_kernel, dim3(1), dim3(64), 0, st, status, counters);
-    const GatesArgs G = gates_args(L, u, theta, g, ws, status);
+    GatesArgs G = gates_args(L, u, theta, g, ws, status);
+    if (ldu > 0) G.ldu = ldu;
     hipLaunchKernelGGL(gates_kernel, dim3(L.BH * L.n_qt), dim3(64), 0, st, G);
     return (int)hipGetLastError();
 }

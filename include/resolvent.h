@@ -229,6 +229,77 @@ int32_t resolvent_chain(const float *u, const float *theta, const void *v, doubl
                         int32_t *status_dev, hipStream_t stream);
 
 /*
+ * resolvent_decode_workspace_bytes -- device workspace for resolvent_decode
+ * (0 for an empty, invalid or unsupported problem).
+ */
+size_t resolvent_decode_workspace_bytes(int64_t B, int64_t H, int64_t Hkv, int64_t n, int64_t d,
+                                        int64_t dv, int32_t qk_dtype, int32_t v_dtype);
+
+/*
+ * resolvent_decode -- one decode step: the readout of the newest position
+ * i = n-1 of every query head (section "Object" of the "Resolvent Operator"
+ * page, its last row; the decode shape of decodeGQA on the Op Specs page:
+ * query head h of a batch entry reads k/v head h / (H / Hkv)), for a new
+ * query against the cached keys and values of positions 0..n-1, the new
+ * position's key and value included.  O(n (d + dv)) per head: the gates and
+ * their products are formed from u, theta afresh, the keys are split over
+ * workgroups of 4 key tiles whose partial sums are merged with the same
+ * max shift as the forward pass.  Equal, up to rounding, to row n-1 of
+ * resolvent_forward_grouped on the same inputs; the weights stay float32
+ * (they are not rounded to bf16 as in the forward's bf16 path).
+ *
+ * Arguments (device pointers; row-major, each head's positions cap apart, so
+ * that a cache allocated for cap positions and filled to n is passed as is):
+ *   q           [B, H, d] the newest position's query (qk_dtype)
+ *   k           [B, Hkv, cap, d] keys; positions 0..n-1 are read (qk_dtype)
+ *   u, theta    [B, H, cap] float32 gate inputs, per query head; positions
+ *               0..n-1 are read
+ *   v           [B, Hkv, cap, dv] values (v_dtype); positions 0..n-1 are read
+ *   beta,qk,g   the switches (f64)
+ *   Hkv         k/v heads, dividing H
+ *   n, cap      positions in the cache (the newest is n-1) and allocated
+ *               positions per head, cap >= n
+ *   d, dv       64 or 128 each
+ *   o_re, o_im  [B, H, dv] float32 outputs
+ *   workspace   at least resolvent_decode_workspace_bytes(...) bytes,
+ *               256-byte aligned
+ *   status_dev, stream  as for resolvent_forward
+ * q, k and v are 16-byte aligned; u, theta, o_re, o_im and status_dev 4-byte.
+ *
+ * Returns, before anything is enqueued, the codes of resolvent_forward_grouped
+ * for the same conditions, RESOLVENT_BAD_SHAPE also for cap < n, (RESOLVENT_OK
+ * with nothing enqueued when n, B or H is 0).  On the device the status word becomes RESOLVENT_NONFINITE for a
+ * non-finite q, k (any position), u or theta, an overflowing g*theta_k or a
+ * float32 logit qk*s_ij (j <= n-1) that overflows; the outputs are then
+ * unspecified.
+ */
+int32_t resolvent_decode(const void *q, const void *k, const float *u, const float *theta,
+                         const void *v, double beta, double qk, double g, int64_t B, int64_t H,
+                         int64_t Hkv, int64_t n, int64_t cap, int64_t d, int64_t dv,
+                         int32_t qk_dtype, int32_t v_dtype, float *o_re, float *o_im,
+                         void *workspace, size_t workspace_bytes, int32_t *status_dev,
+                         hipStream_t stream);
+
+/*
+ * resolvent_chain_step -- one decode step of the chain corner (switches
+ * (0, 0, g); section "The path-product corner is a resolvent"): the state
+ * y = O_{i-1} [B, H, dv] (complex, planar float32, in place) becomes
+ * O_i = a_i y + V_i, with a_i = gate(blend(u_i, theta_i, g)) from u, theta
+ * [B, H] float32 and V_i [B, H, dv] (v_dtype).  O(1) per head and channel;
+ * starting from y = 0 it reproduces resolvent_chain position by position.
+ * Returns RESOLVENT_BAD_SHAPE for a negative size, RESOLVENT_OK with nothing
+ * enqueued when B, H or dv is 0, RESOLVENT_NONFINITE for a non-finite g,
+ * RESOLVENT_UNSUPPORTED for another dtype, dv > 4096 or B H > 2^24,
+ * RESOLVENT_BAD_ARG for a null or misaligned pointer; on the device the status
+ * word becomes RESOLVENT_NONFINITE for a non-finite u, theta or g*theta (the
+ * state of that head is then left as it was).  The caller sets status_dev to
+ * RESOLVENT_OK beforehand: this call never clears it.
+ */
+int32_t resolvent_chain_step(float *y_re, float *y_im, const float *u, const float *theta,
+                             const void *v, double g, int64_t B, int64_t H, int64_t dv,
+                             int32_t v_dtype, int32_t *status_dev, hipStream_t stream);
+
+/*
  * resolvent_status_str -- a static, human-readable name of a status code.
  */
 const char *resolvent_status_str(int32_t status);

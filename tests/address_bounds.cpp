@@ -8,6 +8,7 @@
 // chunk inside the tensor, each (row, chunk) of a tile is copied once, into
 // the LDS slot where the matrix-operand reads look for it, and a 16-lane
 // group of an operand read touches 16 different bank groups.
+#include <algorithm>
 #include <cstdio>
 #include <cstdlib>
 #include <vector>
@@ -234,6 +235,93 @@ static int check_v_reads(int d) {
     return bad;
 }
 
+// The decode step's reads and writes (decode_part_kernel,
+// decode_merge_kernel), walked lane by lane: every 16-byte load of q, k and v
+// lies inside its tensor, every key row 0..n-1 of a query head's k/v head is
+// read whole by the chunks of that head, every gate 0..n-1 is read once, and
+// the chunk product, scale and partial indexes stay inside their workspace
+// regions.  esz_q / esz_v: element bytes of q,k / v; cap: positions per head.
+static int check_decode(int64_t B, int64_t H, int64_t Hkv, int64_t n, int64_t cap, int64_t d,
+                        int64_t dv, int esz_q, int esz_v) {
+    const DecodeLayout DL = make_decode_layout(B, H, Hkv, n, d, dv);
+    const int64_t BH = DL.BH, BHkv = B * Hkv, n_ch = DL.n_ch;
+    const int ke = 16 / esz_q, kl = int(d) / ke, kr_n = 64 / kl;
+    const int ve = 16 / esz_v, vl = int(dv) / ve, vr_n = 64 / vl;
+    const int64_t kbytes = BHkv * cap * d * esz_q, vbytes = BHkv * cap * dv * esz_v;
+    const int64_t pf = dec_part_floats(dv), i = n - 1;
+    const size_t per = 3 * sizeof(double) * size_t(BH) * size_t(n_ch);
+    int bad = 0;
+    auto fail = [&](const char *what, int64_t bh, int64_t x) {
+        if (bad++ < 10)
+            std::printf("decode B=%lld H=%lld Hkv=%lld n=%lld d=%lld dv=%lld: %s (bh %lld, %lld)\n",
+                        (long long)B, (long long)H, (long long)Hkv, (long long)n, (long long)d,
+                        (long long)dv, what, (long long)bh, (long long)x);
+    };
+    if (n_ch * DEC_CHUNK < n || (n_ch - 1) * DEC_CHUNK >= n) fail("chunk count", 0, n_ch);
+    if (DL.prod + per > DL.scale || DL.scale + size_t(16 * BH * n_ch) > DL.part)
+        fail("product/scale regions", 0, 0);
+    if (DL.part + size_t(4 * BH * n_ch * pf) > DL.total) fail("partials region", 0, 0);
+    if ((DL.part % 16) || (pf % 4)) fail("partials not 16-byte aligned", 0, 0);
+    const int seg = int((n_ch + 255) / 256);
+    std::vector<int> cseen(size_t(n_ch), 0);
+    for (int t = 0; t < 256; ++t) {  // decode_merge_kernel's segments cover every chunk once
+        const int64_t c0 = std::min<int64_t>(int64_t(t) * seg, n_ch), c1 = std::min<int64_t>(c0 + seg, n_ch);
+        for (int64_t c = c0; c < c1; ++c) cseen[size_t(c)] += 1;
+    }
+    for (int64_t c = 0; c < n_ch; ++c)
+        if (cseen[size_t(c)] != 1) fail("merge segment", 0, c);
+    for (int64_t bh = 0; bh < BH; ++bh) {
+        const int64_t kvh = (bh / H) * Hkv + (bh % H) / (H / Hkv);
+        if (kvh < 0 || kvh >= BHkv) fail("k/v head", bh, kvh);
+        std::vector<int> kseen(size_t(n) * (d * esz_q / 16), 0),
+            vseen(size_t(n) * (dv * esz_v / 16), 0), useen(size_t(n), 0);
+        for (int64_t ch = 0; ch < n_ch; ++ch) {
+            if (bh * n_ch + ch >= BH * n_ch) fail("chunk index", bh, ch);
+            for (int lane = 0; lane < 64; ++lane) {
+                const int64_t qoff = (bh * d + (lane % kl) * ke) * esz_q;
+                if (qoff < 0 || qoff + 16 > BH * d * esz_q) fail("q load", bh, lane);
+                const int64_t po = (bh * n_ch + ch) * pf;
+                if (lane < vl && po + 4 + dv + (lane % vl) * ve + ve > BH * n_ch * pf)
+                    fail("partial write", bh, lane);
+                // the merge reads chunk ch's partial with CPL channels a lane
+                const int cpl = int(dv / 64);
+                if (po + 4 + dv + lane * cpl + cpl > BH * n_ch * pf) fail("merge read", bh, lane);
+            }
+            for (int tt = DEC_CT - 1; tt >= 0; --tt) {
+                const int64_t t0 = ch * DEC_CHUNK + tt * BK;
+                if (t0 > i) continue;
+                const int cnt = int(i - t0 + 1 < BK ? i - t0 + 1 : BK);
+                for (int lane = 0; lane < 64; ++lane) {
+                    if (t0 + lane < n) {
+                        if (bh * cap + t0 + lane >= BH * cap) fail("u read (part)", bh, lane);
+                        useen[size_t(t0 + lane)] += 1;
+                    }
+                    for (int x = 0; x < BK / kr_n; ++x) {
+                        const int r = x * kr_n + lane / kl, row = r < cnt ? r : cnt - 1;
+                        const int64_t off = (kvh * cap + t0 + row) * d * esz_q + (lane % kl) * ke * esz_q;
+                        if (r >= BK) fail("logit slot", bh, r);
+                        if (off < 0 || off + 16 > kbytes) fail("k load", bh, off);
+                        else kseen[size_t((t0 + row) * (d * esz_q / 16) + lane % kl)] = 1;
+                    }
+                    for (int x = 0; x < BK / vr_n; ++x) {
+                        const int r = x * vr_n + lane / vl, row = r < cnt ? r : cnt - 1;
+                        const int64_t off = (kvh * cap + t0 + row) * dv * esz_v + (lane % vl) * ve * esz_v;
+                        if (off < 0 || off + 16 > vbytes) fail("v load", bh, off);
+                        else vseen[size_t((t0 + row) * (dv * esz_v / 16) + lane % vl)] = 1;
+                    }
+                }
+            }
+        }
+        for (size_t c = 0; c < kseen.size(); ++c)
+            if (!kseen[c]) fail("k chunk never read", bh, int64_t(c));
+        for (size_t c = 0; c < vseen.size(); ++c)
+            if (!vseen[c]) fail("v chunk never read", bh, int64_t(c));
+        for (size_t c = 0; c < useen.size(); ++c)  // every gate checked exactly once
+            if (useen[c] != 1) fail("position's gate not checked once", bh, int64_t(c));
+    }
+    return bad;
+}
+
 int main(int argc, char **argv) {
     int bad = check_tile_layout<16>("K d=128") + check_tile_layout<8>("K d=64 / v^T") +
               check_operand_reads<16>() + check_operand_reads<8>() + check_v_reads(64) +
@@ -246,6 +334,11 @@ int main(int argc, char **argv) {
             for (int64_t Hkv : {H, int64_t(1)}) {
                 bad += check(B, H, n, d, 2, true, Hkv, dv);   // bf16 q, k; bf16 v^T copy
                 bad += check(B, H, n, d, 4, false, Hkv, dv);  // fp32 q, k, v
+                if (H % Hkv == 0 && n <= 40000) {
+                    bad += check_decode(B, H, Hkv, n, n, d, dv, 2, 2);
+                    bad += check_decode(B, H, Hkv, n, n + 37, d, dv, 2, 4);
+                    bad += check_decode(B, H, Hkv, n, n, d, dv, 4, 4);
+                }
             }
         ++cases;
     }

@@ -155,3 +155,62 @@ def test_grouped_host_checks():
     assert ws(2, 8, 2, 512, 128, 128) < ws(2, 8, 8, 512, 128, 128)
     assert ws(2, 8, 8, 512, 128, 128) == binding.resolvent_workspace_bytes(2, 8, 512, 128)
     assert ws(1, 2, 2, 256, 64, 128) > ws(1, 2, 2, 256, 64, 64)
+
+
+def decode_call(B=1, H=4, Hkv=2, n=130, cap=None, d=64, dv=128, beta=1.0, qk=1.0, g=1.0, qdt=0,
+                vdt=0, ws_bytes=None, ptr=FAKE, ws=FAKE):
+    lib = binding._load()
+    if ws_bytes is None:
+        ws_bytes = lib.resolvent_decode_workspace_bytes(1, 4, 2, 130, 64, 128, qdt, vdt)
+    return lib.resolvent_decode(ptr, ptr, ptr, ptr, ptr, beta, qk, g, B, H, Hkv, n,
+                                n if cap is None else cap, d, dv, qdt, vdt, ptr, ptr, ws,
+                                ws_bytes, FAKE, None)
+
+
+def test_decode_host_checks():
+    assert decode_call(B=-1) == S.BAD_SHAPE
+    assert decode_call(n=-1) == S.BAD_SHAPE
+    assert decode_call(n=0, ptr=None) == S.OK  # no position, no readout
+    assert decode_call(Hkv=3) == S.BAD_SHAPE
+    assert decode_call(Hkv=0) == S.BAD_SHAPE
+    assert decode_call(cap=129) == S.BAD_SHAPE  # the cache holds fewer positions than n
+    assert decode_call(dv=0) == S.BAD_SHAPE
+    for bad in (float("nan"), float("inf")):
+        assert decode_call(beta=bad) == S.NONFINITE
+        assert decode_call(qk=bad) == S.NONFINITE
+        assert decode_call(g=bad) == S.NONFINITE
+    assert decode_call(qk=1e308) == S.NONFINITE  # qk log2(e)/sqrt(d) beyond float32
+    assert decode_call(d=96) == S.UNSUPPORTED
+    assert decode_call(dv=256) == S.UNSUPPORTED
+    assert decode_call(qdt=1, vdt=0) == S.UNSUPPORTED  # fp32 q,k with bf16 v
+    assert decode_call(ptr=None) == S.BAD_ARG
+    assert decode_call(ptr=FAKE + 8) == S.BAD_ARG  # q, k, v are 16-byte aligned
+    assert decode_call(ws=FAKE + 16) == S.BAD_ARG
+    assert decode_call(ws_bytes=64) == S.BAD_ARG
+
+
+def test_decode_workspace_sizes():
+    ws = binding.resolvent_decode_workspace_bytes
+    assert ws(1, 4, 3, 128, 64, 64) == 0 and ws(1, 4, 2, 128, 64, 96) == 0
+    assert ws(0, 4, 2, 128, 64, 64) == 0
+    assert 0 < ws(1, 4, 2, 128, 64, 64) < ws(1, 4, 2, 128, 64, 128)  # partials grow with dv
+    bq, _ = binding.resolvent_tile_shape()
+    assert ws(1, 1, 1, bq + 1, 64, 64) > ws(1, 1, 1, bq, 64, 64)
+
+
+def chain_step_call(B=2, H=3, dv=64, g=1.0, vdt=0, ptr=FAKE):
+    lib = binding._load()
+    return lib.resolvent_chain_step(ptr, ptr, ptr, ptr, ptr, g, B, H, dv, vdt, FAKE, None)
+
+
+def test_chain_step_host_checks():
+    assert chain_step_call(B=-1) == S.BAD_SHAPE
+    assert chain_step_call(dv=-1) == S.BAD_SHAPE
+    assert chain_step_call(dv=0, ptr=None) == S.OK
+    assert chain_step_call(H=0, ptr=None) == S.OK
+    for bad in (float("nan"), float("-inf")):
+        assert chain_step_call(g=bad) == S.NONFINITE
+    assert chain_step_call(vdt=7) == S.UNSUPPORTED
+    assert chain_step_call(dv=8192) == S.UNSUPPORTED
+    assert chain_step_call(ptr=None) == S.BAD_ARG
+    assert chain_step_call(ptr=FAKE + 1) == S.BAD_ARG
