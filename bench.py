@@ -417,6 +417,100 @@ def bench_decode(args):
     print(json.dumps(out), flush=True)
 
 
+def bench_operator(args):
+    """The materialising exports at a small-n workload: resolvent_operator
+    writing W [B,H,n,n] (float32) and resolvent_path_product writing G (f64)
+    for the same heads' gates."""
+    import numpy as np
+    import torch
+
+    from gated_causal_attention_amd import binding, inputs
+
+    dev = torch.device("cuda:0")
+    sw = (1, 1, 1)
+    B, H, n, d = 1, 16, 2048, 128
+    inp = inputs.draw(B, H, n, d, 11, u_range=(0.95, 1.0), theta_range=(-0.05, 0.05))
+    t = inputs.as_torch(inp, dev)
+    w_re = torch.empty((B, H, n, n), device=dev, dtype=torch.float32)
+    w_im = torch.empty_like(w_re)
+    ws = torch.empty(binding.resolvent_operator_workspace_bytes(B, H, n, d), device=dev,
+                     dtype=torch.uint8)
+    status = torch.zeros(1, device=dev, dtype=torch.int32)
+    stream = torch.cuda.current_stream(dev)
+    import oracle
+
+    a = np.stack([oracle.gates(inp["u"][0, h], inp["theta"][0, h], 1.0)[1] for h in range(H)])
+    a_re = torch.from_numpy(np.ascontiguousarray(a.real)).to(dev)
+    a_im = torch.from_numpy(np.ascontiguousarray(a.imag)).to(dev)
+    g_re = torch.empty((H, n, n), device=dev, dtype=torch.float64)
+    g_im = torch.empty_like(g_re)
+
+    def timed(fn):
+        for _ in range(args.warmup):
+            fn()
+        torch.cuda.synchronize()
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+              for _ in range(args.steps)]
+        start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        start.record(stream)
+        for x, y in ev:
+            x.record(stream)
+            fn()
+            y.record(stream)
+        end.record(stream)
+        torch.cuda.synchronize()
+        return (start.elapsed_time(end) / args.steps,
+                float(np.mean([x.elapsed_time(y) for x, y in ev])))
+
+    ms_op, call_op = timed(lambda: binding.resolvent_operator(
+        t["q"], t["k"], t["u"], t["theta"], *sw, w_re=w_re, w_im=w_im, workspace=ws,
+        status=status, stream=stream, check=False))
+    assert int(status.item()) == 0
+    ms_pp, _ = timed(lambda: binding.resolvent_path_product(a_re, a_im, g_re=g_re, g_im=g_im,
+                                                            stream=stream))
+    # algorithmic HBM bytes: q, k, u, theta in; W out (float32 complex, n^2 per head)
+    alg = B * H * (2 * n * d * 2 + 8 * n + 8 * n * n)
+    achieved = alg / (call_op * 1e-3) / 1e9
+    out = {
+        "metric": "operator export (resolvent_operator): GB/s of algorithmic HBM traffic",
+        "value": alg / (ms_op * 1e-3) / 1e9,
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_op,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": "operator W of B=1 H=16 heads at n=2048 d=128, bf16 q,k "
+                               "~ N(0,1), u ~ U(0.95,1), theta ~ U(-0.05,0.05), switches "
+                               "(1,1,1), seed 11; path_product of the same heads' gates",
+                   "B": B, "H": H, "n": n, "d": d},
+        "path_product_ms": ms_pp,
+        "path_product_gbs": H * n * n * 16 / (ms_pp * 1e-3) / 1e9,
+        "roofline": {"bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                     "frac": achieved / PEAK_HBM_GBS, "traffic": None,
+                     "kernel": "resolvent_operator (gates + row kernels: one call)",
+                     "bytes_per_launch": alg},
+    }
+    if not args.no_cpu_baseline:
+        heads = [0, 9]
+        t0 = time.perf_counter()
+        for h in heads:
+            st, _ = oracle.operator(inp["q"][0, h], inp["k"][0, h], inp["u"][0, h],
+                                    inp["theta"][0, h], *sw)
+            assert st == oracle.OK
+        dt = time.perf_counter() - t0
+        per_head = 2 * n * d * 2 + 8 * n + 8 * n * n
+        out["cpu_baseline"] = {"value": len(heads) * per_head / dt / 1e9, "unit": "GB/s",
+                               "cores": 1, "kind": "oracle",
+                               "sample": f"the oracle's operator on heads {heads}, fp64, one "
+                                         f"thread; {dt:.2f} s; bytes counted as on the device"}
+    print(json.dumps(out), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -424,11 +518,12 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-bytes", type=int, default=0)
-    ap.add_argument("--path", choices=("forward", "chain", "grouped", "decode"),
+    ap.add_argument("--path", choices=("forward", "chain", "grouped", "decode", "operator"),
                     default="forward",
                     help="forward: the head (the headline line); chain: the chain-corner "
                          "scan; grouped: shared k/v heads and another value width; decode: "
-                         "one decode step against an n-position cache")
+                         "one decode step against an n-position cache; operator: the "
+                         "materialising exports")
     ap.add_argument("--summarize-traffic", nargs=4, metavar=("FETCH", "WRITE", "COPY_FETCH",
                                                               "COPY_WRITE"))
     args = ap.parse_args()
@@ -456,6 +551,9 @@ def main():
         return
     if args.path == "decode":
         bench_decode(args)
+        return
+    if args.path == "operator":
+        bench_operator(args)
         return
 
     from gated_causal_attention_amd import binding, inputs

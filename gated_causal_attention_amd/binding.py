@@ -72,6 +72,13 @@ def _load():
     lib.resolvent_decode.restype = i32
     lib.resolvent_chain_step.argtypes = [vp, vp, vp, vp, vp, dbl, i64, i64, i64, i32, vp, vp]
     lib.resolvent_chain_step.restype = i32
+    lib.resolvent_operator_workspace_bytes.argtypes = [i64, i64, i64, i64, i32]
+    lib.resolvent_operator_workspace_bytes.restype = ctypes.c_size_t
+    lib.resolvent_operator.argtypes = [vp, vp, vp, vp, dbl, dbl, dbl, i64, i64, i64, i64, i32,
+                                       vp, vp, vp, ctypes.c_size_t, vp, vp]
+    lib.resolvent_operator.restype = i32
+    lib.resolvent_path_product.argtypes = [vp, vp, i64, i64, vp, vp, vp]
+    lib.resolvent_path_product.restype = i32
     lib.resolvent_status_str.argtypes = [i32]
     lib.resolvent_status_str.restype = ctypes.c_char_p
     _lib = lib
@@ -337,6 +344,65 @@ def resolvent_chain_step(y_re, y_im, u, theta, v, g, *, status=None, stream=None
                                       _dtype_code(v), status.data_ptr(), handle)
     _finish(rc, stream, dev, status, check and B > 0 and H > 0 and dv > 0)
     return y_re, y_im
+
+
+def resolvent_operator_workspace_bytes(B, H, n, d, qk_dtype=BF16) -> int:
+    return int(_load().resolvent_operator_workspace_bytes(B, H, n, d, qk_dtype))
+
+
+def resolvent_operator(q, k, u, theta, beta, qk, g, *, w_re=None, w_im=None, workspace=None,
+                       status=None, stream=None, check=True):
+    """The operator W of every head: q, k [B, H, n, d]; u, theta [B, H, n].
+    Returns (w_re, w_im), each [B, H, n, n] fp32."""
+    import torch
+
+    B, H, n, d = q.shape
+    for t in (q, k, u, theta):
+        if not t.is_contiguous():
+            raise ValueError("inputs must be contiguous")
+    dev = q.device
+    qk_dt = _dtype_code(q)
+    if w_re is None:
+        w_re = torch.empty((B, H, n, n), device=dev, dtype=torch.float32)
+    if w_im is None:
+        w_im = torch.empty((B, H, n, n), device=dev, dtype=torch.float32)
+    ws_bytes = resolvent_operator_workspace_bytes(B, H, n, d, qk_dt)
+    if workspace is None:
+        workspace = torch.empty(max(ws_bytes, 1), device=dev, dtype=torch.uint8)
+    if status is None:
+        status = torch.zeros(1, device=dev, dtype=torch.int32)
+    stream, handle = _stream_handle(stream, dev)
+    rc = _load().resolvent_operator(
+        q.data_ptr(), k.data_ptr(), u.data_ptr(), theta.data_ptr(), float(beta), float(qk),
+        float(g), B, H, n, d, qk_dt, w_re.data_ptr(), w_im.data_ptr(), workspace.data_ptr(),
+        workspace.numel() * workspace.element_size(), status.data_ptr(), handle)
+    _finish(rc, stream, dev, status, check and n > 0 and B > 0 and H > 0)
+    return w_re, w_im
+
+
+def resolvent_path_product(a_re, a_im, *, g_re=None, g_im=None, stream=None):
+    """G = path_product(a) of each gate sequence: a_re, a_im [..., n] fp64
+    device tensors; returns (g_re, g_im), each [..., n, n] fp64."""
+    import torch
+
+    if a_re.dtype != torch.float64 or a_im.dtype != torch.float64:
+        raise TypeError("gates are float64")
+    if not (a_re.is_contiguous() and a_im.is_contiguous()) or a_re.shape != a_im.shape:
+        raise ValueError("a_re, a_im: contiguous, one shape")
+    n = a_re.shape[-1] if a_re.dim() else 0
+    batch = a_re.numel() // n if n else 0
+    dev = a_re.device
+    shape = tuple(a_re.shape) + (n,)
+    if g_re is None:
+        g_re = torch.empty(shape, device=dev, dtype=torch.float64)
+    if g_im is None:
+        g_im = torch.empty(shape, device=dev, dtype=torch.float64)
+    stream, handle = _stream_handle(stream, dev)
+    rc = _load().resolvent_path_product(a_re.data_ptr(), a_im.data_ptr(), batch, n,
+                                        g_re.data_ptr(), g_im.data_ptr(), handle)
+    if rc != Status.OK:
+        raise ResolventError(rc)
+    return g_re, g_im
 
 
 def forward(q, k, u, theta, v, beta, qk, g, **kw):

@@ -27,10 +27,13 @@
 #include <cmath>
 #include <cstdint>
 
+#include "device_common.h"
 #include "layout.h"
 
 namespace resolvent {
 namespace {
+
+using namespace dev;
 
 constexpr int32_t kDecNonFinite = 1;
 
@@ -49,72 +52,13 @@ struct DecodeArgs {
     int beta_mode, qk_zero;
 };
 
-// A gate or a product of gates: complex value and modulus (f64).
-struct Cg {
-    double re, im, m;
-};
-__device__ __forceinline__ Cg cg_one() { return {1.0, 0.0, 1.0}; }
-__device__ __forceinline__ Cg cg_mul(Cg a, Cg b) {
-    return {a.re * b.re - a.im * b.im, a.re * b.im + a.im * b.re, a.m * b.m};
-}
-__device__ __forceinline__ Cg cg_down(Cg a, int o) {
-    return {__shfl_down(a.re, o), __shfl_down(a.im, o), __shfl_down(a.m, o)};
-}
-__device__ __forceinline__ Cg cg_lane(Cg a, int l) {
-    return {__shfl(a.re, l), __shfl(a.im, l), __shfl(a.m, l)};
-}
-
-// Gate of one position (section "Object": blend, then modulus and phase):
-// l = clamp((1-g) + g u, 0, 1), a = l e^{i g theta}, |a| = l, in f64 as the
-// forward pass's gates kernel evaluates it.
-__device__ __forceinline__ Cg gate_of(float uu, float tt, double g, bool &bad) {
-#pragma clang fp contract(off)
-    double l = (1.0 - g) * 1.0 + g * (double)uu;
-    l = l < 0.0 ? 0.0 : (l > 1.0 ? 1.0 : l);
-    const double tp = g * (double)tt;
-    if (!isfinite(uu) || !isfinite(tt) || !isfinite(tp)) bad = true;
-    return {l * cos(tp), l * sin(tp), l};
-}
-
-// 16 bytes at element offset e (a multiple of 4 resp. 8 elements).
-template <bool F32>
-__device__ __forceinline__ uint4 load16(const void *p, int64_t e) {
-    return *reinterpret_cast<const uint4 *>(static_cast<const char *>(p) + e * (F32 ? 4 : 2));
-}
-// The 4 (fp32) or 8 (bf16) values of a 16-byte word.
-template <bool F32>
-__device__ __forceinline__ void unpack16(uint4 w, float *x) {
-    const uint32_t u[4] = {w.x, w.y, w.z, w.w};
-    if constexpr (F32) {
-#pragma unroll
-        for (int e = 0; e < 4; ++e) x[e] = __uint_as_float(u[e]);
-    } else {
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            x[2 * e] = __uint_as_float(u[e] << 16);
-            x[2 * e + 1] = __uint_as_float(u[e] & 0xFFFF0000u);
-        }
-    }
-}
-
-__device__ __forceinline__ float wave_max(float x) {
-#pragma unroll
-    for (int o = 32; o >= 1; o >>= 1) x = fmaxf(x, __shfl_xor(x, o));
-    return x;
-}
-__device__ __forceinline__ float wave_sum(float x) {
-#pragma unroll
-    for (int o = 32; o >= 1; o >>= 1) x += __shfl_xor(x, o);
-    return x;
-}
-
 // One wave per (head, chunk): blockIdx.x = bh n_ch + chunk.  The chunk's
 // tiles are taken last to first, so that the product from each to the
-// chunk's end is the one after it times that tile's product.  Key rows are read KL lanes to a row
-// (16 bytes a lane: one instruction covers KR whole rows) and their dot
-// products reduced across those lanes; value rows the same way, VL lanes to a
-// row, each lane accumulating VE channels of VR interleaved row groups that are
-// summed at the end.
+// chunk's end is the one after it times that tile's product.  Key rows are
+// read KL lanes to a row (16 bytes a lane: one instruction covers KR whole
+// rows) and their dot products reduced across those lanes; value rows the same
+// way, VL lanes to a row, each lane accumulating VE channels of VR interleaved
+// row groups that are summed at the end.
 template <bool QF32, bool VF32, int D, int DV>
 __global__ __launch_bounds__(64) void decode_part_kernel(DecodeArgs A) {
     constexpr int KE = QF32 ? 4 : 8, KL = D / KE, KR = 64 / KL, KI = BK / KR;

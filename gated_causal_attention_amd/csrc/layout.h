@@ -153,6 +153,26 @@ inline DecodeLayout make_decode_layout(int64_t B, int64_t H, int64_t Hkv, int64_
     return D;
 }
 
+// Workspace of the operator export (resolvent_operator): the gates of every
+// position, f64 (double [BH][n] each: re, im, modulus).
+struct OperatorLayout {
+    int64_t BH = 0, n = 0, d = 0;
+    size_t a_re = 0, a_im = 0, a_m = 0, total = 0;
+};
+
+inline OperatorLayout make_operator_layout(int64_t B, int64_t H, int64_t n, int64_t d) {
+    OperatorLayout O;
+    O.BH = B * H;
+    O.n = n;
+    O.d = d;
+    const size_t per = sizeof(double) * size_t(O.BH) * size_t(n);
+    O.a_re = 0;
+    O.a_im = align_up(per, 256);
+    O.a_m = 2 * align_up(per, 256);
+    O.total = 3 * align_up(per, 256);
+    return O;
+}
+
 // Source byte offsets of the direct global->LDS tile copies, relative to the
 // start of the tensor (q/k/v, or the v^T region for the bf16 path).  Row `r`
 // of key tile `t` is key t*BK + r, clamped into [0, n-1] so that a tile
@@ -292,6 +312,16 @@ int launch_decode(const DecodeLayout &DL, const void *q, const void *k, const fl
                   const float *theta, const void *v, int64_t cap, bool qk_f32, bool v_f32,
                   double g, float c, float beta, int beta_mode, bool qk_zero, float *o_re,
                   float *o_im, unsigned char *ws, int32_t *status, void *stream);
+// The path-product matrices of `batch` gate sequences of length n, f64
+// (export_kernels.hip).  Returns a hipError_t.
+int launch_path_product(const double *a_re, const double *a_im, int64_t batch, int64_t n,
+                        double *g_re, double *g_im, void *stream);
+// The operator W of every head, float32 (export_kernels.hip).  Returns a
+// hipError_t.
+int launch_operator(const OperatorLayout &OL, const void *q, const void *k, const float *u,
+                    const float *theta, bool qk_f32, double g, float c, float beta,
+                    int beta_mode, bool qk_zero, float *w_re, float *w_im, unsigned char *ws,
+                    int32_t *status, void *stream);
 // One step of the gated chain per (head, channel), in place (decode_kernels.hip).
 int launch_chain_step(float *y_re, float *y_im, const float *u, const float *theta,
                       const void *v, bool v_f32, double g, int64_t BH, int64_t dv,

@@ -33,6 +33,16 @@ bool within_limits(int64_t B, int64_t H, int64_t n) {
 
 bool aligned(const void *p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
 
+// The exports write an [n, n] matrix per head: n is capped, and one workgroup
+// per (head, row) must fit a 1-D grid.
+constexpr int64_t kMaxExportN = 65536;
+bool operator_supported(int64_t B, int64_t H, int64_t n, int64_t d, int32_t qk_dtype) {
+    if (d != 64 && d != 128) return false;
+    if (qk_dtype != RESOLVENT_BF16 && qk_dtype != RESOLVENT_F32) return false;
+    if (n > kMaxExportN || B > (int64_t(1) << 24) || H > (int64_t(1) << 24)) return false;
+    return B * H <= (int64_t(1) << 24) && B * H * n < (int64_t(1) << 31);
+}
+
 bool supported_dv(int64_t dv) { return dv == 64 || dv == 128; }
 
 size_t workspace_grouped(int64_t B, int64_t H, int64_t Hkv, int64_t n, int64_t d, int64_t dv,
@@ -233,6 +243,54 @@ int32_t resolvent_chain_step(float *y_re, float *y_im, const float *u, const flo
         return RESOLVENT_BAD_ARG;
     const int err = launch_chain_step(y_re, y_im, u, theta, v, v_dtype == RESOLVENT_F32, g, B * H,
                                       dv, status_dev, stream);
+    return err == 0 ? RESOLVENT_OK : RESOLVENT_DEVICE_ERROR;
+}
+
+size_t resolvent_operator_workspace_bytes(int64_t B, int64_t H, int64_t n, int64_t d,
+                                          int32_t qk_dtype) {
+    if (B <= 0 || H <= 0 || n <= 0 || d <= 0) return 0;
+    if (!operator_supported(B, H, n, d, qk_dtype)) return 0;
+    return make_operator_layout(B, H, n, d).total;
+}
+
+int32_t resolvent_operator(const void *q, const void *k, const float *u, const float *theta,
+                           double beta, double qk, double g, int64_t B, int64_t H, int64_t n,
+                           int64_t d, int32_t qk_dtype, float *w_re, float *w_im,
+                           void *workspace, size_t workspace_bytes, int32_t *status_dev,
+                           hipStream_t stream) {
+    if (B < 0 || H < 0 || n < 0 || d < 0) return RESOLVENT_BAD_SHAPE;
+    if (B == 0 || H == 0 || n == 0) return RESOLVENT_OK;
+    if (d == 0) return RESOLVENT_BAD_SHAPE;
+    if (!std::isfinite(beta) || !std::isfinite(qk) || !std::isfinite(g))
+        return RESOLVENT_NONFINITE;
+    if (!operator_supported(B, H, n, d, qk_dtype)) return RESOLVENT_UNSUPPORTED;
+    if (!q || !k || !u || !theta || !w_re || !w_im || !status_dev || !workspace)
+        return RESOLVENT_BAD_ARG;
+    if (!aligned(q, 16) || !aligned(k, 16) || !aligned(u, 4) || !aligned(theta, 4) ||
+        !aligned(w_re, 4) || !aligned(w_im, 4) || !aligned(status_dev, 4) ||
+        !aligned(workspace, 256))
+        return RESOLVENT_BAD_ARG;
+    const OperatorLayout OL = make_operator_layout(B, H, n, d);
+    if (workspace_bytes < OL.total) return RESOLVENT_BAD_ARG;
+    const double c = qk * 1.4426950408889634074 / std::sqrt((double)d);
+    if (qk != 0.0 && !(std::fabs(c) <= (double)FLT_MAX)) return RESOLVENT_NONFINITE;
+    const int err = launch_operator(OL, q, k, u, theta, qk_dtype == RESOLVENT_F32, g, (float)c,
+                                    (float)beta, beta == 0.0 ? 0 : (beta == 1.0 ? 1 : 2),
+                                    qk == 0.0, w_re, w_im,
+                                    static_cast<unsigned char *>(workspace), status_dev, stream);
+    return err == 0 ? RESOLVENT_OK : RESOLVENT_DEVICE_ERROR;
+}
+
+int32_t resolvent_path_product(const double *a_re, const double *a_im, int64_t batch, int64_t n,
+                               double *g_re, double *g_im, hipStream_t stream) {
+    if (batch < 0 || n < 0) return RESOLVENT_BAD_SHAPE;
+    if (batch == 0 || n == 0) return RESOLVENT_OK;
+    if (n > kMaxExportN || batch > (int64_t(1) << 24) || batch * ((n + 63) / 64) >= (int64_t(1) << 31))
+        return RESOLVENT_UNSUPPORTED;
+    if (!a_re || !a_im || !g_re || !g_im) return RESOLVENT_BAD_ARG;
+    if (!aligned(a_re, 8) || !aligned(a_im, 8) || !aligned(g_re, 8) || !aligned(g_im, 8))
+        return RESOLVENT_BAD_ARG;
+    const int err = launch_path_product(a_re, a_im, batch, n, g_re, g_im, stream);
     return err == 0 ? RESOLVENT_OK : RESOLVENT_DEVICE_ERROR;
 }
 

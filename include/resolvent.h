@@ -300,6 +300,64 @@ int32_t resolvent_chain_step(float *y_re, float *y_im, const float *u, const flo
                              int32_t v_dtype, int32_t *status_dev, hipStream_t stream);
 
 /*
+ * resolvent_operator_workspace_bytes -- device workspace for
+ * resolvent_operator (0 for an empty, invalid or unsupported problem).
+ */
+size_t resolvent_operator_workspace_bytes(int64_t B, int64_t H, int64_t n, int64_t d,
+                                          int32_t qk_dtype);
+
+/*
+ * resolvent_operator -- the operator W of every head, materialised: the
+ * "operator" of the "Resolvent Operator" page's Rust API (section "Object":
+ * W_ij = G_ij e^{qk s_ij} / Z_i^beta for j <= i, 0 above the diagonal),
+ * row-major [n, n] per head, for inspection at small n (the hot path never
+ * forms W).  float32 weights from float32 logits and f64 gate products, the
+ * arithmetic of the decode step applied to every row.
+ *
+ * Arguments (device pointers; contiguous row-major):
+ *   q, k        [B, H, n, d] (qk_dtype: RESOLVENT_BF16 or RESOLVENT_F32),
+ *               16-byte aligned
+ *   u, theta    [B, H, n] float32
+ *   beta,qk,g   the switches (f64)
+ *   d           64 or 128; n <= 65536 and B H n < 2^31
+ *   w_re, w_im  [B, H, n, n] float32 outputs
+ *   workspace   at least resolvent_operator_workspace_bytes(...) bytes,
+ *               256-byte aligned
+ *   status_dev, stream  as for resolvent_forward
+ * Returns the codes of resolvent_forward for the same conditions before
+ * anything is enqueued (RESOLVENT_OK with nothing enqueued when n, B or H is
+ * 0); on the device the status word becomes RESOLVENT_NONFINITE for a
+ * non-finite q, k, u or theta, an overflowing g*theta_k or a float32 logit
+ * that overflows (the outputs are then unspecified).
+ */
+int32_t resolvent_operator(const void *q, const void *k, const float *u, const float *theta,
+                           double beta, double qk, double g, int64_t B, int64_t H, int64_t n,
+                           int64_t d, int32_t qk_dtype, float *w_re, float *w_im,
+                           void *workspace, size_t workspace_bytes, int32_t *status_dev,
+                           hipStream_t stream);
+
+/*
+ * resolvent_path_product -- the "path_product" of the "Resolvent Operator"
+ * page's Rust API for `batch` gate sequences: G_ij = a_{j+1} a_{j+2} ... a_i
+ * for j < i, G_ii = 1, 0 above the diagonal, row-major [n, n] each, in f64.
+ * Each row is accumulated from k = i down to k = j + 1, the order the page
+ * fixes, without fused multiply-adds: the result is that definition evaluated
+ * in that order, to the bit.  a_0 is never read.
+ *
+ * Arguments (device pointers, 8-byte aligned):
+ *   a_re, a_im  [batch, n] the gates (f64)
+ *   g_re, g_im  [batch, n, n] outputs (f64)
+ * Returns RESOLVENT_BAD_SHAPE for a negative size, RESOLVENT_OK with nothing
+ * enqueued when batch or n is 0, RESOLVENT_UNSUPPORTED for n > 65536 or
+ * batch > 2^24, RESOLVENT_BAD_ARG for a null or misaligned pointer,
+ * RESOLVENT_DEVICE_ERROR if the launch failed, else RESOLVENT_OK once the
+ * work is enqueued.  No refusal: non-finite gates propagate as in the page's
+ * definition.
+ */
+int32_t resolvent_path_product(const double *a_re, const double *a_im, int64_t batch, int64_t n,
+                               double *g_re, double *g_im, hipStream_t stream);
+
+/*
  * resolvent_status_str -- a static, human-readable name of a status code.
  */
 const char *resolvent_status_str(int32_t status);

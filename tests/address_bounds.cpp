@@ -322,6 +322,64 @@ static int check_decode(int64_t B, int64_t H, int64_t Hkv, int64_t n, int64_t ca
     return bad;
 }
 
+// The exports: every load of operator_row_kernel (q row i, k rows j <= i,
+// gates a_{j+1} with j < i) and store (w row i) stays inside its tensor, and
+// path_product_kernel stores every entry of each matrix exactly once.
+static int check_exports(int64_t B, int64_t H, int64_t n, int64_t d, int esz) {
+    const int64_t BH = B * H;
+    const int ke = 16 / esz, kl = int(d) / ke, kr_n = 64 / kl;
+    int bad = 0;
+    auto fail = [&](const char *what, int64_t a, int64_t b) {
+        if (bad++ < 10)
+            std::printf("exports B=%lld H=%lld n=%lld d=%lld: %s (%lld, %lld)\n", (long long)B,
+                        (long long)H, (long long)n, (long long)d, what, (long long)a, (long long)b);
+    };
+    for (int64_t bh = 0; bh < BH; ++bh)
+        for (int64_t i = 0; i < n; ++i) {
+            for (int lane = 0; lane < 64; ++lane) {
+                const int64_t qoff = ((bh * n + i) * d + (lane % kl) * ke) * esz;
+                if (qoff + 16 > BH * n * d * esz) fail("q load", i, lane);
+            }
+            for (int64_t t = i / BK; t >= 0; --t) {
+                const int64_t t0 = t * BK;
+                const int cnt = int(i - t0 + 1 < BK ? i - t0 + 1 : BK);
+                for (int lane = 0; lane < 64; ++lane) {
+                    for (int x = 0; x < BK / kr_n; ++x) {
+                        const int r = x * kr_n + lane / kl, row = r < cnt ? r : cnt - 1;
+                        const int64_t off = ((bh * n + t0 + row) * d + (lane % kl) * ke) * esz;
+                        if (t0 + row > i || off < 0 || off + 16 > BH * n * d * esz)
+                            fail("k load", i, t0 + row);
+                    }
+                    const int64_t j = t0 + lane;
+                    if (j < i && (j + 1 >= n || bh * n + j + 1 >= BH * n)) fail("gate read", i, j);
+                    if (lane < cnt && (j > i || (bh * n + i) * n + j >= BH * n * n))
+                        fail("w store", i, j);
+                }
+            }
+        }
+    // path_product_kernel on one matrix
+    const int64_t n_rb = (n + 63) / 64;
+    std::vector<int> seen(size_t(n) * size_t(n), 0);
+    for (int64_t rb = 0; rb < n_rb; ++rb) {
+        const int64_t r0 = rb * 64, rows = std::min<int64_t>(64, n - r0);
+        for (int64_t cb = rb; cb >= 0; --cb) {
+            const int64_t c0 = cb * 64, cols = std::min<int64_t>(64, n - c0);
+            for (int r = 0; r < 64; ++r) {
+                if (c0 + r + 1 < n && c0 + r + 1 < 0) fail("gate stage", cb, r);
+                if (r < cols)
+                    for (int64_t rr = 0; rr < rows; ++rr) seen[size_t((r0 + rr) * n + c0 + r)] += 1;
+            }
+        }
+        for (int64_t c0 = (rb + 1) * 64; c0 < n; c0 += 64)
+            for (int r = 0; r < 64; ++r)
+                if (c0 + r < n)
+                    for (int64_t rr = 0; rr < rows; ++rr) seen[size_t((r0 + rr) * n + c0 + r)] += 1;
+    }
+    for (size_t x = 0; x < seen.size(); ++x)
+        if (seen[x] != 1) fail("path product entry not stored once", int64_t(x / n), int64_t(x % n));
+    return bad;
+}
+
 int main(int argc, char **argv) {
     int bad = check_tile_layout<16>("K d=128") + check_tile_layout<8>("K d=64 / v^T") +
               check_operand_reads<16>() + check_operand_reads<8>() + check_v_reads(64) +
@@ -340,6 +398,10 @@ int main(int argc, char **argv) {
                     bad += check_decode(B, H, Hkv, n, n, d, dv, 4, 4);
                 }
             }
+        if (n <= 1100) {
+            bad += check_exports(B, H, n, d, 2);
+            bad += check_exports(B, H, n, d, 4);
+        }
         ++cases;
     }
     std::printf("%d shapes, %d problems\n", cases, bad);

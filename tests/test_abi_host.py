@@ -214,3 +214,47 @@ def test_chain_step_host_checks():
     assert chain_step_call(dv=8192) == S.UNSUPPORTED
     assert chain_step_call(ptr=None) == S.BAD_ARG
     assert chain_step_call(ptr=FAKE + 1) == S.BAD_ARG
+
+
+def operator_call(B=1, H=2, n=130, d=64, beta=1.0, qk=1.0, g=1.0, qdt=0, ws_bytes=None,
+                  ptr=FAKE, ws=FAKE):
+    lib = binding._load()
+    if ws_bytes is None:
+        ws_bytes = lib.resolvent_operator_workspace_bytes(1, 2, 130, 64, qdt)
+    return lib.resolvent_operator(ptr, ptr, ptr, ptr, beta, qk, g, B, H, n, d, qdt, ptr, ptr, ws,
+                                  ws_bytes, FAKE, None)
+
+
+def test_operator_host_checks():
+    assert operator_call(B=-1) == S.BAD_SHAPE
+    assert operator_call(n=0, ptr=None) == S.OK
+    assert operator_call(d=0) == S.BAD_SHAPE
+    for bad in (float("nan"), float("inf")):
+        assert operator_call(beta=bad) == S.NONFINITE
+        assert operator_call(g=bad) == S.NONFINITE
+    assert operator_call(qk=1e308) == S.NONFINITE
+    assert operator_call(d=96) == S.UNSUPPORTED
+    assert operator_call(qdt=3) == S.UNSUPPORTED
+    assert operator_call(n=65537) == S.UNSUPPORTED  # the [n, n] export is for small n
+    assert operator_call(ptr=None) == S.BAD_ARG
+    assert operator_call(ptr=FAKE + 8) == S.BAD_ARG
+    assert operator_call(ws=FAKE + 64) == S.BAD_ARG
+    assert operator_call(ws_bytes=16) == S.BAD_ARG
+    ws = binding.resolvent_operator_workspace_bytes
+    assert ws(1, 2, 130, 96) == 0 and ws(0, 2, 130, 64) == 0
+    assert 0 < ws(1, 2, 130, 64) < ws(1, 2, 131 + 256, 64)
+
+
+def test_path_product_host_checks():
+    lib = binding._load()
+
+    def call(batch=2, n=100, ptr=FAKE):
+        return lib.resolvent_path_product(ptr, ptr, batch, n, ptr, ptr, None)
+
+    assert call(batch=-1) == S.BAD_SHAPE
+    assert call(n=-1) == S.BAD_SHAPE
+    assert call(n=0, ptr=None) == S.OK
+    assert call(batch=0, ptr=None) == S.OK
+    assert call(n=65537) == S.UNSUPPORTED
+    assert call(ptr=None) == S.BAD_ARG
+    assert call(ptr=FAKE + 4) == S.BAD_ARG
