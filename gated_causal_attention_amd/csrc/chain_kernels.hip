@@ -10,12 +10,12 @@
 // never read, so the chain's first term is the value itself).  This is a
 // first-order complex linear recurrence in each channel; it is scanned in the
 // 64-position key tiles of the forward pass:
-//   chain_agg_kernel    each tile's end value from a zero carry-in, per
-//                       channel: agg_t = sum_{j in t} S_j V_j (S_j the
-//                       exclusive suffix product inside the tile)
+//   chain_agg16_kernel  each tile's end value from a zero carry-in, per
+//   (chain_agg_kernel   channel: agg_t = sum_{j in t} S_j V_j (S_j the
+//    for other widths)  exclusive suffix product inside the tile)
 //   chain_carry_kernel  the carry into each tile, folded over the earlier
 //                       tiles in f64 with the whole-tile gate products:
-//                       Y_t = A_t Y_{t-1} + agg_t
+//                       Y_t = A_t Y_{t-1} + agg_t, in 8 segments per head
 //   chain_out_kernel    each tile's chain from its carry, writing O
 // The gates a_k, the suffix products S_j and the tile products A_t (f64) come
 // from gates_kernel, the forward pass's own, so a closed gate (a_k = 0) cuts
@@ -135,6 +135,78 @@ __global__ __launch_bounds__(64) void chain_agg_kernel(ChainArgs A) {
     for (int e = 0; e < CPL; ++e) A.agg[ci + e] = make_float2(acc_r[e], acc_i[e]);
 }
 
+// The same aggregate with whole 16-byte value loads: one wave per (head,
+// tile) covers all DVW channels; VL lanes read a row (VE channels a lane), so
+// one load instruction covers VR rows and the tile takes VI of them, all in
+// flight at once.  Lane (r, c) accumulates its VE channels over the rows
+// r, r + VR, ...; the suffix factor of a row comes from the lane holding that
+// position (a lane shuffle), and the VR row groups are summed at the end.
+template <bool VF32, int DVW>
+__global__ __launch_bounds__(64) void chain_agg16_kernel(ChainArgs A) {
+    constexpr int VE = VF32 ? 4 : 8, VL = DVW / VE, VR = 64 / VL, VI = BK / VR;
+    static_assert(VL >= 1 && VL <= 64 && 64 % VL == 0, "row split");
+    const int lane = threadIdx.x;
+    const int64_t bh = blockIdx.x / A.n_kt;
+    const int t = int(blockIdx.x % A.n_kt);
+    const int64_t p0 = int64_t(t) * BK;
+    const int cnt = int(A.n - p0 < BK ? A.n - p0 : BK);
+    const int vc = (lane % VL) * VE, vr = lane / VL;
+    float acc_r[VE], acc_i[VE];
+#pragma unroll
+    for (int e = 0; e < VE; ++e) {
+        acc_r[e] = 0.f;
+        acc_i[e] = 0.f;
+    }
+    if (cnt > 0) {
+        const char *vb = static_cast<const char *>(A.v) + ((bh * A.n + p0) * DVW + vc) * (VF32 ? 4 : 2);
+        uint4 w[VI];
+#pragma unroll
+        for (int x = 0; x < VI; ++x) {
+            const int row = x * VR + vr < cnt ? x * VR + vr : cnt - 1;
+            w[x] = *reinterpret_cast<const uint4 *>(vb + int64_t(row) * DVW * (VF32 ? 4 : 2));
+        }
+        // this lane's position's suffix factor (0 past the tile's last value)
+        const float sl_r = lane < cnt ? A.s_re[bh * A.n_pad + p0 + lane] : 0.f;
+        const float sl_i = lane < cnt ? A.s_im[bh * A.n_pad + p0 + lane] : 0.f;
+#pragma unroll
+        for (int x = 0; x < VI; ++x) {
+            const int row = x * VR + vr;
+            const float gr = __shfl(sl_r, row), gi = __shfl(sl_i, row);
+            const uint32_t u[4] = {w[x].x, w[x].y, w[x].z, w[x].w};
+            float xv[VE];
+            if constexpr (VF32) {
+#pragma unroll
+                for (int e = 0; e < 4; ++e) xv[e] = __uint_as_float(u[e]);
+            } else {
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    xv[2 * e] = __uint_as_float(u[e] << 16);
+                    xv[2 * e + 1] = __uint_as_float(u[e] & 0xFFFF0000u);
+                }
+            }
+#pragma unroll
+            for (int e = 0; e < VE; ++e) {
+                acc_r[e] = fmaf(gr, xv[e], acc_r[e]);
+                acc_i[e] = fmaf(gi, xv[e], acc_i[e]);
+            }
+        }
+    }
+#pragma unroll
+    for (int o = VL; o < 64; o <<= 1)
+#pragma unroll
+        for (int e = 0; e < VE; ++e) {
+            acc_r[e] += __shfl_xor(acc_r[e], o);
+            acc_i[e] += __shfl_xor(acc_i[e], o);
+        }
+    if (lane < VL) {
+        float2 *ag = A.agg + (bh * A.n_kt + t) * DVW + vc;
+#pragma unroll
+        for (int e = 0; e < VE; e += 2)
+            *reinterpret_cast<float4 *>(ag + e) =
+                make_float4(acc_r[e], acc_i[e], acc_r[e + 1], acc_i[e + 1]);
+    }
+}
+
 // One wave per (key tile t, head bh) -- flattened as blockIdx.x = bh n_kt + t
 // -- and channel group blockIdx.y of 64 CPL channels; lane L runs the CPL
 // independent chains of channels 64 CPL y + CPL L + e.  The tile's positions
@@ -216,36 +288,76 @@ __global__ __launch_bounds__(64) void chain_out_kernel(ChainArgs A) {
         out_scan<VF32, CPL, false>(A, ar, ai, vb, cnt, yr, yi);
 }
 
-// One wave per (head, 64-channel group): the carries into the tiles, in f64.
-// The tiles' aggregates and products are fetched 16 at a time ahead of the
-// fold, whose steps depend on each other.
-__global__ __launch_bounds__(64) void chain_carry_kernel(ChainArgs A) {
+// The carries into the tiles, in f64: one workgroup of CW waves per (head,
+// 64-channel group), lane = channel.  The tiles are split into CW
+// consecutive segments; wave s folds its segment from a zero carry-in
+// (Y <- A_t Y + agg_t) and records the segment's end value and product; after
+// a barrier it folds the earlier segments' records into its own carry-in and
+// walks its segment again writing the carries.  The fetches run 16 tiles
+// ahead of the dependent steps.
+constexpr int CW = 8;
+__global__ __launch_bounds__(64 * CW) void chain_carry_kernel(ChainArgs A) {
     constexpr int NB = 16;
+    __shared__ double seg_y[2][CW][64];
+    __shared__ double seg_p[2][CW];
+    const int lane = threadIdx.x % 64, s = threadIdx.x / 64;
     const int64_t bh = blockIdx.x;
-    const int c = int(blockIdx.y) * 64 + int(threadIdx.x);
+    const int c = int(blockIdx.y) * 64 + lane;
     const double *__restrict__ tr = A.t_re + bh * A.n_kt;
     const double *__restrict__ ti = A.t_im + bh * A.n_kt;
     const float2 *__restrict__ agg = A.agg + bh * A.n_kt * A.dv + c;
     float2 *__restrict__ carry = A.carry + bh * A.n_kt * A.dv + c;
+    const int len = (A.n_kt + CW - 1) / CW;
+    const int t_lo = s * len < A.n_kt ? s * len : A.n_kt;
+    const int t_hi = t_lo + len < A.n_kt ? t_lo + len : A.n_kt;
+    // pass 0: the segment's own fold (with its product); pass 1: the carries
     double yr = 0.0, yi = 0.0;
-    for (int t0 = 0; t0 < A.n_kt; t0 += NB) {
-        float2 e[NB];
-        double pr[NB], pi[NB];
-#pragma unroll
-        for (int x = 0; x < NB; ++x) {
-            const int t = t0 + x < A.n_kt ? t0 + x : A.n_kt - 1;
-            e[x] = agg[int64_t(t) * A.dv];
-            pr[x] = tr[t];
-            pi[x] = ti[t];
-        }
-#pragma unroll
-        for (int x = 0; x < NB; ++x) {
-            if (t0 + x < A.n_kt) {
-                carry[int64_t(t0 + x) * A.dv] = make_float2((float)yr, (float)yi);
-                const double nr = pr[x] * yr - pi[x] * yi + (double)e[x].x;
-                const double ni = pr[x] * yi + pi[x] * yr + (double)e[x].y;
+    for (int pass = 0; pass < 2; ++pass) {
+        double qr = 1.0, qi = 0.0;  // the segment's gate product
+        if (pass == 1) {
+            __syncthreads();
+            yr = 0.0;
+            yi = 0.0;
+            for (int r = 0; r < s; ++r) {  // Y <- P_r Y + y_r over the earlier segments
+                const double pr = seg_p[0][r], pi = seg_p[1][r];
+                const double nr = pr * yr - pi * yi + seg_y[0][r][lane];
+                const double ni = pr * yi + pi * yr + seg_y[1][r][lane];
                 yr = nr;
                 yi = ni;
+            }
+        }
+        for (int t0 = t_lo; t0 < t_hi; t0 += NB) {
+            float2 e[NB];
+            double pr[NB], pi[NB];
+#pragma unroll
+            for (int x = 0; x < NB; ++x) {
+                const int t = t0 + x < t_hi ? t0 + x : t_hi - 1;
+                e[x] = agg[int64_t(t) * A.dv];
+                pr[x] = tr[t];
+                pi[x] = ti[t];
+            }
+#pragma unroll
+            for (int x = 0; x < NB; ++x) {
+                if (t0 + x < t_hi) {
+                    if (pass == 1) carry[int64_t(t0 + x) * A.dv] = make_float2((float)yr, (float)yi);
+                    const double nr = pr[x] * yr - pi[x] * yi + (double)e[x].x;
+                    const double ni = pr[x] * yi + pi[x] * yr + (double)e[x].y;
+                    yr = nr;
+                    yi = ni;
+                    if (pass == 0) {
+                        const double mr = pr[x] * qr - pi[x] * qi;
+                        qi = pr[x] * qi + pi[x] * qr;
+                        qr = mr;
+                    }
+                }
+            }
+        }
+        if (pass == 0) {
+            seg_y[0][s][lane] = yr;
+            seg_y[1][s][lane] = yi;
+            if (lane == 0) {
+                seg_p[0][s] = qr;
+                seg_p[1][s] = qi;
             }
         }
     }
@@ -277,34 +389,48 @@ int launch_chain(const ChainLayout &C, const float *u, const float *theta, const
     A.n_kt = (int)L.n_kt;
     A.dv = (int)C.dv;
     const dim3 heads((unsigned)L.BH, (unsigned)(C.dv / 64));
+    const dim3 wide((unsigned)(L.BH * L.n_kt));
+    // the aggregate with 16-byte loads when a row of values splits evenly over
+    // the lanes and v is 16-byte aligned
+    const bool v16 = reinterpret_cast<uintptr_t>(v) % 16 == 0;
+    bool agg_done = true;
+    if (v16 && !v_f32 && C.dv == 64)
+        hipLaunchKernelGGL((chain_agg16_kernel<false, 64>), wide, dim3(64), 0, st, A);
+    else if (v16 && !v_f32 && C.dv == 128)
+        hipLaunchKernelGGL((chain_agg16_kernel<false, 128>), wide, dim3(64), 0, st, A);
+    else if (v16 && !v_f32 && C.dv == 256)
+        hipLaunchKernelGGL((chain_agg16_kernel<false, 256>), wide, dim3(64), 0, st, A);
+    else if (v16 && v_f32 && C.dv == 64)
+        hipLaunchKernelGGL((chain_agg16_kernel<true, 64>), wide, dim3(64), 0, st, A);
+    else if (v16 && v_f32 && C.dv == 128)
+        hipLaunchKernelGGL((chain_agg16_kernel<true, 128>), wide, dim3(64), 0, st, A);
+    else
+        agg_done = false;
     // two channels per lane (8-byte stores) when the channels come in whole
     // 128s and the outputs allow it: fewer waves, two independent chains each
     const bool pairs = C.dv % 128 == 0 && reinterpret_cast<uintptr_t>(o_re) % 8 == 0 &&
                        reinterpret_cast<uintptr_t>(o_im) % 8 == 0 &&
                        reinterpret_cast<uintptr_t>(v) % (v_f32 ? 8 : 4) == 0;
-    if (pairs) {
-        const dim3 tiles((unsigned)(L.BH * L.n_kt), (unsigned)(C.dv / 128));
-        if (v_f32) {
+    const dim3 tiles((unsigned)(L.BH * L.n_kt), (unsigned)(C.dv / (pairs ? 128 : 64)));
+    if (!agg_done) {
+        if (pairs && v_f32)
             hipLaunchKernelGGL((chain_agg_kernel<true, 2>), tiles, dim3(64), 0, st, A);
-            hipLaunchKernelGGL(chain_carry_kernel, heads, dim3(64), 0, st, A);
-            hipLaunchKernelGGL((chain_out_kernel<true, 2>), tiles, dim3(64), 0, st, A);
-        } else {
+        else if (pairs)
             hipLaunchKernelGGL((chain_agg_kernel<false, 2>), tiles, dim3(64), 0, st, A);
-            hipLaunchKernelGGL(chain_carry_kernel, heads, dim3(64), 0, st, A);
-            hipLaunchKernelGGL((chain_out_kernel<false, 2>), tiles, dim3(64), 0, st, A);
-        }
-    } else {
-        const dim3 tiles((unsigned)(L.BH * L.n_kt), (unsigned)(C.dv / 64));
-        if (v_f32) {
+        else if (v_f32)
             hipLaunchKernelGGL((chain_agg_kernel<true, 1>), tiles, dim3(64), 0, st, A);
-            hipLaunchKernelGGL(chain_carry_kernel, heads, dim3(64), 0, st, A);
-            hipLaunchKernelGGL((chain_out_kernel<true, 1>), tiles, dim3(64), 0, st, A);
-        } else {
+        else
             hipLaunchKernelGGL((chain_agg_kernel<false, 1>), tiles, dim3(64), 0, st, A);
-            hipLaunchKernelGGL(chain_carry_kernel, heads, dim3(64), 0, st, A);
-            hipLaunchKernelGGL((chain_out_kernel<false, 1>), tiles, dim3(64), 0, st, A);
-        }
     }
+    hipLaunchKernelGGL(chain_carry_kernel, heads, dim3(64 * CW), 0, st, A);
+    if (pairs && v_f32)
+        hipLaunchKernelGGL((chain_out_kernel<true, 2>), tiles, dim3(64), 0, st, A);
+    else if (pairs)
+        hipLaunchKernelGGL((chain_out_kernel<false, 2>), tiles, dim3(64), 0, st, A);
+    else if (v_f32)
+        hipLaunchKernelGGL((chain_out_kernel<true, 1>), tiles, dim3(64), 0, st, A);
+    else
+        hipLaunchKernelGGL((chain_out_kernel<false, 1>), tiles, dim3(64), 0, st, A);
     return (int)hipGetLastError();
 }
 

@@ -380,6 +380,53 @@ static int check_exports(int64_t B, int64_t H, int64_t n, int64_t d, int esz) {
     return bad;
 }
 
+// The chain scan's 16-byte aggregate (chain_agg16_kernel: every value row
+// 0..n-1 of a head read whole, loads and aggregate stores inside their
+// arrays) and the segments of chain_carry_kernel (every tile folded by
+// exactly one segment).  esz: element bytes of v.
+static int check_chain(int64_t B, int64_t H, int64_t n, int64_t dv, int esz) {
+    const ChainLayout C = make_chain_layout(B, H, n, dv);
+    const Layout &L = C.g;
+    const int ve = 16 / esz, vl = int(dv) / ve, vr_n = 64 / vl;
+    int bad = 0;
+    auto fail = [&](const char *what, int64_t a, int64_t b) {
+        if (bad++ < 10)
+            std::printf("chain B=%lld H=%lld n=%lld dv=%lld: %s (%lld, %lld)\n", (long long)B,
+                        (long long)H, (long long)n, (long long)dv, what, (long long)a, (long long)b);
+    };
+    for (int64_t bh = 0; bh < L.BH; ++bh) {
+        std::vector<int> seen(size_t(n) * size_t(vl), 0);
+        for (int64_t t = 0; t < L.n_kt; ++t) {
+            const int64_t p0 = t * BK;
+            const int cnt = int(n - p0 < BK ? n - p0 : BK);
+            if (cnt <= 0) continue;
+            for (int lane = 0; lane < 64; ++lane) {
+                for (int x = 0; x < BK / vr_n; ++x) {
+                    const int r = x * vr_n + lane / vl, row = r < cnt ? r : cnt - 1;
+                    const int64_t off = ((bh * n + p0 + row) * dv + (lane % vl) * ve) * esz;
+                    if (off < 0 || off + 16 > L.BH * n * dv * esz) fail("v load", t, lane);
+                    else seen[size_t((p0 + row) * vl + lane % vl)] = 1;
+                }
+                if (lane < cnt && bh * L.n_pad + p0 + lane >= L.BH * L.n_pad) fail("s read", t, lane);
+                if (lane < vl && (bh * L.n_kt + t) * dv + (lane % vl) * ve + ve > L.BH * L.n_kt * dv)
+                    fail("agg store", t, lane);
+            }
+        }
+        for (size_t x = 0; x < seen.size(); ++x)
+            if (!seen[x]) fail("value chunk never read", bh, int64_t(x));
+    }
+    const int cw = 8, len = int((L.n_kt + cw - 1) / cw);
+    std::vector<int> tseen(size_t(L.n_kt), 0);
+    for (int s = 0; s < cw; ++s) {
+        const int64_t lo = std::min<int64_t>(int64_t(s) * len, L.n_kt);
+        const int64_t hi = std::min<int64_t>(lo + len, L.n_kt);
+        for (int64_t t = lo; t < hi; ++t) tseen[size_t(t)] += 1;
+    }
+    for (int64_t t = 0; t < L.n_kt; ++t)
+        if (tseen[size_t(t)] != 1) fail("carry segment", 0, t);
+    return bad;
+}
+
 int main(int argc, char **argv) {
     int bad = check_tile_layout<16>("K d=128") + check_tile_layout<8>("K d=64 / v^T") +
               check_operand_reads<16>() + check_operand_reads<8>() + check_v_reads(64) +
@@ -398,6 +445,10 @@ int main(int argc, char **argv) {
                     bad += check_decode(B, H, Hkv, n, n, d, dv, 4, 4);
                 }
             }
+        for (int64_t cdv : {int64_t(64), int64_t(128), int64_t(256)}) {
+            bad += check_chain(B, H, n, cdv, 2);
+            if (cdv <= 128) bad += check_chain(B, H, n, cdv, 4);
+        }
         if (n <= 1100) {
             bad += check_exports(B, H, n, d, 2);
             bad += check_exports(B, H, n, d, 4);

@@ -71,6 +71,21 @@ def test_chain_small_in_full(n, dv, v_dtype):
     assert err <= TOL_CHAIN
 
 
+@pytest.mark.parametrize("dv,v_dtype", [(256, inputs.BF16), (192, inputs.BF16),
+                                        (128, inputs.F32), (320, inputs.F32)])
+def test_chain_value_widths(dv, v_dtype):
+    """Widths of the 16-byte aggregate (256 bf16, 128 fp32) and of the
+    per-channel fallback (192, 320), over ragged lengths and more tiles than
+    the carry fold has segments."""
+    announce(f"chain dv={dv} v={'f32' if v_dtype == inputs.F32 else 'bf16'}")
+    for n in (70, 1300):
+        inp = inputs.draw(1, 2, n, 64, seed=n + dv, v_dtype=v_dtype, dv=dv, u_range=(0.8, 1.0))
+        got = gpu_chain(inp, 1.0)
+        err = compare(inp, 1.0, got)
+        print(f"  n={n}: rel err {err:.3e}")
+        assert err <= TOL_CHAIN
+
+
 @pytest.mark.parametrize("g", [0.0, 0.5, 1.0, 2.5])
 def test_chain_gate_switch(g):
     announce(f"chain g={g}")
