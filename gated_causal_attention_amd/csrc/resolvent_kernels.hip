@@ -370,6 +370,18 @@ __device__ __forceinline__ int fresh_lane() {
     return l;
 }
 
+// A wave-uniform value the compiler must treat as new at each use, so that
+// values derived from it are recomputed there instead of held in scalar
+// registers through the loop.
+__device__ __forceinline__ int launder_s(int x) {
+    asm volatile("" : "+s"(x));
+    return x;
+}
+__device__ __forceinline__ int64_t launder_s64(int64_t x) {
+    asm volatile("" : "+s"(x));
+    return x;
+}
+
 // LDS byte address of a pointer into the workgroup's shared memory.
 __device__ __forceinline__ uint32_t lds_addr(const unsigned char *p) {
     return (uint32_t)(uintptr_t)(lds_void *)(p);
@@ -925,20 +937,22 @@ __global__ __launch_bounds__(NTHREADS, 1) void fwd_kernel(FwdArgs A) {
         const uint32_t buf = smem_lds + uint32_t((sg % NBUF) * SM::buf_bytes);
         if constexpr (!F32) {
             if (w < NCOPY) {
+                const int wl = launder_s(w);
                 if ((t + 1) * BK <= n32) {
                     const unsigned char *kt = kh + int64_t(t) * (BK * D * 2);
 #pragma unroll
                     for (int i = 0; i < SM::KCH / NCOPY; ++i)
                         g2lds16(kt + 1024 * NCOPY * i, k_lane,
-                                buf + uint32_t((w + NCOPY * i) * 1024));
+                                buf + uint32_t((wl + NCOPY * i) * 1024));
                 } else {
-                    stage_async<F32, D, DV>(A, buf, kh, vh, t, true, w);
+                    stage_async<F32, D, DV>(A, buf, kh, vh, t, true, wl);
                 }
                 const unsigned char *vt = vh + int64_t(t) * (BK * 2);
+                const int64_t np = launder_s64(A.n_pad);
 #pragma unroll
                 for (int i = 0; i < SM::VINS / NCOPY; ++i)
-                    g2lds16(vt + int64_t(16 * NCOPY * i) * A.n_pad, v_lane,
-                            buf + uint32_t(SM::k_bytes + (w + NCOPY * i) * 1024));
+                    g2lds16(vt + int64_t(16 * NCOPY * i) * np, v_lane,
+                            buf + uint32_t(SM::k_bytes + (wl + NCOPY * i) * 1024));
             }
         } else {
             stage_async<F32, D, DV>(A, buf, kh, vh, t, false, w);
