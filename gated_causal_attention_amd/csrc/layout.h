@@ -49,9 +49,11 @@ struct Layout {
 };
 
 // Hkv k/v heads (each shared by H/Hkv query heads) and dv value channels;
-// 0 means Hkv = H and dv = d.
+// 0 means Hkv = H and dv = d.  with_ctab = false leaves out the carry table
+// (its size grows with the square of the query tiles), for the calls that
+// use only the gates and their scans.
 inline Layout make_layout(int64_t B, int64_t H, int64_t n, int64_t d, bool bf16_path,
-                          int64_t Hkv = 0, int64_t dv = 0) {
+                          int64_t Hkv = 0, int64_t dv = 0, bool with_ctab = true) {
     Layout L;
     L.BH = B * H;
     L.n = n;
@@ -76,7 +78,7 @@ inline Layout make_layout(int64_t B, int64_t H, int64_t n, int64_t d, bool bf16_
         off = align_up(off + per_kt, 256);
     }
     L.ctab = off;
-    off = align_up(off + 16 * size_t(L.BH) * size_t(ctab_entries(L.n_qt)), 256);
+    if (with_ctab) off = align_up(off + 16 * size_t(L.BH) * size_t(ctab_entries(L.n_qt)), 256);
     const size_t per_qt = sizeof(uint32_t) * size_t(L.BH) * size_t(L.n_qt);
     L.qstat = off;
     off = align_up(off + per_qt, 256);
@@ -104,7 +106,7 @@ struct ChainLayout {
 
 inline ChainLayout make_chain_layout(int64_t B, int64_t H, int64_t n, int64_t dv) {
     ChainLayout C;
-    C.g = make_layout(B, H, n, dv, false);
+    C.g = make_layout(B, H, n, dv, false, 0, 0, false);
     C.dv = dv;
     const size_t per = 8 * size_t(C.g.BH) * size_t(C.g.n_kt) * size_t(dv);
     size_t off = C.g.total;
