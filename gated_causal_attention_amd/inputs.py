@@ -3,7 +3,7 @@
 This module holds no arithmetic of the method: it only draws random numbers,
 rounds them to the storage type of each workload and hands the same values to
 the HIP path and to the fp64 oracle.  The pages measure nothing on a dataset,
-so these draws stand in for the workloads (five shapes, see ``CONFIGS``).
+so these draws stand in for the workloads (five shapes, see ``WORKLOADS``).
 
 Draw order for a workload: q, k, v (``standard_normal(float32)`` over
 [B, H, n, d], then scaled), then u, then theta ([B, H, n]), all from
@@ -37,7 +37,7 @@ class Workload:
     description: str = ""
 
 
-CONFIGS = {
+WORKLOADS = {
     1: Workload(1, 1, 1, 256, 64, F32, F32, 1.0, "uniform", (0.0, 1.0), (-np.pi, np.pi),
                 ((1, 1, 0), (0, 1, 0), (0, 0, 1), (0.5, 0.7, 0.5)),
                 "single head, fp32; q,k scaled by 0.3 at the (0,1,0) corner"),
@@ -100,7 +100,7 @@ def make_config(idx: int, switches=None, seed=None, n=None, B=None, H=None):
     """Inputs of workload ``idx`` (seed = idx unless given).  ``switches``
     selects the workload-1 variant whose q,k are scaled by 0.3 at (0,1,0).
     ``n``/``B``/``H`` shrink the shape for tests while keeping the recipe."""
-    w = CONFIGS[idx]
+    w = WORKLOADS[idx]
     scale = w.qk_scale
     if idx == 1 and switches is not None and tuple(switches) == (0, 1, 0):
         scale = 0.3

@@ -26,7 +26,7 @@ def announce(*a):
 
 
 # ------------------------------------------------------------ small, in full
-@pytest.mark.parametrize("sw", inputs.CONFIGS[1].switches)
+@pytest.mark.parametrize("sw", inputs.WORKLOADS[1].switches)
 def test_workload1_fp32_corners(sw):
     announce("workload 1", sw)
     inp = inputs.make_config(1, switches=sw)
@@ -67,7 +67,7 @@ def test_switch_grid_multi_tile(sw):
 
 
 def test_workload2_full():
-    for sw in inputs.CONFIGS[2].switches:
+    for sw in inputs.WORKLOADS[2].switches:
         announce("workload 2", sw)
         inp = inputs.make_config(2)
         got = gu.gpu_forward(inp, sw)
@@ -113,7 +113,7 @@ def test_workload5_switch_sweep():
     rng = np.random.default_rng(5)
     heads = [(0, 0), (7, 31), (3, 12)]
     rows = gu.sample_rows(inp["n"], rng, extra=12)
-    for sw in inputs.CONFIGS[5].switches:
+    for sw in inputs.WORKLOADS[5].switches:
         announce("workload 5", sw)
         o_re, o_im = binding.resolvent_forward(t["q"], t["k"], t["u"], t["theta"], t["v"], *sw)
         got = o_re.double().cpu().numpy() + 1j * o_im.double().cpu().numpy()
