@@ -41,7 +41,7 @@ struct Layout {
     // that tile to the query tile, rounded to float, as (C_re, C_im, C_m, 0)
     // (float4 [BH][ctab_entries(n_qt)], query tile qt from ctab_entries(qt))
     size_t ctab = 0;
-    size_t qstat = 0, kstat = 0;  // per query tile max |q|, max |k| bits (uint32 [BH][n_qt])
+    size_t qstat = 0, kstat = 0;  // per head max |q|, max |k| bits (uint32 [BH])
     size_t noff = 0;  // per query tile: key tiles before it that the forward visits (int32 [BH][n_qt])
     size_t counters = 0;  // uint32 [2]: key tiles processed before the query tiles; spare
     size_t vt = 0;        // bf16 [BHkv][dv][n_pad], keys permuted inside groups of 16
@@ -81,9 +81,9 @@ inline Layout make_layout(int64_t B, int64_t H, int64_t n, int64_t d, bool bf16_
     if (with_ctab) off = align_up(off + 16 * size_t(L.BH) * size_t(ctab_entries(L.n_qt)), 256);
     const size_t per_qt = sizeof(uint32_t) * size_t(L.BH) * size_t(L.n_qt);
     L.qstat = off;
-    off = align_up(off + per_qt, 256);
+    off = align_up(off + sizeof(uint32_t) * size_t(L.BH), 256);
     L.kstat = off;
-    off = align_up(off + per_qt, 256);
+    off = align_up(off + sizeof(uint32_t) * size_t(L.BH), 256);
     L.noff = off;
     off = align_up(off + per_qt, 256);
     L.counters = off;

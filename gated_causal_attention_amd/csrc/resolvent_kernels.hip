@@ -752,7 +752,9 @@ __global__ __launch_bounds__(64) void schedule_kernel(const double *__restrict__
                                                       const double *__restrict__ tmm, int n_kt,
                                                       int n_qt, int32_t *__restrict__ noff,
                                                       float *__restrict__ ctab,
-                                                      int64_t ctab_head) {
+                                                      int64_t ctab_head,
+                                                      uint32_t *__restrict__ qstat,
+                                                      uint32_t *__restrict__ kstat) {
 #pragma clang fp contract(off)
     const int L = blockIdx.x;
     const int64_t bh = L / n_qt;
@@ -808,6 +810,10 @@ __global__ __launch_bounds__(64) void schedule_kernel(const double *__restrict__
         }
     }
     if (lane == 0) noff[L] = result;
+    if (qt == 0 && lane == 0) {  // the head's |q|, |k| extrema, folded in by fwd_kernel
+        qstat[bh] = 0u;
+        kstat[bh] = 0u;
+    }
 }
 
 // Weights W~ of one 32-key block as the B operand of O^T += V^T W~^T, per
@@ -1431,8 +1437,8 @@ __global__ __launch_bounds__(NTHREADS, 1) void fwd_kernel(FwdArgs A) {
     __syncthreads();
     if (tid == 0) {
         const uint32_t qb = misc[2], kb = misc[3];
-        A.qstat[bh * A.n_qt + qt] = qb;
-        A.kstat[bh * A.n_qt + qt] = kb;
+        atomicMax(&A.qstat[bh], qb);
+        atomicMax(&A.kstat[bh], kb);
         if (qb >= kInfBits || kb >= kInfBits) A.status[0] = kNonFinite;
         atomicAdd(&A.counters[0], uint32_t(n_off));
     }
@@ -1440,7 +1446,7 @@ __global__ __launch_bounds__(NTHREADS, 1) void fwd_kernel(FwdArgs A) {
 
 // --------------------------------------------------------------------------
 // Refusal of an overflowing logit (section "Evaluation and refusals").  The
-// extrema of |q| and |k| that fwd_kernel recorded bound every logit by
+// per-head extrema of |q| and |k| that fwd_kernel folded in bound every logit by
 // |c| d max|q| max|k|; only a head where that bound reaches the float32 range
 // recomputes its logits (with the same MFMA code and scale as fwd_kernel) and
 // checks every j <= i.
@@ -1454,11 +1460,7 @@ __global__ __launch_bounds__(NTHREADS) void logit_check_kernel(FwdArgs A) {
     const int64_t qt = A.n_qt - 1 - L / A.BH;
     const int64_t bh = L % A.BH;
     if (tid == 0) {
-        uint32_t qm = 0, km = 0;
-        for (int t = 0; t < A.n_qt; ++t) {
-            qm = max(qm, A.qstat[bh * A.n_qt + t]);
-            km = max(km, A.kstat[bh * A.n_qt + t]);
-        }
+        const uint32_t qm = A.qstat[bh], km = A.kstat[bh];
         const double bound = fabs((double)A.c) * (double)D * (double)__uint_as_float(qm) *
                              (double)__uint_as_float(km) * 1.01;
         go = !(bound < 3.0e38);
@@ -1552,7 +1554,9 @@ int launch_typed(const Problem &P, hipStream_t st, hipEvent_t const *marks) {
     int32_t *noff = reinterpret_cast<int32_t *>(ws + L.noff);
     float *ctab = reinterpret_cast<float *>(ws + L.ctab);
     hipLaunchKernelGGL(schedule_kernel, dim3(BH * L.n_qt), dim3(64), 0, st, G.t_re, G.t_im,
-                       G.t_m, (int)L.n_kt, (int)L.n_qt, noff, ctab, ctab_entries(L.n_qt));
+                       G.t_m, (int)L.n_kt, (int)L.n_qt, noff, ctab, ctab_entries(L.n_qt),
+                       reinterpret_cast<uint32_t *>(ws + L.qstat),
+                       reinterpret_cast<uint32_t *>(ws + L.kstat));
 
     FwdArgs F;
     F.q = P.q;
