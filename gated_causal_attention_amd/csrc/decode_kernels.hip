@@ -15,7 +15,8 @@
 //                         online shift and their V contraction -> partial
 //                         (M, z, O) and the chunk product P_c; clears the
 //                         status word (block 0)
-//   decode_merge_kernel   one workgroup per head: the carries C_c by a suffix
+//   decode_merge_kernel   one workgroup per head (decode_merge_small_kernel
+//                         for heads of few chunks): the carries C_c by a suffix
 //                         scan of the chunk products, then
 //                         O = sum_c C_c 2^(M_c - M) O_c, z likewise with |C_c|,
 //                         scaled by exp2((1-beta) M) z^-beta; sets the status
@@ -364,6 +365,120 @@ __global__ __launch_bounds__(64 * MW) void decode_merge_kernel(DecodeArgs A) {
     }
 }
 
+// The same merge for a head of at most NG NX chunks (NG = 256 / DV chunk
+// groups): every load it needs -- the chunk products and headers (one chunk
+// per thread) and this thread's channel of each of its NX chunks' partials --
+// is issued first, so the merge takes one trip to memory; the carries come
+// from a suffix scan across the threads (lanes, then waves through LDS), and
+// the scales go through LDS.
+template <int DV, int NX>
+__global__ __launch_bounds__(64 * MW) void decode_merge_small_kernel(DecodeArgs A) {
+    constexpr int NT = 64 * MW, NG = NT / DV;
+    constexpr int64_t PF = dec_part_floats(DV);
+    static_assert(NG * NX <= NT, "one chunk per thread");
+    __shared__ double wtot[3][MW];
+    __shared__ float red[MW];
+    __shared__ float4 sc_s[NG * NX];
+    __shared__ float ore_s[NG][DV], oim_s[NG][DV];
+    __shared__ float zs[NG];
+    const int tid = threadIdx.x, lane = tid % 64, w = tid / 64;
+    const int64_t bh = blockIdx.x;
+    const int n_ch = A.n_ch;
+    const int64_t base = bh * n_ch;
+    const float *p0 = A.part + base * PF;
+    const int r = tid / DV, chn = tid % DV;
+    // ---- every load, up front ---------------------------------------------
+    const bool mine = tid < n_ch;  // thread tid owns chunk tid
+    Cg q = cg_one();
+    float4 hd = make_float4(-INFINITY, 0.f, 0.f, 0.f);
+    if (mine) {
+        q = Cg{A.p_re[base + tid], A.p_im[base + tid], A.p_m[base + tid]};
+        hd = *reinterpret_cast<const float4 *>(p0 + tid * PF);
+    }
+    float ar[NX], ai[NX], zc[NX];
+#pragma unroll
+    for (int x = 0; x < NX; ++x) {
+        const int c = r + NG * x;
+        const bool ok = c < n_ch;
+        const float *pc = p0 + (ok ? c : 0) * PF;
+        ar[x] = ok ? pc[4 + chn] : 0.f;
+        ai[x] = ok ? pc[4 + DV + chn] : 0.f;
+        zc[x] = ok ? pc[1] : 0.f;
+    }
+    // ---- carries: C_c = the product of the chunk products after c -----------
+    Cg incl = q;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {  // inclusive suffix inside the wave
+        const Cg x = cg_down(incl, o);
+        if (lane + o < 64) incl = cg_mul(incl, x);
+    }
+    if (lane == 0) {
+        wtot[0][w] = incl.re;
+        wtot[1][w] = incl.im;
+        wtot[2][w] = incl.m;
+    }
+    __syncthreads();
+    Cg C = cg_down(incl, 1);
+    if (lane == 63) C = cg_one();
+    for (int v = w + 1; v < MW; ++v) C = cg_mul(C, Cg{wtot[0][v], wtot[1][v], wtot[2][v]});
+    // ---- the shift over the chunks that reach position i, and refusals -------
+    float Mh = (mine && C.m > 0.0) ? hd.x : -INFINITY;
+    const bool refused_here = mine && hd.z != 0.f;
+    Mh = wave_max(Mh);
+    if (lane == 0) red[w] = Mh;
+    const bool refused = __syncthreads_or(refused_here);
+    Mh = red[0];
+#pragma unroll
+    for (int v = 1; v < MW; ++v) Mh = fmaxf(Mh, red[v]);
+    if (refused) {
+        if (tid == 0) A.status[0] = kDecNonFinite;
+        return;  // the outputs are unspecified
+    }
+    if (mine) {
+        float4 sc = make_float4(0.f, 0.f, 0.f, 0.f);
+        if (C.m > 0.0 && hd.x != -INFINITY) {
+            const double e = (double)exp2f(hd.x - Mh);
+            sc = make_float4(float(C.re * e), float(C.im * e), float(C.m * e), 0.f);
+        }
+        sc_s[tid] = sc;
+    }
+    __syncthreads();
+    // ---- O = sum_c s_c O_c, z = sum_c |s_c| z_c ------------------------------
+    float hre = 0.f, him = 0.f, zh = 0.f;
+#pragma unroll
+    for (int x = 0; x < NX; ++x) {
+        const int c = r + NG * x;
+        if (c < n_ch) {
+            const float4 sc = sc_s[c];
+            hre = fmaf(sc.x, ar[x], fmaf(-sc.y, ai[x], hre));
+            him = fmaf(sc.x, ai[x], fmaf(sc.y, ar[x], him));
+            zh = fmaf(sc.z, zc[x], zh);
+        }
+    }
+    ore_s[r][chn] = hre;
+    oim_s[r][chn] = him;
+    if (chn == 0) zs[r] = zh;
+    __syncthreads();
+    if (tid < DV) {
+        float sr = 0.f, si = 0.f, z = 0.f;
+#pragma unroll
+        for (int g = 0; g < NG; ++g) {
+            sr += ore_s[g][tid];
+            si += oim_s[g][tid];
+            z += zs[g];
+        }
+        float f;
+        if (A.beta_mode == 1)
+            f = 1.0f / z;
+        else if (A.beta_mode == 0)
+            f = exp2f(Mh);
+        else
+            f = exp2f(A.one_minus_beta * Mh - A.beta * log2f(z));
+        A.o_re[bh * DV + tid] = sr * f;
+        A.o_im[bh * DV + tid] = si * f;
+    }
+}
+
 template <bool F32>
 __device__ __forceinline__ float load_e(const void *p, int64_t i) {
     if constexpr (F32) {
@@ -452,7 +567,14 @@ int launch_decode(const DecodeLayout &DL, const void *q, const void *k, const fl
         case 15: launch_part<true, true, 128, 128>(A, st, BH); break;
         default: return (int)hipErrorInvalidValue;
     }
-    if (DL.dv == 128)
+    // heads of few chunks (up to 16 per chunk group) take the one-trip merge
+    if (DL.dv == 128 && DL.n_ch <= 2 * 16)
+        hipLaunchKernelGGL((decode_merge_small_kernel<128, 16>), dim3((unsigned)BH), dim3(64 * MW),
+                           0, st, A);
+    else if (DL.dv == 64 && DL.n_ch <= 4 * 16)
+        hipLaunchKernelGGL((decode_merge_small_kernel<64, 16>), dim3((unsigned)BH), dim3(64 * MW),
+                           0, st, A);
+    else if (DL.dv == 128)
         hipLaunchKernelGGL(decode_merge_kernel<128>, dim3((unsigned)BH), dim3(64 * MW), 0, st, A);
     else
         hipLaunchKernelGGL(decode_merge_kernel<64>, dim3((unsigned)BH), dim3(64 * MW), 0, st, A);

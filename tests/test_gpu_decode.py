@@ -196,6 +196,18 @@ def test_decode_headline_shape():
     assert err <= TOL_DEC
 
 
+@pytest.mark.parametrize("n,dv", [(20000, 64), (8192, 128), (16384, 64), (8193, 128)])
+def test_decode_merge_paths(n, dv):
+    """Heads of up to 32 (dv = 128) or 64 (dv = 64) chunks take the one-trip
+    merge, longer ones the general merge: both sides of each boundary."""
+    announce(f"decode merge path n={n} dv={dv}")
+    inp = decode_inputs(1, 2, 1, n, 128, dv, seed=n + dv, u_range=(0.995, 1.0), qk_scale=0.3)
+    got = gpu_decode(inp, (1, 1, 1))
+    err = decode_err(inp, (1, 1, 1), got)
+    print(f"  rel err {err:.3e}")
+    assert err <= TOL_DEC
+
+
 def test_decode_long_cache():
     """n = 32768 with slowly decaying gates (u in (0.999, 1)): far keys keep
     weight, so the chunks' partial sums and their merge all matter."""
