@@ -1189,35 +1189,99 @@ __global__ __launch_bounds__(NTHREADS, 1) void fwd_kernel(FwdArgs A) {
     // the block holds a dead column or the wave a dead row
     auto vstep_off = [&](const unsigned char *buf, int kb, bool masked) __attribute__((always_inline)) {
         const float *side = reinterpret_cast<const float *>(buf + SM::side_off);
-        if (!QKZ && masked) {
+        if constexpr (F32) {
+            if (!QKZ && masked) {
+#pragma unroll
+                for (int kc = 0; kc < 2; ++kc) {
+                    const float4 m0 =
+                        *reinterpret_cast<const float4 *>(side + 2 * BK + kb + 16 * kc + 8 * h);
+                    const float4 m1 =
+                        *reinterpret_cast<const float4 *>(side + 2 * BK + kb + 16 * kc + 8 * h + 4);
+                    const float mm[8] = {m0.x, m0.y, m0.z, m0.w, m1.x, m1.y, m1.z, m1.w};
+#pragma unroll
+                    for (int e = 0; e < 8; ++e)
+                        x[8 * kc + e] = (mm[e] > 0.0f && row_live) ? x[8 * kc + e] : dead_s;
+                }
+            }
+            const float msub = block_shift();
 #pragma unroll
             for (int kc = 0; kc < 2; ++kc) {
-                const float4 m0 =
-                    *reinterpret_cast<const float4 *>(side + 2 * BK + kb + 16 * kc + 8 * h);
-                const float4 m1 =
-                    *reinterpret_cast<const float4 *>(side + 2 * BK + kb + 16 * kc + 8 * h + 4);
-                const float mm[8] = {m0.x, m0.y, m0.z, m0.w, m1.x, m1.y, m1.z, m1.w};
+                float fre[8], fim[8], fm[8];
+                const int s0 = kb + 16 * kc + 8 * h;
 #pragma unroll
-                for (int e = 0; e < 8; ++e)
-                    x[8 * kc + e] = (mm[e] > 0.0f && row_live) ? x[8 * kc + e] : dead_s;
+                for (int e = 0; e < 8; e += 4) {
+                    const float4 a = *reinterpret_cast<const float4 *>(side + s0 + e);
+                    const float4 b = *reinterpret_cast<const float4 *>(side + BK + s0 + e);
+                    const float4 c = *reinterpret_cast<const float4 *>(side + 2 * BK + s0 + e);
+                    fre[e] = a.x; fre[e + 1] = a.y; fre[e + 2] = a.z; fre[e + 3] = a.w;
+                    fim[e] = b.x; fim[e + 1] = b.y; fim[e + 2] = b.z; fim[e + 3] = b.w;
+                    fm[e] = c.x; fm[e + 1] = c.y; fm[e + 2] = c.z; fm[e + 3] = c.w;
+                }
+                weights(buf, kb, kc, msub, fre, fim, fm, !masked, row_live);
+                __builtin_amdgcn_sched_barrier(0);  // one chunk's side data at a time
             }
-        }
-        const float msub = block_shift();
+        } else {
+            // The side data of the lane's keys (T_re, T_im, R_T; planes BK floats
+            // apart; chunk kc at float 16 kc), the first chunk's requested before
+            // the shift and the second's while the first chunk's weights form, so
+            // that their LDS latency overlaps arithmetic.  (Volatile 16-byte
+            // reads: the compiler would otherwise split them and wait for each.)
+            typedef float v4f __attribute__((ext_vector_type(4)));
+            typedef __attribute__((address_space(3))) const v4f lds_v4f;
+            lds_v4f *sv = (lds_v4f *)(lds_void *)(side + kb + 8 * h);
+#define RD128(r, off) r = __builtin_nontemporal_load(sv + (off) / 16)
+            auto unpack = [](const v4f &a, const v4f &b, float (&o)[8]) __attribute__((always_inline)) {
+                o[0] = a.x; o[1] = a.y; o[2] = a.z; o[3] = a.w;
+                o[4] = b.x; o[5] = b.y; o[6] = b.z; o[7] = b.w;
+            };
+            v4f a0, a1, b0, b1, c0, c1;
+            __builtin_amdgcn_sched_barrier(0);
+            RD128(a0, 0); RD128(a1, 16); RD128(b0, 4 * BK); RD128(b1, 4 * BK + 16); RD128(c0, 8 * BK); RD128(c1, 8 * BK + 16);
+            __builtin_amdgcn_sched_barrier(0);
+            if (!QKZ && masked) {
+                v4f m0, m1;
+                RD128(m0, 8 * BK + 64); RD128(m1, 8 * BK + 80);
+                float fm0[8], fm1[8];
+                unpack(c0, c1, fm0);
+                unpack(m0, m1, fm1);
 #pragma unroll
-        for (int kc = 0; kc < 2; ++kc) {
+                for (int e = 0; e < 8; ++e) {
+                    x[e] = (fm0[e] > 0.0f && row_live) ? x[e] : dead_s;
+                    x[8 + e] = (fm1[e] > 0.0f && row_live) ? x[8 + e] : dead_s;
+                }
+            }
+            const float msub = block_shift();
+            __builtin_amdgcn_sched_barrier(0);
             float fre[8], fim[8], fm[8];
-            const int s0 = kb + 16 * kc + 8 * h;
+            unpack(a0, a1, fre);
+            unpack(b0, b1, fim);
+            unpack(c0, c1, fm);
+            float ex[8];
 #pragma unroll
-            for (int e = 0; e < 8; e += 4) {
-                const float4 a = *reinterpret_cast<const float4 *>(side + s0 + e);
-                const float4 b = *reinterpret_cast<const float4 *>(side + BK + s0 + e);
-                const float4 c = *reinterpret_cast<const float4 *>(side + 2 * BK + s0 + e);
-                fre[e] = a.x; fre[e + 1] = a.y; fre[e + 2] = a.z; fre[e + 3] = a.w;
-                fim[e] = b.x; fim[e + 1] = b.y; fim[e + 2] = b.z; fim[e + 3] = b.w;
-                fm[e] = c.x; fm[e + 1] = c.y; fm[e + 2] = c.z; fm[e + 3] = c.w;
+            for (int e = 0; e < 8; ++e) {
+                if constexpr (QKZ)
+                    ex[e] = (!masked || (fm[e] > 0.0f && row_live)) ? 1.0f : 0.0f;
+                else
+                    ex[e] = __builtin_amdgcn_exp2f(fmaf(x[e], A.c, -msub));
+                z += ex[e] * fm[e];
             }
-            weights(buf, kb, kc, msub, fre, fim, fm, !masked, row_live);
-            __builtin_amdgcn_sched_barrier(0);  // one chunk's side data at a time
+            __builtin_amdgcn_sched_barrier(0);
+            RD128(a0, 64); RD128(a1, 80); RD128(b0, 4 * BK + 64); RD128(b1, 4 * BK + 80);
+            __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                wk.r[0][e] = (__bf16)(ex[e] * fre[e]);
+                wk.i[0][e] = (__bf16)(ex[e] * fim[e]);
+            }
+            __builtin_amdgcn_sched_barrier(0);
+            RD128(c0, 8 * BK + 64); RD128(c1, 8 * BK + 80);
+            __builtin_amdgcn_sched_barrier(0);
+            unpack(a0, a1, fre);
+            unpack(b0, b1, fim);
+            unpack(c0, c1, fm);
+            weights(buf, kb, 1, msub, fre, fim, fm, !masked, row_live);
+            __builtin_amdgcn_sched_barrier(0);
+#undef RD128
         }
     };
     // vector step of a block of the query tile's own keys: explicit G_ij by a
