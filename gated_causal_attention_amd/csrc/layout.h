@@ -43,6 +43,7 @@ struct Layout {
     size_t ctab = 0;
     size_t qstat = 0, kstat = 0;  // per head max |q|, max |k| bits (uint32 [BH])
     size_t noff = 0;  // per query tile: key tiles before it that the forward visits (int32 [BH][n_qt])
+    size_t gbad = 0;  // per query tile: 1 if its gates saw a refused input (int32 [BH][n_qt])
     size_t counters = 0;  // uint32 [2]: key tiles processed before the query tiles; spare
     size_t vt = 0;        // bf16 [BHkv][dv][n_pad], keys permuted inside groups of 16
     size_t total = 0;
@@ -85,6 +86,8 @@ inline Layout make_layout(int64_t B, int64_t H, int64_t n, int64_t d, bool bf16_
     L.kstat = off;
     off = align_up(off + sizeof(uint32_t) * size_t(L.BH), 256);
     L.noff = off;
+    off = align_up(off + per_qt, 256);
+    L.gbad = off;
     off = align_up(off + per_qt, 256);
     L.counters = off;
     off = align_up(off + 2 * sizeof(uint32_t), 256);

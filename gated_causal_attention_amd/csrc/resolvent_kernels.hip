@@ -20,8 +20,8 @@
 // order the page's "Rust API" section fixes.
 //
 // Kernels, in launch order on the caller's stream:
-//   vt_kernel / clear_status_kernel  status := OK; (bf16 path) v -> bf16 v^T
-//   gates_kernel                     blend + gate in f64, in-tile scans
+//   prep_kernel                      status := OK; blend + gate in f64 and the
+//                                    in-tile scans; (bf16 path) v -> bf16 v^T
 //   schedule_kernel                  key tiles each query tile visits, and
 //                                    the carried product C_t of each visit
 //   fwd_kernel                       the fused forward (MFMA)
@@ -74,7 +74,8 @@ __device__ __forceinline__ uint32_t absbits_f4(float4 v) {
 }
 
 // --------------------------------------------------------------------------
-// Status and counter clear (fp32 path; the bf16 path clears them in vt_kernel).
+// Status and counter clear (before the gates alone, which the chain-corner
+// scan runs).
 __global__ void clear_status_kernel(int32_t *status, uint32_t *counters) {
     if (threadIdx.x == 0) status[0] = 0;
     if (threadIdx.x < 2) counters[threadIdx.x] = 0;
@@ -82,20 +83,15 @@ __global__ void clear_status_kernel(int32_t *status, uint32_t *counters) {
 
 // --------------------------------------------------------------------------
 // v [BH][n][D] (bf16 or fp32) -> v^T [BH][D][n_pad] bf16, keys stored in
-// perm16 order inside each group of 16 and zero past n.  Block 0 also clears
-// the status word and the counters (this kernel runs first on the bf16 path).
+// perm16 order inside each group of 16 and zero past n.
+// One key tile of one k/v head per 256-thread block (tile index blk).
 template <int D, bool VF32>
-__global__ __launch_bounds__(256) void vt_kernel(const void *__restrict__ v,
-                                                  uint16_t *__restrict__ vt, int64_t n,
-                                                  int64_t n_pad, int n_kt,
-                                                  int32_t *__restrict__ status,
-                                                  uint32_t *__restrict__ counters) {
+__device__ __forceinline__ void vt_tile(const void *__restrict__ v, uint16_t *__restrict__ vt,
+                                        int64_t n, int64_t n_pad, int n_kt, int64_t blk) {
     __shared__ __align__(16) uint16_t tile[D][BK + 8];
     const int tid = threadIdx.x;
-    if (blockIdx.x == 0 && tid == 0) status[0] = 0;
-    if (blockIdx.x == 0 && tid < 2) counters[tid] = 0;
-    const int64_t bh = blockIdx.x / n_kt;
-    const int64_t kt = blockIdx.x % n_kt;
+    const int64_t bh = blk / n_kt;
+    const int64_t kt = blk % n_kt;
     for (int c = tid; c < BK * D / 8; c += 256) {
         const int key = c / (D / 8), c8 = c % (D / 8);
         const int64_t p = kt * BK + key;
@@ -151,6 +147,7 @@ struct GatesArgs {
     int64_t n, n_pad;
     int64_t ldu;  // positions between heads in u, theta (>= n)
     int n_qt, n_kt;
+    int64_t BH;
     float *a_re, *a_im, *a_m, *s_re, *s_im, *s_m, *p_re, *p_im, *p_m;
     double *t_re, *t_im, *t_m;
     int32_t *status;
@@ -162,13 +159,12 @@ __device__ __forceinline__ void cmul_d(double xr, double xi, double yr, double y
     i = xr * yi + xi * yr;
 }
 
-__global__ __launch_bounds__(64) void gates_kernel(GatesArgs A) {
+// One query tile qt of head bh on one wave (lane 0..63); returns whether this
+// lane saw a refused input.
+__device__ __forceinline__ bool gates_tile(const GatesArgs &A, int64_t bh, int64_t qt, int lane) {
 #pragma clang fp contract(off)
     constexpr int PPL = BQ / 64;
     constexpr int SEG = BK / PPL;  // lanes per key tile
-    const int lane = threadIdx.x;
-    const int64_t bh = blockIdx.x / A.n_qt;
-    const int64_t qt = blockIdx.x % A.n_qt;
     const int64_t p0 = qt * BQ + PPL * lane;
     double ar[PPL], ai[PPL], am[PPL];
     bool bad = false;
@@ -191,7 +187,6 @@ __global__ __launch_bounds__(64) void gates_kernel(GatesArgs A) {
             am[e] = 1.0;
         }
     }
-    if (bad) A.status[0] = kNonFinite;
 
     // inclusive prefix inside the query tile
     double lr[PPL], li[PPL], lm[PPL];
@@ -277,6 +272,39 @@ __global__ __launch_bounds__(64) void gates_kernel(GatesArgs A) {
         A.t_re[bh * A.n_kt + kt] = xr;
         A.t_im[bh * A.n_kt + kt] = xi;
         A.t_m[bh * A.n_kt + kt] = xm;
+    }
+    return bad;
+}
+
+// One wave per query tile.
+__global__ __launch_bounds__(64) void gates_kernel(GatesArgs A) {
+    if (gates_tile(A, blockIdx.x / A.n_qt, blockIdx.x % A.n_qt, threadIdx.x))
+        A.status[0] = kNonFinite;
+}
+
+// The forward pass's first launch: clears the status word and the counters
+// (block 0), runs the gates of four query tiles per block in blocks
+// [0, ngb) -- a refusal is noted in gbad[query tile], always written, which
+// schedule_kernel folds into the status word -- and (bf16 path) the v^T tiles
+// in the blocks after them, so that the latency-bound gate scans overlap the
+// bandwidth-bound transpose.
+template <int D, bool VF32, bool VT>
+__global__ __launch_bounds__(256) void prep_kernel(GatesArgs G, int ngb, int32_t *__restrict__ gbad,
+                                                   const void *__restrict__ v,
+                                                   uint16_t *__restrict__ vt, int n_kt,
+                                                   uint32_t *__restrict__ counters) {
+    const int tid = threadIdx.x;
+    if (blockIdx.x == 0 && tid == 0) G.status[0] = 0;
+    if (blockIdx.x == 0 && tid < 2) counters[tid] = 0;
+    if ((int)blockIdx.x < ngb) {
+        const int64_t tq = 4 * int64_t(blockIdx.x) + (tid >> 6);  // query tile, all heads
+        if (tq < G.BH * G.n_qt) {
+            const bool bad = gates_tile(G, tq / G.n_qt, tq % G.n_qt, tid & 63);
+            const bool any_bad = __any(bad);
+            if ((tid & 63) == 0) gbad[tq] = any_bad ? 1 : 0;
+        }
+    } else if constexpr (VT) {
+        vt_tile<D, VF32>(v, vt, G.n, G.n_pad, n_kt, int64_t(blockIdx.x) - ngb);
     }
 }
 
@@ -754,9 +782,12 @@ __global__ __launch_bounds__(64) void schedule_kernel(const double *__restrict__
                                                       float *__restrict__ ctab,
                                                       int64_t ctab_head,
                                                       uint32_t *__restrict__ qstat,
-                                                      uint32_t *__restrict__ kstat) {
+                                                      uint32_t *__restrict__ kstat,
+                                                      const int32_t *__restrict__ gbad,
+                                                      int32_t *__restrict__ status) {
 #pragma clang fp contract(off)
     const int L = blockIdx.x;
+    if (threadIdx.x == 0 && gbad[L] != 0) status[0] = kNonFinite;  // the query tile's gates
     const int64_t bh = L / n_qt;
     const int qt = L % n_qt;
     const int lane = threadIdx.x;
@@ -1575,6 +1606,7 @@ GatesArgs gates_args(const Layout &L, const float *u, const float *theta, double
     G.ldu = L.n;
     G.n_qt = (int)L.n_qt;
     G.n_kt = (int)L.n_kt;
+    G.BH = L.BH;
     G.a_re = fptr(0);
     G.a_im = fptr(1);
     G.a_m = fptr(2);
@@ -1600,27 +1632,30 @@ int launch_typed(const Problem &P, hipStream_t st, hipEvent_t const *marks) {
     if (marks) (void)hipEventRecord(marks[0], st);
     const int BH = (int)L.BH;
 
-    if constexpr (!F32) {
-        uint16_t *vt = reinterpret_cast<uint16_t *>(ws + L.vt);
-        const unsigned vblocks = (unsigned)(L.BHkv * L.n_kt);  // one per k/v head and key tile
-        if (P.v_f32)
-            hipLaunchKernelGGL((vt_kernel<DV, true>), dim3(vblocks), dim3(256), 0, st, P.v, vt,
-                               L.n, L.n_pad, (int)L.n_kt, P.status, counters);
-        else
-            hipLaunchKernelGGL((vt_kernel<DV, false>), dim3(vblocks), dim3(256), 0, st, P.v, vt,
-                               L.n, L.n_pad, (int)L.n_kt, P.status, counters);
-    } else {
-        hipLaunchKernelGGL(clear_status_kernel, dim3(1), dim3(64), 0, st, P.status, counters);
-    }
-
+    // gates (four query tiles per block) and, on the bf16 path, v^T (one
+    // block per k/v head and key tile) in one launch
     const GatesArgs G = gates_args(L, P.u, P.theta, P.g, ws, P.status);
-    hipLaunchKernelGGL(gates_kernel, dim3(BH * L.n_qt), dim3(64), 0, st, G);
+    int32_t *gbad = reinterpret_cast<int32_t *>(ws + L.gbad);
+    const int ngb = (int)((BH * L.n_qt + 3) / 4);
+    uint16_t *vt = reinterpret_cast<uint16_t *>(ws + L.vt);
+    if constexpr (!F32) {
+        const unsigned blocks = (unsigned)(ngb + L.BHkv * L.n_kt);
+        if (P.v_f32)
+            hipLaunchKernelGGL((prep_kernel<DV, true, true>), dim3(blocks), dim3(256), 0, st, G,
+                               ngb, gbad, P.v, vt, (int)L.n_kt, counters);
+        else
+            hipLaunchKernelGGL((prep_kernel<DV, false, true>), dim3(blocks), dim3(256), 0, st, G,
+                               ngb, gbad, P.v, vt, (int)L.n_kt, counters);
+    } else {
+        hipLaunchKernelGGL((prep_kernel<DV, true, false>), dim3(ngb), dim3(256), 0, st, G, ngb,
+                           gbad, P.v, vt, (int)L.n_kt, counters);
+    }
     int32_t *noff = reinterpret_cast<int32_t *>(ws + L.noff);
     float *ctab = reinterpret_cast<float *>(ws + L.ctab);
     hipLaunchKernelGGL(schedule_kernel, dim3(BH * L.n_qt), dim3(64), 0, st, G.t_re, G.t_im,
                        G.t_m, (int)L.n_kt, (int)L.n_qt, noff, ctab, ctab_entries(L.n_qt),
                        reinterpret_cast<uint32_t *>(ws + L.qstat),
-                       reinterpret_cast<uint32_t *>(ws + L.kstat));
+                       reinterpret_cast<uint32_t *>(ws + L.kstat), gbad, P.status);
 
     FwdArgs F;
     F.q = P.q;
