@@ -83,53 +83,61 @@ __global__ void clear_status_kernel(int32_t *status, uint32_t *counters) {
 
 // --------------------------------------------------------------------------
 // v [BH][n][D] (bf16 or fp32) -> v^T [BH][D][n_pad] bf16, keys stored in
-// perm16 order inside each group of 16 and zero past n.
-// One key tile of one k/v head per 256-thread block (tile index blk).
+// perm16 order inside each group of 16 and zero past n.  A thread moves an
+// 8 x 8 block through its registers: the 8 keys of slots 8so..8so+7 (slot p
+// holds key perm64(p)) at the 8 channels of chunk c, read as 8 16-byte key
+// rows and written as 8 16-byte channel rows.  A wave reads 8 whole 128-byte
+// row halves and writes 8 whole 128-byte row segments per instruction; no LDS.
+// D threads per key tile, 256 / D tiles per 256-thread block (index blk).
 template <int D, bool VF32>
-__device__ __forceinline__ void vt_tile(const void *__restrict__ v, uint16_t *__restrict__ vt,
-                                        int64_t n, int64_t n_pad, int n_kt, int64_t blk) {
-    __shared__ __align__(16) uint16_t tile[D][BK + 8];
+__device__ __forceinline__ void vt_tiles(const void *__restrict__ v, uint16_t *__restrict__ vt,
+                                         int64_t n, int64_t n_pad, int n_kt, int64_t blk) {
     const int tid = threadIdx.x;
-    const int64_t bh = blk / n_kt;
-    const int64_t kt = blk % n_kt;
-    for (int c = tid; c < BK * D / 8; c += 256) {
-        const int key = c / (D / 8), c8 = c % (D / 8);
-        const int64_t p = kt * BK + key;
-        uint16_t vals[8];
+    const int64_t tl = blk * (256 / D) + tid / D;  // key tile over all k/v heads
+    const int r = tid % D;
+    const int so = r & 7, c = r >> 3;
+    const int64_t bh = tl / n_kt, kt = tl % n_kt;
+    uint32_t in[8][4];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        const int64_t p = kt * BK + perm64(8 * so + i);
         if (p < n) {
             if constexpr (VF32) {
-                const float *src = static_cast<const float *>(v) + (bh * n + p) * D + 8 * c8;
+                const float *src = static_cast<const float *>(v) + (bh * n + p) * D + 8 * c;
                 const float4 f0 = *reinterpret_cast<const float4 *>(src);
                 const float4 f1 = *reinterpret_cast<const float4 *>(src + 4);
                 const float fs[8] = {f0.x, f0.y, f0.z, f0.w, f1.x, f1.y, f1.z, f1.w};
 #pragma unroll
-                for (int e = 0; e < 8; ++e) {
-                    __bf16 b = (__bf16)fs[e];
-                    vals[e] = __builtin_bit_cast(uint16_t, b);
+                for (int e = 0; e < 4; ++e) {
+                    const uint32_t lo = __builtin_bit_cast(uint16_t, (__bf16)fs[2 * e]);
+                    const uint32_t hi = __builtin_bit_cast(uint16_t, (__bf16)fs[2 * e + 1]);
+                    in[i][e] = lo | (hi << 16);
                 }
             } else {
-                const uint16_t *src = static_cast<const uint16_t *>(v) + (bh * n + p) * D + 8 * c8;
-                const uint4 raw = *reinterpret_cast<const uint4 *>(src);
-                const uint32_t ws[4] = {raw.x, raw.y, raw.z, raw.w};
-#pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    vals[2 * e] = uint16_t(ws[e] & 0xFFFFu);
-                    vals[2 * e + 1] = uint16_t(ws[e] >> 16);
-                }
+                const uint4 raw = *reinterpret_cast<const uint4 *>(
+                    static_cast<const uint16_t *>(v) + (bh * n + p) * D + 8 * c);
+                in[i][0] = raw.x;
+                in[i][1] = raw.y;
+                in[i][2] = raw.z;
+                in[i][3] = raw.w;
             }
         } else {
 #pragma unroll
-            for (int e = 0; e < 8; ++e) vals[e] = 0;
+            for (int e = 0; e < 4; ++e) in[i][e] = 0u;
         }
-        const int slot = perm64(key);
-#pragma unroll
-        for (int e = 0; e < 8; ++e) tile[8 * c8 + e][slot] = vals[e];
     }
-    __syncthreads();
-    for (int c = tid; c < D * BK / 8; c += 256) {
-        const int d = c / (BK / 8), c8 = c % (BK / 8);
-        const uint4 val = *reinterpret_cast<const uint4 *>(&tile[d][8 * c8]);
-        *reinterpret_cast<uint4 *>(vt + (bh * D + d) * n_pad + kt * BK + 8 * c8) = val;
+    uint16_t *dst = vt + (bh * D + 8 * c) * n_pad + kt * BK + 8 * so;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+        // channel 8c+e of slots 8so..8so+7: the 16-bit half e%2 of word e/2
+        // of each key, two keys per word
+        const uint32_t sel = (e & 1) ? 0x07060302u : 0x05040100u;
+        uint4 o;
+        o.x = __builtin_amdgcn_perm(in[1][e / 2], in[0][e / 2], sel);
+        o.y = __builtin_amdgcn_perm(in[3][e / 2], in[2][e / 2], sel);
+        o.z = __builtin_amdgcn_perm(in[5][e / 2], in[4][e / 2], sel);
+        o.w = __builtin_amdgcn_perm(in[7][e / 2], in[6][e / 2], sel);
+        *reinterpret_cast<uint4 *>(dst + int64_t(e) * n_pad) = o;
     }
 }
 
@@ -304,7 +312,7 @@ __global__ __launch_bounds__(256) void prep_kernel(GatesArgs G, int ngb, int32_t
             if ((tid & 63) == 0) gbad[tq] = any_bad ? 1 : 0;
         }
     } else if constexpr (VT) {
-        vt_tile<D, VF32>(v, vt, G.n, G.n_pad, n_kt, int64_t(blockIdx.x) - ngb);
+        vt_tiles<D, VF32>(v, vt, G.n, G.n_pad, n_kt, int64_t(blockIdx.x) - ngb);
     }
 }
 
@@ -1632,14 +1640,15 @@ int launch_typed(const Problem &P, hipStream_t st, hipEvent_t const *marks) {
     if (marks) (void)hipEventRecord(marks[0], st);
     const int BH = (int)L.BH;
 
-    // gates (four query tiles per block) and, on the bf16 path, v^T (one
-    // block per k/v head and key tile) in one launch
+    // gates (four query tiles per block) and, on the bf16 path, v^T (256/dv
+    // key tiles per block; the key tiles of a head are a multiple of 4) in
+    // one launch
     const GatesArgs G = gates_args(L, P.u, P.theta, P.g, ws, P.status);
     int32_t *gbad = reinterpret_cast<int32_t *>(ws + L.gbad);
     const int ngb = (int)((BH * L.n_qt + 3) / 4);
     uint16_t *vt = reinterpret_cast<uint16_t *>(ws + L.vt);
     if constexpr (!F32) {
-        const unsigned blocks = (unsigned)(ngb + L.BHkv * L.n_kt);
+        const unsigned blocks = (unsigned)(ngb + L.BHkv * L.n_kt * DV / 256);
         if (P.v_f32)
             hipLaunchKernelGGL((prep_kernel<DV, true, true>), dim3(blocks), dim3(256), 0, st, G,
                                ngb, gbad, P.v, vt, (int)L.n_kt, counters);
