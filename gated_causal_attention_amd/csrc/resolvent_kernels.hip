@@ -1327,17 +1327,24 @@ __global__ __launch_bounds__(NTHREADS, 1) void fwd_kernel(FwdArgs A) {
     // running product per row, a_i a_{i-1} ... a_{j+1}, last key first; the
     // product restarts at 1 on the diagonal and is 0 above it
     auto vstep_own = [&](const unsigned char *buf, int kb, int dpos) __attribute__((always_inline)) {
+        // The block's gates a_{j+1} are the same for every lane: lane L holds
+        // those of key L mod 32 (one LDS read per plane), and each step of the
+        // chains takes its key's value from that lane into a scalar register,
+        // so the chains never wait on LDS.
         const float *side = reinterpret_cast<const float *>(buf + SM::side_off);
+        const int kl = kb + (lane & 31);
+        const float vre = side[kl], vim = side[BK + kl], vm = side[2 * BK + kl];
+        auto key_gate = [](float v, int j) __attribute__((always_inline)) {
+            return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), j));
+        };
         // pass 1: modulus R_{row,j} of the 16 keys this lane holds
         float Gm[16];
         const float gre0 = gre, gim0 = gim;
-        // (fences every four keys keep few side values live at a time)
 #pragma unroll
         for (int jj = 31; jj >= 0; --jj) {
-            const float nm = gm * side[2 * BK + kb + jj];
+            const float nm = gm * key_gate(vm, jj);
             gm = (jj == dpos) ? 1.0f : nm;
             if (h == ((jj >> 2) & 1)) Gm[4 * (jj >> 3) + (jj & 3)] = gm;
-            if ((jj & 3) == 0) __builtin_amdgcn_sched_barrier(0);
         }
         if constexpr (!QKZ) {
 #pragma unroll
@@ -1352,7 +1359,7 @@ __global__ __launch_bounds__(NTHREADS, 1) void fwd_kernel(FwdArgs A) {
             float fre[8], fim[8], fm[8];
 #pragma unroll
             for (int jj = 16 * kc + 15; jj >= 16 * kc; --jj) {
-                const float dr = side[kb + jj], di = side[BK + kb + jj];
+                const float dr = key_gate(vre, jj), di = key_gate(vim, jj);
                 const float nr = gre * dr - gim * di;
                 const float ni = gre * di + gim * dr;
                 const bool diag = (jj == dpos);
@@ -1363,7 +1370,6 @@ __global__ __launch_bounds__(NTHREADS, 1) void fwd_kernel(FwdArgs A) {
                     fre[e] = gre;
                     fim[e] = gim;
                 }
-                if ((jj & 3) == 0) __builtin_amdgcn_sched_barrier(0);
             }
 #pragma unroll
             for (int e = 0; e < 8; ++e) fm[e] = Gm[8 * kc + e];
