@@ -23,10 +23,6 @@ static_assert(BQ % BK == 0, "a query tile must hold whole key tiles");
 
 constexpr size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
-// Carry-table entries of the query tiles before query tile qt (query tile q
-// visits at most q*BQ/BK key tiles before itself).
-RESOLVENT_HD constexpr int64_t ctab_entries(int64_t qt) { return (BQ / BK) * qt * (qt - 1) / 2; }
-
 struct Layout {
     int64_t BH = 0, n = 0, d = 0;
     int64_t H = 0, Hkv = 0, BHkv = 0, dv = 0;  // query heads per batch entry; k/v heads;
@@ -36,11 +32,7 @@ struct Layout {
     // byte offsets into the workspace
     size_t gate[9] = {};  // a_re a_im a_m | s_re s_im s_m | p_re p_im p_m  (float [BH][n_pad])
     size_t tile[3] = {};  // A_re A_im A_m per key tile (double [BH][n_kt])
-    // per query tile qt and each key tile it visits before itself (visit s =
-    // key tile qt*BQ/BK - 1 - s): the carried gate product C from the end of
-    // that tile to the query tile, rounded to float, as (C_re, C_im, C_m, 0)
-    // (float4 [BH][ctab_entries(n_qt)], query tile qt from ctab_entries(qt))
-    size_t ctab = 0;
+    size_t tile4 = 0;     // the same packed, (A_re, A_im, A_m, 0) per key tile (double4 [BH][n_kt])
     size_t qstat = 0, kstat = 0;  // per head max |q|, max |k| bits (uint32 [BH])
     size_t noff = 0;  // per query tile: key tiles before it that the forward visits (int32 [BH][n_qt])
     size_t gbad = 0;  // per query tile: 1 if its gates saw a refused input (int32 [BH][n_qt])
@@ -50,11 +42,9 @@ struct Layout {
 };
 
 // Hkv k/v heads (each shared by H/Hkv query heads) and dv value channels;
-// 0 means Hkv = H and dv = d.  with_ctab = false leaves out the carry table
-// (its size grows with the square of the query tiles), for the calls that
-// use only the gates and their scans.
+// 0 means Hkv = H and dv = d.
 inline Layout make_layout(int64_t B, int64_t H, int64_t n, int64_t d, bool bf16_path,
-                          int64_t Hkv = 0, int64_t dv = 0, bool with_ctab = true) {
+                          int64_t Hkv = 0, int64_t dv = 0) {
     Layout L;
     L.BH = B * H;
     L.n = n;
@@ -78,8 +68,8 @@ inline Layout make_layout(int64_t B, int64_t H, int64_t n, int64_t d, bool bf16_
         L.tile[i] = off;
         off = align_up(off + per_kt, 256);
     }
-    L.ctab = off;
-    if (with_ctab) off = align_up(off + 16 * size_t(L.BH) * size_t(ctab_entries(L.n_qt)), 256);
+    L.tile4 = off;
+    off = align_up(off + 4 * per_kt, 256);
     const size_t per_qt = sizeof(uint32_t) * size_t(L.BH) * size_t(L.n_qt);
     L.qstat = off;
     off = align_up(off + sizeof(uint32_t) * size_t(L.BH), 256);
@@ -109,7 +99,7 @@ struct ChainLayout {
 
 inline ChainLayout make_chain_layout(int64_t B, int64_t H, int64_t n, int64_t dv) {
     ChainLayout C;
-    C.g = make_layout(B, H, n, dv, false, 0, 0, false);
+    C.g = make_layout(B, H, n, dv, false, 0, 0);
     C.dv = dv;
     const size_t per = 8 * size_t(C.g.BH) * size_t(C.g.n_kt) * size_t(dv);
     size_t off = C.g.total;

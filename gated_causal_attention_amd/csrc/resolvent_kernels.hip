@@ -158,6 +158,7 @@ struct GatesArgs {
     int64_t BH;
     float *a_re, *a_im, *a_m, *s_re, *s_im, *s_m, *p_re, *p_im, *p_m;
     double *t_re, *t_im, *t_m;
+    double *t4;  // (A_re, A_im, A_m, 0) per key tile
     int32_t *status;
 };
 
@@ -280,6 +281,11 @@ __device__ __forceinline__ bool gates_tile(const GatesArgs &A, int64_t bh, int64
         A.t_re[bh * A.n_kt + kt] = xr;
         A.t_im[bh * A.n_kt + kt] = xi;
         A.t_m[bh * A.n_kt + kt] = xm;
+        double *t4 = A.t4 + 4 * (bh * A.n_kt + kt);
+        t4[0] = xr;
+        t4[1] = xi;
+        t4[2] = xm;
+        t4[3] = 0.0;
     }
     return bad;
 }
@@ -323,8 +329,7 @@ struct FwdArgs {
     const uint16_t *vt;
     const float *a_re, *a_im, *a_m, *s_re, *s_im, *s_m, *p_re, *p_im, *p_m;
     const double *t_re, *t_im, *t_m;
-    const float *ctab;    // carried gate products of the visited key tiles
-    int64_t ctab_head;    // entries per head
+    const double *t4;     // (A_re, A_im, A_m, 0) per key tile [BH][n_kt]
     const float *gates;   // gate plane 0; plane k starts `plane` floats later
     int64_t plane;
     float *o_re, *o_im;
@@ -364,18 +369,20 @@ struct Smem {
     static constexpr size_t k_bytes = size_t(KCH) * BK * 16;
     static constexpr size_t v_bytes = F32 ? size_t(VKCH) * BK * 16 : size_t(VCH) * DV * 16;
     static constexpr size_t side_off = k_bytes + v_bytes;
-    // side data: 3 x BK floats; raw: S_j as 3 x BK floats and the tile's
-    // carried product C (C_re, C_im, C_m, 0) as floats; then 2 flag words
+    // side data: 3 x BK floats; raw: S_j as 3 x BK floats and the product of
+    // the tile's gates (A_re, A_im, A_m, 0) as doubles; then 2 flag words
     // (32-key block b of the staged tile holds a dead column)
     static constexpr size_t raw_off = side_off + 3 * BK * sizeof(float);
-    static constexpr size_t carry_off = raw_off + 3 * BK * sizeof(float);
-    static constexpr size_t flag_off = carry_off + 4 * sizeof(float);
+    static constexpr size_t tprod_off = raw_off + 3 * BK * sizeof(float);
+    static constexpr size_t flag_off = tprod_off + 4 * sizeof(double);
     static constexpr size_t buf_bytes = (flag_off + 16 + 255) / 256 * 256;
     // four buffers keep two tiles in flight while two are read, when they
     // fit into the 160 KB of LDS (not the larger fp32 tiles)
     static constexpr int NBUF = 4 * buf_bytes + 64 <= 160 * 1024 ? 4 : 2;
     static constexpr size_t misc_off = NBUF * buf_bytes;
-    static constexpr size_t bytes = misc_off + 8 * sizeof(uint32_t);
+    // the running carried product of the landings (3 doubles)
+    static constexpr size_t carry_off = misc_off + 8 * sizeof(uint32_t);
+    static constexpr size_t bytes = carry_off + 4 * sizeof(double);
     static_assert(KCH % NCOPY == 0 && VINS % NCOPY == 0, "whole wave copies");
 };
 
@@ -459,15 +466,16 @@ __device__ __forceinline__ void g2lds4(const unsigned char *base, uint32_t off, 
         : "memory");
 }
 
-// 16 bytes in lane 0 only (lane 0 reads base + off and writes lds; the other
-// lanes are masked off for the one instruction and restored).
-__device__ __forceinline__ void g2lds16x1(const unsigned char *base, uint32_t off, uint32_t lds) {
+// 16 bytes in each of lanes 0 and 1 (lane L reads base + off and writes
+// lds + 16 L; the other lanes are masked off for the one instruction and
+// restored).
+__device__ __forceinline__ void g2lds16x2(const unsigned char *base, uint32_t off, uint32_t lds) {
     const uint32_t la = __builtin_amdgcn_readfirstlane(lds);
     uint32_t saved;
     uint64_t ex;
     asm volatile(
         "s_mov_b64 %1, exec\n\t"
-        "s_mov_b64 exec, 1\n\t"
+        "s_mov_b64 exec, 3\n\t"
         "s_mov_b32 %0, m0\n\t"
         "s_mov_b32 m0, %4\n\t"
         "s_nop 0\n\t"
@@ -773,22 +781,21 @@ __device__ __forceinline__ void mstep_bf16(const unsigned char *bv, int kbv,
 constexpr float kLazy = 8.0f;
 
 // --------------------------------------------------------------------------
-// Visit count and carried gate products per query tile.  The key tiles before
-// query tile qt are visited last to first; visit s carries
+// Visit count per query tile.  The key tiles before query tile qt are
+// visited last to first; visit s carries
 //     C_s = A_{t0-1} A_{t0-2} ... A_{t0-s}   (C_0 = 1; A_t the whole-tile
 // product of key tile t, t0 the query tile's first key tile), the gate
 // product from the end of the visited tile up to the query tile.  C is
-// accumulated in f64 in visiting order and stored rounded to float; the
-// visits stop after the tile whose product makes the modulus of C zero in
-// float32: every key before it sits behind a closed gate (section "Object")
-// and is exactly dead.  One wave per query tile: the lanes fetch 64 tile
-// products at a time and the product is accumulated in order.
+// accumulated in f64 in visiting order (fwd_kernel repeats this recurrence
+// as it lands the tiles); the visits stop after the tile whose product makes
+// the modulus of C zero in float32: every key before it sits behind a closed
+// gate (section "Object") and is exactly dead.  One wave per query tile: the
+// lanes fetch 64 tile products at a time and the product is accumulated in
+// order.
 __global__ __launch_bounds__(64) void schedule_kernel(const double *__restrict__ tre,
                                                       const double *__restrict__ tim,
                                                       const double *__restrict__ tmm, int n_kt,
                                                       int n_qt, int32_t *__restrict__ noff,
-                                                      float *__restrict__ ctab,
-                                                      int64_t ctab_head,
                                                       uint32_t *__restrict__ qstat,
                                                       uint32_t *__restrict__ kstat,
                                                       const int32_t *__restrict__ gbad,
@@ -801,7 +808,6 @@ __global__ __launch_bounds__(64) void schedule_kernel(const double *__restrict__
     const int lane = threadIdx.x;
     const int t0 = qt * (BQ / BK);  // first key tile of the query tile
     const double *pr = tre + bh * n_kt, *pi = tim + bh * n_kt, *pm = tmm + bh * n_kt;
-    float *cq = ctab + 4 * (bh * ctab_head + ctab_entries(qt));
     double cr = 1.0, ci = 0.0, cm = 1.0;
     int result = t0;  // every tile before the query tile
     auto lane_f64 = [](double x, int s) {
@@ -816,14 +822,8 @@ __global__ __launch_bounds__(64) void schedule_kernel(const double *__restrict__
         const double ar = valid ? pr[t] : 1.0, ai = valid ? pi[t] : 0.0,
                      am = valid ? pm[t] : 1.0;
         const int cnt = min(64, t0 - base);
-        float mr = 0.f, mi = 0.f, mm = 0.f;  // C of this lane's visit
         int found = -1;
         for (int s = 0; s < cnt; ++s) {
-            if (lane == s) {
-                mr = (float)cr;
-                mi = (float)ci;
-                mm = (float)cm;
-            }
             const double xr = lane_f64(ar, s), xi = lane_f64(ai, s), xm = lane_f64(am, s);
             const double nr = xr * cr - xi * ci;
             const double ni = xr * ci + xi * cr;
@@ -834,14 +834,6 @@ __global__ __launch_bounds__(64) void schedule_kernel(const double *__restrict__
                 found = base + s + 1;
                 break;
             }
-        }
-        if (valid && (found < 0 || base + lane < found)) {
-            float4 e;
-            e.x = mr;
-            e.y = mi;
-            e.z = mm;
-            e.w = 0.f;
-            reinterpret_cast<float4 *>(cq)[base + lane] = e;
         }
         if (found >= 0) {
             result = found;
@@ -972,10 +964,10 @@ __global__ __launch_bounds__(NTHREADS, 1) void fwd_kernel(FwdArgs A) {
         k_lane = k_lane_off<D / 8>(w, lane);
         v_lane = vt_lane_off(A.n_pad, w, lane);
     }
-    // this head's S_j planes, a_{j+1} planes and the query tile's carry entries
+    // this head's S_j planes, a_{j+1} planes and tile products
+    const double *t4 = uniform_ptr(A.t4 + 4 * bh * A.n_kt);
     const float *gS = uniform_ptr(A.gates + 3 * A.plane + bh * A.n_pad);
     const float *gA = uniform_ptr(A.gates + bh * A.n_pad + 1);
-    const float *cq = uniform_ptr(A.ctab + 4 * (bh * A.ctab_head + ctab_entries(qt)));
     auto issue = [&](int sg) __attribute__((always_inline)) {
         if (sg >= n_tiles) return;
         const int t = tile_of(sg);
@@ -1011,34 +1003,57 @@ __global__ __launch_bounds__(NTHREADS, 1) void fwd_kernel(FwdArgs A) {
             g2lds4(reinterpret_cast<const unsigned char *>(g), lo, dst);
             g2lds4(reinterpret_cast<const unsigned char *>(g + A.plane), lo, dst + BK * 4);
             g2lds4(reinterpret_cast<const unsigned char *>(g + 2 * A.plane), lo, dst + 2 * BK * 4);
-            // the carried product of the visit (16 bytes, lane 0); an own
-            // tile copies 16 bytes of its gates instead (unused), so that
-            // every tile costs wave 0 the same copies
-            const float *cs = off ? cq + 4 * sg : g;
-            g2lds16x1(reinterpret_cast<const unsigned char *>(cs), 0u,
-                      buf + uint32_t(SM::carry_off));
+            // the product of the tile's gates (32 bytes, lanes 0 and 1; an own
+            // tile copies its own too, unused, so that every tile costs wave
+            // 0 the same copies)
+            g2lds16x2(reinterpret_cast<const unsigned char *>(t4 + 4 * t),
+                      uint32_t(fresh_lane() * 16), buf + uint32_t(SM::tprod_off));
         }
     };
     uint32_t kbits = 0;
     // Landing of tile sg, once this wave's copies of it are in.  Wave 0 forms
     // T_j = C S_j of its 64 keys (C the visit's carried product, rounded to
     // float; one float rounding per product, far below the bf16 rounding of
-    // the weights) with the dead flags.  For an own tile every copying wave
-    // takes the largest |k| of the K bytes it copied.
+    // the weights) with the dead flags.  C_s of visit s is accumulated by
+    // wave 0 in f64 with the recurrence and rounding of the visit-count scan
+    // (schedule_kernel): C_0 = 1, C_{s+1} = A_t C_s, A_t the product of the
+    // gates of visit s's key tile t (copied with the tile); the running value
+    // lives in LDS.  For an own tile every copying wave takes the largest |k|
+    // of the K bytes it copied.
+    double *cst = reinterpret_cast<double *>(smem + SM::carry_off);
     auto land = [&](int sg) __attribute__((always_inline)) {
         if (sg >= n_tiles) return;
         unsigned char *buf = tile_buf(sg);
         if (sg < n_off) {
             if (w == 0) {
+                const int ln = fresh_lane();
+                double c_re = 1.0, c_im = 0.0, c_m = 1.0;
+                if (sg > 0) {
+                    c_re = cst[0];
+                    c_im = cst[1];
+                    c_m = cst[2];
+                }
+                {
+#pragma clang fp contract(off)
+                    const double *at = reinterpret_cast<const double *>(buf + SM::tprod_off);
+                    const double ar = at[0], ai = at[1], am = at[2];
+                    const double nr = ar * c_re - ai * c_im;
+                    const double ni = ar * c_im + ai * c_re;
+                    const double nm = am * c_m;
+                    if (ln == 0) {
+                        cst[0] = nr;
+                        cst[1] = ni;
+                        cst[2] = nm;
+                    }
+                }
+                const float ccx = (float)c_re, ccy = (float)c_im, ccz = (float)c_m;
                 const float *raw = reinterpret_cast<const float *>(buf + SM::raw_off);
                 float *sd = reinterpret_cast<float *>(buf + SM::side_off);
-                const int ln = fresh_lane();
                 const float g0 = raw[ln], g1 = raw[BK + ln], g2 = raw[2 * BK + ln];
-                const float4 cc = *reinterpret_cast<const float4 *>(buf + SM::carry_off);
-                const float rt = cc.z * g2;
+                const float rt = ccz * g2;
                 const int slot = perm64(ln);
-                sd[slot] = cc.x * g0 - cc.y * g1;
-                sd[BK + slot] = cc.x * g1 + cc.y * g0;
+                sd[slot] = ccx * g0 - ccy * g1;
+                sd[BK + slot] = ccx * g1 + ccy * g0;
                 sd[2 * BK + slot] = rt;
                 const uint64_t dead = __ballot(rt == 0.0f);
                 if (ln == 0) {
@@ -1633,6 +1648,7 @@ GatesArgs gates_args(const Layout &L, const float *u, const float *theta, double
     G.t_re = dptr(0);
     G.t_im = dptr(1);
     G.t_m = dptr(2);
+    G.t4 = reinterpret_cast<double *>(ws + L.tile4);
     G.status = status;
     return G;
 }
@@ -1666,9 +1682,8 @@ int launch_typed(const Problem &P, hipStream_t st, hipEvent_t const *marks) {
                            gbad, P.v, vt, (int)L.n_kt, counters);
     }
     int32_t *noff = reinterpret_cast<int32_t *>(ws + L.noff);
-    float *ctab = reinterpret_cast<float *>(ws + L.ctab);
     hipLaunchKernelGGL(schedule_kernel, dim3(BH * L.n_qt), dim3(64), 0, st, G.t_re, G.t_im,
-                       G.t_m, (int)L.n_kt, (int)L.n_qt, noff, ctab, ctab_entries(L.n_qt),
+                       G.t_m, (int)L.n_kt, (int)L.n_qt, noff,
                        reinterpret_cast<uint32_t *>(ws + L.qstat),
                        reinterpret_cast<uint32_t *>(ws + L.kstat), gbad, P.status);
 
@@ -1689,8 +1704,7 @@ int launch_typed(const Problem &P, hipStream_t st, hipEvent_t const *marks) {
     F.t_re = G.t_re;
     F.t_im = G.t_im;
     F.t_m = G.t_m;
-    F.ctab = ctab;
-    F.ctab_head = ctab_entries(L.n_qt);
+    F.t4 = G.t4;
     F.gates = G.a_re;
     F.plane = int64_t(L.gate[1] - L.gate[0]) / int64_t(sizeof(float));
     F.o_re = P.o_re;

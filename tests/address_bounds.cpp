@@ -140,18 +140,17 @@ static int check(int64_t B, int64_t H, int64_t n, int64_t d, int esz, bool bf16_
                                             p, (long long)n, (long long)t, lane);
                         }
                     }
-    // the carried-product copies: visit s < qt*BQ/BK of query tile qt, 16 bytes
+    // the tile-product copies: lanes 0 and 1 read 16 bytes each of the
+    // key tile's (A_re, A_im, A_m, 0) doubles
     for (int64_t bh = 0; bh < L.BH; bh += (L.BH > 2 ? L.BH - 1 : 1))
-        for (int64_t qt = 0; qt < L.n_qt; ++qt)
-            for (int64_t sg = 0; sg < qt * (BQ / BK); ++sg) {
-                const int64_t e = bh * ctab_entries(L.n_qt) + ctab_entries(qt) + sg;
-                const int64_t off = int64_t(L.ctab) + 16 * e;
-                const bool own_head = e >= bh * ctab_entries(L.n_qt) &&
-                                      e < (bh + 1) * ctab_entries(L.n_qt);
-                const bool own_tile = sg < ctab_entries(qt + 1) - ctab_entries(qt);
-                if ((!own_head || !own_tile || off + 16 > int64_t(L.total)) && bad++ < 5)
-                    std::printf("carry entry out of range: n=%lld qt=%lld s=%lld\n",
-                                (long long)n, (long long)qt, (long long)sg);
+        for (int64_t t = 0; t < L.n_kt; ++t)
+            for (int lane = 0; lane < 2; ++lane) {
+                const int64_t off = int64_t(L.tile4) + 32 * (bh * L.n_kt + t) + 16 * lane;
+                if ((off < int64_t(L.tile4) || off + 16 > int64_t(L.tile4) + 32 * L.BH * L.n_kt ||
+                     off + 16 > int64_t(L.total)) &&
+                    bad++ < 5)
+                    std::printf("tile product out of range: n=%lld t=%lld lane=%d\n",
+                                (long long)n, (long long)t, lane);
             }
     return bad;
 }
