@@ -87,6 +87,12 @@ def test_workspace_sizes():
     off = binding.resolvent_counters_offset(4, 16, 8192, 128)
     assert 0 < off < ws(4, 16, 8192, 128)
     assert binding.resolvent_counters_offset(1, 1, 0, 64) == 2 ** 64 - 1
+    # linear in n: the carried products of the visits are not stored per visit,
+    # so a 4x longer sequence needs ~4x the workspace (not ~16x), and the
+    # longest accepted sequence stays within a few GB
+    s1, s4 = ws(1, 1, 1 << 18, 128), ws(1, 1, 1 << 20, 128)
+    assert 3.9 < s4 / s1 < 4.1
+    assert ws(1, 1, 1 << 22, 128) < 4 << 30
 
 
 def test_status_strings():
