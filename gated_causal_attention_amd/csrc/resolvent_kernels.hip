@@ -1126,7 +1126,10 @@ __global__ __launch_bounds__(NTHREADS, 1) void fwd_kernel(FwdArgs A) {
         }
     };
 
-    // ---- prologue: Q, the row's prefix product, the first tiles
+    // ---- prologue: the first tiles, Q, the row's prefix product (the copies
+    // first, so that their latency and that of the loads overlap)
+#pragma unroll
+    for (int sg = 0; sg < NBUF / 2; ++sg) issue(sg);
     typename FR::type qf[FR::count];
     const uint32_t qbits = load_q<F32, D>(A, bh, row, row_ok, h, qf);
     // a row whose prefix inside the query tile holds a closed gate sees no
@@ -1135,8 +1138,6 @@ __global__ __launch_bounds__(NTHREADS, 1) void fwd_kernel(FwdArgs A) {
     const float prow_m = A.p_m[gbase + row];
     const bool row_live = !(prow_m == 0.0f);
     const bool wave_dead_rows = __any(!row_live);
-#pragma unroll
-    for (int sg = 0; sg < NBUF / 2; ++sg) issue(sg);
     wait_vmcnt<0>();
     land(0);
     lds_barrier();
