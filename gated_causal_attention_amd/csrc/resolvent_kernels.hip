@@ -1496,13 +1496,15 @@ __global__ __launch_bounds__(NTHREADS, 1) void fwd_kernel(FwdArgs A) {
     // vector step in phase 2k + 1 + lag; a barrier ends every phase, and the
     // trailing waves pass one extra barrier first, the leading ones one last.
     // The copies of a phase (leading waves only) run around its step.
-    // A wave in its matrix step takes issue priority over its SIMD partner in
-    // its vector step, so that the partner's vector instructions fill the
-    // cycles between matrix instructions instead of delaying them.
+    // Both waves of a SIMD keep issue priority 0. Raising it for the wave in
+    // its matrix step (2 against 0) measured slower. The explicit priority-0
+    // writes at each step measured about 0.7% faster than none at all; the
+    // compiled loops differ only in those instructions and in the order of a
+    // few scalar ones, so the gain is most likely one of code placement.
     if (lag) lds_barrier();
     int k = 0;
     for (; k < 2 * n_off; ++k) {
-        __builtin_amdgcn_s_setprio(2);
+        __builtin_amdgcn_s_setprio(0);
         m_step_off(k);
         after_m(k);
         lds_barrier();
@@ -1512,7 +1514,7 @@ __global__ __launch_bounds__(NTHREADS, 1) void fwd_kernel(FwdArgs A) {
         lds_barrier();
     }
     for (; k < 2 * n_tiles; ++k) {
-        __builtin_amdgcn_s_setprio(2);
+        __builtin_amdgcn_s_setprio(0);
         m_step(k);
         after_m(k);
         lds_barrier();
@@ -1521,7 +1523,7 @@ __global__ __launch_bounds__(NTHREADS, 1) void fwd_kernel(FwdArgs A) {
         after_v(k);
         lds_barrier();
     }
-    __builtin_amdgcn_s_setprio(2);
+    __builtin_amdgcn_s_setprio(0);
     m_step(k);  // the last block's W~ V
     after_m(k);
     lds_barrier();
