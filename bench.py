@@ -1,9 +1,11 @@
 """Benchmark of the resolvent-head forward pass on one MI355X.
 
 One step is one resolvent_forward call over the headline workload (B=4, H=16,
-n=8192, d=128, bf16 q,k,v, switches (1,1,1)): status clear + v transpose, gate
-scans, the fused forward kernel and the logit-overflow check, with the inputs
-already resident in HBM.  Prints one JSON line (see the design doc for every field).
+n=8192, d=128, bf16 q,k,v, switches (1,1,1)): the prologue (status clear, gates
+and their in-tile products, bf16 v^T), the visit-count scan, the fused forward
+kernel and the logit-overflow check, with the inputs already resident in HBM.
+Prints one JSON line: the throughput, the per-stage times from HIP events, the
+roofline object of the fused kernel and the oracle's CPU rate.
 
   python bench.py [--steps K] [--warmup W] [--gpus 1] [--no-cpu-baseline]
   python bench.py --copy-bytes N   # a plain copy kernel, for counter calibration
@@ -532,7 +534,8 @@ def main():
         return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU: the resolvent head's heads are independent and the "
-              "build has no multi-GPU path (see DESIGN.md, 'Sharding'); run with --gpus 1",
+              "library has no multi-GPU path (a sharded run would split the (batch, head) "
+              "pairs over the GPUs); run with --gpus 1",
               file=sys.stderr)
         sys.exit(2)
 
