@@ -360,8 +360,8 @@ __global__ __launch_bounds__(64 * MW) void decode_merge_kernel(DecodeArgs A) {
             f = exp2f(Mh);
         else
             f = exp2f(A.one_minus_beta * Mh - A.beta * log2f(z));
-        A.o_re[bh * DV + tid] = sr * f;
-        A.o_im[bh * DV + tid] = si * f;
+        A.o_re[bh * DV + tid] = scale_keep_zero(sr, f);
+        A.o_im[bh * DV + tid] = scale_keep_zero(si, f);
     }
 }
 
@@ -474,8 +474,8 @@ __global__ __launch_bounds__(64 * MW) void decode_merge_small_kernel(DecodeArgs 
             f = exp2f(Mh);
         else
             f = exp2f(A.one_minus_beta * Mh - A.beta * log2f(z));
-        A.o_re[bh * DV + tid] = sr * f;
-        A.o_im[bh * DV + tid] = si * f;
+        A.o_re[bh * DV + tid] = scale_keep_zero(sr, f);
+        A.o_im[bh * DV + tid] = scale_keep_zero(si, f);
     }
 }
 

@@ -58,6 +58,11 @@ __device__ __forceinline__ void unpack16(uint4 w, float *x) {
     }
 }
 
+// x f for the final scale of a readout or weight: an exactly zero x stays
+// (signed) zero when f overflows to inf ("Evaluation and refusals": an
+// overflowing weight reads +inf, a zero lane of a product stays 0, never NaN).
+__device__ __forceinline__ float scale_keep_zero(float x, float f) { return x == 0.0f ? x : x * f; }
+
 __device__ __forceinline__ float wave_max(float x) {
 #pragma unroll
     for (int o = 32; o >= 1; o >>= 1) x = fmaxf(x, __shfl_xor(x, o));

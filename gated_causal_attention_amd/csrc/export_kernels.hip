@@ -122,7 +122,7 @@ __global__ __launch_bounds__(64) void clear_word_kernel(int32_t *w) {
 // across lanes of b_j = a_{j+1} (1 from j = i on) times the product of the
 // later tiles.  Pass 0 forms the shift M (largest live logit) and the
 // normaliser; pass 1 recomputes the same logits and products and writes
-// W_ij = G_ij 2^(L_j - M) exp2((1-beta) M) z^-beta.
+// W_ij = G_ij 2^(L_j - M) exp2((1-beta) M) z^-beta (one exponential per entry).
 template <bool QF32, int D>
 __global__ __launch_bounds__(64) void operator_row_kernel(OpArgs A) {
     constexpr int KE = QF32 ? 4 : 8, KL = D / KE, KR = 64 / KL, KI = BK / KR;
@@ -197,19 +197,21 @@ __global__ __launch_bounds__(64) void operator_row_kernel(OpArgs A) {
                 }
                 if (live) z = fmaf(gm, exp2f(L - M), z);
             } else if (key) {
-                const float e = live ? exp2f(L - M) * f : 0.f;
-                wr[j] = float(G.re) * e;
-                wi[j] = float(G.im) * e;
+                // one exponential per entry, 2^((L - M) + log2 f): no product of an
+                // underflowed and an overflowed factor
+                const float e = live ? exp2f((L - M) + f) : 0.f;
+                wr[j] = scale_keep_zero(float(G.re), e);
+                wi[j] = scale_keep_zero(float(G.im), e);
             }
         }
-        if (pass == 0) {
+        if (pass == 0) {  // f: log2 of the row's scale 2^((1-beta) M) z^-beta
             const float zt = wave_sum(z);
             if (A.beta_mode == 1)
-                f = 1.0f / zt;
+                f = -log2f(zt);
             else if (A.beta_mode == 0)
-                f = exp2f(M);
+                f = M;
             else
-                f = exp2f(A.one_minus_beta * M - A.beta * log2f(zt));
+                f = A.one_minus_beta * M - A.beta * log2f(zt);
         }
     }
     for (int64_t j = i + 1 + lane; j < A.n; j += 64) {  // above the diagonal

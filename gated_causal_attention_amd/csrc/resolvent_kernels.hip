@@ -67,6 +67,10 @@ __device__ __forceinline__ uint32_t absbits_u4_bf16(uint4 v) {
     uint32_t b = max(absbits_bf16x2(v.z), absbits_bf16x2(v.w));
     return max(a, b);
 }
+// x f for the epilogue's scale: an exactly zero accumulator stays (signed)
+// zero when f overflows to inf (a zero lane of G stays 0, never NaN).
+__device__ __forceinline__ float scale_keep_zero(float x, float f) { return x == 0.0f ? x : x * f; }
+
 __device__ __forceinline__ uint32_t absbits_f4(float4 v) {
     uint32_t a = max(__float_as_uint(v.x) & 0x7FFFFFFFu, __float_as_uint(v.y) & 0x7FFFFFFFu);
     uint32_t b = max(__float_as_uint(v.z) & 0x7FFFFFFFu, __float_as_uint(v.w) & 0x7FFFFFFFu);
@@ -1214,17 +1218,26 @@ __global__ __launch_bounds__(NTHREADS, 1) void fwd_kernel(FwdArgs A) {
     // W~ = e * gate factor: packed for the next matrix step (bf16 path) or
     // multiplied into O right away (fp32 path).  QKZ: e is 1 on live entries
     // (all_live, or a non-zero modulus on a live row), else 0.
+    // own: the exponent is formed as the rounded logit c*S minus the shift,
+    // the shift being the rounded logit of the row's maximum when it was set,
+    // so a row whose maximum sets the shift weighs that entry exactly 1 (the
+    // query tile's own keys: every row's diagonal entry is live there).
     auto weights = [&](const unsigned char *buf, int kb, int kc, float msub, const float (&fre)[8],
                        const float (&fim)[8], const float (&fm)[8], bool all_live,
-                       bool rlive) __attribute__((always_inline)) {
+                       bool rlive, bool own) __attribute__((always_inline)) {
         float wre[8], wim[8];
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
             float ex;
-            if constexpr (QKZ)
+            if constexpr (QKZ) {
                 ex = (all_live || (fm[e] > 0.0f && rlive)) ? 1.0f : 0.0f;
-            else
+            } else if (own) {
+#pragma clang fp contract(off)
+                const float lg = x[8 * kc + e] * A.c;
+                ex = __builtin_amdgcn_exp2f(lg - msub);
+            } else {
                 ex = __builtin_amdgcn_exp2f(fmaf(x[8 * kc + e], A.c, -msub));
+            }
             z += ex * fm[e];
             wre[e] = ex * fre[e];
             wim[e] = ex * fim[e];
@@ -1272,7 +1285,7 @@ __global__ __launch_bounds__(NTHREADS, 1) void fwd_kernel(FwdArgs A) {
                     fim[e] = b.x; fim[e + 1] = b.y; fim[e + 2] = b.z; fim[e + 3] = b.w;
                     fm[e] = c.x; fm[e + 1] = c.y; fm[e + 2] = c.z; fm[e + 3] = c.w;
                 }
-                weights(buf, kb, kc, msub, fre, fim, fm, !masked, row_live);
+                weights(buf, kb, kc, msub, fre, fim, fm, !masked, row_live, false);
                 __builtin_amdgcn_sched_barrier(0);  // one chunk's side data at a time
             }
         } else {
@@ -1334,7 +1347,7 @@ __global__ __launch_bounds__(NTHREADS, 1) void fwd_kernel(FwdArgs A) {
             unpack(a0, a1, fre);
             unpack(b0, b1, fim);
             unpack(c0, c1, fm);
-            weights(buf, kb, 1, msub, fre, fim, fm, !masked, row_live);
+            weights(buf, kb, 1, msub, fre, fim, fm, !masked, row_live, false);
             __builtin_amdgcn_sched_barrier(0);
 #undef RD128
         }
@@ -1389,7 +1402,7 @@ __global__ __launch_bounds__(NTHREADS, 1) void fwd_kernel(FwdArgs A) {
             }
 #pragma unroll
             for (int e = 0; e < 8; ++e) fm[e] = Gm[8 * kc + e];
-            weights(buf, kb, kc, msub, fre, fim, fm, false, true);
+            weights(buf, kb, kc, msub, fre, fim, fm, false, true, true);
             __builtin_amdgcn_sched_barrier(0);
         }
     };
@@ -1549,14 +1562,14 @@ __global__ __launch_bounds__(NTHREADS, 1) void fwd_kernel(FwdArgs A) {
             for (int g4 = 0; g4 < 4; ++g4) {
                 const int d0 = 32 * db + 8 * g4 + 4 * h;
                 float4 vr, vi;
-                vr.x = ore[db][4 * g4 + 0] * f;
-                vr.y = ore[db][4 * g4 + 1] * f;
-                vr.z = ore[db][4 * g4 + 2] * f;
-                vr.w = ore[db][4 * g4 + 3] * f;
-                vi.x = oim[db][4 * g4 + 0] * f;
-                vi.y = oim[db][4 * g4 + 1] * f;
-                vi.z = oim[db][4 * g4 + 2] * f;
-                vi.w = oim[db][4 * g4 + 3] * f;
+                vr.x = scale_keep_zero(ore[db][4 * g4 + 0], f);
+                vr.y = scale_keep_zero(ore[db][4 * g4 + 1], f);
+                vr.z = scale_keep_zero(ore[db][4 * g4 + 2], f);
+                vr.w = scale_keep_zero(ore[db][4 * g4 + 3], f);
+                vi.x = scale_keep_zero(oim[db][4 * g4 + 0], f);
+                vi.y = scale_keep_zero(oim[db][4 * g4 + 1], f);
+                vi.z = scale_keep_zero(oim[db][4 * g4 + 2], f);
+                vi.w = scale_keep_zero(oim[db][4 * g4 + 3], f);
                 *reinterpret_cast<float4 *>(orp + d0) = vr;
                 *reinterpret_cast<float4 *>(oip + d0) = vi;
             }

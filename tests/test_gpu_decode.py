@@ -220,6 +220,25 @@ def test_decode_long_cache():
     assert err <= TOL_DEC
 
 
+def test_decode_overflow_at_beta_zero():
+    """an_overflowing_logit_never_becomes_nan on a decode step: at beta = 0 and
+    g = 0 a query whose logits pass the float32 range reads +inf (all values
+    positive, so no inf - inf), and the imaginary part stays exactly 0."""
+    announce("decode overflow at beta = 0")
+    n = 300
+    inp = decode_inputs(1, 2, 2, n, 64, 64, seed=95, qk_dtype=inputs.F32, v_dtype=inputs.F32)
+    inp["v"] = np.abs(inp["v"]) + 0.5
+    inp["q"][0, 1] = np.abs(inp["q"][0, 1]) * 40.0
+    inp["k"][0, 1] = np.abs(inp["k"][0, 1]) * 40.0
+    sw = (0, 1, 0)
+    got = gpu_decode(inp, sw)
+    ref = oracle_decode(inp, sw)
+    assert not np.isnan(got.real).any() and not np.isnan(got.imag).any()
+    assert np.all(got.imag == 0)
+    assert np.isinf(ref[1].real).all() and np.all(np.isposinf(got[0, 1].real))
+    assert gu.rel_err(got[0, 0], ref[0]) <= TOL_DEC
+
+
 def test_decode_refusals_and_empty():
     announce("decode refusals")
     inp = decode_inputs(1, 2, 1, 300, 64, 64, seed=3)

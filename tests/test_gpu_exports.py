@@ -164,3 +164,34 @@ def test_operator_refusals():
             binding.resolvent_operator(args["q"], args["k"], args["u"], args["theta"], 1, 1, 1)
         assert e.value.status == binding.Status.NONFINITE, name
     binding.resolvent_operator(t["q"], t["k"], t["u"], t["theta"], 1, 1, 1)
+
+
+def test_operator_overflow_at_beta_zero():
+    """an_overflowing_logit_never_becomes_nan on the export: at beta = 0 the
+    weights whose logits pass the float32 range read +inf exactly where the
+    oracle's do, every other entry matches the oracle, the imaginary part (g = 0:
+    exactly zero lanes of G) stays 0, and no entry is NaN."""
+    announce("operator overflow at beta = 0")
+    n, d = 200, 64
+    inp = inputs.draw(1, 1, n, d, seed=93, qk_dtype=inputs.F32)
+    inp["q"][0, 0, 120:] = np.abs(inp["q"][0, 0, 120:]) * 40.0
+    inp["k"][0, 0, 120:] = np.abs(inp["k"][0, 0, 120:]) * 40.0
+    sw = (0, 1, 0)
+    W = gpu_operator(inp, sw)[0, 0]
+    st, ref = oracle.operator(inp["q"][0, 0], inp["k"][0, 0], inp["u"][0, 0],
+                              inp["theta"][0, 0], *sw)
+    assert st == oracle.OK
+    assert not np.isnan(W.real).any() and not np.isnan(W.imag).any()
+    assert np.all(W.imag == 0)
+    big = np.isinf(ref.real)
+    assert big.any()
+    # float32 overflows earlier than f64: every oracle inf is an inf here, and
+    # an entry that is inf only here has a float32-overflowing weight
+    assert np.all(np.isposinf(W.real[big]))
+    fin = np.isfinite(W.real)
+    assert np.all(ref.real[~fin] > 3.0e38)
+    # the finite weights here reach 1e38: their float32 logits near 88 carry an
+    # absolute rounding error of a few 1e-4 (64-term dot products of entries
+    # near 1e2), so they are held to the bf16 bound, as in the forward's large-
+    # logit test
+    assert gu.rel_err(W[fin & ~big], ref[fin & ~big]) <= gu.TOL_BF16

@@ -12,6 +12,7 @@ import numpy as np
 import pytest
 import torch
 
+import oracle
 from gated_causal_attention_amd import binding, inputs
 from tests import gpu_util as gu
 
@@ -137,17 +138,43 @@ def test_bare_row_is_i_plus_one_bitwise():
 
 def test_closed_gates_leave_identity():
     """an_empty_sequence_is_empty_and_no_row_is_ever_all_masked: all gates
-    closed at beta = 1 gives W = I: O = V bitwise at qk = 0 (every weight is
-    exactly 1), and within float32 rounding of the exponent at qk = 1."""
+    closed at beta = 1 gives W = I, so O = V bitwise and Im O = 0, at qk = 0
+    and at qk = 1 (the only live entry of a row is its diagonal, which sets
+    the row's shift and so weighs exactly 1)."""
     for qk_dtype in ("bf16", "f32"):
-        inp = inputs.draw(2, 2, 333, 128, seed=11, qk_dtype=qk_dtype, v_dtype=qk_dtype)
-        inp["u"][:] = 0.0
-        got = gu.gpu_forward(inp, (1, 0, 1))
-        assert np.array_equal(got.real, inp["v"].astype(np.float64))
-        assert np.all(got.imag == 0)
-        got = gu.gpu_forward(inp, (1, 1, 1))
-        assert np.abs(got.real - inp["v"]).max() <= 1e-6 * np.abs(inp["v"]).max()
-        assert np.all(got.imag == 0)
+        for d in (64, 128):
+            inp = inputs.draw(2, 2, 333, d, seed=11, qk_dtype=qk_dtype, v_dtype=qk_dtype)
+            inp["u"][:] = 0.0
+            for sw in ((1, 0, 1), (1, 1, 1), (1, -0.7, 1)):
+                got = gu.gpu_forward(inp, sw)
+                assert np.array_equal(got.real, inp["v"].astype(np.float64)), (qk_dtype, d, sw)
+                assert np.all(got.imag == 0), (qk_dtype, d, sw)
+
+
+def test_overflow_at_beta_zero_is_inf_never_nan():
+    """an_overflowing_logit_never_becomes_nan: at beta = 0 with g = 0 a row whose
+    logits pass the float32 range reads +-inf where the oracle's weights are
+    +inf, and the imaginary part, a sum of exactly zero lanes of G, stays 0
+    (not 0 * inf).  Rows whose weights stay in range match the oracle."""
+    n, d = 300, 64
+    inp = inputs.draw(1, 1, n, d, seed=91, qk_dtype="f32", v_dtype="f32")
+    inp["v"] = np.abs(inp["v"]) + 0.5  # one sign per channel: no inf - inf in a sum
+    inp["q"][0, 0, 150:] *= 40.0
+    inp["k"][0, 0, 150:] = np.abs(inp["k"][0, 0, 150:]) * 40.0
+    inp["q"][0, 0, 150:] = np.abs(inp["q"][0, 0, 150:])
+    sw = (0, 1, 0)
+    got = gu.gpu_forward(inp, sw)
+    st, ref = oracle.forward_rows(inp["q"][0, 0], inp["k"][0, 0], inp["u"][0, 0],
+                                  inp["theta"][0, 0], inp["v"][0, 0], *sw, rows=np.arange(n))
+    assert st == oracle.OK
+    g = got[0, 0]
+    assert np.isinf(ref.real[150:]).all()
+    assert not np.isnan(g.real).any() and not np.isnan(g.imag).any()
+    assert np.all(g.imag == 0)
+    assert np.all(np.isposinf(g.real[150:]))
+    fin = np.isfinite(ref.real).all(axis=1)
+    assert fin[:150].all()
+    assert gu.rel_err(g[fin], ref[fin]) <= gu.TOL_F32
 
 
 def test_causality_bitwise():

@@ -59,6 +59,29 @@ def test_brute_force_definition(n, d):
         assert st == oracle.OK
         Ob = np.array([[complex(x) for x in row] for row in brute.readout(Wb.tolist(), v.tolist())])
         assert np.abs(O - Ob).max() <= 1e-13 * max(1.0, np.abs(Ob).max()), (beta, qk, g)
+        # the Rust API's readout applied to the operator: the same rows
+        Or = oracle.readout(W, v)
+        assert np.abs(Or - Ob).max() <= 1e-13 * max(1.0, np.abs(Ob).max()), (beta, qk, g)
+        assert np.abs(Or - O).max() <= 1e-13 * max(1.0, np.abs(O).max()), (beta, qk, g)
+
+
+@pytest.mark.parametrize("n,dv", [(1, 1), (4, 7), (9, 2), (16, 16)])
+def test_readout_is_causal_product(n, dv):
+    """Sections "Rust API" (readout of W [seq, seq] and V [seq, value_dim])
+    and "Object" (O_i sums W_ij V_j over j <= i only): for any complex W,
+    including entries above the diagonal that the readout must ignore, the
+    oracle's readout equals tril(W) V from numpy's matrix product, real and
+    imaginary parts separately, to 1e-13."""
+    rng = np.random.default_rng(900 + 10 * n + dv)
+    W = rng.standard_normal((n, n)) + 1j * rng.standard_normal((n, n))
+    v = rng.standard_normal((n, dv))
+    got = oracle.readout(W, v)
+    want = np.tril(W) @ v
+    assert got.shape == (n, dv)
+    assert np.abs(got - want).max() <= 1e-13 * max(1.0, np.abs(want).max())
+    # a change above the diagonal leaves the readout bitwise unchanged
+    W2 = W + np.triu(rng.standard_normal((n, n)), 1)
+    assert np.array_equal(oracle.readout(W2, v), got)
 
 
 # ------------------------------------------------------------------- corners
