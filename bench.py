@@ -109,6 +109,76 @@ def summarize_traffic(fetch_dir, write_dir, copy_fetch_dir, copy_write_dir, copy
     }
 
 
+COUNTER_FILE = os.path.join(ROOT, "profiles", "fwd_kernel_counters_headline.json")
+# rocprofv3 --pmc passes over the headline bench (each within one pass's
+# hardware limits: at most 8 SQ_, 4 TCC_ and 2 GRBM_ counters)
+COUNTER_PASSES = (
+    "SQ_VALU_MFMA_BUSY_CYCLES SQ_BUSY_CYCLES SQ_INSTS_MFMA SQ_INSTS_VALU SQ_INSTS_SALU "
+    "SQ_INSTS_LDS SQ_WAVES GRBM_GUI_ACTIVE",
+    "SQ_VALU_MFMA_COEXEC_CYCLES SQ_ACTIVE_INST_VALU SQ_INSTS_VALU_MFMA_MOPS_BF16 SQ_WAVE_CYCLES "
+    "SQ_WAIT_INST_LDS SQ_INSTS_VALU_TRANS_F32 GRBM_GUI_ACTIVE",
+    "SQ_LDS_BANK_CONFLICT SQ_LDS_IDX_ACTIVE SQ_LDS_ADDR_CONFLICT TCC_HIT_sum TCC_MISS_sum "
+    "GRBM_GUI_ACTIVE",
+)
+SIMDS = 256 * 4  # MI355X: 256 CUs of 4 SIMDs
+
+
+def summarize_counters(dirs):
+    """Utilisation figures of the fused kernel from the COUNTER_PASSES runs
+    (one directory per pass, in order).  Every counter is the mean per
+    dispatch of fwd_kernel; the SQ_ counters are summed over the chip by
+    rocprofv3, GRBM_GUI_ACTIVE is the GPU's active cycles during the dispatch.
+      mfma_busy_pct   = SQ_VALU_MFMA_BUSY_CYCLES / (GRBM_GUI_ACTIVE x 1024 SIMDs)
+      mfma_coexec_pct = SQ_VALU_MFMA_COEXEC_CYCLES / SQ_VALU_MFMA_BUSY_CYCLES
+                        (share of the matrix-busy cycles in which a vector
+                        instruction also issued on the SIMD)
+      mfma_flops      = SQ_INSTS_VALU_MFMA_MOPS_BF16 x 512
+      valu_per_mfma   = (SQ_INSTS_VALU - SQ_INSTS_MFMA) / SQ_INSTS_MFMA
+                        (SQ_INSTS_VALU counts the MFMAs too)
+      lds_bank_conflict_pct = SQ_LDS_BANK_CONFLICT / SQ_LDS_IDX_ACTIVE
+      l2_hit_pct      = TCC_HIT_sum / (TCC_HIT_sum + TCC_MISS_sum)"""
+    vals = {}
+    for d, names in zip(dirs, COUNTER_PASSES):
+        for c in names.split():
+            vals.setdefault(c, counter_per_dispatch(d, c, "fwd_kernel")[0])
+    busy = vals["SQ_VALU_MFMA_BUSY_CYCLES"]
+    gui = vals["GRBM_GUI_ACTIVE"]
+    out = {
+        "kernel": "fwd_kernel<bf16, d=128> (headline workload, switches (1,1,1))",
+        "kernel_source_sha256": kernel_source_sha(),
+        "counters_per_dispatch": vals,
+        "mfma_busy_pct": 100.0 * busy / (gui * SIMDS),
+        "mfma_coexec_pct": 100.0 * vals["SQ_VALU_MFMA_COEXEC_CYCLES"] / busy,
+        "mfma_flops_per_dispatch": vals["SQ_INSTS_VALU_MFMA_MOPS_BF16"] * 512.0,
+        "valu_per_mfma": (vals["SQ_INSTS_VALU"] - vals["SQ_INSTS_MFMA"]) / vals["SQ_INSTS_MFMA"],
+        "salu_per_mfma": vals["SQ_INSTS_SALU"] / vals["SQ_INSTS_MFMA"],
+        "lds_per_mfma": vals["SQ_INSTS_LDS"] / vals["SQ_INSTS_MFMA"],
+        "lds_bank_conflict_pct": 100.0 * vals["SQ_LDS_BANK_CONFLICT"] / vals["SQ_LDS_IDX_ACTIVE"],
+        "l2_hit_pct": 100.0 * vals["TCC_HIT_sum"] / (vals["TCC_HIT_sum"] + vals["TCC_MISS_sum"]),
+        "derivation": summarize_counters.__doc__.split("\n", 4)[4].strip(),
+        "commands": [f"rocprofv3 --pmc {p} -d P{i} -o run --output-format csv -- python3 "
+                     f"bench.py --steps 2 --warmup 1 --no-cpu-baseline"
+                     for i, p in enumerate(COUNTER_PASSES)] +
+                    ["python3 bench.py --summarize-counters P0 P1 P2"],
+    }
+    return out
+
+
+def measured_counters(sha):
+    """The utilisation summary of the committed counter runs, if they were
+    taken on this exact kernel source; else None."""
+    try:
+        with open(COUNTER_FILE) as f:
+            rec = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if rec.get("kernel_source_sha256") != sha:
+        return None
+    keys = ("mfma_busy_pct", "mfma_coexec_pct", "mfma_flops_per_dispatch", "valu_per_mfma",
+            "salu_per_mfma", "lds_per_mfma", "lds_bank_conflict_pct", "l2_hit_pct")
+    return {k: rec[k] for k in keys}
+
+
 def cpu_baseline(inp, sw, heads):
     """The fp64 oracle, as it stands, on whole heads of the same inputs."""
     import numpy as np
@@ -528,9 +598,14 @@ def main():
                          "materialising exports")
     ap.add_argument("--summarize-traffic", nargs=4, metavar=("FETCH", "WRITE", "COPY_FETCH",
                                                               "COPY_WRITE"))
+    ap.add_argument("--summarize-counters", nargs=len(COUNTER_PASSES),
+                    metavar=tuple(f"PASS{i}" for i in range(len(COUNTER_PASSES))))
     args = ap.parse_args()
     if args.summarize_traffic:
         print(json.dumps(summarize_traffic(*args.summarize_traffic, args.copy_bytes), indent=1))
+        return
+    if args.summarize_counters:
+        print(json.dumps(summarize_counters(args.summarize_counters), indent=1))
         return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU: the resolvent head's heads are independent and the "
@@ -650,7 +725,8 @@ def main():
                      "unit": "TFLOP/s", "frac": achieved / PEAK_BF16_TFLOPS,
                      "traffic": traffic, "kernel": "fwd_kernel<bf16, d=128>",
                      "flops_per_launch": alg_flops, "executed_mfma_flops": exec_flops,
-                     "executed_mfma_tflops": exec_flops / (fwd_avg * 1e-3) / 1e12},
+                     "executed_mfma_tflops": exec_flops / (fwd_avg * 1e-3) / 1e12,
+                     "counters": measured_counters(sha)},
     }
     if not args.no_cpu_baseline:
         heads = [(b, h) for b in range(4) for h in range(0, 16, 2)]  # half of the 64 heads
