@@ -121,14 +121,16 @@ COUNTER_PASSES = (
     "GRBM_GUI_ACTIVE",
 )
 SIMDS = 256 * 4  # MI355X: 256 CUs of 4 SIMDs
+XCDS = 8
 
 
 def summarize_counters(dirs):
     """Utilisation figures of the fused kernel from the COUNTER_PASSES runs
     (one directory per pass, in order).  Every counter is the mean per
     dispatch of fwd_kernel; the SQ_ counters are summed over the chip by
-    rocprofv3, GRBM_GUI_ACTIVE is the GPU's active cycles during the dispatch.
-      mfma_busy_pct   = SQ_VALU_MFMA_BUSY_CYCLES / (GRBM_GUI_ACTIVE x 1024 SIMDs)
+    rocprofv3, and GRBM_GUI_ACTIVE (active cycles) is summed over the 8 XCDs,
+    so the GPU's active cycles during the dispatch are GRBM_GUI_ACTIVE / 8.
+      mfma_busy_pct   = SQ_VALU_MFMA_BUSY_CYCLES / (GRBM_GUI_ACTIVE / 8 x 1024 SIMDs)
       mfma_coexec_pct = SQ_VALU_MFMA_COEXEC_CYCLES / SQ_VALU_MFMA_BUSY_CYCLES
                         (share of the matrix-busy cycles in which a vector
                         instruction also issued on the SIMD)
@@ -147,7 +149,8 @@ def summarize_counters(dirs):
         "kernel": "fwd_kernel<bf16, d=128> (headline workload, switches (1,1,1))",
         "kernel_source_sha256": kernel_source_sha(),
         "counters_per_dispatch": vals,
-        "mfma_busy_pct": 100.0 * busy / (gui * SIMDS),
+        "mfma_busy_pct": 100.0 * busy / (gui / XCDS * SIMDS),
+        "active_cycles": gui / XCDS,
         "mfma_coexec_pct": 100.0 * vals["SQ_VALU_MFMA_COEXEC_CYCLES"] / busy,
         "mfma_flops_per_dispatch": vals["SQ_INSTS_VALU_MFMA_MOPS_BF16"] * 512.0,
         "valu_per_mfma": (vals["SQ_INSTS_VALU"] - vals["SQ_INSTS_MFMA"]) / vals["SQ_INSTS_MFMA"],
@@ -155,7 +158,7 @@ def summarize_counters(dirs):
         "lds_per_mfma": vals["SQ_INSTS_LDS"] / vals["SQ_INSTS_MFMA"],
         "lds_bank_conflict_pct": 100.0 * vals["SQ_LDS_BANK_CONFLICT"] / vals["SQ_LDS_IDX_ACTIVE"],
         "l2_hit_pct": 100.0 * vals["TCC_HIT_sum"] / (vals["TCC_HIT_sum"] + vals["TCC_MISS_sum"]),
-        "derivation": summarize_counters.__doc__.split("\n", 4)[4].strip(),
+        "derivation": summarize_counters.__doc__.split("\n", 5)[5].strip(),
         "commands": [f"rocprofv3 --pmc {p} -d P{i} -o run --output-format csv -- python3 "
                      f"bench.py --steps 2 --warmup 1 --no-cpu-baseline"
                      for i, p in enumerate(COUNTER_PASSES)] +

@@ -261,6 +261,79 @@ RESOLVENT_HD constexpr int vfrag_base(int qi, int h) {
     return qi * 128 + 16 * (h ^ chunk_swz<8>(qi));
 }
 
+// Padded bf16 tiles of the fused forward (bf16 path).  A K row of d bf16
+// values takes KSL = d/8 + 1 sixteen-byte slots in LDS and a v^T row of the BK
+// keys of a tile VSL = 2 BK/16 + 1 = 9 slots; the last slot of each row is
+// padding.  With a row stride of an odd number of slots, the 16 rows that a
+// half-wave reads at one chunk fall into 16 different bank groups, and every
+// matrix-operand read is a per-lane base plus an immediate offset.  The K
+// tile occupies slots [0, 64 KSL) of a buffer and v^T the next 9 dv slots; copy
+// instruction j of a tile (a direct global->LDS copy of 16 bytes per lane)
+// fills slots [64 j, 64 j + 64): lane L slot 64 j + L.  The padding slot of a
+// row is filled with a copy of the row's last chunk.
+template <int D>
+RESOLVENT_HD constexpr int pad_kslots() { return D / 8 + 1; }
+constexpr int PAD_VSLOTS = BK * 2 / 16 + 1;
+template <int D>
+RESOLVENT_HD constexpr int pad_kcopies() { return pad_kslots<D>(); }  // BK rows x KSL slots / 64
+template <int DV>
+RESOLVENT_HD constexpr int pad_vcopies() { return DV * PAD_VSLOTS / 64; }
+// The NC = KSL + 9 dv / 64 copy instructions of a tile are shared by waves
+// 1..NWAVES-1 (wave 0 copies the gate data): copying wave w issues, as its
+// i-th of pad_copies_per_wave, instruction j = w - 1 + (NWAVES - 1) i, the
+// last one repeated past NC (the same bytes to the same slots).
+template <int D, int DV>
+RESOLVENT_HD constexpr int pad_copies() { return pad_kcopies<D>() + pad_vcopies<DV>(); }
+template <int D, int DV>
+RESOLVENT_HD constexpr int pad_copies_per_wave() {
+    return (pad_copies<D, DV>() + NWAVES - 2) / (NWAVES - 1);
+}
+template <int D, int DV>
+RESOLVENT_HD inline int pad_copy_j(int w, int i) {
+    const int j = w - 1 + (NWAVES - 1) * i;
+    return j < pad_copies<D, DV>() ? j : pad_copies<D, DV>() - 1;
+}
+// Source byte offset of copy instruction j, lane `lane`: for j < KSL inside
+// the K rows of the tile, relative to the tile's first key row (rows of 2d
+// bytes); otherwise inside v^T [dv][n_pad] bf16, relative to the tile's first
+// column of row 0.  (The whole tile inside the sequence; see pad_kcopy_src_ragged.)
+template <int D>
+RESOLVENT_HD inline uint32_t pad_copy_src(int j, int lane, int64_t n_pad) {
+    constexpr int KSL = pad_kslots<D>();
+    if (j < KSL) {
+        const int p = 64 * j + lane, r = p / KSL;
+        const int c = p % KSL < KSL - 1 ? p % KSL : KSL - 2;
+        return uint32_t(r * D * 2 + 16 * c);
+    }
+    const int p = 64 * (j - KSL) + lane, r = p / PAD_VSLOTS;
+    const int c = p % PAD_VSLOTS < PAD_VSLOTS - 1 ? p % PAD_VSLOTS : PAD_VSLOTS - 2;
+    return uint32_t(int64_t(r) * n_pad * 2 + 16 * c);
+}
+// The K copy source of tile t when the tile reaches past key n - 1 (or lies
+// wholly past it, as own tiles of the last query tile can): rows past it
+// repeat key n - 1 (their entries are masked).  Relative to the head's first
+// key row (32 bits for n <= 2^22).
+template <int D>
+RESOLVENT_HD inline uint32_t pad_kcopy_src_ragged(int j, int lane, int64_t n, int64_t t) {
+    constexpr int KSL = pad_kslots<D>();
+    const int p = 64 * j + lane, r = p / KSL;
+    const int c = p % KSL < KSL - 1 ? p % KSL : KSL - 2;
+    const int64_t key = t * BK + r < n ? t * BK + r : n - 1;
+    return uint32_t(key * D * 2 + 16 * c);
+}
+// Byte offsets, inside a buffer, of the operand reads of lane (qi, h) of a
+// 32x32x16 bf16 product: K row kb + qi, chunk 2s + h (step s); v^T row
+// 32 db + qi, chunk kb/8 + 2 kc + h.  Each is a lane part plus a constant.
+template <int D>
+RESOLVENT_HD constexpr int pad_kread(int kb, int s, int qi, int h) {
+    return (kb + qi) * 16 * pad_kslots<D>() + 16 * (2 * s + h);
+}
+template <int D>
+RESOLVENT_HD constexpr int pad_vread(int kb, int kc, int db, int qi, int h) {
+    return 16 * BK * pad_kslots<D>() + (32 * db + qi) * 16 * PAD_VSLOTS +
+           16 * (kb / 8 + 2 * kc + h);
+}
+
 // Float index, inside a gate plane [BH][n_pad], of the datum lane `lane`
 // copies for key tile t: S_j of key t*BK + lane (a tile before the query
 // tile), or a_{j+1} (own) -- one past the head's last position this is the

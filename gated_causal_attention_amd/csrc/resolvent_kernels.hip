@@ -441,7 +441,8 @@ __device__ __forceinline__ uint32_t lds_addr(const unsigned char *p) {
 // aliasing rules would otherwise hold every later LDS read of any buffer until
 // the copy lands.  Readers wait for the copy explicitly (wait_vmcnt() and a
 // barrier).  m0 carries the LDS address and is restored afterwards.
-__device__ __forceinline__ void g2lds16(const unsigned char *base, uint32_t off, uint32_t lds) {
+__device__ __forceinline__ void g2lds16(const unsigned char *base_, uint32_t off, uint32_t lds) {
+    const unsigned char *base = uniform_ptr(base_);
     const uint32_t la = __builtin_amdgcn_readfirstlane(lds);
     uint32_t saved;
     asm volatile(
@@ -456,7 +457,8 @@ __device__ __forceinline__ void g2lds16(const unsigned char *base, uint32_t off,
 }
 
 // The same for 4 bytes per lane (lane L writes lds + 4 L).
-__device__ __forceinline__ void g2lds4(const unsigned char *base, uint32_t off, uint32_t lds) {
+__device__ __forceinline__ void g2lds4(const unsigned char *base_, uint32_t off, uint32_t lds) {
+    const unsigned char *base = uniform_ptr(base_);
     const uint32_t la = __builtin_amdgcn_readfirstlane(lds);
     uint32_t saved;
     asm volatile(
@@ -473,7 +475,8 @@ __device__ __forceinline__ void g2lds4(const unsigned char *base, uint32_t off, 
 // 16 bytes in each of lanes 0 and 1 (lane L reads base + off and writes
 // lds + 16 L; the other lanes are masked off for the one instruction and
 // restored).
-__device__ __forceinline__ void g2lds16x2(const unsigned char *base, uint32_t off, uint32_t lds) {
+__device__ __forceinline__ void g2lds16x2(const unsigned char *base_, uint32_t off, uint32_t lds) {
+    const unsigned char *base = uniform_ptr(base_);
     const uint32_t la = __builtin_amdgcn_readfirstlane(lds);
     uint32_t saved;
     uint64_t ex;
@@ -1638,6 +1641,834 @@ __global__ __launch_bounds__(NTHREADS) void logit_check_kernel(FwdArgs A) {
     if (__any(bad) && lane == 0) A.status[0] = kNonFinite;
 }
 
+// --------------------------------------------------------------------------
+// Fused forward, bf16 path: padded tiles (row strides of an odd number of
+// 16-byte slots, so every matrix-operand read is a per-lane base plus an
+// immediate offset and a half-wave's rows fall into distinct bank groups),
+// and a phase loop unrolled per key tile, so that the step of each block is
+// fixed at compile time.  Waves 1..7 copy the K and v^T tiles; wave 0 copies
+// the gate planes and the tile products and lands the tiles.
+template <int D, int DV>
+struct PSmem {
+    static constexpr int KSL = pad_kslots<D>();
+    static constexpr int KROW = 16 * KSL;          // bytes per K row
+    static constexpr int VROW = 16 * PAD_VSLOTS;   // bytes per v^T row
+    static constexpr int NKC = pad_kcopies<D>();   // copy instructions of a K tile
+    static constexpr int NVC = pad_vcopies<DV>();  // of a v^T tile
+    static constexpr int NC = NKC + NVC;
+    static constexpr int CPW = pad_copies_per_wave<D, DV>();  // per copying wave and tile
+    static constexpr size_t k_bytes = size_t(1024) * NKC;
+    static constexpr size_t v_bytes = size_t(1024) * NVC;
+    static constexpr size_t side_off = k_bytes + v_bytes;
+    static constexpr size_t raw_off = side_off + 3 * BK * sizeof(float);
+    static constexpr size_t tprod_off = raw_off + 3 * BK * sizeof(float);
+    static constexpr size_t flag_off = tprod_off + 4 * sizeof(double);
+    static constexpr size_t buf_bytes = (flag_off + 16 + 255) / 256 * 256;
+    static constexpr int NBUF = 4;
+    static constexpr size_t misc_off = NBUF * buf_bytes;
+    static constexpr size_t carry_off = misc_off + 8 * sizeof(uint32_t);
+    // per-lane source offsets of each copying wave's copies, [NWAVES-1][CPW][64]
+    static constexpr size_t coff_off = carry_off + 4 * sizeof(double);
+    static constexpr size_t bytes = coff_off + size_t(NWAVES - 1) * CPW * 64 * sizeof(uint32_t);
+    // every copying wave issues CPW distinct copies, instruction j = w - 1 + 7 i:
+    // the first NKHI (waves 1..WSPLIT) or NKHI - 1 (the others) are K copies
+    static constexpr bool EXACT = (NWAVES - 1) * CPW == NC;
+    static constexpr int NKHI = (NKC + NWAVES - 2) / (NWAVES - 1);
+    static constexpr int WSPLIT = NKC - (NWAVES - 1) * (NKHI - 1);
+    static_assert(bytes <= 160 * 1024, "LDS");
+    static_assert(size_t(BK) * KROW == k_bytes && size_t(DV) * VROW == v_bytes, "whole copies");
+    static_assert(CPW <= 5, "copy batch");
+};
+
+// The copies of one wave for one tile when every copying wave issues CPW = 5
+// distinct ones (j = w - 1 + 7 i): the first NK read K rows (base kb), the
+// others v^T rows (base vb); copy i writes at LDS address l0 + 7168 i.  m0 is
+// saved once, set before each direct global->LDS load (lane L reads base +
+// o[i], writes 16 bytes at m0 + 16 L) and restored at the end.
+#define RESOLVENT_G2LS(v, s, imm) \
+    "s_add_u32 m0, %8, " #imm "\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %" #v ", %" #s "\n\t"
+template <int NK>
+__device__ __forceinline__ void g2l_split5(const uint32_t (&o)[5], const unsigned char *kb,
+                                           const unsigned char *vb, uint32_t l0) {
+    static_assert(NK == 2 || NK == 3, "split");
+    uint32_t sv;
+    if constexpr (NK == 3)
+        asm volatile("s_mov_b32 %0, m0\n\t" RESOLVENT_G2LS(1, 6, 0) RESOLVENT_G2LS(2, 6, 7168)
+                     RESOLVENT_G2LS(3, 6, 14336) RESOLVENT_G2LS(4, 7, 21504)
+                     RESOLVENT_G2LS(5, 7, 28672) "s_mov_b32 m0, %0"
+                     : "=&s"(sv)
+                     : "v"(o[0]), "v"(o[1]), "v"(o[2]), "v"(o[3]), "v"(o[4]), "s"(kb), "s"(vb), "s"(l0)
+                     : "memory");
+    else
+        asm volatile("s_mov_b32 %0, m0\n\t" RESOLVENT_G2LS(1, 6, 0) RESOLVENT_G2LS(2, 6, 7168)
+                     RESOLVENT_G2LS(3, 7, 14336) RESOLVENT_G2LS(4, 7, 21504)
+                     RESOLVENT_G2LS(5, 7, 28672) "s_mov_b32 m0, %0"
+                     : "=&s"(sv)
+                     : "v"(o[0]), "v"(o[1]), "v"(o[2]), "v"(o[3]), "v"(o[4]), "s"(kb), "s"(vb), "s"(l0)
+                     : "memory");
+}
+#undef RESOLVENT_G2LS
+
+// The copies of one wave for one tile, as one instruction group: m0 is saved
+// once, set to each copy's LDS address (wave-uniform) before its direct
+// global->LDS load (lane L reads base + off and writes 16 bytes at
+// m0 + 16 L), and restored at the end.
+#define RESOLVENT_G2L(v, s, l) \
+    "s_mov_b32 m0, %" #l "\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %" #v ", %" #s "\n\t"
+template <int N>
+struct G2LBatch;
+template <>
+struct G2LBatch<1> {
+    __device__ __forceinline__ static void go(const uint32_t (&o)[1], const unsigned char *const (&b)[1],
+                                              const uint32_t (&l)[1]) {
+        uint32_t sv;
+        asm volatile("s_mov_b32 %0, m0\n\t" RESOLVENT_G2L(1, 2, 3) "s_mov_b32 m0, %0"
+                     : "=&s"(sv) : "v"(o[0]), "s"(b[0]), "s"(l[0]) : "memory");
+    }
+};
+template <>
+struct G2LBatch<2> {
+    __device__ __forceinline__ static void go(const uint32_t (&o)[2], const unsigned char *const (&b)[2],
+                                              const uint32_t (&l)[2]) {
+        uint32_t sv;
+        asm volatile("s_mov_b32 %0, m0\n\t" RESOLVENT_G2L(1, 3, 5) RESOLVENT_G2L(2, 4, 6)
+                     "s_mov_b32 m0, %0"
+                     : "=&s"(sv) : "v"(o[0]), "v"(o[1]), "s"(b[0]), "s"(b[1]), "s"(l[0]), "s"(l[1])
+                     : "memory");
+    }
+};
+template <>
+struct G2LBatch<3> {
+    __device__ __forceinline__ static void go(const uint32_t (&o)[3], const unsigned char *const (&b)[3],
+                                              const uint32_t (&l)[3]) {
+        uint32_t sv;
+        asm volatile("s_mov_b32 %0, m0\n\t" RESOLVENT_G2L(1, 4, 7) RESOLVENT_G2L(2, 5, 8)
+                     RESOLVENT_G2L(3, 6, 9) "s_mov_b32 m0, %0"
+                     : "=&s"(sv)
+                     : "v"(o[0]), "v"(o[1]), "v"(o[2]), "s"(b[0]), "s"(b[1]), "s"(b[2]), "s"(l[0]),
+                       "s"(l[1]), "s"(l[2])
+                     : "memory");
+    }
+};
+template <>
+struct G2LBatch<4> {
+    __device__ __forceinline__ static void go(const uint32_t (&o)[4], const unsigned char *const (&b)[4],
+                                              const uint32_t (&l)[4]) {
+        uint32_t sv;
+        asm volatile("s_mov_b32 %0, m0\n\t" RESOLVENT_G2L(1, 5, 9) RESOLVENT_G2L(2, 6, 10)
+                     RESOLVENT_G2L(3, 7, 11) RESOLVENT_G2L(4, 8, 12) "s_mov_b32 m0, %0"
+                     : "=&s"(sv)
+                     : "v"(o[0]), "v"(o[1]), "v"(o[2]), "v"(o[3]), "s"(b[0]), "s"(b[1]), "s"(b[2]),
+                       "s"(b[3]), "s"(l[0]), "s"(l[1]), "s"(l[2]), "s"(l[3])
+                     : "memory");
+    }
+};
+template <>
+struct G2LBatch<5> {
+    __device__ __forceinline__ static void go(const uint32_t (&o)[5], const unsigned char *const (&b)[5],
+                                              const uint32_t (&l)[5]) {
+        uint32_t sv;
+        asm volatile("s_mov_b32 %0, m0\n\t" RESOLVENT_G2L(1, 6, 11) RESOLVENT_G2L(2, 7, 12)
+                     RESOLVENT_G2L(3, 8, 13) RESOLVENT_G2L(4, 9, 14) RESOLVENT_G2L(5, 10, 15)
+                     "s_mov_b32 m0, %0"
+                     : "=&s"(sv)
+                     : "v"(o[0]), "v"(o[1]), "v"(o[2]), "v"(o[3]), "v"(o[4]), "s"(b[0]), "s"(b[1]),
+                       "s"(b[2]), "s"(b[3]), "s"(b[4]), "s"(l[0]), "s"(l[1]), "s"(l[2]), "s"(l[3]),
+                       "s"(l[4])
+                     : "memory");
+    }
+};
+#undef RESOLVENT_G2L
+
+// Matrix step on padded tiles: O^T += V^T W~^T for the block whose v^T rows
+// start at vb (lane part included) at key offset KBV (PV), and S^T = K Q^T for
+// the block at K offset KBS of the K tile at kb (lane part included) (S).
+// Operand fragments stream four deep through pf; NPRE of each kind were
+// requested before (pstep_prefetch).
+template <int D, int DV, int KBV, int KBS, bool PV, bool S, int I0, int I1>
+__device__ __forceinline__ void pstep_prefetch(const unsigned char *vb, const unsigned char *kb,
+                                               MPrefetch &pf) {
+    constexpr int NV = PV ? 2 * (DV / 32) : 0;
+    constexpr int NK = S ? D / 16 : 0;
+#pragma unroll
+    for (int i = I0; i < I1; ++i) {
+        if (i < NV) {
+            const int kc = i / (DV / 32), db = i % (DV / 32);
+            pf.vf[i] = *reinterpret_cast<const bf16x8 *>(vb + 2 * KBV + 32 * kc +
+                                                        db * 32 * (16 * PAD_VSLOTS));
+        }
+        if (i < NK)
+            pf.kf[i] = *reinterpret_cast<const bf16x8 *>(kb + KBS * 16 * pad_kslots<D>() + 32 * i);
+    }
+}
+template <int D, int DV, int KBV, int KBS, bool PV, bool S, int NPRE>
+__device__ __forceinline__ void pstep(const unsigned char *vb, const unsigned char *kb,
+                                      MPrefetch &pf, const bf16x8 (&wr)[2], const bf16x8 (&wi)[2],
+                                      const bf16x8 (&qf)[D / 16], f32x16 (&ore)[DV / 32],
+                                      f32x16 (&oim)[DV / 32], f32x16 &sacc) {
+    constexpr int NDB = DV / 32;
+    constexpr int NV = PV ? 2 * NDB : 0;
+    constexpr int NK = S ? D / 16 : 0;
+    constexpr int NSTEP = NV > NK ? NV : NK;
+    pstep_prefetch<D, DV, KBV, KBS, PV, S, NPRE, MDEPTH>(vb, kb, pf);
+#pragma unroll
+    for (int i = 0; i < NSTEP; ++i) {
+        __builtin_amdgcn_sched_barrier(0);
+        if (i < NV) {
+            const int kc = i / NDB, db = i % NDB;
+            const bf16x8 a = pf.vf[i % MDEPTH];
+            ore[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, wr[kc], ore[db], 0, 0, 0);
+            oim[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, wi[kc], oim[db], 0, 0, 0);
+            if (i + MDEPTH < NV) {
+                const int kc2 = (i + MDEPTH) / NDB, db2 = (i + MDEPTH) % NDB;
+                pf.vf[i % MDEPTH] = *reinterpret_cast<const bf16x8 *>(
+                    vb + 2 * KBV + 32 * kc2 + db2 * 32 * (16 * PAD_VSLOTS));
+            }
+        }
+        if (i < NK) {
+            sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(pf.kf[i % MDEPTH], qf[i],
+                                                            i == 0 ? f32x16{} : sacc, 0, 0, 0);
+            if (i + MDEPTH < NK)
+                pf.kf[i % MDEPTH] = *reinterpret_cast<const bf16x8 *>(
+                    kb + KBS * 16 * pad_kslots<D>() + 32 * (i + MDEPTH));
+        }
+    }
+    __builtin_amdgcn_sched_barrier(0);
+}
+
+template <int D, int DV, bool QKZ>
+__global__ __launch_bounds__(NTHREADS, 1) void fwd_pad_kernel(FwdArgs A) {
+    using SM = PSmem<D, DV>;
+    constexpr int NBUF = SM::NBUF;
+    constexpr int NDIAG = BQ / BK;  // key tiles inside the query tile
+    constexpr int NDB = 2 * NDIAG;  // 32-key blocks inside the query tile
+    constexpr int CPW = SM::CPW;
+    constexpr int KROW = SM::KROW, VROW = SM::VROW;
+    extern __shared__ __align__(16) unsigned char smem[];
+    uint32_t *misc = reinterpret_cast<uint32_t *>(smem + SM::misc_off);
+    // misc[2]: largest |q|; misc[3]: largest |k|
+
+    const int tid = threadIdx.x, lane = tid & 63, h = lane >> 5, qi = lane & 31;
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int lag = w / (NWAVES / 2);  // 0: leading waves, 1: trailing waves
+    // work item (as fwd_kernel): round-robin over the XCDs, one head at a
+    // time per XCD when the heads split evenly, heaviest query tile first
+    const int L = blockIdx.x;
+    int64_t qt, bh;
+    if ((A.BH & 7) == 0) {
+        const int x = L & 7, j = L >> 3;
+        bh = x + 8 * (j / A.n_qt);
+        qt = A.n_qt - 1 - (j % A.n_qt);
+    } else {
+        qt = A.n_qt - 1 - L / A.BH;
+        bh = L % A.BH;
+    }
+    const int64_t i0 = qt * BQ;
+    const int64_t row = i0 + 32 * w + qi;
+    const bool row_ok = row < A.n;
+    const int64_t gbase = bh * A.n_pad;
+    const int t_diag0 = int(i0 / BK);
+    const int n_off = __builtin_amdgcn_readfirstlane(A.noff[bh * A.n_qt + qt]);
+    const int n_tiles = n_off + NDIAG;
+    const unsigned char *kh, *vh;
+    head_bases<false, D, DV>(A, kv_head(A, bh), kh, vh);
+    if (tid == 0) {
+        misc[2] = 0;
+        misc[3] = 0;
+    }
+    auto tile_of = [&](int sg) __attribute__((always_inline)) {
+        return sg < n_off ? t_diag0 - 1 - sg : t_diag0 + NDIAG - 1 - (sg - n_off);
+    };
+    auto tile_buf = [&](int sg) __attribute__((always_inline)) {
+        return smem + (sg & (NBUF - 1)) * SM::buf_bytes;
+    };
+    const uint32_t smem_lds = lds_addr(smem);
+    const int n32 = int(A.n);  // n <= 2^22 (checked on the host)
+
+    // ---- copies: waves 1..7 copy K and v^T, CPW instructions each per tile,
+    // with per-lane source offsets computed once; wave 0 copies the three gate
+    // planes of the tile's 64 keys (S_j into the raw area for a tile before
+    // the query tile, a_{j+1} into the side area for an own tile) and the tile
+    // product.
+    uint32_t *coffs = reinterpret_cast<uint32_t *>(smem + SM::coff_off);
+    if (w > 0) {
+#pragma unroll
+        for (int i = 0; i < CPW; ++i)
+            coffs[((w - 1) * CPW + i) * 64 + lane] =
+                pad_copy_src<D>(pad_copy_j<D, DV>(w, i), lane, A.n_pad);
+    }
+    const double *t4 = uniform_ptr(A.t4 + 4 * bh * A.n_kt);
+    const float *gS = uniform_ptr(A.gates + 3 * A.plane + bh * A.n_pad);
+    const float *gA = uniform_ptr(A.gates + bh * A.n_pad + 1);
+    auto issue = [&](int sg) __attribute__((always_inline)) {
+        if (sg >= n_tiles) return;
+        const int t = tile_of(sg);
+        const uint32_t buf = smem_lds + uint32_t((sg & (NBUF - 1)) * SM::buf_bytes);
+        if (w > 0) {
+            // a tile reaching past key n-1 takes K rows clamped to it, with
+            // offsets relative to the head's rows
+            const bool ragged = (t + 1) * BK > n32;
+            const unsigned char *kt =
+                uniform_ptr(ragged ? kh : kh + int64_t(t) * (BK * D * 2));
+            const unsigned char *vt = uniform_ptr(vh + int64_t(t) * (BK * 2));
+            const uint32_t *co = coffs + (w - 1) * CPW * 64 + fresh_lane();
+            uint32_t o[CPW];
+#pragma unroll
+            for (int i = 0; i < CPW; ++i) o[i] = co[64 * i];
+            if (ragged) {
+#pragma unroll
+                for (int i = 0; i < CPW; ++i) {
+                    const int j = pad_copy_j<D, DV>(w, i);
+                    if (j < SM::NKC) o[i] = pad_kcopy_src_ragged<D>(j, fresh_lane(), A.n, t);
+                }
+            }
+            if constexpr (SM::EXACT && CPW == 5) {
+                const uint32_t l0 = __builtin_amdgcn_readfirstlane(buf + uint32_t(1024 * (w - 1)));
+                if (w <= SM::WSPLIT)
+                    g2l_split5<SM::NKHI>(o, kt, vt, l0);
+                else
+                    g2l_split5<SM::NKHI - 1>(o, kt, vt, l0);
+            } else {
+                uint32_t l[CPW];
+                const unsigned char *b[CPW];
+#pragma unroll
+                for (int i = 0; i < CPW; ++i) {
+                    const int j = pad_copy_j<D, DV>(w, i);
+                    b[i] = j < SM::NKC ? kt : vt;
+                    l[i] = __builtin_amdgcn_readfirstlane(buf + uint32_t(1024 * j));
+                }
+                G2LBatch<CPW>::go(o, b, l);
+            }
+        } else {
+            const bool off = sg < n_off;
+            const uint32_t lo = uint32_t(fresh_lane() * 4);
+            const float *g = uniform_ptr((off ? gS : gA) + t * BK);
+            const uint32_t dst = buf + uint32_t(off ? SM::raw_off : SM::side_off);
+            g2lds4(reinterpret_cast<const unsigned char *>(g), lo, dst);
+            g2lds4(reinterpret_cast<const unsigned char *>(g + A.plane), lo, dst + BK * 4);
+            g2lds4(reinterpret_cast<const unsigned char *>(g + 2 * A.plane), lo, dst + 2 * BK * 4);
+            g2lds16x2(reinterpret_cast<const unsigned char *>(uniform_ptr(t4 + 4 * t)),
+                      uint32_t(fresh_lane() * 16), buf + uint32_t(SM::tprod_off));
+        }
+    };
+    // Landing of tile sg once the wave's copies of it are in (as fwd_kernel):
+    // wave 0 forms T_j = C S_j of the 64 keys of a tile before the query tile
+    // (C the visit's carried product, accumulated in f64 in LDS with the
+    // recurrence and rounding of the visit-count scan) and its dead-column
+    // flags; for an own tile each copying wave takes the largest |k| of the K
+    // slots it copied.
+    uint32_t kbits = 0;
+    double *cst = reinterpret_cast<double *>(smem + SM::carry_off);
+    auto land = [&](int sg) __attribute__((always_inline)) {
+        if (sg >= n_tiles) return;
+        unsigned char *buf = tile_buf(sg);
+        if (sg < n_off) {
+            if (w == 0) {
+                const int ln = fresh_lane();
+                double c_re = 1.0, c_im = 0.0, c_m = 1.0;
+                if (sg > 0) {
+                    c_re = cst[0];
+                    c_im = cst[1];
+                    c_m = cst[2];
+                }
+                {
+#pragma clang fp contract(off)
+                    const double *at = reinterpret_cast<const double *>(buf + SM::tprod_off);
+                    const double ar = at[0], ai = at[1], am = at[2];
+                    const double nr = ar * c_re - ai * c_im;
+                    const double ni = ar * c_im + ai * c_re;
+                    const double nm = am * c_m;
+                    if (ln == 0) {
+                        cst[0] = nr;
+                        cst[1] = ni;
+                        cst[2] = nm;
+                    }
+                }
+                const float ccx = (float)c_re, ccy = (float)c_im, ccz = (float)c_m;
+                const float *raw = reinterpret_cast<const float *>(buf + SM::raw_off);
+                float *sd = reinterpret_cast<float *>(buf + SM::side_off);
+                const float g0 = raw[ln], g1 = raw[BK + ln], g2 = raw[2 * BK + ln];
+                const float rt = ccz * g2;
+                const int slot = perm64(ln);
+                sd[slot] = ccx * g0 - ccy * g1;
+                sd[BK + slot] = ccx * g1 + ccy * g0;
+                sd[2 * BK + slot] = rt;
+                const uint64_t dead = __ballot(rt == 0.0f);
+                if (ln == 0) {
+                    uint32_t *fl = reinterpret_cast<uint32_t *>(buf + SM::flag_off);
+                    fl[0] = (uint32_t)(dead & 0xFFFFFFFFull) != 0u;
+                    fl[1] = (uint32_t)(dead >> 32) != 0u;
+                }
+            }
+        } else if (w > 0) {
+#pragma unroll
+            for (int i = 0; i < CPW; ++i) {
+                const int j = pad_copy_j<D, DV>(w, i);
+                if (j < SM::NKC) {
+                    const uint4 v =
+                        *reinterpret_cast<const uint4 *>(buf + 1024 * j + 16 * fresh_lane());
+                    kbits = max(kbits, absbits_u4_bf16(v));
+                }
+            }
+        }
+    };
+    // wait for this wave's copies of the tile landing now, leaving those of
+    // the tile after it (if started) in flight, then land it
+    auto land_wait = [&](int m) __attribute__((always_inline)) {
+        if (m + 2 >= n_tiles)
+            wait_vmcnt<0>();
+        else if (w == 0)
+            wait_vmcnt<4>();
+        else
+            wait_vmcnt<CPW>();
+        land(m + 1);
+    };
+
+    // ---- prologue: the first two tiles, Q (negated when c < 0, so that the
+    // largest logit is the largest score), the row's prefix product
+    issue(0);
+    issue(1);
+    bf16x8 qf[D / 16];
+    const uint32_t qbits = load_q<false, D>(A, bh, row, row_ok, h, qf);
+    const float c = fabsf(A.c);  // logits are c S in log2 units
+    if (A.c < 0.0f) {
+#pragma unroll
+        for (int s = 0; s < D / 16; ++s) {
+            uint4 u = __builtin_bit_cast(uint4, qf[s]);
+            u.x ^= 0x80008000u;
+            u.y ^= 0x80008000u;
+            u.z ^= 0x80008000u;
+            u.w ^= 0x80008000u;
+            qf[s] = __builtin_bit_cast(bf16x8, u);
+        }
+    }
+    const float prow_re = A.p_re[gbase + row], prow_im = A.p_im[gbase + row];
+    const float prow_m = A.p_m[gbase + row];
+    const bool row_live = !(prow_m == 0.0f);
+    const bool wave_dead_rows = __any(!row_live);
+    wait_vmcnt<0>();
+    land(0);
+    lds_barrier();
+    atomicMax(&misc[2], qbits);
+
+    f32x16 ore[DV / 32], oim[DV / 32];
+#pragma unroll
+    for (int db = 0; db < DV / 32; ++db)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+            ore[db][r] = 0.f;
+            oim[db][r] = 0.f;
+        }
+    float M = QKZ ? 0.0f : -INFINITY;
+    float z = 0.f;
+    float gre = 0.f, gim = 0.f, gm = 0.f;
+    f32x16 x;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) x[r] = 0.f;
+    BlockW<false> wk;
+    constexpr float dead_s = -INFINITY;
+
+    // per-lane parts of the operand and side-data reads
+    const int klane = qi * KROW + 16 * h;
+    const int vlane = int(SM::k_bytes) + qi * VROW + 16 * h;
+    const int slane = int(SM::side_off) + 32 * h;
+
+    auto block_shift = [&]() __attribute__((always_inline)) -> float {
+        if constexpr (QKZ) {
+            return 0.0f;
+        } else {
+            float ts = x[0];
+#pragma unroll
+            for (int r = 1; r < 16; ++r) ts = fmaxf(ts, x[r]);
+            const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(ts),
+                                                             __float_as_uint(ts), false, false);
+            ts = fmaxf(ts, fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1])));
+            float t;
+            {
+#pragma clang fp contract(off)
+                t = ts * c;
+            }
+            const bool grow = (t > M + kLazy) | ((M == -INFINITY) & (t > M));
+            const bool resc = grow & (M != -INFINITY);
+            if (__any(resc)) {
+                const float alpha = resc ? __builtin_amdgcn_exp2f(M - t) : 1.0f;
+#pragma unroll
+                for (int db = 0; db < DV / 32; ++db)
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) {
+                        ore[db][r] *= alpha;
+                        oim[db][r] *= alpha;
+                    }
+                z *= alpha;
+            }
+            M = grow ? t : M;
+            return (M == -INFINITY) ? 0.0f : M;
+        }
+    };
+    // exponentials, normaliser and packed weights of one 16-key chunk (own:
+    // the exponent is the rounded logit minus the shift, as in fwd_kernel)
+    auto weights = [&](int kc, float msub, const float (&fre)[8], const float (&fim)[8],
+                       const float (&fm)[8], bool all_live, bool rlive,
+                       bool own) __attribute__((always_inline)) {
+        float wre[8], wim[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            float ex;
+            if constexpr (QKZ) {
+                ex = (all_live || (fm[e] > 0.0f && rlive)) ? 1.0f : 0.0f;
+            } else if (own) {
+#pragma clang fp contract(off)
+                const float lg = x[8 * kc + e] * c;
+                ex = __builtin_amdgcn_exp2f(lg - msub);
+            } else {
+                ex = __builtin_amdgcn_exp2f(fmaf(x[8 * kc + e], c, -msub));
+            }
+            z += ex * fm[e];
+            wre[e] = ex * fre[e];
+            wim[e] = ex * fim[e];
+        }
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            wk.r[kc][e] = (__bf16)wre[e];
+            wk.i[kc][e] = (__bf16)wim[e];
+        }
+    };
+    // vector step of the block at KB of a tile before the query tile (side
+    // data at sb, lane part included): G = S_j C_t P_i (P_i applied to O once,
+    // when the query tile's own keys begin); masked: a dead column or row
+    typedef float v4f __attribute__((ext_vector_type(4)));
+    typedef __attribute__((address_space(3))) const v4f lds_v4f;
+    auto unpack = [](const v4f &a, const v4f &b, float (&o)[8]) __attribute__((always_inline)) {
+        o[0] = a.x; o[1] = a.y; o[2] = a.z; o[3] = a.w;
+        o[4] = b.x; o[5] = b.y; o[6] = b.z; o[7] = b.w;
+    };
+    auto vstep_off = [&](const unsigned char *sb, int kb, bool masked) __attribute__((always_inline)) {
+        lds_v4f *sv = (lds_v4f *)(lds_void *)(sb + 4 * kb);
+#define RD128(r, off) r = __builtin_nontemporal_load(sv + (off) / 16)
+        v4f a0, a1, b0, b1, c0, c1;
+        __builtin_amdgcn_sched_barrier(0);
+        RD128(a0, 0); RD128(a1, 16); RD128(b0, 4 * BK); RD128(b1, 4 * BK + 16); RD128(c0, 8 * BK); RD128(c1, 8 * BK + 16);
+        __builtin_amdgcn_sched_barrier(0);
+        if (!QKZ && masked) {
+            v4f m0, m1;
+            RD128(m0, 8 * BK + 64); RD128(m1, 8 * BK + 80);
+            float fm0[8], fm1[8];
+            unpack(c0, c1, fm0);
+            unpack(m0, m1, fm1);
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                x[e] = (fm0[e] > 0.0f && row_live) ? x[e] : dead_s;
+                x[8 + e] = (fm1[e] > 0.0f && row_live) ? x[8 + e] : dead_s;
+            }
+        }
+        const float msub = block_shift();
+        __builtin_amdgcn_sched_barrier(0);
+        float fre[8], fim[8], fm[8];
+        unpack(a0, a1, fre);
+        unpack(b0, b1, fim);
+        unpack(c0, c1, fm);
+        float ex[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            if constexpr (QKZ)
+                ex[e] = (!masked || (fm[e] > 0.0f && row_live)) ? 1.0f : 0.0f;
+            else
+                ex[e] = __builtin_amdgcn_exp2f(fmaf(x[e], c, -msub));
+            z += ex[e] * fm[e];
+        }
+        __builtin_amdgcn_sched_barrier(0);
+        RD128(a0, 64); RD128(a1, 80); RD128(b0, 4 * BK + 64); RD128(b1, 4 * BK + 80);
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            wk.r[0][e] = (__bf16)(ex[e] * fre[e]);
+            wk.i[0][e] = (__bf16)(ex[e] * fim[e]);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+        RD128(c0, 8 * BK + 64); RD128(c1, 8 * BK + 80);
+        __builtin_amdgcn_sched_barrier(0);
+        unpack(a0, a1, fre);
+        unpack(b0, b1, fim);
+        unpack(c0, c1, fm);
+        weights(1, msub, fre, fim, fm, !masked, row_live, false);
+        __builtin_amdgcn_sched_barrier(0);
+#undef RD128
+    };
+    // vector step of a block of the query tile's own keys: explicit G_ij by a
+    // running product per row, a_i a_{i-1} ... a_{j+1}, last key first (as
+    // fwd_kernel)
+    auto vstep_own = [&](const unsigned char *buf, int kb, int dpos) __attribute__((always_inline)) {
+        const float *side = reinterpret_cast<const float *>(buf + SM::side_off);
+        const int kl = kb + (lane & 31);
+        const float vre = side[kl], vim = side[BK + kl], vm = side[2 * BK + kl];
+        auto key_gate = [](float v, int j) __attribute__((always_inline)) {
+            return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), j));
+        };
+        float Gm[16];
+        const float gre0 = gre, gim0 = gim;
+#pragma unroll
+        for (int jj = 31; jj >= 0; --jj) {
+            const float nm = gm * key_gate(vm, jj);
+            gm = (jj == dpos) ? 1.0f : nm;
+            if (h == ((jj >> 2) & 1)) Gm[4 * (jj >> 3) + (jj & 3)] = gm;
+        }
+        if constexpr (!QKZ) {
+#pragma unroll
+            for (int r = 0; r < 16; ++r) x[r] = (Gm[r] > 0.0f) ? x[r] : dead_s;
+        }
+        const float msub = block_shift();
+        gre = gre0;
+        gim = gim0;
+#pragma unroll
+        for (int kc = 1; kc >= 0; --kc) {
+            float fre[8], fim[8], fm[8];
+#pragma unroll
+            for (int jj = 16 * kc + 15; jj >= 16 * kc; --jj) {
+                const float dr = key_gate(vre, jj), di = key_gate(vim, jj);
+                const float nr = gre * dr - gim * di;
+                const float ni = gre * di + gim * dr;
+                const bool diag = (jj == dpos);
+                gre = diag ? 1.0f : nr;
+                gim = diag ? 0.0f : ni;
+                if (h == ((jj >> 2) & 1)) {
+                    const int e = 4 * ((jj - 16 * kc) >> 3) + (jj & 3);
+                    fre[e] = gre;
+                    fim[e] = gim;
+                }
+            }
+#pragma unroll
+            for (int e = 0; e < 8; ++e) fm[e] = Gm[8 * kc + e];
+            weights(kc, msub, fre, fim, fm, false, true, true);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+    };
+    auto settle_weights = [&]() __attribute__((always_inline)) {
+        settle(wk.r[0]);
+        settle(wk.r[1]);
+        settle(wk.i[0]);
+        settle(wk.i[1]);
+        settle(z);
+    };
+    // an own-tile block (visit index kk = 0..7, highest keys first) is
+    // skipped by the waves whose rows all lie above it
+    auto own_active = [&](int kk) __attribute__((always_inline)) { return kk >= NDB - 1 - w; };
+    auto flag_of = [&](const unsigned char *buf, int blk) __attribute__((always_inline)) {
+        return reinterpret_cast<const uint32_t *>(buf + SM::flag_off)[blk];
+    };
+
+    MPrefetch pf;
+    constexpr int NPRE = 2;  // fragments of each kind requested at the end of a vector step
+    auto zero_w = [&]() __attribute__((always_inline)) {
+#pragma unroll
+        for (int kc = 0; kc < 2; ++kc)
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                wk.r[kc][e] = (__bf16)0.0f;
+                wk.i[kc][e] = (__bf16)0.0f;
+            }
+    };
+    // ---- the phases.  Block k has its matrix step in phase 2k + lag and its
+    // vector step in phase 2k + 1 + lag; a barrier ends every phase.  Tile m
+    // holds blocks 2m and 2m+1.  Every wave issues its copies of tile m+2
+    // after its matrix step of block 2m and waits for its copies of tile m+1
+    // in phase 4m+2 (the leading waves after their matrix step of block 2m+1,
+    // where wave 0 also lands the tile; the trailing ones after their vector
+    // step of block 2m), so that the barrier closing phase 4m+2 publishes
+    // tile m+1.  Every matrix step runs the W~ V of the block before it (W~ = 0
+    // before the first block and after a block a wave skips, so that it adds
+    // exact zeros) and the scores of its own block (ignored by a wave that
+    // skips the block), one instruction sequence for every block: vb below
+    // points at the v^T columns of the previous block.  The first operand
+    // fragments of a matrix step are requested at the end of the vector step
+    // before it.
+    zero_w();
+    const unsigned char *vprev = tile_buf(0) + vlane;
+    if (n_off > 0)
+        pstep_prefetch<D, DV, 0, 0, true, !QKZ, 0, NPRE>(vprev, tile_buf(0) + klane, pf);
+    else
+        pstep_prefetch<D, DV, 0, 32, true, !QKZ, 0, NPRE>(vprev, tile_buf(0) + klane, pf);
+    if (lag) lds_barrier();
+    int m = 0;
+    for (; m < n_off; ++m) {
+        const unsigned char *bufm = tile_buf(m);
+        const unsigned char *kb_ = bufm + klane;
+        const unsigned char *vb_ = bufm + vlane;
+        // block 2m (keys 0..31 of tile m)
+        const uint32_t kflag0 = flag_of(bufm, 0);
+        pstep<D, DV, 0, 0, true, !QKZ, NPRE>(vprev, kb_, pf, wk.r, wk.i, qf, ore, oim, x);
+        issue(m + 2);
+        lds_barrier();
+        vstep_off(bufm + slane, 0, wave_dead_rows || __builtin_amdgcn_readfirstlane(kflag0) != 0u);
+        settle_weights();
+        pstep_prefetch<D, DV, 0, 32, true, !QKZ, 0, NPRE>(vb_, kb_, pf);
+        if (lag) land_wait(m);
+        lds_barrier();
+        // block 2m+1 (keys 32..63)
+        const uint32_t kflag1 = flag_of(bufm, 1);
+        pstep<D, DV, 0, 32, true, !QKZ, NPRE>(vb_, kb_, pf, wk.r, wk.i, qf, ore, oim, x);
+        if (!lag) land_wait(m);
+        lds_barrier();
+        vstep_off(bufm + slane, 32, wave_dead_rows || __builtin_amdgcn_readfirstlane(kflag1) != 0u);
+        settle_weights();
+        vprev = vb_ + 2 * 32;
+        if (m + 1 < n_off)
+            pstep_prefetch<D, DV, 0, 0, true, !QKZ, 0, NPRE>(vprev, tile_buf(m + 1) + klane, pf);
+        else
+            pstep_prefetch<D, DV, 0, 32, true, !QKZ, 0, NPRE>(vprev, tile_buf(m + 1) + klane, pf);
+        lds_barrier();
+    }
+    // ---- the query tile's own tiles: blocks visited highest keys first
+    // (keys 32..63 of a tile, then 0..31); the block of visit index kk of the
+    // NDB is active for wave w when kk >= NDB-1-w.
+    for (int mm = 0; mm < NDIAG; ++mm, ++m) {
+        const unsigned char *bufm = tile_buf(m);
+        const unsigned char *kb_ = bufm + klane;
+        const unsigned char *vb_ = bufm + vlane;
+        const int tl = NDIAG - 1 - mm;  // key tile, counted from t_diag0
+        // block 2mm: keys 32..63 of the tile
+        pstep<D, DV, 0, 32, true, !QKZ, NPRE>(vprev, kb_, pf, wk.r, wk.i, qf, ore, oim, x);
+        issue(m + 2);
+        lds_barrier();
+        if (mm == 0 && n_off > 0) {  // the blocks before the query tile are in O: rotate by P_i
+#pragma unroll
+            for (int db = 0; db < DV / 32; ++db)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    const float xr = ore[db][r], xi = oim[db][r];
+                    ore[db][r] = prow_re * xr - prow_im * xi;
+                    oim[db][r] = prow_re * xi + prow_im * xr;
+                }
+            z *= prow_m;
+        }
+        if (own_active(2 * mm))
+            vstep_own(bufm, 32, 32 * w + qi - (tl * BK + 32));
+        else
+            zero_w();
+        settle_weights();
+        pstep_prefetch<D, DV, 0, 0, true, !QKZ, 0, NPRE>(vb_ + 2 * 32, kb_, pf);
+        if (lag) land_wait(m);
+        lds_barrier();
+        // block 2mm+1: keys 0..31 of the tile
+        pstep<D, DV, 0, 0, true, !QKZ, NPRE>(vb_ + 2 * 32, kb_, pf, wk.r, wk.i, qf, ore, oim, x);
+        if (!lag) land_wait(m);
+        lds_barrier();
+        if (own_active(2 * mm + 1))
+            vstep_own(bufm, 0, 32 * w + qi - tl * BK);
+        else
+            zero_w();
+        settle_weights();
+        vprev = vb_;
+        if (mm + 1 < NDIAG)
+            pstep_prefetch<D, DV, 0, 32, true, !QKZ, 0, NPRE>(vprev, tile_buf(m + 1) + klane, pf);
+        else
+            pstep_prefetch<D, DV, 0, 0, true, false, 0, NPRE>(vprev, vprev, pf);
+        lds_barrier();
+    }
+    // the last block's W~ V (keys 0..31 of the lowest own tile: every wave)
+    pstep<D, DV, 0, 0, true, false, NPRE>(vprev, vprev, pf, wk.r, wk.i, qf, ore, oim, x);
+    lds_barrier();
+    if (!lag) lds_barrier();
+    atomicMax(&misc[3], kbits);
+
+    // ---- epilogue: O *= exp2((1-beta) M) z^-beta -------------------------
+    const float zt = z + __shfl_xor(z, 32);
+    float f;
+    if (A.beta_mode == 1)
+        f = 1.0f / zt;
+    else if (A.beta_mode == 0)
+        f = exp2f(M);
+    else
+        f = exp2f(A.one_minus_beta * M - A.beta * log2f(zt));
+    if (row_ok) {
+        float *orp = A.o_re + (bh * A.n + row) * DV;
+        float *oip = A.o_im + (bh * A.n + row) * DV;
+#pragma unroll
+        for (int db = 0; db < DV / 32; ++db)
+#pragma unroll
+            for (int g4 = 0; g4 < 4; ++g4) {
+                const int d0 = 32 * db + 8 * g4 + 4 * h;
+                float4 vr, vi;
+                vr.x = scale_keep_zero(ore[db][4 * g4 + 0], f);
+                vr.y = scale_keep_zero(ore[db][4 * g4 + 1], f);
+                vr.z = scale_keep_zero(ore[db][4 * g4 + 2], f);
+                vr.w = scale_keep_zero(ore[db][4 * g4 + 3], f);
+                vi.x = scale_keep_zero(oim[db][4 * g4 + 0], f);
+                vi.y = scale_keep_zero(oim[db][4 * g4 + 1], f);
+                vi.z = scale_keep_zero(oim[db][4 * g4 + 2], f);
+                vi.w = scale_keep_zero(oim[db][4 * g4 + 3], f);
+                *reinterpret_cast<float4 *>(orp + d0) = vr;
+                *reinterpret_cast<float4 *>(oip + d0) = vi;
+            }
+    }
+    __syncthreads();
+    if (tid == 0) {
+        const uint32_t qb = misc[2], kb = misc[3];
+        atomicMax(&A.qstat[bh], qb);
+        atomicMax(&A.kstat[bh], kb);
+        if (qb >= kInfBits || kb >= kInfBits) A.status[0] = kNonFinite;
+        atomicAdd(&A.counters[0], uint32_t(n_off));
+    }
+}
+
+// Refusal of an overflowing logit on the bf16 path (padded K tiles): as
+// logit_check_kernel, staging each key tile with the padded copies.
+template <int D>
+__global__ __launch_bounds__(NTHREADS) void logit_check_pad_kernel(FwdArgs A) {
+    constexpr int KSL = pad_kslots<D>();
+    extern __shared__ __align__(16) unsigned char smem[];
+    __shared__ int go;
+    const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, h = lane >> 5, qi = lane & 31;
+    const int L = blockIdx.x;
+    const int64_t qt = A.n_qt - 1 - L / A.BH;
+    const int64_t bh = L % A.BH;
+    if (tid == 0) {
+        const uint32_t qm = A.qstat[bh], km = A.kstat[bh];
+        const double bound = fabs((double)A.c) * (double)D * (double)__uint_as_float(qm) *
+                             (double)__uint_as_float(km) * 1.01;
+        go = !(bound < 3.0e38);
+    }
+    __syncthreads();
+    if (!go) return;
+    const int64_t i0 = qt * BQ;
+    const int64_t row = i0 + 32 * w + qi;
+    const bool row_ok = row < A.n;
+    bf16x8 qf[D / 16];
+    load_q<false, D>(A, bh, row, row_ok, h, qf);
+    const unsigned char *kh, *vh;
+    head_bases<false, D, D>(A, kv_head(A, bh), kh, vh);
+    bool bad = false;
+    const int wu = __builtin_amdgcn_readfirstlane(w);
+    for (int64_t t = 0; t < (i0 + BQ) / BK; ++t) {
+        __syncthreads();
+        for (int j = wu; j < KSL; j += NWAVES)
+            g2lds16(kh, pad_kcopy_src_ragged<D>(j, lane, A.n, t), lds_addr(smem) + uint32_t(1024 * j));
+        __builtin_amdgcn_s_waitcnt(0);
+        __syncthreads();
+#pragma unroll
+        for (int blk = 0; blk < 2; ++blk) {
+            f32x16 s;
+#pragma unroll
+            for (int r = 0; r < 16; ++r) s[r] = 0.f;
+#pragma unroll
+            for (int st = 0; st < D / 16; ++st) {
+                const bf16x8 a =
+                    *reinterpret_cast<const bf16x8 *>(smem + pad_kread<D>(32 * blk, st, qi, h));
+                s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[st], s, 0, 0, 0);
+            }
+            {
+#pragma clang fp contract(off)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    const int64_t j = t * BK + 32 * blk + 8 * (r / 4) + 4 * h + (r % 4);
+                    const float xx = s[r] * A.c;
+                    if (row_ok && j <= row && j < A.n && !isfinite(xx)) bad = true;
+                }
+            }
+        }
+    }
+    if (__any(bad) && lane == 0) A.status[0] = kNonFinite;
+}
+
 GatesArgs gates_args(const Layout &L, const float *u, const float *theta, double g,
                      unsigned char *ws, int32_t *status) {
     auto fptr = [&](int i) { return reinterpret_cast<float *>(ws + L.gate[i]); };
@@ -1742,26 +2573,49 @@ int launch_typed(const Problem &P, hipStream_t st, hipEvent_t const *marks) {
     F.one_minus_beta = 1.0f - P.beta;
     F.beta_mode = P.beta_mode;
     F.qk_zero = P.qk_zero ? 1 : 0;
-    const size_t shm = SM::bytes;
-    if (shm > 65536) {
-        (void)hipFuncSetAttribute(reinterpret_cast<const void *>(&fwd_kernel<F32, D, DV, false>),
-                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)shm);
-        (void)hipFuncSetAttribute(reinterpret_cast<const void *>(&fwd_kernel<F32, D, DV, true>),
-                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)shm);
-        (void)hipFuncSetAttribute(reinterpret_cast<const void *>(&logit_check_kernel<F32, D>),
-                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)shm);
+    if constexpr (F32) {
+        const size_t shm = SM::bytes;
+        if (shm > 65536) {
+            (void)hipFuncSetAttribute(reinterpret_cast<const void *>(&fwd_kernel<F32, D, DV, false>),
+                                      hipFuncAttributeMaxDynamicSharedMemorySize, (int)shm);
+            (void)hipFuncSetAttribute(reinterpret_cast<const void *>(&fwd_kernel<F32, D, DV, true>),
+                                      hipFuncAttributeMaxDynamicSharedMemorySize, (int)shm);
+            (void)hipFuncSetAttribute(reinterpret_cast<const void *>(&logit_check_kernel<F32, D>),
+                                      hipFuncAttributeMaxDynamicSharedMemorySize, (int)shm);
+        }
+        if (marks) (void)hipEventRecord(marks[1], st);
+        if (P.qk_zero)
+            hipLaunchKernelGGL((fwd_kernel<F32, D, DV, true>), dim3(BH * L.n_qt), dim3(NTHREADS),
+                               shm, st, F);
+        else
+            hipLaunchKernelGGL((fwd_kernel<F32, D, DV, false>), dim3(BH * L.n_qt), dim3(NTHREADS),
+                               shm, st, F);
+        if (marks) (void)hipEventRecord(marks[2], st);
+        if (!P.qk_zero)
+            hipLaunchKernelGGL((logit_check_kernel<F32, D>), dim3(BH * L.n_qt), dim3(NTHREADS),
+                               shm, st, F);
+    } else {
+        const size_t shm = PSmem<D, DV>::bytes;
+        if (shm > 65536) {
+            (void)hipFuncSetAttribute(reinterpret_cast<const void *>(&fwd_pad_kernel<D, DV, false>),
+                                      hipFuncAttributeMaxDynamicSharedMemorySize, (int)shm);
+            (void)hipFuncSetAttribute(reinterpret_cast<const void *>(&fwd_pad_kernel<D, DV, true>),
+                                      hipFuncAttributeMaxDynamicSharedMemorySize, (int)shm);
+            (void)hipFuncSetAttribute(reinterpret_cast<const void *>(&logit_check_pad_kernel<D>),
+                                      hipFuncAttributeMaxDynamicSharedMemorySize, (int)shm);
+        }
+        if (marks) (void)hipEventRecord(marks[1], st);
+        if (P.qk_zero)
+            hipLaunchKernelGGL((fwd_pad_kernel<D, DV, true>), dim3(BH * L.n_qt), dim3(NTHREADS),
+                               shm, st, F);
+        else
+            hipLaunchKernelGGL((fwd_pad_kernel<D, DV, false>), dim3(BH * L.n_qt), dim3(NTHREADS),
+                               shm, st, F);
+        if (marks) (void)hipEventRecord(marks[2], st);
+        if (!P.qk_zero)
+            hipLaunchKernelGGL((logit_check_pad_kernel<D>), dim3(BH * L.n_qt), dim3(NTHREADS),
+                               shm, st, F);
     }
-    if (marks) (void)hipEventRecord(marks[1], st);
-    if (P.qk_zero)
-        hipLaunchKernelGGL((fwd_kernel<F32, D, DV, true>), dim3(BH * L.n_qt), dim3(NTHREADS), shm,
-                           st, F);
-    else
-        hipLaunchKernelGGL((fwd_kernel<F32, D, DV, false>), dim3(BH * L.n_qt), dim3(NTHREADS),
-                           shm, st, F);
-    if (marks) (void)hipEventRecord(marks[2], st);
-    if (!P.qk_zero)
-        hipLaunchKernelGGL((logit_check_kernel<F32, D>), dim3(BH * L.n_qt), dim3(NTHREADS), shm,
-                           st, F);
     if (marks) (void)hipEventRecord(marks[3], st);
     return (int)hipGetLastError();
 }

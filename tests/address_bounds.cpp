@@ -78,6 +78,38 @@ static int check(int64_t B, int64_t H, int64_t n, int64_t d, int esz, bool bf16_
                                             (long long)n, (long long)t, dd, c);
                         }
                     }
+            // the padded copies of fwd_pad_kernel, lane by lane: a tile reaching
+            // past key n-1 takes head-relative, clamped K offsets
+            if (bf16_path) {
+                const int64_t head_k = bh * n * row_bytes, head_vt = bh * dv * L.n_pad * 2;
+                const int ksl = d == 128 ? pad_kslots<128>() : pad_kslots<64>();
+                const int nc = ksl + int(dv) * PAD_VSLOTS / 64;
+                for (int j = 0; j < nc; ++j)
+                    for (int lane = 0; lane < 64; ++lane) {
+                        int64_t lo, hi, off;
+                        if (j < ksl) {
+                            lo = head_k;
+                            hi = head_k + n * row_bytes;
+                            if ((t + 1) * BK > n)
+                                off = head_k + (d == 128 ? pad_kcopy_src_ragged<128>(j, lane, n, t)
+                                                         : pad_kcopy_src_ragged<64>(j, lane, n, t));
+                            else
+                                off = head_k + t * BK * row_bytes +
+                                      (d == 128 ? pad_copy_src<128>(j, lane, L.n_pad)
+                                                : pad_copy_src<64>(j, lane, L.n_pad));
+                        } else {
+                            lo = head_vt;
+                            hi = head_vt + dv * L.n_pad * 2;
+                            off = head_vt + t * BK * 2 +
+                                  (d == 128 ? pad_copy_src<128>(j, lane, L.n_pad)
+                                            : pad_copy_src<64>(j, lane, L.n_pad));
+                        }
+                        if ((off < lo || off + 16 > hi) && bad++ < 5)
+                            std::printf("padded copy out of its head: n=%lld d=%lld dv=%lld t=%lld "
+                                        "j=%d lane=%d\n", (long long)n, (long long)d, (long long)dv,
+                                        (long long)t, j, lane);
+                    }
+            }
             // the bf16 copy instructions, lane by lane (kernel helpers)
             if (bf16_path) {
                 const int64_t head_k = bh * n * row_bytes, head_vt = bh * dv * L.n_pad * 2;
@@ -231,6 +263,97 @@ static int check_v_reads(int d) {
                         std::printf("v^T read (kb %d kc %d db %d group %d): bank groups %04x\n", kb,
                                     kc, db, g, used);
                 }
+    return bad;
+}
+
+// The padded bf16 tiles of fwd_pad_kernel (d = D, value width DV), independent
+// of the shape: every copy instruction j < NC is issued by some copying wave;
+// the 64 slots of instruction j (lane L -> slot 64 j + L) hold, for a K slot
+// (row r, chunk c < KSL - 1) exactly the chunk the operand read of (row r,
+// chunk c) addresses, every (row, chunk) of the K and v^T tiles is held by
+// exactly one non-padding slot, every operand read stays inside the K or
+// v^T tile, and each 16-lane group of an operand read touches 16 distinct
+// bank groups (16-byte units modulo 16).
+template <int D, int DV>
+static int check_pad_layout() {
+    constexpr int KSL = pad_kslots<D>(), NC = pad_copies<D, DV>(), CPW = pad_copies_per_wave<D, DV>();
+    constexpr int kbytes = 1024 * pad_kcopies<D>(), vbytes = 1024 * pad_vcopies<DV>();
+    int bad = 0;
+    auto fail = [&](const char *what, int a, int b) {
+        if (bad++ < 10) std::printf("pad layout d=%d dv=%d: %s (%d, %d)\n", D, DV, what, a, b);
+    };
+    std::vector<int> issued(NC, 0);
+    for (int w = 1; w < NWAVES; ++w)
+        for (int i = 0; i < CPW; ++i) {
+            const int j = pad_copy_j<D, DV>(w, i);
+            if (j < 0 || j >= NC) fail("copy index", w, i);
+            else issued[j] += 1;
+        }
+    for (int j = 0; j < NC; ++j)
+        if (!issued[j]) fail("copy never issued", j, 0);
+    if (1024 * NC != kbytes + vbytes) fail("copies do not tile the buffer", NC, 0);
+    // which slot holds (row, chunk): from the copies (source side)
+    std::vector<int> kslot(BK * (D / 8), -1), vslot(DV * 8, -1);
+    const int64_t n_pad = 4096;  // any v^T row stride
+    for (int j = 0; j < NC; ++j)
+        for (int lane = 0; lane < 64; ++lane) {
+            const int p = 64 * j + lane;
+            const uint32_t src = pad_copy_src<D>(j, lane, n_pad);
+            if (j < KSL) {
+                const int r = int(src / (D * 2)), c = int(src % (D * 2)) / 16;
+                if (r < 0 || r >= BK || c < 0 || c >= D / 8) { fail("K copy source", j, lane); continue; }
+                if (p % KSL != KSL - 1) {  // not the padding slot
+                    if (kslot[r * (D / 8) + c] != -1) fail("K chunk copied twice", r, c);
+                    kslot[r * (D / 8) + c] = p;
+                    if (p / KSL != r || p % KSL != c) fail("K slot holds another chunk", r, c);
+                }
+            } else {
+                const int q = p - 64 * KSL;
+                const int r = int(src / (n_pad * 2)), c = int(src % (n_pad * 2)) / 16;
+                if (r < 0 || r >= DV || c < 0 || c >= 8) { fail("v^T copy source", j, lane); continue; }
+                if (q % PAD_VSLOTS != PAD_VSLOTS - 1) {
+                    if (vslot[r * 8 + c] != -1) fail("v^T chunk copied twice", r, c);
+                    vslot[r * 8 + c] = p;
+                    if (q / PAD_VSLOTS != r || q % PAD_VSLOTS != c) fail("v^T slot holds another chunk", r, c);
+                }
+            }
+        }
+    for (size_t x = 0; x < kslot.size(); ++x)
+        if (kslot[x] < 0) fail("K chunk never copied", int(x / (D / 8)), int(x % (D / 8)));
+    for (size_t x = 0; x < vslot.size(); ++x)
+        if (vslot[x] < 0) fail("v^T chunk never copied", int(x / 8), int(x % 8));
+    // operand reads (reader side)
+    for (int kb = 0; kb < BK; kb += 32) {
+        for (int st = 0; st < D / 16; ++st)
+            for (int g = 0; g < 4; ++g) {
+                const int h = g >> 1;
+                unsigned used = 0;
+                for (int q = 0; q < 16; ++q) {
+                    const int qi = 16 * (g & 1) + q;
+                    const int off = pad_kread<D>(kb, st, qi, h);
+                    if (off < 0 || off + 16 > kbytes) fail("K read outside the K tile", kb, st);
+                    else if (off != 16 * kslot[(kb + qi) * (D / 8) + 2 * st + h])
+                        fail("K read misses its chunk", kb + qi, 2 * st + h);
+                    used |= 1u << ((off / 16) % 16);
+                }
+                if (used != 0xFFFFu) fail("K read bank groups", kb, int(used));
+            }
+        for (int kc = 0; kc < 2; ++kc)
+            for (int db = 0; db < DV / 32; ++db)
+                for (int g = 0; g < 4; ++g) {
+                    const int h = g >> 1;
+                    unsigned used = 0;
+                    for (int q = 0; q < 16; ++q) {
+                        const int qi = 16 * (g & 1) + q;
+                        const int off = pad_vread<D>(kb, kc, db, qi, h);
+                        if (off < kbytes || off + 16 > kbytes + vbytes) fail("v^T read outside the tile", kb, kc);
+                        else if (off != 16 * vslot[(32 * db + qi) * 8 + kb / 8 + 2 * kc + h])
+                            fail("v^T read misses its chunk", 32 * db + qi, kb / 8 + 2 * kc + h);
+                        used |= 1u << ((off / 16) % 16);
+                    }
+                    if (used != 0xFFFFu) fail("v^T read bank groups", kb, int(used));
+                }
+    }
     return bad;
 }
 
@@ -427,7 +550,9 @@ static int check_chain(int64_t B, int64_t H, int64_t n, int64_t dv, int esz) {
 }
 
 int main(int argc, char **argv) {
-    int bad = check_tile_layout<16>("K d=128") + check_tile_layout<8>("K d=64 / v^T") +
+    int bad = check_pad_layout<128, 128>() + check_pad_layout<128, 64>() +
+              check_pad_layout<64, 128>() + check_pad_layout<64, 64>();
+    bad += check_tile_layout<16>("K d=128") + check_tile_layout<8>("K d=64 / v^T") +
               check_operand_reads<16>() + check_operand_reads<8>() + check_v_reads(64) +
               check_v_reads(128);
     int cases = 0;
