@@ -25,6 +25,7 @@ PEAK_HBM_GBS = 8000.0
 KERNEL_SOURCE = os.path.join(ROOT, "gated_causal_attention_amd", "csrc", "resolvent_kernels.hip")
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "fwd_kernel_traffic_headline.json")
 METRIC = "resolvent-head fwd TFLOP/s + Mtokens/s at n=8192,d=128; % bf16 MFMA peak"
+FWD_KERNEL = "fwd_pad_kernel"  # the fused kernel of the bf16 path (rocprofv3 kernel-name filter)
 
 
 def kernel_source_sha():
@@ -78,8 +79,8 @@ def summarize_traffic(fetch_dir, write_dir, copy_fetch_dir, copy_write_dir, copy
     dispatch), each divided by what the same counter reads per byte of a plain
     device copy of copy_bytes (torch copy_ of one device tensor into another: the
     runtime's copyBuffer kernel, which reads and writes copy_bytes)."""
-    kf, nkf = counter_per_dispatch(fetch_dir, "FETCH_SIZE", "fwd_kernel")
-    kw, nkw = counter_per_dispatch(write_dir, "WRITE_SIZE", "fwd_kernel")
+    kf, nkf = counter_per_dispatch(fetch_dir, "FETCH_SIZE", FWD_KERNEL)
+    kw, nkw = counter_per_dispatch(write_dir, "WRITE_SIZE", FWD_KERNEL)
     cf, _ = counter_per_dispatch(copy_fetch_dir, "FETCH_SIZE", "copyBuffer")
     cw, _ = counter_per_dispatch(copy_write_dir, "WRITE_SIZE", "copyBuffer")
     f_fac = cf * 1024.0 / copy_bytes
@@ -87,7 +88,7 @@ def summarize_traffic(fetch_dir, write_dir, copy_fetch_dir, copy_write_dir, copy
     fetch = kf * 1024.0 / f_fac
     write = kw * 1024.0 / w_fac
     return {
-        "kernel": "fwd_kernel<bf16, d=128> (headline workload, switches (1,1,1))",
+        "kernel": "fwd_pad_kernel<d=128, dv=128> (headline workload, switches (1,1,1))",
         "kernel_source_sha256": kernel_source_sha(),
         "fetch_size_kib_per_dispatch": kf, "write_size_kib_per_dispatch": kw,
         "dispatches": [nkf, nkw],
@@ -142,11 +143,11 @@ def summarize_counters(dirs):
     vals = {}
     for d, names in zip(dirs, COUNTER_PASSES):
         for c in names.split():
-            vals.setdefault(c, counter_per_dispatch(d, c, "fwd_kernel")[0])
+            vals.setdefault(c, counter_per_dispatch(d, c, FWD_KERNEL)[0])
     busy = vals["SQ_VALU_MFMA_BUSY_CYCLES"]
     gui = vals["GRBM_GUI_ACTIVE"]
     out = {
-        "kernel": "fwd_kernel<bf16, d=128> (headline workload, switches (1,1,1))",
+        "kernel": "fwd_pad_kernel<d=128, dv=128> (headline workload, switches (1,1,1))",
         "kernel_source_sha256": kernel_source_sha(),
         "counters_per_dispatch": vals,
         "mfma_busy_pct": 100.0 * busy / (gui / XCDS * SIMDS),
@@ -726,7 +727,7 @@ def main():
                      "logit_check": float(np.mean(post_ms))},
         "roofline": {"bound": "mfma", "achieved": achieved, "peak": PEAK_BF16_TFLOPS,
                      "unit": "TFLOP/s", "frac": achieved / PEAK_BF16_TFLOPS,
-                     "traffic": traffic, "kernel": "fwd_kernel<bf16, d=128>",
+                     "traffic": traffic, "kernel": "fwd_pad_kernel<d=128, dv=128>",
                      "flops_per_launch": alg_flops, "executed_mfma_flops": exec_flops,
                      "executed_mfma_tflops": exec_flops / (fwd_avg * 1e-3) / 1e12,
                      "counters": measured_counters(sha)},
