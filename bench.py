@@ -23,7 +23,7 @@ sys.path.insert(0, ROOT)
 PEAK_BF16_TFLOPS = 2516.6  # MI355X dense bf16 MFMA: 256 CU x 4096 FLOP/clk x 2.4 GHz
 PEAK_HBM_GBS = 8000.0
 KERNEL_SOURCE = os.path.join(ROOT, "gated_causal_attention_amd", "csrc", "resolvent_kernels.hip")
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "fwd_kernel_traffic_headline.json")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "fwd_pad_kernel_traffic_headline.json")
 METRIC = "resolvent-head fwd TFLOP/s + Mtokens/s at n=8192,d=128; % bf16 MFMA peak"
 FWD_KERNEL = "fwd_pad_kernel"  # the fused kernel of the bf16 path (rocprofv3 kernel-name filter)
 
@@ -110,7 +110,7 @@ def summarize_traffic(fetch_dir, write_dir, copy_fetch_dir, copy_write_dir, copy
     }
 
 
-COUNTER_FILE = os.path.join(ROOT, "profiles", "fwd_kernel_counters_headline.json")
+COUNTER_FILE = os.path.join(ROOT, "profiles", "fwd_pad_kernel_counters_headline.json")
 # rocprofv3 --pmc passes over the headline bench (each within one pass's
 # hardware limits: at most 8 SQ_, 4 TCC_ and 2 GRBM_ counters)
 COUNTER_PASSES = (
