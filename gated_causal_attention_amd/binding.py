@@ -41,6 +41,13 @@ def _load():
         raise RuntimeError(
             f"{library_path} is missing: build it first (python -c 'import __graft_entry__ as g; "
             "g.build()'); there is no fallback implementation")
+    # torch ships its own HIP runtime (libamdhip64) and HSA runtime.  Loading
+    # torch first lets the library's libamdhip64.so.7 dependency resolve to
+    # that same runtime by soname; loaded the other way round the process
+    # holds two HIP runtimes, torch's streams and device state are not the
+    # library's, and its HIP calls can fail (hipErrorNoDevice) or misbehave.
+    import torch  # noqa: F401
+
     lib = ctypes.CDLL(library_path)
     i64, i32, vp, dbl = ctypes.c_int64, ctypes.c_int32, ctypes.c_void_p, ctypes.c_double
     lib.resolvent_workspace_bytes.argtypes = [i64, i64, i64, i64, i32, i32]
