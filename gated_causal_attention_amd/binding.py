@@ -22,6 +22,7 @@ class Status(enum.IntEnum):
     BAD_ARG = 3
     UNSUPPORTED = 4
     DEVICE_ERROR = 5
+    TOO_LARGE = 6
 
 
 class ResolventError(RuntimeError):
@@ -57,6 +58,11 @@ def _load():
     lib.resolvent_forward.restype = i32
     lib.resolvent_forward_marked.argtypes = lib.resolvent_forward.argtypes + [vp]
     lib.resolvent_forward_marked.restype = i32
+    lib.resolvent_forward_noalloc.argtypes = [vp, vp, vp, vp, vp, dbl, dbl, dbl, i64, i64, i64,
+                                              i64, i32, i32, vp, vp, vp, vp]
+    lib.resolvent_forward_noalloc.restype = i32
+    lib.resolvent_noalloc_scratch_bytes.argtypes = []
+    lib.resolvent_noalloc_scratch_bytes.restype = ctypes.c_size_t
     lib.resolvent_counters_offset.argtypes = [i64, i64, i64, i64, i32, i32]
     lib.resolvent_counters_offset.restype = ctypes.c_size_t
     lib.resolvent_tile_shape.argtypes = [ctypes.POINTER(i32), ctypes.POINTER(i32)]
@@ -159,6 +165,42 @@ def resolvent_forward(q, k, u, theta, v, beta, qk, g, *, o_re=None, o_im=None, w
     else:
         arr = (ctypes.c_void_p * 4)(*marks)
         rc = _load().resolvent_forward_marked(*args, arr)
+    if rc != Status.OK:
+        raise ResolventError(rc)
+    if check and n > 0 and B > 0 and H > 0:
+        if hasattr(stream, "synchronize"):
+            stream.synchronize()
+        else:
+            torch.cuda.synchronize(dev)
+        st = int(status.item())
+        if st != Status.OK:
+            raise ResolventError(st)
+    return o_re, o_im
+
+
+def resolvent_noalloc_scratch_bytes() -> int:
+    return int(_load().resolvent_noalloc_scratch_bytes())
+
+
+def resolvent_forward_noalloc(q, k, u, theta, v, beta, qk, g, *, o_re, o_im, status,
+                              stream=None, check=True):
+    """resolvent_forward with the library's fixed device scratch as workspace:
+    the caller passes every buffer (outputs and status included) and nothing
+    is allocated.  Raises ResolventError(TOO_LARGE) beyond the scratch size."""
+    import torch
+
+    B, H, n, d = q.shape
+    for t in (q, k, v, u, theta, o_re, o_im):
+        if not t.is_contiguous():
+            raise ValueError("tensors must be contiguous")
+    dev = q.device
+    if stream is None:
+        stream = torch.cuda.current_stream(dev)
+    handle = stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
+    rc = _load().resolvent_forward_noalloc(
+        q.data_ptr(), k.data_ptr(), u.data_ptr(), theta.data_ptr(), v.data_ptr(), float(beta),
+        float(qk), float(g), B, H, n, d, _dtype_code(q), _dtype_code(v), o_re.data_ptr(),
+        o_im.data_ptr(), status.data_ptr(), handle)
     if rc != Status.OK:
         raise ResolventError(rc)
     if check and n > 0 and B > 0 and H > 0:

@@ -32,7 +32,8 @@ def build_library(verbose: bool = False) -> str:
     os.makedirs(BUILD, exist_ok=True)
     hipcc = _hipcc()
     kobjs = []
-    for src in ("resolvent_kernels", "chain_kernels", "decode_kernels", "export_kernels"):
+    for src in ("resolvent_kernels", "chain_kernels", "decode_kernels", "export_kernels",
+                "noalloc"):
         kobjs.append(os.path.join(BUILD, src + ".o"))
         _run([hipcc, f"--offload-arch={ARCH}", *COMMON, *DEVICE_FLAGS, "-c",
               os.path.join(CSRC, src + ".hip"), "-o", kobjs[-1]], verbose)

@@ -302,6 +302,7 @@ const char *resolvent_status_str(int32_t status) {
         case RESOLVENT_BAD_ARG: return "bad argument";
         case RESOLVENT_UNSUPPORTED: return "unsupported head_dim or dtype";
         case RESOLVENT_DEVICE_ERROR: return "device error";
+        case RESOLVENT_TOO_LARGE: return "problem exceeds the no-allocation scratch";
         default: return "unknown status";
     }
 }

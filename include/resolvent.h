@@ -47,7 +47,8 @@ enum resolvent_status {
     RESOLVENT_BAD_SHAPE = 2,   /* negative size, or head_dim 0 with n > 0     */
     RESOLVENT_BAD_ARG = 3,     /* null/misaligned pointer, small workspace    */
     RESOLVENT_UNSUPPORTED = 4, /* head_dim or dtype pair this build lacks     */
-    RESOLVENT_DEVICE_ERROR = 5 /* a HIP launch failed                         */
+    RESOLVENT_DEVICE_ERROR = 5, /* a HIP launch failed                        */
+    RESOLVENT_TOO_LARGE = 6     /* beyond resolvent_forward_noalloc's scratch  */
 };
 
 /* Storage types of q, k and v. */
@@ -123,6 +124,38 @@ int32_t resolvent_forward_marked(const void *q, const void *k, const float *u,
                                  int32_t qk_dtype, int32_t v_dtype, float *o_re, float *o_im,
                                  void *workspace, size_t workspace_bytes, int32_t *status_dev,
                                  hipStream_t stream, hipEvent_t *marks);
+
+/*
+ * resolvent_forward_noalloc -- resolvent_forward for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc): no workspace argument; the workspace is a
+ * fixed array of RESOLVENT_NOALLOC_SCRATCH_BYTES bytes inside the library,
+ * one per device, held from the library's first use on that device until the
+ * process ends.  The call allocates nothing; the caller still owns q, k, u,
+ * theta, v, o_re, o_im and status_dev, with the meanings, layouts and checks
+ * of resolvent_forward.
+ *
+ * Returns RESOLVENT_TOO_LARGE, before anything is enqueued, when
+ * resolvent_workspace_bytes(B, H, n, d, qk_dtype, v_dtype) exceeds
+ * RESOLVENT_NOALLOC_SCRATCH_BYTES (64 MiB: for example B*H = 16 heads of
+ * n = 8192 at d = 128 in bf16 need 36.6 MiB); RESOLVENT_DEVICE_ERROR when the
+ * array's device address cannot be obtained; otherwise what resolvent_forward
+ * returns.  The stream must belong to the current device.  Every call on a
+ * device uses that device's one array, so calls that overlap in time on one
+ * device (two streams, two threads) race and give unspecified outputs; calls
+ * ordered on one stream are safe.  Each call clears on the device whatever
+ * of the array must start at zero, so what an earlier call left there does
+ * not matter.
+ */
+#define RESOLVENT_NOALLOC_SCRATCH_BYTES (64u << 20)
+
+size_t resolvent_noalloc_scratch_bytes(void);
+
+int32_t resolvent_forward_noalloc(const void *q, const void *k, const float *u,
+                                  const float *theta, const void *v, double beta, double qk,
+                                  double g, int64_t B, int64_t H, int64_t n, int64_t d,
+                                  int32_t qk_dtype, int32_t v_dtype, float *o_re, float *o_im,
+                                  int32_t *status_dev, hipStream_t stream);
 
 /*
  * resolvent_workspace_bytes_grouped -- device workspace for

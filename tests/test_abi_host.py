@@ -95,6 +95,23 @@ def test_workspace_sizes():
     assert ws(1, 1, 1 << 22, 128) < 4 << 30
 
 
+def test_noalloc_host_checks():
+    lib = binding._load()
+    assert lib.resolvent_noalloc_scratch_bytes() == 64 << 20
+
+    def na(B=1, H=1, n=128, d=64):
+        return lib.resolvent_forward_noalloc(FAKE, FAKE, FAKE, FAKE, FAKE, 1.0, 1.0, 1.0, B, H,
+                                             n, d, 0, 0, FAKE, FAKE, FAKE, None)
+
+    # refused on the host before the scratch array is looked up
+    assert lib.resolvent_workspace_bytes(4, 16, 8192, 128, 0, 0) > 64 << 20
+    assert na(B=4, H=16, n=8192, d=128) == S.TOO_LARGE
+    assert na(B=-1) == S.BAD_SHAPE
+    assert na(n=0) == S.OK
+    assert na(d=0) == S.BAD_SHAPE
+    assert na(d=96) == S.UNSUPPORTED
+
+
 def test_status_strings():
     for s in S:
         text = binding.resolvent_status_str(int(s))
