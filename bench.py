@@ -8,6 +8,9 @@ Prints one JSON line: the throughput, the per-stage times from HIP events, the
 roofline object of the fused kernel and the oracle's CPU rate.
 
   python bench.py [--steps K] [--warmup W] [--gpus 1] [--no-cpu-baseline]
+  python bench.py --workload {2,4,5} [--fp32]   # other workloads, one line per
+                                                # switch setting; --fp32: the fp32 path
+  python bench.py --path {chain,grouped,decode,operator}   # the other entry points
   python bench.py --copy-bytes N   # a plain copy kernel, for counter calibration
 """
 import argparse
@@ -183,15 +186,21 @@ def measured_counters(sha):
     return {k: rec[k] for k in keys}
 
 
-def cpu_baseline(inp, sw, heads):
-    """The fp64 oracle, as it stands, on whole heads of the same inputs."""
+def cpu_baseline(inp, sw, heads, rows=None, flops_per_pair=None):
+    """The fp64 oracle, as it stands, on the given heads (all rows, or the given
+    rows) of the same inputs; FLOPs are counted dense-causal: row i has i+1
+    pairs of flops_per_pair (default 6 d) each."""
     import numpy as np
 
     import oracle
 
     threads = oracle.default_threads()
     n, d = inp["n"], inp["d"]
-    rows = np.arange(n)
+    if flops_per_pair is None:
+        flops_per_pair = 6 * d
+    all_rows = rows is None
+    if all_rows:
+        rows = np.arange(n)
     t0 = time.perf_counter()
     for b, h in heads:
         st, _ = oracle.forward_rows(inp["q"][b, h], inp["k"][b, h], inp["u"][b, h],
@@ -199,12 +208,27 @@ def cpu_baseline(inp, sw, heads):
                                     nthreads=threads)
         assert st == oracle.OK
     dt = time.perf_counter() - t0
-    flops = 3.0 * n * (n + 1) * d * len(heads)  # dense-causal MFMA-equivalent FLOPs
+    flops = float(flops_per_pair) * float(np.sum(rows + 1)) * len(heads)
+    what = (f"all {n} rows" if all_rows
+            else f"{len(rows)} of {n} rows (every {rows[1] - rows[0]}th from {rows[0]})")
     return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
-            "sample": f"{len(heads)} whole heads (b,h) = {heads} of the same workload, all "
-                      f"{n} rows, fp64; {dt:.2f} s; FLOPs counted dense-causal (3 n(n+1) d "
-                      f"per head)",
-            "seconds": dt, "head_tokens_per_s": len(heads) * n / dt}
+            "sample": f"{len(heads)} heads (b,h) = {heads} of the same workload, {what}, "
+                      f"fp64; {dt:.2f} s; FLOPs counted dense-causal ({flops_per_pair} per "
+                      f"(query, key) pair, i+1 pairs in row i)",
+            "cpu_model": cpu_model(),
+            "seconds": dt, "head_tokens_per_s": len(heads) * len(rows) / dt}
+
+
+def cpu_model():
+    """The host CPU's model name, from /proc/cpuinfo."""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
 
 
 def chain_cpu_baseline(inp, g, heads):
@@ -224,6 +248,7 @@ def chain_cpu_baseline(inp, g, heads):
     dt = time.perf_counter() - t0
     nbytes = len(heads) * n * (8 + 2 * dv + 8 * dv)
     return {"value": nbytes / dt / 1e9, "unit": "GB/s", "cores": 1, "kind": "oracle",
+            "cpu_model": cpu_model(),
             "sample": f"{len(heads)} whole heads of the same inputs, all {dv} channels, fp64, "
                       f"one thread; {dt:.2f} s; bytes counted as on the device (u, theta, "
                       f"bf16 v in, fp32 O out)",
@@ -393,6 +418,7 @@ def bench_grouped(args):
         flops = (d + 2 * dv) * n * (n + 1) * len(heads)
         out["cpu_baseline"] = {"value": flops / dt / 1e12, "unit": "TFLOP/s",
                                "cores": oracle.default_threads(), "kind": "oracle",
+                               "cpu_model": cpu_model(),
                                "sample": f"{len(heads)} whole heads {heads}, all {n} rows, fp64; "
                                          f"{dt:.2f} s; FLOPs counted dense-causal"}
     print(json.dumps(out), flush=True)
@@ -486,7 +512,7 @@ def bench_decode(args):
             done += 1
         dt = time.perf_counter() - t0
         out["cpu_baseline"] = {"value": done * per_head / dt / 1e9, "unit": "GB/s", "cores": 1,
-                               "kind": "oracle",
+                               "kind": "oracle", "cpu_model": cpu_model(),
                                "sample": f"{done} head decode steps (row n-1 of the same "
                                          f"heads, cycled), fp64, one thread; {dt:.2f} s; "
                                          f"bytes counted as on the device"}
@@ -581,77 +607,69 @@ def bench_operator(args):
         dt = time.perf_counter() - t0
         per_head = 2 * n * d * 2 + 8 * n + 8 * n * n
         out["cpu_baseline"] = {"value": len(heads) * per_head / dt / 1e9, "unit": "GB/s",
-                               "cores": 1, "kind": "oracle",
+                               "cores": 1, "kind": "oracle", "cpu_model": cpu_model(),
                                "sample": f"the oracle's operator on heads {heads}, fp64, one "
                                          f"thread; {dt:.2f} s; bytes counted as on the device"}
     print(json.dumps(out), flush=True)
 
 
-def main():
-    ap = argparse.ArgumentParser()
-    ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--copy-bytes", type=int, default=0)
-    ap.add_argument("--path", choices=("forward", "chain", "grouped", "decode", "operator"),
-                    default="forward",
-                    help="forward: the head (the headline line); chain: the chain-corner "
-                         "scan; grouped: shared k/v heads and another value width; decode: "
-                         "one decode step against an n-position cache; operator: the "
-                         "materialising exports")
-    ap.add_argument("--summarize-traffic", nargs=4, metavar=("FETCH", "WRITE", "COPY_FETCH",
-                                                              "COPY_WRITE"))
-    ap.add_argument("--summarize-counters", nargs=len(COUNTER_PASSES),
-                    metavar=tuple(f"PASS{i}" for i in range(len(COUNTER_PASSES))))
-    args = ap.parse_args()
-    if args.summarize_traffic:
-        print(json.dumps(summarize_traffic(*args.summarize_traffic, args.copy_bytes), indent=1))
-        return
-    if args.summarize_counters:
-        print(json.dumps(summarize_counters(args.summarize_counters), indent=1))
-        return
-    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py measures one GPU: the resolvent head's heads are independent and the "
-              "library has no multi-GPU path (a sharded run would split the (batch, head) "
-              "pairs over the GPUs); run with --gpus 1",
-              file=sys.stderr)
-        sys.exit(2)
+PEAK_FP32_MFMA_TFLOPS = 157.3  # MI355X dense fp32 MFMA
 
+
+def _workload_inputs(widx, fp32):
+    """The seeded inputs of workload widx; with fp32 the same draw (seed, shape,
+    distributions) in fp32 q, k, v storage, for the fp32 MFMA path."""
+    from gated_causal_attention_amd import inputs
+
+    if not fp32:
+        return inputs.make_config(widx)
+    w = inputs.WORKLOADS[widx]
+    return inputs.draw(w.B, w.H, w.n, w.d, widx, inputs.F32, inputs.F32, w.qk_scale, w.gates,
+                       w.u_range, w.theta_range)
+
+
+def _describe(inp, widx, sw, fp32):
+    from gated_causal_attention_amd import inputs
+
+    w = inputs.WORKLOADS[widx]
+    dt = "fp32 q,k,v" if fp32 else f"{w.qk_dtype} q,k, {w.v_dtype} v"
+    if w.gates == "bedm":
+        gates = "gates in {-1,0,+1} with p = (0.05, 0.01, 0.94)"
+    elif w.theta_range[0] == w.theta_range[1]:
+        gates = f"u ~ U{tuple(w.u_range)}, theta = {w.theta_range[0]}"
+    else:
+        gates = (f"u ~ U{tuple(w.u_range)}, theta ~ U({w.theta_range[0]:.3g},"
+                 f"{w.theta_range[1]:.3g})")
+    scale = "" if w.qk_scale == 1.0 else f", q,k scaled by {w.qk_scale}"
+    return (f"resolvent head B={inp['B']} H={inp['H']} n={inp['n']} d={inp['d']}, {dt} "
+            f"~ N(0,1){scale}, {gates}, switches {tuple(sw)}, seed {widx}")
+
+
+def forward_line(args, widx, sw, fp32, headline, inp=None):
+    """Time resolvent_forward on workload widx at switches sw and print one JSON
+    line: throughput, stage times from HIP events on the call's stream, the
+    fused kernel's roofline (matrix or HBM bound, whichever its algorithmic
+    work puts first at peak) and the oracle's CPU rate on a bounded sample."""
     import numpy as np
     import torch
-
-    if args.copy_bytes:  # the calibration copy of the traffic counters
-        copy_calibration(args.copy_bytes)
-        return
-
-    if args.path == "chain":
-        bench_chain(args)
-        return
-    if args.path == "grouped":
-        bench_grouped(args)
-        return
-    if args.path == "decode":
-        bench_decode(args)
-        return
-    if args.path == "operator":
-        bench_operator(args)
-        return
 
     from gated_causal_attention_amd import binding, inputs
 
     dev = torch.device("cuda:0")
-    sw = (1, 1, 1)
-    inp = inputs.make_config(3)
+    if inp is None:
+        inp = _workload_inputs(widx, fp32)
     B, H, n, d = inp["B"], inp["H"], inp["n"], inp["d"]
+    dv = inp["v"].shape[-1]
+    qdt = binding.F32 if inp["qk_dtype"] == inputs.F32 else binding.BF16
+    vdt = binding.F32 if inp["v_dtype"] == inputs.F32 else binding.BF16
     t = inputs.as_torch(inp, dev)
     o_re = torch.empty((B, H, n, d), device=dev, dtype=torch.float32)
     o_im = torch.empty_like(o_re)
-    ws_bytes = binding.resolvent_workspace_bytes(B, H, n, d, binding.BF16, binding.BF16)
+    ws_bytes = binding.resolvent_workspace_bytes(B, H, n, d, qdt, vdt)
     ws = torch.empty(ws_bytes, device=dev, dtype=torch.uint8)
     status = torch.zeros(1, device=dev, dtype=torch.int32)
     stream = torch.cuda.current_stream(dev)
-    cnt_off = binding.resolvent_counters_offset(B, H, n, d, binding.BF16, binding.BF16)
+    cnt_off = binding.resolvent_counters_offset(B, H, n, d, qdt, vdt)
 
     def step(marks=None):
         binding.resolvent_forward(t["q"], t["k"], t["u"], t["theta"], t["v"], *sw, o_re=o_re,
@@ -692,16 +710,37 @@ def main():
     diag_pairs = B * H * sum(min(BQ, n - q * BQ) * (min(BQ, n - q * BQ) + 1) // 2
                              for q in range(n_qt))
     eval_pairs = off_tiles * BQ * BK + diag_pairs
-    flops_per_pair = 6 * d  # 2d logit + 4d complex readout (two real-by-real products)
+    # 2d for the logit (none at qk = 0, where the logit matrix is skipped) and
+    # 4 dv for the complex readout (two real-by-real products)
+    flops_per_pair = (2 * d if sw[1] != 0 else 0) + 4 * dv
     alg_flops = flops_per_pair * eval_pairs
-    dense_flops = 3.0 * n * (n + 1) * d * B * H
+    dense_flops = (flops_per_pair / 2.0) * n * (n + 1) * B * H
     nw = BQ // 32  # waves per query tile; wave w runs w+1 blocks of 32x32 on the diagonal
     diag_blocks_exec = B * H * n_qt * (nw * (nw + 1) // 2)
     exec_flops = flops_per_pair * (off_tiles * BQ * BK + diag_blocks_exec * 32 * 32)
-
-    achieved = alg_flops / (fwd_avg * 1e-3) / 1e12
+    # HBM bytes the problem moves once: q, k, v and u, theta in; O_re, O_im out
+    esz = {inputs.F32: 4, inputs.BF16: 2}
+    alg_bytes = B * H * n * (2 * d * esz[inp["qk_dtype"]] + dv * esz[inp["v_dtype"]] + 8
+                             + 8 * dv)
+    peak_flops = PEAK_FP32_MFMA_TFLOPS if fp32 else PEAK_BF16_TFLOPS
+    mfma_bound = alg_flops / (peak_flops * 1e12) >= alg_bytes / (PEAK_HBM_GBS * 1e9)
+    kname = (f"fwd_kernel<fp32, d={d}, dv={dv}>" if fp32
+             else f"fwd_pad_kernel<d={d}, dv={dv}{', qk=0' if sw[1] == 0 else ''}>")
+    if mfma_bound:
+        achieved = alg_flops / (fwd_avg * 1e-3) / 1e12
+        roof = {"bound": "mfma", "achieved": achieved, "peak": peak_flops, "unit": "TFLOP/s",
+                "frac": achieved / peak_flops}
+    else:
+        achieved = alg_bytes / (fwd_avg * 1e-3) / 1e9
+        roof = {"bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                "frac": achieved / PEAK_HBM_GBS}
     sha = kernel_source_sha()
-    traffic = measured_traffic(sha)
+    roof.update({"traffic": measured_traffic(sha) if headline else None, "kernel": kname,
+                 "flops_per_launch": alg_flops, "bytes_per_launch": alg_bytes,
+                 "executed_mfma_flops": exec_flops,
+                 "executed_mfma_tflops": exec_flops / (fwd_avg * 1e-3) / 1e12})
+    if headline:
+        roof["counters"] = measured_counters(sha)
     out = {
         "metric": METRIC,
         "value": alg_flops / (ms_per_step * 1e-3) / 1e12,
@@ -713,29 +752,111 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16",
+        "dtype": "f32" if fp32 else "bf16",
         "data": "synthetic",
-        "config": {"workload": "resolvent head B=4 H=16 n=8192 d=128, bf16 q,k,v ~ N(0,1), "
-                               "u ~ U(0.95,1), theta ~ U(-0.05,0.05), switches (1,1,1), seed 3",
-                   "B": B, "H": H, "n": n, "d": d, "switches": list(sw)},
+        "config": {"workload": _describe(inp, widx, sw, fp32), "B": B, "H": H, "n": n, "d": d,
+                   "switches": list(sw)},
         "mtokens_per_s": B * n / (ms_per_step * 1e-3) / 1e6,
         "head_mtokens_per_s": B * H * n / (ms_per_step * 1e-3) / 1e6,
-        "pct_bf16_mfma_peak": 100.0 * achieved / PEAK_BF16_TFLOPS,
+        "hbm_gbs_whole_call": alg_bytes / (ms_per_step * 1e-3) / 1e9,
+        "pct_mfma_peak": 100.0 * alg_flops / (fwd_avg * 1e-3) / 1e12 / peak_flops,
         "dense_causal_equiv_tflops": dense_flops / (ms_per_step * 1e-3) / 1e12,
         "evaluated_pair_fraction": eval_pairs * 2.0 / (n * (n + 1) * B * H),
         "stage_ms": {"prologue": float(np.mean(pre_ms)), "fwd_kernel": fwd_avg,
                      "logit_check": float(np.mean(post_ms))},
-        "roofline": {"bound": "mfma", "achieved": achieved, "peak": PEAK_BF16_TFLOPS,
-                     "unit": "TFLOP/s", "frac": achieved / PEAK_BF16_TFLOPS,
-                     "traffic": traffic, "kernel": "fwd_pad_kernel<d=128, dv=128>",
-                     "flops_per_launch": alg_flops, "executed_mfma_flops": exec_flops,
-                     "executed_mfma_tflops": exec_flops / (fwd_avg * 1e-3) / 1e12,
-                     "counters": measured_counters(sha)},
+        "roofline": roof,
     }
+    if headline:
+        out["pct_bf16_mfma_peak"] = out["pct_mfma_peak"]
     if not args.no_cpu_baseline:
-        heads = [(b, h) for b in range(4) for h in range(0, 16, 2)]  # half of the 64 heads
-        out["cpu_baseline"] = cpu_baseline(inp, sw, heads)
+        heads, rows = _cpu_sample(widx, B, H, n)
+        out["cpu_baseline"] = cpu_baseline(inp, sw, heads, rows, flops_per_pair)
     print(json.dumps(out), flush=True)
+
+
+def _cpu_sample(widx, B, H, n):
+    """Heads (and rows) of a workload that the oracle finishes in ~5-30 s."""
+    import numpy as np
+
+    if widx == 3:
+        return [(b, h) for b in range(B) for h in range(0, H, 2)], None  # half the 64 heads
+    if widx == 4:  # one head of n = 32768: every 4th row (row i costs O(i d))
+        return [(0, 0)], np.arange(3, n, 4)
+    if widx == 5:  # 15 of the 256 heads
+        return [(b, 0) for b in range(B)] + [(0, h) for h in range(1, 8)], None
+    return [(b, h) for b in range(B) for h in range(H)], None
+
+
+def bench_workload(args):
+    """--workload W [--fp32]: one JSON line per switch setting of workload W."""
+    from gated_causal_attention_amd import inputs
+
+    widx = args.workload
+    inp = _workload_inputs(widx, args.fp32)
+    for sw in inputs.WORKLOADS[widx].switches:
+        forward_line(args, widx, sw, args.fp32, headline=False, inp=inp)
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-bytes", type=int, default=0)
+    ap.add_argument("--path", choices=("forward", "chain", "grouped", "decode", "operator"),
+                    default="forward",
+                    help="forward: the head (the headline line); chain: the chain-corner "
+                         "scan; grouped: shared k/v heads and another value width; decode: "
+                         "one decode step against an n-position cache; operator: the "
+                         "materialising exports")
+    ap.add_argument("--workload", type=int, choices=(2, 3, 4, 5), default=3,
+                    help="forward path on another workload's shape, distributions and "
+                         "switch settings (one line per setting); 3 is the headline")
+    ap.add_argument("--fp32", action="store_true",
+                    help="forward path with fp32 q, k, v (the fp32 MFMA path)")
+    ap.add_argument("--summarize-traffic", nargs=4, metavar=("FETCH", "WRITE", "COPY_FETCH",
+                                                              "COPY_WRITE"))
+    ap.add_argument("--summarize-counters", nargs=len(COUNTER_PASSES),
+                    metavar=tuple(f"PASS{i}" for i in range(len(COUNTER_PASSES))))
+    args = ap.parse_args()
+    if args.summarize_traffic:
+        print(json.dumps(summarize_traffic(*args.summarize_traffic, args.copy_bytes), indent=1))
+        return
+    if args.summarize_counters:
+        print(json.dumps(summarize_counters(args.summarize_counters), indent=1))
+        return
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU: the resolvent head's heads are independent and the "
+              "library has no multi-GPU path (a sharded run would split the (batch, head) "
+              "pairs over the GPUs); run with --gpus 1",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    if args.copy_bytes:  # the calibration copy of the traffic counters
+        copy_calibration(args.copy_bytes)
+        return
+
+    if args.path == "chain":
+        bench_chain(args)
+        return
+    if args.path == "grouped":
+        bench_grouped(args)
+        return
+    if args.path == "decode":
+        bench_decode(args)
+        return
+    if args.path == "operator":
+        bench_operator(args)
+        return
+
+    if args.workload != 3 or args.fp32:
+        bench_workload(args)
+        return
+    forward_line(args, 3, (1, 1, 1), fp32=False, headline=True)
 
 
 if __name__ == "__main__":
