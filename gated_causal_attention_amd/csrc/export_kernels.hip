@@ -90,6 +90,7 @@ struct OpArgs {
     const void *q, *k;              // [BH][n][d]
     const float *u, *theta;         // [BH][n]
     double *a_re, *a_im, *a_m;      // gates [BH][n] (workspace)
+    double *s_re, *s_im, *s_m;      // a_{p+1} ... a_{t0+64} in p's tile [BH][n] (workspace)
     float *w_re, *w_im;             // [BH][n][n]
     int32_t *status;
     double g;
@@ -98,16 +99,71 @@ struct OpArgs {
     int beta_mode, qk_zero;
 };
 
-// Gates of every position, one thread each; refuses a non-finite u, theta or
-// g theta (the status word was cleared by the kernel before it).
+typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8;
+typedef __attribute__((__vector_size__(16 * sizeof(float)))) float f32x16;
+
+constexpr int OB = 64;  // rows of a query block = keys of a key tile
+
+// An opaque 0: indexing a table with it each tile keeps the compiler from
+// hoisting that table's (loop-invariant) LDS reads into registers.
+__device__ __forceinline__ int opaque_zero() {
+    int z;
+    asm volatile("v_mov_b32 %0, 0" : "=v"(z));
+    return z;
+}
+
+__device__ __forceinline__ float4 cg_f4(Cg a) { return {float(a.re), float(a.im), float(a.m), 0.f}; }
+
+// Inclusive scans of 64 lanes' gates in f64: prefix (lane l gets x_0 ... x_l)
+// and suffix (lane l gets x_l ... x_63).
+__device__ __forceinline__ Cg scan_prefix(Cg x, int lane) {
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+        const Cg y = {__shfl_up(x.re, o), __shfl_up(x.im, o), __shfl_up(x.m, o)};
+        if (lane >= o) x = cg_mul(y, x);
+    }
+    return x;
+}
+__device__ __forceinline__ Cg scan_suffix(Cg x, int lane) {
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+        const Cg y = cg_down(x, o);
+        if (lane + o < 64) x = cg_mul(x, y);
+    }
+    return x;
+}
+
+// Gates of every position, one wave per 64-position tile (4 tiles per
+// workgroup), and for each position p of tile t0 the product of the gates
+// after it to one past the tile's end, a_{p+1} ... a_{t0+64} (f64 suffix scan;
+// gates past n count as 1).  Refuses a non-finite u, theta or g theta (the
+// status word was cleared by the kernel before it).
 __global__ __launch_bounds__(256) void op_gates_kernel(OpArgs A) {
-    const int64_t x = int64_t(blockIdx.x) * 256 + threadIdx.x;
-    if (x >= A.BH * A.n) return;
+    const int lane = threadIdx.x & 63;
+    const int64_t n = A.n, nt = (n + OB - 1) / OB;
+    const int64_t tile = int64_t(blockIdx.x) * 4 + (threadIdx.x >> 6);
+    if (tile >= A.BH * nt) return;  // whole waves
+    const int64_t bh = tile / nt, t0 = (tile % nt) * OB, p = t0 + lane, x = bh * n + p;
     bool bad = false;
-    const Cg a = gate_of(A.u[x], A.theta[x], A.g, bad);
-    A.a_re[x] = a.re;
-    A.a_im[x] = a.im;
-    A.a_m[x] = a.m;
+    Cg a = cg_one();
+    if (p < n) {
+        a = gate_of(A.u[x], A.theta[x], A.g, bad);
+        A.a_re[x] = a.re;
+        A.a_im[x] = a.im;
+        A.a_m[x] = a.m;
+    }
+    Cg b = cg_down(a, 1);  // a_{p+1}
+    if (lane == OB - 1) {  // the first gate of the next tile
+        bool unused = false;
+        b = p + 1 < n ? gate_of(A.u[x + 1], A.theta[x + 1], A.g, unused) : cg_one();
+    }
+    if (p + 1 >= n) b = cg_one();
+    const Cg sfx = scan_suffix(b, lane);
+    if (p < n) {
+        A.s_re[x] = sfx.re;
+        A.s_im[x] = sfx.im;
+        A.s_m[x] = sfx.m;
+    }
     if (bad) A.status[0] = kExpNonFinite;
 }
 
@@ -115,116 +171,305 @@ __global__ __launch_bounds__(64) void clear_word_kernel(int32_t *w) {
     if (threadIdx.x == 0) w[0] = 0;
 }
 
-// One wave per (head, row i): blockIdx.x = bh n + i.  Key tiles are taken from
-// the row's own tile down to 0; lane j of a tile holds key t0 + j.  Key rows
-// are read KL lanes to a row (16 bytes a lane) and their dot products reduced
-// across those lanes; the gates after each key come from a suffix product
-// across lanes of b_j = a_{j+1} (1 from j = i on) times the product of the
-// later tiles.  Pass 0 forms the shift M (largest live logit) and the
-// normaliser; pass 1 recomputes the same logits and products and writes
-// W_ij = G_ij 2^(L_j - M) exp2((1-beta) M) z^-beta (one exponential per entry).
+// W of one block of 64 rows per workgroup of 4 waves (section "Object"):
+// blockIdx.x = (blocks from the last) * BH + bh, so the longest rows start
+// first.  Key tiles of 64 go from the block's own tile down to 0; wave w
+// takes rows 32 (w/2) .. +32 and keys 32 (w%2) .. +32 of each 64 x 64 tile.
+// The logits come from one 32x32 MFMA product per wave (q in registers, the
+// key tile in LDS); lane (c, h) of a wave holds key c and, in register r, row
+// 8 (r/4) + 4h + r%4 of the wave's rows, so each store writes two rows' 128
+// consecutive bytes.  Below the own tile the path product factors as
+// G_ij = P_i (C S_j) -- P_i the gates r0+1..i, C those from the tile's end
+// to r0, S_j the suffix inside the tile -- all f64 scans rounded to f32 once
+// and multiplied per entry in f32; a zero gate still gives an exact 0.  On
+// the own tile the 32x32 diagonal sub-blocks take each key's running product
+// down its rows (f64), and the lower-left sub-block splits at row 32.  Pass 0
+// keeps a running largest live logit and normaliser per (lane, row), merged
+// across the 64 keys' lanes at the end; pass 1 recomputes the same logits and
+// products and writes W_ij = G_ij 2^((L - M) + f), f = log2 of the row scale
+// 2^((1-beta) M) z^-beta.
 template <bool QF32, int D>
-__global__ __launch_bounds__(64) void operator_row_kernel(OpArgs A) {
-    constexpr int KE = QF32 ? 4 : 8, KL = D / KE, KR = 64 / KL, KI = BK / KR;
-    constexpr int KB = QF32 ? 4 : 2;
-    __shared__ float dots[BK];
-    const int lane = threadIdx.x;
-    const int64_t bh = blockIdx.x / A.n, i = blockIdx.x % A.n;
-    const int kc = (lane % KL) * KE, kr = lane / KL;
-    const uint32_t koff = uint32_t(kc * KB);
-    const char *kbase = static_cast<const char *>(A.k) + bh * A.n * (D * KB);
-    const double *ar = A.a_re + bh * A.n, *ai = A.a_im + bh * A.n, *am = A.a_m + bh * A.n;
-    float *wr = A.w_re + (bh * A.n + i) * A.n, *wi = A.w_im + (bh * A.n + i) * A.n;
+__global__ __launch_bounds__(256, 2) void operator_block_kernel(OpArgs A) {
+    constexpr int ESZ = QF32 ? 4 : 2;
+    constexpr int KH = D / 2;               // elements of a row each lane half covers
+    constexpr int NCH = D * ESZ / 16;       // 16-byte chunks of a key row
+    constexpr int ROWB = D * ESZ + 16;      // padded LDS key row (conflict-free reads)
+    constexpr int NQ = KH * ESZ / 16;       // 16-byte words of q a lane holds
+    __shared__ __align__(16) unsigned char ks[OB * ROWB];
+    __shared__ float4 pr[OB];       // P_i of the block's rows
+    __shared__ float4 p2[OB / 2];   // rows 32..63: gates r0+33 .. i
+    __shared__ float4 s1[OB / 2];   // keys 0..31: gates j+1 .. r0+32
+    __shared__ double ga[3][OB];    // the block's gates a_{r0+l} (re, im, |a|)
+    __shared__ float2 part[OB];     // (M, z) of keys 32..63, per row
+    __shared__ float2 mf[OB];       // (M, f) per row
+    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+    const int wr = w >> 1, wc = w & 1, h = lane >> 5, c32 = lane & 31;
+    // positions fit in int (n <= 65536); head offsets are 64-bit
+    const int n = int(A.n);
+    const int nb = (n + OB - 1) / OB;
+    const int64_t bh = int64_t(blockIdx.x) % A.BH;
+    const int qb = nb - 1 - int(int64_t(blockIdx.x) / A.BH);
+    const int r0 = qb * OB;
+    const double *ar = A.a_re + bh * n, *ai = A.a_im + bh * n, *am = A.a_m + bh * n;
+    const char *kbase = static_cast<const char *>(A.k) + bh * n * (D * ESZ);
     bool bad = false;
-    float qv[KE];
-    unpack16<QF32>(load16<QF32>(A.q, (bh * A.n + i) * D + kc), qv);
+
+    // the block's gates and their scans (wave 0)
+    if (w == 0) {
+        const int p = r0 + lane;
+        const Cg a = p < n ? Cg{ar[p], ai[p], am[p]} : cg_one();
+        ga[0][lane] = a.re;
+        ga[1][lane] = a.im;
+        ga[2][lane] = a.m;
+        pr[lane] = cg_f4(scan_prefix(lane == 0 ? cg_one() : a, lane));
+        // split at 32: rows 32.. take gates r0+33 .. i; keys ..31 gates j+1 .. r0+32
+        const Cg x2 = lane <= 32 ? cg_one() : a;
+        const Cg q2 = scan_prefix(x2, lane);
+        if (lane >= 32) p2[lane - 32] = cg_f4(q2);
+        const Cg x1 = (lane >= 1 && lane <= 32) ? a : cg_one();
+        const Cg q1 = scan_suffix(x1, lane);  // lane l: gates l .. 32 (l >= 1)
+        const Cg s = cg_lane(q1, lane + 1 < 64 ? lane + 1 : 63);
+        if (lane < 32) s1[lane] = cg_f4(s);
+    }
+
+    // q of the wave's rows: lane (c, h) holds row 32 wr + c, elements KH h ..
+    const int qrow = min(r0 + 32 * wr + c32, n - 1);
+    uint4 qw[NQ];
+    {
+        const char *qp = static_cast<const char *>(A.q) + ((bh * n + qrow) * D + KH * h) * ESZ;
 #pragma unroll
-    for (int e = 0; e < KE; ++e)
-        if (!isfinite(qv[e])) bad = true;
-    const int ti = int(i / BK);
-    float M = -INFINITY, z = 0.f, f = 0.f;
+        for (int x = 0; x < NQ; ++x) qw[x] = *reinterpret_cast<const uint4 *>(qp + 16 * x);
+        float qv[16 / ESZ];
+#pragma unroll
+        for (int x = 0; x < NQ; ++x) {
+            unpack16<QF32>(qw[x], qv);
+#pragma unroll
+            for (int e = 0; e < 16 / ESZ; ++e)
+                if (!isfinite(qv[e])) bad = true;
+        }
+    }
+    __syncthreads();
+    float Mv[16], zv[16];
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+        Mv[r] = -INFINITY;
+        zv[r] = 0.f;
+    }
+    // rows of the block (uniform base) and the lane's byte offsets from it
+    float *const wre = A.w_re + (bh * n + r0) * n, *const wim = A.w_im + (bh * n + r0) * n;
+    const uint32_t rowb = uint32_t(n) * 4u;
+    // the lane's key tile words, and the in-tile suffix products a_{j+1} ...
+    // a_{t0+64} of its key j (gates kernel)
+    constexpr int KX = OB * NCH / 256;
+    constexpr bool KPRE = !(QF32 && D == 128);  // prefetch the next tile (registers allow)
+    const double *sre = A.s_re + bh * n, *sim = A.s_im + bh * n, *smo = A.s_m + bh * n;
+    auto load_k = [&](int t, uint4 (&v)[KX]) __attribute__((always_inline)) {
+#pragma unroll
+        for (int x = 0; x < KX; ++x) {
+            const int ci = tid + 256 * x, row = ci / NCH, ch = ci % NCH;
+            v[x] = uint4{0u, 0u, 0u, 0u};
+            if (t * OB + row < n)
+                v[x] = *reinterpret_cast<const uint4 *>(
+                    kbase + uint32_t((t * OB + row) * (D * ESZ) + 16 * ch));
+        }
+    };
     for (int pass = 0; pass < 2; ++pass) {
-        Cg carry = cg_one();  // the gates from the current tile's end to i
-        for (int t = ti; t >= 0; --t) {
-            const int64_t t0 = int64_t(t) * BK;
-            const int cnt = i - t0 + 1 < BK ? int(i - t0 + 1) : BK;
-            const char *kt = kbase + t0 * (D * KB);
-            uint4 kw[KI];
+        Cg carry = cg_one();  // the gates from the current tile's end + 1 to r0
+        Cg sj = cg_one(), sj_next = cg_one();    // the lane key's in-tile suffix
+        Cg ft = cg_one(), ft_next = cg_one();    // the tile's product a_{t0+1} ... a_{t0+64}
+        uint4 kv[KX];
+        if constexpr (KPRE) load_k(qb, kv);
+        for (int t = qb; t >= 0; --t) {
+            const int t0 = t * OB;
+            const bool own = (t == qb);
+            if constexpr (!KPRE) load_k(t, kv);
+            // stage the key tile (rows past n are zeros)
 #pragma unroll
-            for (int x = 0; x < KI; ++x) {
-                const int row = x * KR + kr < cnt ? x * KR + kr : cnt - 1;
-                kw[x] = *reinterpret_cast<const uint4 *>(kt + (uint32_t(row) * (D * KB) + koff));
-            }
+            for (int x = 0; x < KX; ++x) {
+                const int ci = tid + 256 * x, row = ci / NCH, ch = ci % NCH;
+                if (own && pass == 0) {  // each key is checked once, by its own block
+                    float kf[16 / ESZ];
+                    unpack16<QF32>(kv[x], kf);
 #pragma unroll
-            for (int x = 0; x < KI; ++x) {
-                float kx[KE];
-                unpack16<QF32>(kw[x], kx);
-                float part = 0.f;
-#pragma unroll
-                for (int e = 0; e < KE; ++e) {
-                    if (!isfinite(kx[e])) bad = true;
-                    part = fmaf(qv[e], kx[e], part);
+                    for (int e = 0; e < 16 / ESZ; ++e)
+                        if (!isfinite(kf[e])) bad = true;
                 }
-#pragma unroll
-                for (int o = 1; o < KL; o <<= 1) part += __shfl_xor(part, o);
-                if (lane % KL == 0) dots[x * KR + kr] = part;
+                *reinterpret_cast<uint4 *>(ks + row * ROWB + 16 * ch) = kv[x];
             }
             __syncthreads();
-            const bool key = lane < cnt;
-            float L = 0.f;
-            if (!A.qk_zero) {
-#pragma clang fp contract(off)
-                L = dots[lane] * A.c;
-                if (key && !isfinite(L)) bad = true;
+            if (t > 0) {  // the next tile's words and the lane's key suffix in it
+                if constexpr (KPRE) load_k(t - 1, kv);
+                const int jn = t0 - OB + 32 * wc + c32;
+                sj_next = Cg{sre[jn], sim[jn], smo[jn]};
+                ft_next = Cg{sre[t0 - OB], sim[t0 - OB], smo[t0 - OB]};
             }
-            __syncthreads();  // dots is rewritten by the next tile
-            const int64_t j = t0 + lane;
-            Cg sfx = j < i ? Cg{ar[j + 1], ai[j + 1], am[j + 1]} : cg_one();
+
+            // logits of the wave's 32 x 32 sub-block
+            f32x16 acc;
 #pragma unroll
-            for (int o = 1; o < 64; o <<= 1) {
-                const Cg x = cg_down(sfx, o);
-                if (lane + o < 64) sfx = cg_mul(sfx, x);
-            }
-            const Cg G = cg_mul(sfx, carry);
-            carry = cg_mul(cg_lane(sfx, 0), carry);
-            const float gm = float(G.m);
-            const bool live = key && gm > 0.0f;
-            if (pass == 0) {
-                const float tmax = wave_max(live ? L : -INFINITY);
-                if (tmax > M) {
-                    z *= M == -INFINITY ? 0.f : exp2f(M - tmax);
-                    M = tmax;
+            for (int r = 0; r < 16; ++r) acc[r] = 0.f;
+            if (!A.qk_zero) {
+                const unsigned char *kp = ks + (32 * wc + c32) * ROWB + KH * ESZ * h;
+                if constexpr (!QF32) {
+                    bf16x8 kb[NQ];  // all fragments in flight before the first product
+#pragma unroll
+                    for (int s = 0; s < NQ; ++s) kb[s] = *reinterpret_cast<const bf16x8 *>(kp + 16 * s);
+#pragma unroll
+                    for (int s = 0; s < NQ; ++s)
+                        acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+                            __builtin_bit_cast(bf16x8, qw[s]), kb[s], acc, 0, 0, 0);
+                } else {
+#pragma unroll
+                    for (int s = 0; s < NQ; ++s) {
+                        const float4 kf = *reinterpret_cast<const float4 *>(kp + 16 * s);
+                        const float4 qf = __builtin_bit_cast(float4, qw[s]);
+                        acc = __builtin_amdgcn_mfma_f32_32x32x2f32(qf.x, kf.x, acc, 0, 0, 0);
+                        acc = __builtin_amdgcn_mfma_f32_32x32x2f32(qf.y, kf.y, acc, 0, 0, 0);
+                        acc = __builtin_amdgcn_mfma_f32_32x32x2f32(qf.z, kf.z, acc, 0, 0, 0);
+                        acc = __builtin_amdgcn_mfma_f32_32x32x2f32(qf.w, kf.w, acc, 0, 0, 0);
+                    }
                 }
-                if (live) z = fmaf(gm, exp2f(L - M), z);
-            } else if (key) {
-                // one exponential per entry, 2^((L - M) + log2 f): no product of an
-                // underflowed and an overflowed factor
-                const float e = live ? exp2f((L - M) + f) : 0.f;
-                wr[j] = scale_keep_zero(float(G.re), e);
-                wi[j] = scale_keep_zero(float(G.im), e);
+            }
+
+            // the lane's key, and its first row relative to r0 (recomputed each
+            // tile: per-row values derived from it then stay short-lived)
+            const int j = t0 + 32 * wc + c32;
+            const int rb = 32 * wr + 4 * h + opaque_zero();
+            // one entry: register r of the lane, path product (g_re, g_im, |g|);
+            // below: the key tile lies below the block (every key is causal).
+            // v_exp_f32 directly: a result below the normal range reads 0.
+            auto entry = [&](int r, float g_re, float g_im, float g_m, bool below)
+                __attribute__((always_inline)) {
+                const int irel = rb + 8 * (r >> 2) + (r & 3);
+                const int i = r0 + irel;
+                const bool key = (below || j <= i) && i < n;
+                float L = 0.f;
+                if (!A.qk_zero) {
+#pragma clang fp contract(off)
+                    L = acc[r] * A.c;
+                }
+                const bool live = key && g_m > 0.f;
+                if (pass == 0) {
+                    if (key && !isfinite(L)) bad = true;
+                    const float mn = live ? fmaxf(Mv[r], L) : Mv[r];
+                    const float sc = Mv[r] == mn ? 1.f : __builtin_amdgcn_exp2f(Mv[r] - mn);
+                    const float e = live ? __builtin_amdgcn_exp2f(L - mn) : 0.f;
+                    zv[r] = fmaf(g_m, e, zv[r] * sc);
+                    Mv[r] = mn;
+                } else if (i < n && j < n) {
+                    // a dead entry gets e = 0 and a finite G: W = 0
+                    const float e = live ? __builtin_amdgcn_exp2f((L - Mv[r]) + zv[r]) : 0.f;
+                    const uint32_t off = uint32_t(irel) * rowb + uint32_t(j) * 4u;
+                    *reinterpret_cast<float *>(reinterpret_cast<char *>(wre) + off) =
+                        scale_keep_zero(g_re, e);
+                    *reinterpret_cast<float *>(reinterpret_cast<char *>(wim) + off) =
+                        scale_keep_zero(g_im, e);
+                }
+            };
+            if (!own) {  // G_ij = P_i (C S_j)
+                const float4 c = cg_f4(cg_mul(carry, sj));
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    const float4 p = pr[rb + 8 * (r >> 2) + (r & 3)];
+                    entry(r, p.x * c.x - p.y * c.y, p.x * c.y + p.y * c.x, p.z * c.z, true);
+                }
+            } else if (wr != wc) {
+                if (wr == 0) {  // keys above every row of the sub-block
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) entry(r, 0.f, 0.f, 0.f, false);
+                } else {        // rows 32.., keys ..31: split at row 32
+                    const float4 c = s1[c32];
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) {
+                        const float4 p = p2[rb - 32 + 8 * (r >> 2) + (r & 3)];
+                        entry(r, p.x * c.x - p.y * c.y, p.x * c.y + p.y * c.x, p.z * c.z,
+                              true);
+                    }
+                }
+            } else {            // diagonal sub-block: key c's product down the rows
+                const int base = 32 * wr;
+                Cg R = cg_one();
+#pragma unroll
+                for (int rel = 0; rel < 32; ++rel) {
+                    if (rel > c32) R = cg_mul(R, Cg{ga[0][base + rel], ga[1][base + rel],
+                                                    ga[2][base + rel]});
+                    // row rel belongs to lane half (rel / 4) % 2, register 4 (rel / 8) + rel % 4
+                    const bool mine = ((rel >> 2) & 1) == h, on = rel >= c32;
+                    const int r = 4 * (rel >> 3) + (rel & 3);
+                    if (__any(mine))
+                        if (mine)
+                            entry(r, on ? float(R.re) : 0.f, on ? float(R.im) : 0.f,
+                                  on ? float(R.m) : 0.f, false);
+                }
+            }
+            if (!own) carry = cg_mul(ft, carry);  // C for the tile below
+            sj = sj_next;
+            ft = ft_next;
+            __syncthreads();  // the tile buffer is rewritten next
+        }
+        if (pass == 0) {
+            // merge (M, z) over the 32 keys of each lane half, then the two waves
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+#pragma unroll
+                for (int o = 1; o < 32; o <<= 1) {
+                    const float Mo = __shfl_xor(Mv[r], o), zo = __shfl_xor(zv[r], o);
+                    const float Mn = fmaxf(Mv[r], Mo);
+                    if (Mn != -INFINITY)
+                        zv[r] = zv[r] * exp2f(Mv[r] - Mn) + zo * exp2f(Mo - Mn);
+                    Mv[r] = Mn;
+                }
+            }
+            if (wc == 1 && c32 == 0) {
+#pragma unroll
+                for (int r = 0; r < 16; ++r)
+                    part[32 * wr + 8 * (r >> 2) + 4 * h + (r & 3)] = make_float2(Mv[r], zv[r]);
+            }
+            __syncthreads();
+            if (wc == 0 && c32 == 0) {
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    const int row = 32 * wr + 8 * (r >> 2) + 4 * h + (r & 3);
+                    const float2 o = part[row];
+                    const float Mn = fmaxf(Mv[r], o.x);
+                    const float zt = zv[r] * exp2f(Mv[r] - Mn) + o.y * exp2f(o.x - Mn);
+                    float f;
+                    if (A.beta_mode == 1)
+                        f = -log2f(zt);
+                    else if (A.beta_mode == 0)
+                        f = Mn;
+                    else
+                        f = A.one_minus_beta * Mn - A.beta * log2f(zt);
+                    mf[row] = make_float2(Mn, f);
+                }
+            }
+            __syncthreads();
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {  // pass 1: Mv = M, zv = f
+                const float2 x = mf[32 * wr + 8 * (r >> 2) + 4 * h + (r & 3)];
+                Mv[r] = x.x;
+                zv[r] = x.y;
             }
         }
-        if (pass == 0) {  // f: log2 of the row's scale 2^((1-beta) M) z^-beta
-            const float zt = wave_sum(z);
-            if (A.beta_mode == 1)
-                f = -log2f(zt);
-            else if (A.beta_mode == 0)
-                f = M;
-            else
-                f = A.one_minus_beta * M - A.beta * log2f(zt);
+    }
+    // columns right of the block's own tile are zeros
+    const int c0 = r0 + OB, rows = min(OB, n - r0);
+    if (c0 < n)
+        for (int rr = 0; rr < rows; ++rr) {
+            float *zr = A.w_re + (bh * n + r0 + rr) * n, *zi = A.w_im + (bh * n + r0 + rr) * n;
+            for (int jj = c0 + tid; jj < n; jj += 256) {
+                zr[jj] = 0.f;
+                zi[jj] = 0.f;
+            }
         }
-    }
-    for (int64_t j = i + 1 + lane; j < A.n; j += 64) {  // above the diagonal
-        wr[j] = 0.f;
-        wi[j] = 0.f;
-    }
     if (__any(bad) && lane == 0) A.status[0] = kExpNonFinite;
 }
 
 template <bool QF32, int D>
-void launch_rows(const OpArgs &A, hipStream_t st) {
-    hipLaunchKernelGGL((operator_row_kernel<QF32, D>), dim3((unsigned)(A.BH * A.n)), dim3(64), 0,
-                       st, A);
+void launch_blocks(const OpArgs &A, hipStream_t st) {
+    const int64_t nb = (A.n + OB - 1) / OB;
+    hipLaunchKernelGGL((operator_block_kernel<QF32, D>), dim3((unsigned)(A.BH * nb)), dim3(256),
+                       0, st, A);
 }
 
 }  // namespace
@@ -251,6 +496,9 @@ int launch_operator(const OperatorLayout &OL, const void *q, const void *k, cons
     A.a_re = reinterpret_cast<double *>(ws + OL.a_re);
     A.a_im = reinterpret_cast<double *>(ws + OL.a_im);
     A.a_m = reinterpret_cast<double *>(ws + OL.a_m);
+    A.s_re = reinterpret_cast<double *>(ws + OL.s_re);
+    A.s_im = reinterpret_cast<double *>(ws + OL.s_im);
+    A.s_m = reinterpret_cast<double *>(ws + OL.s_m);
     A.w_re = w_re;
     A.w_im = w_im;
     A.status = status;
@@ -263,14 +511,14 @@ int launch_operator(const OperatorLayout &OL, const void *q, const void *k, cons
     A.beta_mode = beta_mode;
     A.qk_zero = qk_zero ? 1 : 0;
     hipLaunchKernelGGL(clear_word_kernel, dim3(1), dim3(64), 0, st, status);
-    hipLaunchKernelGGL(op_gates_kernel, dim3((unsigned)((OL.BH * OL.n + 255) / 256)), dim3(256),
-                       0, st, A);
+    const int64_t tiles = OL.BH * ((OL.n + OB - 1) / OB);
+    hipLaunchKernelGGL(op_gates_kernel, dim3((unsigned)((tiles + 3) / 4)), dim3(256), 0, st, A);
     const int key = (qk_f32 ? 2 : 0) + (OL.d == 128 ? 1 : 0);
     switch (key) {
-        case 0: launch_rows<false, 64>(A, st); break;
-        case 1: launch_rows<false, 128>(A, st); break;
-        case 2: launch_rows<true, 64>(A, st); break;
-        case 3: launch_rows<true, 128>(A, st); break;
+        case 0: launch_blocks<false, 64>(A, st); break;
+        case 1: launch_blocks<false, 128>(A, st); break;
+        case 2: launch_blocks<true, 64>(A, st); break;
+        case 3: launch_blocks<true, 128>(A, st); break;
     }
     return (int)hipGetLastError();
 }

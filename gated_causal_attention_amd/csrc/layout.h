@@ -148,11 +148,15 @@ inline DecodeLayout make_decode_layout(int64_t B, int64_t H, int64_t Hkv, int64_
     return D;
 }
 
-// Workspace of the operator export (resolvent_operator): the gates of every
-// position, f64 (double [BH][n] each: re, im, modulus).
+// Workspace of the operator export (resolvent_operator), f64 planes
+// (double [BH][n] each: re, im, modulus): the gate of every position, and
+// the product of the gates after it up to the end of its 64-position tile
+// plus one (a_{p+1} ... a_{t0+64}; gates past n count as 1).
 struct OperatorLayout {
     int64_t BH = 0, n = 0, d = 0;
-    size_t a_re = 0, a_im = 0, a_m = 0, total = 0;
+    size_t a_re = 0, a_im = 0, a_m = 0;  // the gates a_p
+    size_t s_re = 0, s_im = 0, s_m = 0;  // a_{p+1} ... a_{t0+64} inside p's tile of 64
+    size_t total = 0;
 };
 
 inline OperatorLayout make_operator_layout(int64_t B, int64_t H, int64_t n, int64_t d) {
@@ -161,10 +165,14 @@ inline OperatorLayout make_operator_layout(int64_t B, int64_t H, int64_t n, int6
     O.n = n;
     O.d = d;
     const size_t per = sizeof(double) * size_t(O.BH) * size_t(n);
+    const size_t plane = align_up(per, 256);
     O.a_re = 0;
-    O.a_im = align_up(per, 256);
-    O.a_m = 2 * align_up(per, 256);
-    O.total = 3 * align_up(per, 256);
+    O.a_im = plane;
+    O.a_m = 2 * plane;
+    O.s_re = 3 * plane;
+    O.s_im = 4 * plane;
+    O.s_m = 5 * plane;
+    O.total = 6 * plane;
     return O;
 }
 

@@ -96,6 +96,16 @@ def draw(B, H, n, d, seed, qk_dtype=BF16, v_dtype=BF16, qk_scale=1.0, gates="uni
             "v_dtype": v_dtype, "B": B, "H": H, "n": n, "d": d, "seed": seed}
 
 
+def draw_complex_gates(batch, n, seed, mod_range=(0.95, 1.0), arg_range=(-0.05, 0.05)):
+    """Random complex numbers r e^{i phi} (float64 planes [batch, n]) with
+    r ~ U(mod_range), phi ~ U(arg_range): ready-made gates for the path-product
+    export, drawn directly rather than from u and theta."""
+    rng = np.random.Generator(np.random.PCG64(seed))
+    r = rng.uniform(*mod_range, size=(batch, n))
+    phi = rng.uniform(*arg_range, size=(batch, n))
+    return r * np.cos(phi), r * np.sin(phi)
+
+
 def make_config(idx: int, switches=None, seed=None, n=None, B=None, H=None):
     """Inputs of workload ``idx`` (seed = idx unless given).  ``switches``
     selects the workload-1 variant whose q,k are scaled by 0.3 at (0,1,0).

@@ -7,10 +7,11 @@ multiply-adds), so it is compared with ``oracle.path_product`` bit for bit.
 resolvent_operator writes W_ij = G_ij e^{qk s_ij} / Z_i^beta (section
 "Object") in float32; the reference is ``oracle.operator`` per head.
 Tolerance, from the arithmetic: float32 logits (a few 2^-24 of
-sum_e |q_e k_e| |c|), exp2 of them, gate products in f64 rounded to float,
-and a normaliser summed 64 + log2(64) terms deep per lane and wave: a few 1e-6
-of the largest weight, held to the fp32 bar 1e-4 of max |dW| / (max |W| + 1e-6)
-per head.  Entries the definition makes exactly zero (above the diagonal,
+sum_e |q_e k_e| |c|), exp2 of them, gate scans in f64 rounded to float once
+and combined by two float32 complex products, and a normaliser summed per
+lane over its keys (one per 64-key tile, at most n/64 terms) and then over the
+64 keys' lanes in a tree: a few 1e-6 of the largest weight, held to the fp32
+bar 1e-4 of max |dW| / (max |W| + 1e-6) per head.  Entries the definition makes exactly zero (above the diagonal,
 behind a closed gate) are checked to be exactly zero.
 """
 import numpy as np
@@ -107,6 +108,21 @@ def test_operator_shapes(n, d, qdt):
     inp = inputs.draw(1, 2, n, d, seed=n + d, qk_dtype=qdt, u_range=(0.6, 1.0))
     W = gpu_operator(inp, (1, 1, 1))
     assert W.shape == (1, 2, n, n)
+    err = operator_err(inp, (1, 1, 1), W)
+    print(f"  rel err {err:.3e}")
+    assert err <= TOL_OP
+
+
+@pytest.mark.parametrize("B,H,n,d,qdt,seed", [(1, 1, 1000, 128, inputs.BF16, 51),
+                                               (1, 3, 700, 64, inputs.F32, 52),
+                                               (2, 1, 1500, 64, inputs.BF16, 53)])
+def test_operator_many_tiles(B, H, n, d, qdt, seed):
+    """Rows that span many 64-key tiles (the carried product across tiles),
+    a ragged last block, and several heads per launch."""
+    announce(f"operator B={B} H={H} n={n} d={d} qk dtype {qdt}")
+    inp = inputs.draw(B, H, n, d, seed=seed, qk_dtype=qdt, u_range=(0.97, 1.0),
+                      theta_range=(-0.3, 0.3))
+    W = gpu_operator(inp, (1, 1, 1))
     err = operator_err(inp, (1, 1, 1), W)
     print(f"  rel err {err:.3e}")
     assert err <= TOL_OP
