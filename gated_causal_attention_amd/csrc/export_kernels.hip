@@ -16,6 +16,7 @@
 
 #include <cmath>
 #include <cstdint>
+#include <type_traits>
 
 #include "device_common.h"
 #include "layout.h"
@@ -104,8 +105,8 @@ typedef __attribute__((__vector_size__(16 * sizeof(float)))) float f32x16;
 
 constexpr int OB = 64;  // rows of a query block = keys of a key tile
 
-// An opaque 0: indexing a table with it each tile keeps the compiler from
-// hoisting that table's (loop-invariant) LDS reads into registers.
+// An opaque 0: offsetting a table's index by it each tile keeps the compiler
+// from hoisting that table's loop-invariant LDS reads into registers.
 __device__ __forceinline__ int opaque_zero() {
     int z;
     asm volatile("v_mov_b32 %0, 0" : "=v"(z));
@@ -175,19 +176,20 @@ __global__ __launch_bounds__(64) void clear_word_kernel(int32_t *w) {
 // blockIdx.x = (blocks from the last) * BH + bh, so the longest rows start
 // first.  Key tiles of 64 go from the block's own tile down to 0; wave w
 // takes rows 32 (w/2) .. +32 and keys 32 (w%2) .. +32 of each 64 x 64 tile.
-// The logits come from one 32x32 MFMA product per wave (q in registers, the
-// key tile in LDS); lane (c, h) of a wave holds key c and, in register r, row
-// 8 (r/4) + 4h + r%4 of the wave's rows, so each store writes two rows' 128
-// consecutive bytes.  Below the own tile the path product factors as
-// G_ij = P_i (C S_j) -- P_i the gates r0+1..i, C those from the tile's end
-// to r0, S_j the suffix inside the tile -- all f64 scans rounded to f32 once
-// and multiplied per entry in f32; a zero gate still gives an exact 0.  On
-// the own tile the 32x32 diagonal sub-blocks take each key's running product
-// down its rows (f64), and the lower-left sub-block splits at row 32.  Pass 0
-// keeps a running largest live logit and normaliser per (lane, row), merged
-// across the 64 keys' lanes at the end; pass 1 recomputes the same logits and
-// products and writes W_ij = G_ij 2^((L - M) + f), f = log2 of the row scale
-// 2^((1-beta) M) z^-beta.
+// The logits come from one 32x32 MFMA product per wave (the key tile in LDS,
+// q in registers); lane (c, h) holds row c of the wave's rows and, in
+// register r, key 8 (r/4) + 4h + r%4 of its keys, so a lane's four registers
+// r = 4a .. 4a+3 are four consecutive keys of one row: one 16-byte store per
+// plane.  The row's running largest live logit and normaliser are per lane.
+// Below the own tile the path product factors as G_ij = P_i (C S_j) -- P_i
+// the gates r0+1 .. i, C those from the tile's end to r0, S_j the suffix
+// inside the tile (gates kernel) -- f64 scans rounded to f32 once and
+// multiplied per entry in f32; a zero gate still gives an exact 0.  On the
+// own tile the 32x32 diagonal sub-blocks take each row's running product
+// across its keys (f64), and the lower-left sub-block splits at row 32.
+// Pass 0 forms the shift M and the normaliser z of every row; pass 1
+// recomputes the same logits and products and writes
+// W_ij = G_ij 2^((L - M) + f), f = log2 of the row scale 2^((1-beta) M) z^-beta.
 template <bool QF32, int D>
 __global__ __launch_bounds__(256, 2) void operator_block_kernel(OpArgs A) {
     constexpr int ESZ = QF32 ? 4 : 2;
@@ -196,10 +198,12 @@ __global__ __launch_bounds__(256, 2) void operator_block_kernel(OpArgs A) {
     constexpr int ROWB = D * ESZ + 16;      // padded LDS key row (conflict-free reads)
     constexpr int NQ = KH * ESZ / 16;       // 16-byte words of q a lane holds
     __shared__ __align__(16) unsigned char ks[OB * ROWB];
+    __shared__ float4 cs[OB];       // C S_j of the tile's keys (f32)
     __shared__ float4 pr[OB];       // P_i of the block's rows
     __shared__ float4 p2[OB / 2];   // rows 32..63: gates r0+33 .. i
     __shared__ float4 s1[OB / 2];   // keys 0..31: gates j+1 .. r0+32
     __shared__ double ga[3][OB];    // the block's gates a_{r0+l} (re, im, |a|)
+    __shared__ float gd[2][3][32][33];  // G of the two 32x32 diagonal sub-blocks [row][key]
     __shared__ float2 part[OB];     // (M, z) of keys 32..63, per row
     __shared__ float2 mf[OB];       // (M, f) per row
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
@@ -211,6 +215,7 @@ __global__ __launch_bounds__(256, 2) void operator_block_kernel(OpArgs A) {
     const int qb = nb - 1 - int(int64_t(blockIdx.x) / A.BH);
     const int r0 = qb * OB;
     const double *ar = A.a_re + bh * n, *ai = A.a_im + bh * n, *am = A.a_m + bh * n;
+    const double *sre = A.s_re + bh * n, *sim = A.s_im + bh * n, *smo = A.s_m + bh * n;
     const char *kbase = static_cast<const char *>(A.k) + bh * n * (D * ESZ);
     bool bad = false;
 
@@ -232,10 +237,11 @@ __global__ __launch_bounds__(256, 2) void operator_block_kernel(OpArgs A) {
         if (lane < 32) s1[lane] = cg_f4(s);
     }
 
-    // q of the wave's rows: lane (c, h) holds row 32 wr + c, elements KH h ..
-    const int qrow = min(r0 + 32 * wr + c32, n - 1);
+    // q of the lane's row 32 wr + c, elements KH h ..
+    const int irel = 32 * wr + c32, i = r0 + irel;
     uint4 qw[NQ];
     {
+        const int qrow = min(i, n - 1);
         const char *qp = static_cast<const char *>(A.q) + ((bh * n + qrow) * D + KH * h) * ESZ;
 #pragma unroll
         for (int x = 0; x < NQ; ++x) qw[x] = *reinterpret_cast<const uint4 *>(qp + 16 * x);
@@ -249,20 +255,32 @@ __global__ __launch_bounds__(256, 2) void operator_block_kernel(OpArgs A) {
         }
     }
     __syncthreads();
-    float Mv[16], zv[16];
-#pragma unroll
-    for (int r = 0; r < 16; ++r) {
-        Mv[r] = -INFINITY;
-        zv[r] = 0.f;
+    if (wr == wc) {  // the diagonal sub-blocks: row c's running product over its keys
+        const int base = 32 * wr;
+        Cg R = {0.0, 0.0, 0.0};
+        for (int kk = 31; kk >= 0; --kk) {
+            if (kk == c32)
+                R = cg_one();
+            else if (kk < c32)
+                R = cg_mul(R, Cg{ga[0][base + kk + 1], ga[1][base + kk + 1], ga[2][base + kk + 1]});
+            if (((kk >> 2) & 1) == h) {
+                gd[wr][0][c32][kk] = float(R.re);
+                gd[wr][1][c32][kk] = float(R.im);
+                gd[wr][2][c32][kk] = float(R.m);
+            }
+        }
     }
-    // rows of the block (uniform base) and the lane's byte offsets from it
-    float *const wre = A.w_re + (bh * n + r0) * n, *const wim = A.w_im + (bh * n + r0) * n;
-    const uint32_t rowb = uint32_t(n) * 4u;
-    // the lane's key tile words, and the in-tile suffix products a_{j+1} ...
-    // a_{t0+64} of its key j (gates kernel)
+    __syncthreads();
+    const float4 prow = pr[irel];               // P_i of the lane's row
+    const float4 p2row = p2[c32];               // (rows 32..: used by waves with wr = 1)
+    const bool row_ok = i < n;
+    float M = -INFINITY, z = 0.f;
+    // the lane row's output rows (64-bit base, 32-bit column offsets)
+    float *const wre = A.w_re + (bh * n + i) * n, *const wim = A.w_im + (bh * n + i) * n;
+    const bool vec4 = (n & 3) == 0;             // rows start 16-byte aligned
+
     constexpr int KX = OB * NCH / 256;
     constexpr bool KPRE = !(QF32 && D == 128);  // prefetch the next tile (registers allow)
-    const double *sre = A.s_re + bh * n, *sim = A.s_im + bh * n, *smo = A.s_m + bh * n;
     auto load_k = [&](int t, uint4 (&v)[KX]) __attribute__((always_inline)) {
 #pragma unroll
         for (int x = 0; x < KX; ++x) {
@@ -273,17 +291,33 @@ __global__ __launch_bounds__(256, 2) void operator_block_kernel(OpArgs A) {
                     kbase + uint32_t((t * OB + row) * (D * ESZ) + 16 * ch));
         }
     };
-    for (int pass = 0; pass < 2; ++pass) {
-        Cg carry = cg_one();  // the gates from the current tile's end + 1 to r0
-        Cg sj = cg_one(), sj_next = cg_one();    // the lane key's in-tile suffix
-        Cg ft = cg_one(), ft_next = cg_one();    // the tile's product a_{t0+1} ... a_{t0+64}
+    // four consecutive keys j0.. of the lane's row (W_re, W_im planes)
+    auto store4 = [&](int j0, const float (&re)[4], const float (&im)[4])
+        __attribute__((always_inline)) {
+        if (vec4 && j0 + 3 < n) {
+            *reinterpret_cast<float4 *>(wre + j0) = make_float4(re[0], re[1], re[2], re[3]);
+            *reinterpret_cast<float4 *>(wim + j0) = make_float4(im[0], im[1], im[2], im[3]);
+        } else {
+#pragma unroll
+            for (int e4 = 0; e4 < 4; ++e4)
+                if (j0 + e4 < n) {
+                    wre[j0 + e4] = re[e4];
+                    wim[j0 + e4] = im[e4];
+                }
+        }
+    };
+    // the two passes as separate code: each keeps only its own registers live
+    auto run_pass = [&](auto pass_c) __attribute__((always_inline)) {
+        constexpr int pass = decltype(pass_c)::value;
+        Cg carry = cg_one();                  // wave 0: gates from the tile's end + 1 to r0
+        Cg sj = cg_one(), sj_next = cg_one(); // wave 0: in-tile suffix of key t0 + lane
+        Cg ft = cg_one(), ft_next = cg_one(); // wave 0: a_{t0+1} ... a_{t0+64}
         uint4 kv[KX];
         if constexpr (KPRE) load_k(qb, kv);
         for (int t = qb; t >= 0; --t) {
             const int t0 = t * OB;
             const bool own = (t == qb);
             if constexpr (!KPRE) load_k(t, kv);
-            // stage the key tile (rows past n are zeros)
 #pragma unroll
             for (int x = 0; x < KX; ++x) {
                 const int ci = tid + 256 * x, row = ci / NCH, ch = ci % NCH;
@@ -296,172 +330,221 @@ __global__ __launch_bounds__(256, 2) void operator_block_kernel(OpArgs A) {
                 }
                 *reinterpret_cast<uint4 *>(ks + row * ROWB + 16 * ch) = kv[x];
             }
+            if (w == 0 && !own) cs[lane] = cg_f4(cg_mul(carry, sj));
             __syncthreads();
-            if (t > 0) {  // the next tile's words and the lane's key suffix in it
+            if (t > 0) {  // the next tile's words; wave 0: its key suffixes, its product
                 if constexpr (KPRE) load_k(t - 1, kv);
-                const int jn = t0 - OB + 32 * wc + c32;
-                sj_next = Cg{sre[jn], sim[jn], smo[jn]};
-                ft_next = Cg{sre[t0 - OB], sim[t0 - OB], smo[t0 - OB]};
+                if (w == 0) {
+                    const int jn = t0 - OB + lane;
+                    sj_next = Cg{sre[jn], sim[jn], smo[jn]};
+                    ft_next = Cg{sre[t0 - OB], sim[t0 - OB], smo[t0 - OB]};
+                }
             }
 
-            // logits of the wave's 32 x 32 sub-block
+            // S^T of the wave's sub-block: A = 32 keys (LDS), B = 32 rows (q)
             f32x16 acc;
 #pragma unroll
             for (int r = 0; r < 16; ++r) acc[r] = 0.f;
             if (!A.qk_zero) {
                 const unsigned char *kp = ks + (32 * wc + c32) * ROWB + KH * ESZ * h;
                 if constexpr (!QF32) {
-                    bf16x8 kb[NQ];  // all fragments in flight before the first product
+                    // fragments read two ahead of the product that uses them
+                    bf16x8 kb[2];
+                    kb[0] = *reinterpret_cast<const bf16x8 *>(kp);
+                    kb[1] = *reinterpret_cast<const bf16x8 *>(kp + 16);
 #pragma unroll
-                    for (int s = 0; s < NQ; ++s) kb[s] = *reinterpret_cast<const bf16x8 *>(kp + 16 * s);
-#pragma unroll
-                    for (int s = 0; s < NQ; ++s)
+                    for (int s = 0; s < NQ; ++s) {
                         acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-                            __builtin_bit_cast(bf16x8, qw[s]), kb[s], acc, 0, 0, 0);
+                            kb[s & 1], __builtin_bit_cast(bf16x8, qw[s]), acc, 0, 0, 0);
+                        if (s + 2 < NQ) kb[s & 1] = *reinterpret_cast<const bf16x8 *>(kp + 16 * (s + 2));
+                    }
                 } else {
 #pragma unroll
                     for (int s = 0; s < NQ; ++s) {
                         const float4 kf = *reinterpret_cast<const float4 *>(kp + 16 * s);
                         const float4 qf = __builtin_bit_cast(float4, qw[s]);
-                        acc = __builtin_amdgcn_mfma_f32_32x32x2f32(qf.x, kf.x, acc, 0, 0, 0);
-                        acc = __builtin_amdgcn_mfma_f32_32x32x2f32(qf.y, kf.y, acc, 0, 0, 0);
-                        acc = __builtin_amdgcn_mfma_f32_32x32x2f32(qf.z, kf.z, acc, 0, 0, 0);
-                        acc = __builtin_amdgcn_mfma_f32_32x32x2f32(qf.w, kf.w, acc, 0, 0, 0);
+                        acc = __builtin_amdgcn_mfma_f32_32x32x2f32(kf.x, qf.x, acc, 0, 0, 0);
+                        acc = __builtin_amdgcn_mfma_f32_32x32x2f32(kf.y, qf.y, acc, 0, 0, 0);
+                        acc = __builtin_amdgcn_mfma_f32_32x32x2f32(kf.z, qf.z, acc, 0, 0, 0);
+                        acc = __builtin_amdgcn_mfma_f32_32x32x2f32(kf.w, qf.w, acc, 0, 0, 0);
                     }
                 }
             }
 
-            // the lane's key, and its first row relative to r0 (recomputed each
-            // tile: per-row values derived from it then stay short-lived)
-            const int j = t0 + 32 * wc + c32;
-            const int rb = 32 * wr + 4 * h + opaque_zero();
-            // one entry: register r of the lane, path product (g_re, g_im, |g|);
-            // below: the key tile lies below the block (every key is causal).
-            // v_exp_f32 directly: a result below the normal range reads 0.
-            auto entry = [&](int r, float g_re, float g_im, float g_m, bool below)
-                __attribute__((always_inline)) {
-                const int irel = rb + 8 * (r >> 2) + (r & 3);
-                const int i = r0 + irel;
-                const bool key = (below || j <= i) && i < n;
-                float L = 0.f;
-                if (!A.qk_zero) {
-#pragma clang fp contract(off)
-                    L = acc[r] * A.c;
-                }
-                const bool live = key && g_m > 0.f;
-                if (pass == 0) {
-                    if (key && !isfinite(L)) bad = true;
-                    const float mn = live ? fmaxf(Mv[r], L) : Mv[r];
-                    const float sc = Mv[r] == mn ? 1.f : __builtin_amdgcn_exp2f(Mv[r] - mn);
-                    const float e = live ? __builtin_amdgcn_exp2f(L - mn) : 0.f;
-                    zv[r] = fmaf(g_m, e, zv[r] * sc);
-                    Mv[r] = mn;
-                } else if (i < n && j < n) {
-                    // a dead entry gets e = 0 and a finite G: W = 0
-                    const float e = live ? __builtin_amdgcn_exp2f((L - Mv[r]) + zv[r]) : 0.f;
-                    const uint32_t off = uint32_t(irel) * rowb + uint32_t(j) * 4u;
-                    *reinterpret_cast<float *>(reinterpret_cast<char *>(wre) + off) =
-                        scale_keep_zero(g_re, e);
-                    *reinterpret_cast<float *>(reinterpret_cast<char *>(wim) + off) =
-                        scale_keep_zero(g_im, e);
-                }
-            };
-            if (!own) {  // G_ij = P_i (C S_j)
-                const float4 c = cg_f4(cg_mul(carry, sj));
-#pragma unroll
-                for (int r = 0; r < 16; ++r) {
-                    const float4 p = pr[rb + 8 * (r >> 2) + (r & 3)];
-                    entry(r, p.x * c.x - p.y * c.y, p.x * c.y + p.y * c.x, p.z * c.z, true);
-                }
-            } else if (wr != wc) {
-                if (wr == 0) {  // keys above every row of the sub-block
-#pragma unroll
-                    for (int r = 0; r < 16; ++r) entry(r, 0.f, 0.f, 0.f, false);
-                } else {        // rows 32.., keys ..31: split at row 32
-                    const float4 c = s1[c32];
+            const int oz = opaque_zero();
+            const int jb = t0 + 32 * wc + 4 * h;  // key of register 0; register r: jb + 8 (r/4) + r%4
+            if (!own) {
+                // below the block: every key is causal; G_ij = P_i (C S_j)
+                const float4 *ctab = cs + 32 * wc + oz + 4 * h;
+                if constexpr (pass == 0) {
+                    float L[16], gmv[16], chk = 0.f, tmax = -INFINITY;
 #pragma unroll
                     for (int r = 0; r < 16; ++r) {
-                        const float4 p = p2[rb - 32 + 8 * (r >> 2) + (r & 3)];
-                        entry(r, p.x * c.x - p.y * c.y, p.x * c.y + p.y * c.x, p.z * c.z,
-                              true);
+                        gmv[r] = prow.z * ctab[8 * (r >> 2) + (r & 3)].z;
+                        L[r] = 0.f;
+                        if (!A.qk_zero) {
+#pragma clang fp contract(off)
+                            L[r] = acc[r] * A.c;
+                        }
+                        chk = fmaf(L[r], 0.f, chk);  // NaN once any logit is not finite
+                        tmax = fmaxf(tmax, gmv[r] > 0.f ? L[r] : -INFINITY);
+                    }
+                    if (row_ok) {
+                        if (!isfinite(chk)) bad = true;
+                        if (tmax > M) {
+                            z *= M == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(M - tmax);
+                            M = tmax;
+                        }
+#pragma unroll
+                        for (int r = 0; r < 16; ++r)  // a dead entry adds 0
+                            z = fmaf(gmv[r], gmv[r] > 0.f ? __builtin_amdgcn_exp2f(L[r] - M) : 0.f, z);
+                    }
+                } else if (row_ok) {
+#pragma unroll
+                    for (int a = 0; a < 4; ++a) {
+                        float wv_re[4], wv_im[4];
+#pragma unroll
+                        for (int e4 = 0; e4 < 4; ++e4) {
+                            const int r = 4 * a + e4;
+                            const float4 c = ctab[8 * a + e4];
+                            float L = 0.f;
+                            if (!A.qk_zero) {
+#pragma clang fp contract(off)
+                                L = acc[r] * A.c;
+                            }
+                            const float e = prow.z * c.z > 0.f
+                                                ? __builtin_amdgcn_exp2f((L - M) + z) : 0.f;
+                            wv_re[e4] = scale_keep_zero(prow.x * c.x - prow.y * c.y, e);
+                            wv_im[e4] = scale_keep_zero(prow.x * c.y + prow.y * c.x, e);
+                        }
+                        store4(jb + 8 * a, wv_re, wv_im);
                     }
                 }
-            } else {            // diagonal sub-block: key c's product down the rows
-                const int base = 32 * wr;
-                Cg R = cg_one();
+            } else {
+            // own tile: path products of the lane's 16 entries (re, im, |G|)
+            float gr[16], gi[16], gm[16];
+            if (wr != wc) {
+                if (wr == 0) {  // keys above every row of the sub-block
 #pragma unroll
-                for (int rel = 0; rel < 32; ++rel) {
-                    if (rel > c32) R = cg_mul(R, Cg{ga[0][base + rel], ga[1][base + rel],
-                                                    ga[2][base + rel]});
-                    // row rel belongs to lane half (rel / 4) % 2, register 4 (rel / 8) + rel % 4
-                    const bool mine = ((rel >> 2) & 1) == h, on = rel >= c32;
-                    const int r = 4 * (rel >> 3) + (rel & 3);
-                    if (__any(mine))
-                        if (mine)
-                            entry(r, on ? float(R.re) : 0.f, on ? float(R.im) : 0.f,
-                                  on ? float(R.m) : 0.f, false);
+                    for (int r = 0; r < 16; ++r) gr[r] = gi[r] = gm[r] = 0.f;
+                } else {  // rows 32.., keys ..31: (gates r0+33 .. i)(gates j+1 .. r0+32)
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) {
+                        const float4 c = s1[oz + 8 * (r >> 2) + 4 * h + (r & 3)];
+                        gr[r] = p2row.x * c.x - p2row.y * c.y;
+                        gi[r] = p2row.x * c.y + p2row.y * c.x;
+                        gm[r] = p2row.z * c.z;
+                    }
                 }
-            }
-            if (!own) carry = cg_mul(ft, carry);  // C for the tile below
-            sj = sj_next;
-            ft = ft_next;
-            __syncthreads();  // the tile buffer is rewritten next
-        }
-        if (pass == 0) {
-            // merge (M, z) over the 32 keys of each lane half, then the two waves
-#pragma unroll
-            for (int r = 0; r < 16; ++r) {
-#pragma unroll
-                for (int o = 1; o < 32; o <<= 1) {
-                    const float Mo = __shfl_xor(Mv[r], o), zo = __shfl_xor(zv[r], o);
-                    const float Mn = fmaxf(Mv[r], Mo);
-                    if (Mn != -INFINITY)
-                        zv[r] = zv[r] * exp2f(Mv[r] - Mn) + zo * exp2f(Mo - Mn);
-                    Mv[r] = Mn;
-                }
-            }
-            if (wc == 1 && c32 == 0) {
-#pragma unroll
-                for (int r = 0; r < 16; ++r)
-                    part[32 * wr + 8 * (r >> 2) + 4 * h + (r & 3)] = make_float2(Mv[r], zv[r]);
-            }
-            __syncthreads();
-            if (wc == 0 && c32 == 0) {
+            } else {  // diagonal sub-block (products formed once per block)
 #pragma unroll
                 for (int r = 0; r < 16; ++r) {
-                    const int row = 32 * wr + 8 * (r >> 2) + 4 * h + (r & 3);
-                    const float2 o = part[row];
-                    const float Mn = fmaxf(Mv[r], o.x);
-                    const float zt = zv[r] * exp2f(Mv[r] - Mn) + o.y * exp2f(o.x - Mn);
-                    float f;
-                    if (A.beta_mode == 1)
-                        f = -log2f(zt);
-                    else if (A.beta_mode == 0)
-                        f = Mn;
-                    else
-                        f = A.one_minus_beta * Mn - A.beta * log2f(zt);
-                    mf[row] = make_float2(Mn, f);
+                    const int kk = oz + 8 * (r >> 2) + 4 * h + (r & 3);
+                    gr[r] = gd[wr][0][c32][kk];
+                    gi[r] = gd[wr][1][c32][kk];
+                    gm[r] = gd[wr][2][c32][kk];
                 }
             }
-            __syncthreads();
+            if constexpr (pass == 0) {
+                // this tile's largest live logit of the row, then one rescale
+                float L[16], tmax = -INFINITY;
 #pragma unroll
-            for (int r = 0; r < 16; ++r) {  // pass 1: Mv = M, zv = f
-                const float2 x = mf[32 * wr + 8 * (r >> 2) + 4 * h + (r & 3)];
-                Mv[r] = x.x;
-                zv[r] = x.y;
+                for (int r = 0; r < 16; ++r) {
+                    const int j = jb + 8 * (r >> 2) + (r & 3);
+                    const bool key = j <= i && row_ok;
+                    L[r] = 0.f;
+                    if (!A.qk_zero) {
+#pragma clang fp contract(off)
+                        L[r] = acc[r] * A.c;
+                    }
+                    if (key && !isfinite(L[r])) bad = true;
+                    const bool live = key && gm[r] > 0.f;
+                    if (!live) gm[r] = 0.f;
+                    tmax = live ? fmaxf(tmax, L[r]) : tmax;
+                }
+                if (tmax > M) {
+                    z *= M == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(M - tmax);
+                    M = tmax;
+                }
+#pragma unroll
+                for (int r = 0; r < 16; ++r)  // a dead entry has gm = 0: adds 0
+                    z = fmaf(gm[r], gm[r] > 0.f ? __builtin_amdgcn_exp2f(L[r] - M) : 0.f, z);
+            } else if (row_ok) {
+#pragma unroll
+                for (int a = 0; a < 4; ++a) {
+                    float wv_re[4], wv_im[4];
+#pragma unroll
+                    for (int e4 = 0; e4 < 4; ++e4) {
+                        const int r = 4 * a + e4, j = jb + 8 * a + e4;
+                        float L = 0.f;
+                        if (!A.qk_zero) {
+#pragma clang fp contract(off)
+                            L = acc[r] * A.c;
+                        }
+                        const bool live = j <= i && gm[r] > 0.f;
+                        const float e = live ? __builtin_amdgcn_exp2f((L - M) + z) : 0.f;
+                        wv_re[e4] = scale_keep_zero(gr[r], e);
+                        wv_im[e4] = scale_keep_zero(gi[r], e);
+                    }
+                    store4(jb + 8 * a, wv_re, wv_im);
+                }
             }
+            }
+            if (w == 0 && !own) carry = cg_mul(ft, carry);  // C for the tile below
+            sj = sj_next;
+            ft = ft_next;
+            __syncthreads();  // the tile buffers are rewritten next
         }
-    }
+        if constexpr (pass == 0) {
+            // merge (M, z) over the two lane halves, then the two waves of the row
+            {
+                const float Mo = __shfl_xor(M, 32), zo = __shfl_xor(z, 32);
+                const float Mn = fmaxf(M, Mo);
+                if (Mn != -INFINITY) z = z * exp2f(M - Mn) + zo * exp2f(Mo - Mn);
+                M = Mn;
+            }
+            if (wc == 1 && h == 0) part[irel] = make_float2(M, z);
+            __syncthreads();
+            if (wc == 0 && h == 0) {
+                const float2 o = part[irel];
+                const float Mn = fmaxf(M, o.x);
+                const float zt = z * exp2f(M - Mn) + o.y * exp2f(o.x - Mn);
+                float f;
+                if (A.beta_mode == 1)
+                    f = -log2f(zt);
+                else if (A.beta_mode == 0)
+                    f = Mn;
+                else
+                    f = A.one_minus_beta * Mn - A.beta * log2f(zt);
+                mf[irel] = make_float2(Mn, f);
+            }
+            __syncthreads();
+            const float2 x = mf[irel];  // pass 1: M = the row's shift, z = f
+            M = x.x;
+            z = x.y;
+        }
+    };
+    run_pass(std::integral_constant<int, 0>{});
+    run_pass(std::integral_constant<int, 1>{});
     // columns right of the block's own tile are zeros
     const int c0 = r0 + OB, rows = min(OB, n - r0);
-    if (c0 < n)
-        for (int rr = 0; rr < rows; ++rr) {
-            float *zr = A.w_re + (bh * n + r0 + rr) * n, *zi = A.w_im + (bh * n + r0 + rr) * n;
-            for (int jj = c0 + tid; jj < n; jj += 256) {
-                zr[jj] = 0.f;
-                zi[jj] = 0.f;
+    if (c0 < n) {
+        float *zr = A.w_re + (bh * n + r0) * n, *zi = A.w_im + (bh * n + r0) * n;
+        if (vec4) {
+            const int n4 = (n - c0) / 4;
+            for (int x = tid; x < rows * n4; x += 256) {
+                const int rr = x / n4, c = c0 + 4 * (x % n4);
+                *reinterpret_cast<float4 *>(zr + int64_t(rr) * n + c) = make_float4(0.f, 0.f, 0.f, 0.f);
+                *reinterpret_cast<float4 *>(zi + int64_t(rr) * n + c) = make_float4(0.f, 0.f, 0.f, 0.f);
             }
+        } else {
+            for (int rr = 0; rr < rows; ++rr)
+                for (int jj = c0 + tid; jj < n; jj += 256) {
+                    zr[int64_t(rr) * n + jj] = 0.f;
+                    zi[int64_t(rr) * n + jj] = 0.f;
+                }
         }
+    }
     if (__any(bad) && lane == 0) A.status[0] = kExpNonFinite;
 }
 
