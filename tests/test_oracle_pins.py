@@ -457,8 +457,9 @@ def test_non_finite_input_is_refused():
 
 def test_empty_sequence_and_no_all_masked_row():
     """an_empty_sequence_is_empty_and_no_row_is_ever_all_masked: n = 0 gives
-    an empty result; closing every gate leaves the identity at beta = 1 and
-    diag(e^{qk s_ii}) at beta = 0; head_dim = 0 with n > 0 is a shape error."""
+    an empty result; with every gate shut each row keeps only its own key, so W
+    is I at beta = 1 and diag(e^{qk s_ii}) at beta = 0; head_dim = 0 with n > 0
+    is a shape error."""
     e = np.zeros((0, 4))
     st, O = oracle.forward_rows(e, e, np.zeros(0), np.zeros(0), e, 1, 1, 1, rows=[])
     assert st == oracle.OK and O.shape == (0, 4)
