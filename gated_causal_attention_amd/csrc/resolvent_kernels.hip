@@ -1512,38 +1512,27 @@ __global__ __launch_bounds__(NTHREADS, 1) void fwd_kernel(FwdArgs A) {
     // vector step in phase 2k + 1 + lag; a barrier ends every phase, and the
     // trailing waves pass one extra barrier first, the leading ones one last.
     // The copies of a phase (leading waves only) run around its step.
-    // Both waves of a SIMD keep issue priority 0. Raising it for the wave in
-    // its matrix step (2 against 0) measured slower. The explicit priority-0
-    // writes at each step measured about 0.7% faster than none at all; the
-    // compiled loops differ only in those instructions and in the order of a
-    // few scalar ones, so the gain is most likely one of code placement.
     if (lag) lds_barrier();
     int k = 0;
     for (; k < 2 * n_off; ++k) {
-        __builtin_amdgcn_s_setprio(0);
         m_step_off(k);
         after_m(k);
         lds_barrier();
-        __builtin_amdgcn_s_setprio(0);
         v_step_off(k);
         after_v(k);
         lds_barrier();
     }
     for (; k < 2 * n_tiles; ++k) {
-        __builtin_amdgcn_s_setprio(0);
         m_step(k);
         after_m(k);
         lds_barrier();
-        __builtin_amdgcn_s_setprio(0);
         v_step_own(k);
         after_v(k);
         lds_barrier();
     }
-    __builtin_amdgcn_s_setprio(0);
     m_step(k);  // the last block's W~ V
     after_m(k);
     lds_barrier();
-    __builtin_amdgcn_s_setprio(0);
     if (!lag) lds_barrier();
     atomicMax(&misc[3], kbits);
 
