@@ -1953,40 +1953,49 @@ __global__ __launch_bounds__(NTHREADS, 1) void fwd_pad_kernel(FwdArgs A) {
         unsigned char *buf = tile_buf(sg);
         if (sg < n_off) {
             if (w == 0) {
+                // every LDS read first, so that they share one round trip:
+                // the tile's gate factors (one key per lane), the tile's
+                // product and the carried product before the tile
                 const int ln = fresh_lane();
+                const float *raw = reinterpret_cast<const float *>(buf + SM::raw_off);
+                const float g0 = raw[ln], g1 = raw[BK + ln], g2 = raw[2 * BK + ln];
+                const double *at = reinterpret_cast<const double *>(buf + SM::tprod_off);
+                const double ar = at[0], ai = at[1], am = at[2];
                 double c_re = 1.0, c_im = 0.0, c_m = 1.0;
                 if (sg > 0) {
                     c_re = cst[0];
                     c_im = cst[1];
                     c_m = cst[2];
                 }
-                {
-#pragma clang fp contract(off)
-                    const double *at = reinterpret_cast<const double *>(buf + SM::tprod_off);
-                    const double ar = at[0], ai = at[1], am = at[2];
-                    const double nr = ar * c_re - ai * c_im;
-                    const double ni = ar * c_im + ai * c_re;
-                    const double nm = am * c_m;
-                    if (ln == 0) {
-                        cst[0] = nr;
-                        cst[1] = ni;
-                        cst[2] = nm;
-                    }
-                }
+                settle(ar);
+                settle(ai);
+                settle(am);
                 const float ccx = (float)c_re, ccy = (float)c_im, ccz = (float)c_m;
-                const float *raw = reinterpret_cast<const float *>(buf + SM::raw_off);
                 float *sd = reinterpret_cast<float *>(buf + SM::side_off);
-                const float g0 = raw[ln], g1 = raw[BK + ln], g2 = raw[2 * BK + ln];
                 const float rt = ccz * g2;
                 const int slot = perm64(ln);
-                sd[slot] = ccx * g0 - ccy * g1;
-                sd[BK + slot] = ccx * g1 + ccy * g0;
+                // explicit fused forms: the rounding does not depend on
+                // which product the compiler would contract
+                sd[slot] = fmaf(ccx, g0, -(ccy * g1));
+                sd[BK + slot] = fmaf(ccx, g1, ccy * g0);
                 sd[2 * BK + slot] = rt;
+                // the carried product of the next tile (the visit-count
+                // recurrence and rounding), and the dead keys of this one as
+                // a 64-bit mask: a word is nonzero when its 32-key block holds
+                // a dead key
                 const uint64_t dead = __ballot(rt == 0.0f);
+                double nr, ni, nm;
+                {
+#pragma clang fp contract(off)
+                    nr = ar * c_re - ai * c_im;
+                    ni = ar * c_im + ai * c_re;
+                    nm = am * c_m;
+                }
                 if (ln == 0) {
-                    uint32_t *fl = reinterpret_cast<uint32_t *>(buf + SM::flag_off);
-                    fl[0] = (uint32_t)(dead & 0xFFFFFFFFull) != 0u;
-                    fl[1] = (uint32_t)(dead >> 32) != 0u;
+                    cst[0] = nr;
+                    cst[1] = ni;
+                    cst[2] = nm;
+                    *reinterpret_cast<uint64_t *>(buf + SM::flag_off) = dead;
                 }
             }
         } else if (w > 0) {
