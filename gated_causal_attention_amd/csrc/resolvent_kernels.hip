@@ -2283,8 +2283,6 @@ __global__ __launch_bounds__(NTHREADS, 1) void fwd_pad_kernel(FwdArgs A) {
     const unsigned char *vprev = tile_buf(0) + vlane;
     if (n_off > 0)
         pstep_prefetch<D, DV, 0, 0, true, !QKZ, 0, NPRE>(vprev, tile_buf(0) + klane, pf);
-    else
-        pstep_prefetch<D, DV, 0, 32, true, !QKZ, 0, NPRE>(vprev, tile_buf(0) + klane, pf);
     if (lag) lds_barrier();
     int m = 0;
     for (; m < n_off; ++m) {
@@ -2312,60 +2310,60 @@ __global__ __launch_bounds__(NTHREADS, 1) void fwd_pad_kernel(FwdArgs A) {
         if (m + 1 < n_off)
             pstep_prefetch<D, DV, 0, 0, true, !QKZ, 0, NPRE>(vprev, tile_buf(m + 1) + klane, pf);
         else
-            pstep_prefetch<D, DV, 0, 32, true, !QKZ, 0, NPRE>(vprev, tile_buf(m + 1) + klane, pf);
+            pstep_prefetch<D, DV, 0, 0, true, false, 0, NPRE>(vprev, vprev, pf);
         lds_barrier();
     }
     // ---- the query tile's own tiles: blocks visited highest keys first
     // (keys 32..63 of a tile, then 0..31); the block of visit index kk of the
-    // NDB is active for wave w when kk >= NDB-1-w.
+    // NDB is active for wave w when kk >= NDB-1-w.  Once the trailing waves
+    // have finished the last vector step before the query tile, every wave
+    // runs its active blocks back to back, without a barrier between steps:
+    // no buffer is written while a tile's blocks run (the copies of the tile
+    // two ahead go to a buffer every wave has finished), and one barrier per
+    // own tile publishes the next one, landed by the copy waits before it.
+    if (!lag) lds_barrier();
+    if (n_off > 0) {
+        // the W~ V of the last block before the query tile; then the blocks
+        // before the query tile are in O: rotate by P_i
+        pstep<D, DV, 0, 0, true, false, NPRE>(vprev, vprev, pf, wk.r, wk.i, qf, ore, oim, x);
+#pragma unroll
+        for (int db = 0; db < DV / 32; ++db)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const float xr = ore[db][r], xi = oim[db][r];
+                ore[db][r] = prow_re * xr - prow_im * xi;
+                oim[db][r] = prow_re * xi + prow_im * xr;
+            }
+        z *= prow_m;
+    }
+    // until a wave's first active block its W~ is zero and the W~ V of the
+    // step before that block reads the first own tile's v^T (never rewritten)
+    zero_w();
+    vprev = tile_buf(m) + vlane;
     for (int mm = 0; mm < NDIAG; ++mm, ++m) {
         const unsigned char *bufm = tile_buf(m);
         const unsigned char *kb_ = bufm + klane;
         const unsigned char *vb_ = bufm + vlane;
         const int tl = NDIAG - 1 - mm;  // key tile, counted from t_diag0
-        // block 2mm: keys 32..63 of the tile
-        pstep<D, DV, 0, 32, true, !QKZ, NPRE>(vprev, kb_, pf, wk.r, wk.i, qf, ore, oim, x);
         issue(m + 2);
-        lds_barrier();
-        if (mm == 0 && n_off > 0) {  // the blocks before the query tile are in O: rotate by P_i
-#pragma unroll
-            for (int db = 0; db < DV / 32; ++db)
-#pragma unroll
-                for (int r = 0; r < 16; ++r) {
-                    const float xr = ore[db][r], xi = oim[db][r];
-                    ore[db][r] = prow_re * xr - prow_im * xi;
-                    oim[db][r] = prow_re * xi + prow_im * xr;
-                }
-            z *= prow_m;
-        }
-        if (own_active(2 * mm))
+        if (own_active(2 * mm)) {  // keys 32..63 of the tile
+            pstep_prefetch<D, DV, 0, 32, true, !QKZ, 0, NPRE>(vprev, kb_, pf);
+            pstep<D, DV, 0, 32, true, !QKZ, NPRE>(vprev, kb_, pf, wk.r, wk.i, qf, ore, oim, x);
             vstep_own(bufm, 32, 32 * w + qi - (tl * BK + 32));
-        else
-            zero_w();
-        settle_weights();
-        pstep_prefetch<D, DV, 0, 0, true, !QKZ, 0, NPRE>(vb_ + 2 * 32, kb_, pf);
-        if (lag) land_wait(m);
-        lds_barrier();
-        // block 2mm+1: keys 0..31 of the tile
-        pstep<D, DV, 0, 0, true, !QKZ, NPRE>(vb_ + 2 * 32, kb_, pf, wk.r, wk.i, qf, ore, oim, x);
-        if (!lag) land_wait(m);
-        lds_barrier();
-        if (own_active(2 * mm + 1))
+            vprev = vb_ + 2 * 32;
+        }
+        if (own_active(2 * mm + 1)) {  // keys 0..31 of the tile
+            pstep_prefetch<D, DV, 0, 0, true, !QKZ, 0, NPRE>(vprev, kb_, pf);
+            pstep<D, DV, 0, 0, true, !QKZ, NPRE>(vprev, kb_, pf, wk.r, wk.i, qf, ore, oim, x);
             vstep_own(bufm, 0, 32 * w + qi - tl * BK);
-        else
-            zero_w();
-        settle_weights();
-        vprev = vb_;
-        if (mm + 1 < NDIAG)
-            pstep_prefetch<D, DV, 0, 32, true, !QKZ, 0, NPRE>(vprev, tile_buf(m + 1) + klane, pf);
-        else
-            pstep_prefetch<D, DV, 0, 0, true, false, 0, NPRE>(vprev, vprev, pf);
+            vprev = vb_;
+        }
+        land_wait(m);
         lds_barrier();
     }
     // the last block's W~ V (keys 0..31 of the lowest own tile: every wave)
+    pstep_prefetch<D, DV, 0, 0, true, false, 0, NPRE>(vprev, vprev, pf);
     pstep<D, DV, 0, 0, true, false, NPRE>(vprev, vprev, pf, wk.r, wk.i, qf, ore, oim, x);
-    lds_barrier();
-    if (!lag) lds_barrier();
     atomicMax(&misc[3], kbits);
 
     // ---- epilogue: O *= exp2((1-beta) M) z^-beta -------------------------
