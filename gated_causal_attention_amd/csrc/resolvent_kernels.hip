@@ -1998,7 +1998,29 @@ __global__ __launch_bounds__(NTHREADS, 1) void fwd_pad_kernel(FwdArgs A) {
                     *reinterpret_cast<uint64_t *>(buf + SM::flag_off) = dead;
                 }
             }
-        } else if (w > 0) {
+        } else if (w == 0) {
+            // an own tile: the inclusive suffix products of its gate factors
+            // inside each group of 8 keys, S8_l = c_l c_{l+1} ... c_{8g+7}
+            // (c_l = a_{t0+l+1}, g = l / 8), into the raw area
+            const int ln = fresh_lane();
+            const float *sd = reinterpret_cast<const float *>(buf + SM::side_off);
+            float sr = sd[ln], si = sd[BK + ln], sm = sd[2 * BK + ln];
+#pragma unroll
+            for (int k = 1; k < 8; k <<= 1) {
+                const float orr = __shfl_down(sr, k), oi = __shfl_down(si, k), om = __shfl_down(sm, k);
+                if ((ln & 7) + k < 8) {
+                    const float nr = fmaf(sr, orr, -(si * oi));
+                    const float ni = fmaf(sr, oi, si * orr);
+                    sr = nr;
+                    si = ni;
+                    sm = sm * om;
+                }
+            }
+            float *s8 = reinterpret_cast<float *>(buf + SM::raw_off);
+            s8[ln] = sr;
+            s8[BK + ln] = si;
+            s8[2 * BK + ln] = sm;
+        } else {
 #pragma unroll
             for (int i = 0; i < CPW; ++i) {
                 const int j = pad_copy_j<D, DV>(w, i);
@@ -2195,50 +2217,114 @@ __global__ __launch_bounds__(NTHREADS, 1) void fwd_pad_kernel(FwdArgs A) {
     // vector step of a block of the query tile's own keys: explicit G_ij by a
     // running product per row, a_i a_{i-1} ... a_{j+1}, last key first (as
     // fwd_kernel)
-    auto vstep_own = [&](const unsigned char *buf, int kb, int dpos) __attribute__((always_inline)) {
+    // vector step of a block of the query tile's own keys.  The block's
+    // keys fall in four groups of 8; for key j of group g and row i,
+    // G_ij = a_i a_{i-1} ... a_{j+1} is S8_j (the suffix product inside the
+    // group, formed when the tile landed) times R_i(g+1), the row's product
+    // from the top of group g down to the row, when group g lies below the
+    // row's own group; inside the row's own group it is the row's running
+    // product taken key by key (restarting at the row's own key); above the
+    // row it is 0.  R steps down a group at a time, R_i(g) = S8_{8g} R_i(g+1),
+    // and starts at the row's own group, or, for a block wholly below the
+    // wave's rows (diag false), at the row's running product carried from
+    // the blocks above; R_i(0) is carried to the next block.
+    auto vstep_own = [&](const unsigned char *buf, int kb, bool diag) __attribute__((always_inline)) {
         const float *side = reinterpret_cast<const float *>(buf + SM::side_off);
-        const int kl = kb + (lane & 31);
-        const float vre = side[kl], vim = side[BK + kl], vm = side[2 * BK + kl];
-        auto key_gate = [](float v, int j) __attribute__((always_inline)) {
-            return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), j));
-        };
+        const float *s8 = reinterpret_cast<const float *>(buf + SM::raw_off);
+        lds_v4f *sv = (lds_v4f *)(lds_void *)(s8 + kb + 4 * h);
+        lds_v4f *cv = (lds_v4f *)(lds_void *)(side + kb + 8 * (qi >> 3));
+        const int gi = diag ? (qi >> 3) : 4;  // the row's own group (4: above the block)
+        const int pi = qi & 7;                // the row's key inside its group
+        // moduli
         float Gm[16];
-        const float gre0 = gre, gim0 = gim;
+        float rm_next;
+        {
+            float own[4] = {0.f, 0.f, 0.f, 0.f}, pre = 0.f;
+            if (diag) {
+                const v4f c0 = cv[(2 * BK) / 4], c1 = cv[(2 * BK) / 4 + 1];
+                const float c[8] = {c0.x, c0.y, c0.z, c0.w, c1.x, c1.y, c1.z, c1.w};
+                float v[8];
+                float g = 0.f;
 #pragma unroll
-        for (int jj = 31; jj >= 0; --jj) {
-            const float nm = gm * key_gate(vm, jj);
-            gm = (jj == dpos) ? 1.0f : nm;
-            if (h == ((jj >> 2) & 1)) Gm[4 * (jj >> 3) + (jj & 3)] = gm;
+                for (int t = 7; t >= 0; --t) {
+                    g = (t == pi) ? 1.0f : g * c[t];
+                    v[t] = g;
+                }
+#pragma unroll
+                for (int e = 0; e < 4; ++e) own[e] = h ? v[4 + e] : v[e];
+                pre = v[0];
+            }
+            float rm = diag ? 0.f : gm;
+#pragma unroll
+            for (int g = 3; g >= 0; --g) {
+                const v4f q = sv[(2 * BK + 8 * g) / 4];
+                const float qv[4] = {q.x, q.y, q.z, q.w};
+#pragma unroll
+                for (int e = 0; e < 4; ++e) Gm[4 * g + e] = (g == gi) ? own[e] : qv[e] * rm;
+                rm = (g == gi) ? pre : s8[2 * BK + kb + 8 * g] * rm;
+            }
+            rm_next = rm;
         }
         if constexpr (!QKZ) {
 #pragma unroll
             for (int r = 0; r < 16; ++r) x[r] = (Gm[r] > 0.0f) ? x[r] : dead_s;
         }
         const float msub = block_shift();
-        gre = gre0;
-        gim = gim0;
+        // complex values, a chunk of two groups at a time
+        float own_r[4] = {0.f, 0.f, 0.f, 0.f}, own_i[4] = {0.f, 0.f, 0.f, 0.f};
+        float pre_r = 0.f, pre_i = 0.f;
+        if (diag) {
+            const v4f r0 = cv[0], r1 = cv[1], i0 = cv[BK / 4], i1 = cv[BK / 4 + 1];
+            const float cr[8] = {r0.x, r0.y, r0.z, r0.w, r1.x, r1.y, r1.z, r1.w};
+            const float ci[8] = {i0.x, i0.y, i0.z, i0.w, i1.x, i1.y, i1.z, i1.w};
+            float vr[8], vi[8];
+            float gr_ = 0.f, gi_ = 0.f;
+#pragma unroll
+            for (int t = 7; t >= 0; --t) {
+                const float nr = fmaf(gr_, cr[t], -(gi_ * ci[t]));
+                const float ni = fmaf(gr_, ci[t], gi_ * cr[t]);
+                gr_ = (t == pi) ? 1.0f : nr;
+                gi_ = (t == pi) ? 0.0f : ni;
+                vr[t] = gr_;
+                vi[t] = gi_;
+            }
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                own_r[e] = h ? vr[4 + e] : vr[e];
+                own_i[e] = h ? vi[4 + e] : vi[e];
+            }
+            pre_r = vr[0];
+            pre_i = vi[0];
+        }
+        float rr = diag ? 0.f : gre, ri = diag ? 0.f : gim;
 #pragma unroll
         for (int kc = 1; kc >= 0; --kc) {
             float fre[8], fim[8], fm[8];
 #pragma unroll
-            for (int jj = 16 * kc + 15; jj >= 16 * kc; --jj) {
-                const float dr = key_gate(vre, jj), di = key_gate(vim, jj);
-                const float nr = gre * dr - gim * di;
-                const float ni = gre * di + gim * dr;
-                const bool diag = (jj == dpos);
-                gre = diag ? 1.0f : nr;
-                gim = diag ? 0.0f : ni;
-                if (h == ((jj >> 2) & 1)) {
-                    const int e = 4 * ((jj - 16 * kc) >> 3) + (jj & 3);
-                    fre[e] = gre;
-                    fim[e] = gim;
+            for (int g = 2 * kc + 1; g >= 2 * kc; --g) {
+                const v4f qr = sv[(8 * g) / 4], qi4 = sv[(BK + 8 * g) / 4];
+                const float tr[4] = {qr.x, qr.y, qr.z, qr.w};
+                const float ti[4] = {qi4.x, qi4.y, qi4.z, qi4.w};
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const int k = 4 * (g - 2 * kc) + e;
+                    fre[k] = (g == gi) ? own_r[e] : fmaf(tr[e], rr, -(ti[e] * ri));
+                    fim[k] = (g == gi) ? own_i[e] : fmaf(tr[e], ri, ti[e] * rr);
                 }
+                const float fr8 = s8[kb + 8 * g], fi8 = s8[BK + kb + 8 * g];
+                const float nr = fmaf(fr8, rr, -(fi8 * ri));
+                const float ni = fmaf(fr8, ri, fi8 * rr);
+                rr = (g == gi) ? pre_r : nr;
+                ri = (g == gi) ? pre_i : ni;
             }
 #pragma unroll
             for (int e = 0; e < 8; ++e) fm[e] = Gm[8 * kc + e];
             weights(kc, msub, fre, fim, fm, false, true, true);
             __builtin_amdgcn_sched_barrier(0);
         }
+        gre = rr;
+        gim = ri;
+        gm = rm_next;
     };
     auto settle_weights = [&]() __attribute__((always_inline)) {
         settle(wk.r[0]);
@@ -2349,13 +2435,13 @@ __global__ __launch_bounds__(NTHREADS, 1) void fwd_pad_kernel(FwdArgs A) {
         if (own_active(2 * mm)) {  // keys 32..63 of the tile
             pstep_prefetch<D, DV, 0, 32, true, !QKZ, 0, NPRE>(vprev, kb_, pf);
             pstep<D, DV, 0, 32, true, !QKZ, NPRE>(vprev, kb_, pf, wk.r, wk.i, qf, ore, oim, x);
-            vstep_own(bufm, 32, 32 * w + qi - (tl * BK + 32));
+            vstep_own(bufm, 32, __builtin_amdgcn_readfirstlane(32 * w - (tl * BK + 32)) < 32);
             vprev = vb_ + 2 * 32;
         }
         if (own_active(2 * mm + 1)) {  // keys 0..31 of the tile
             pstep_prefetch<D, DV, 0, 0, true, !QKZ, 0, NPRE>(vprev, kb_, pf);
             pstep<D, DV, 0, 0, true, !QKZ, NPRE>(vprev, kb_, pf, wk.r, wk.i, qf, ore, oim, x);
-            vstep_own(bufm, 0, 32 * w + qi - tl * BK);
+            vstep_own(bufm, 0, __builtin_amdgcn_readfirstlane(32 * w - tl * BK) < 32);
             vprev = vb_;
         }
         land_wait(m);
