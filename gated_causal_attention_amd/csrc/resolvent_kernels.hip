@@ -2097,9 +2097,11 @@ __global__ __launch_bounds__(NTHREADS, 1) void fwd_pad_kernel(FwdArgs A) {
         if constexpr (QKZ) {
             return 0.0f;
         } else {
-            float ts = x[0];
-#pragma unroll
-            for (int r = 1; r < 16; ++r) ts = fmaxf(ts, x[r]);
+            // a tree of depth 3 (the maximum is the same in any order)
+            const float m0 = fmaxf(fmaxf(x[0], x[1]), x[2]), m1 = fmaxf(fmaxf(x[3], x[4]), x[5]);
+            const float m2 = fmaxf(fmaxf(x[6], x[7]), x[8]), m3 = fmaxf(fmaxf(x[9], x[10]), x[11]);
+            const float m4 = fmaxf(fmaxf(x[12], x[13]), x[14]);
+            float ts = fmaxf(fmaxf(fmaxf(m0, m1), m2), fmaxf(fmaxf(m3, m4), x[15]));
             const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(ts),
                                                              __float_as_uint(ts), false, false);
             ts = fmaxf(ts, fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1])));
@@ -2130,22 +2132,33 @@ __global__ __launch_bounds__(NTHREADS, 1) void fwd_pad_kernel(FwdArgs A) {
     auto weights = [&](int kc, float msub, const float (&fre)[8], const float (&fim)[8],
                        const float (&fm)[8], bool all_live, bool rlive,
                        bool own) __attribute__((always_inline)) {
-        float wre[8], wim[8];
+        float wre[8], wim[8], ex[8];
+        if constexpr (QKZ) {
+#pragma unroll
+            for (int e = 0; e < 8; ++e) ex[e] = (all_live || (fm[e] > 0.0f && rlive)) ? 1.0f : 0.0f;
+        } else {
+            // the exponents first, then the exponentials, then their uses
+            float t[8];
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                if (own) {
+#pragma clang fp contract(off)
+                    const float lg = x[8 * kc + e] * c;
+                    t[e] = lg - msub;
+                } else {
+                    t[e] = fmaf(x[8 * kc + e], c, -msub);
+                }
+            }
+            __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int e = 0; e < 8; ++e) ex[e] = __builtin_amdgcn_exp2f(t[e]);
+            __builtin_amdgcn_sched_barrier(0);
+        }
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
-            float ex;
-            if constexpr (QKZ) {
-                ex = (all_live || (fm[e] > 0.0f && rlive)) ? 1.0f : 0.0f;
-            } else if (own) {
-#pragma clang fp contract(off)
-                const float lg = x[8 * kc + e] * c;
-                ex = __builtin_amdgcn_exp2f(lg - msub);
-            } else {
-                ex = __builtin_amdgcn_exp2f(fmaf(x[8 * kc + e], c, -msub));
-            }
-            z += ex * fm[e];
-            wre[e] = ex * fre[e];
-            wim[e] = ex * fim[e];
+            z += ex[e] * fm[e];
+            wre[e] = ex[e] * fre[e];
+            wim[e] = ex[e] * fim[e];
         }
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
@@ -2188,14 +2201,20 @@ __global__ __launch_bounds__(NTHREADS, 1) void fwd_pad_kernel(FwdArgs A) {
         unpack(b0, b1, fim);
         unpack(c0, c1, fm);
         float ex[8];
+        if constexpr (QKZ) {
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-            if constexpr (QKZ)
-                ex[e] = (!masked || (fm[e] > 0.0f && row_live)) ? 1.0f : 0.0f;
-            else
-                ex[e] = __builtin_amdgcn_exp2f(fmaf(x[e], c, -msub));
-            z += ex[e] * fm[e];
+            for (int e = 0; e < 8; ++e) ex[e] = (!masked || (fm[e] > 0.0f && row_live)) ? 1.0f : 0.0f;
+        } else {
+            float t[8];
+#pragma unroll
+            for (int e = 0; e < 8; ++e) t[e] = fmaf(x[e], c, -msub);
+            __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int e = 0; e < 8; ++e) ex[e] = __builtin_amdgcn_exp2f(t[e]);
+            __builtin_amdgcn_sched_barrier(0);
         }
+#pragma unroll
+        for (int e = 0; e < 8; ++e) z += ex[e] * fm[e];
         __builtin_amdgcn_sched_barrier(0);
         RD128(a0, 64); RD128(a1, 80); RD128(b0, 4 * BK + 64); RD128(b1, 4 * BK + 80);
         __builtin_amdgcn_sched_barrier(0);
