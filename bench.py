@@ -2,7 +2,7 @@
 
 One step is one resolvent_forward call over the headline workload (B=4, H=16,
 n=8192, d=128, bf16 q,k,v, switches (1,1,1)): the prologue (status clear, gates
-and their in-tile products, bf16 v^T), the visit-count scan, the fused forward
+and their in-tile products), the visit-count scan, the fused forward
 kernel and the logit-overflow check, with the inputs already resident in HBM.
 Prints one JSON line: the throughput, the per-stage times from HIP events, the
 roofline object of the fused kernel and the oracle's CPU rate.

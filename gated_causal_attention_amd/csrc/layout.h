@@ -37,14 +37,15 @@ struct Layout {
     size_t noff = 0;  // per query tile: key tiles before it that the forward visits (int32 [BH][n_qt])
     size_t gbad = 0;  // per query tile: 1 if its gates saw a refused input (int32 [BH][n_qt])
     size_t counters = 0;  // uint32 [2]: key tiles processed before the query tiles; spare
-    size_t vt = 0;        // bf16 [BHkv][dv][n_pad], keys permuted inside groups of 16
+    size_t v16 = 0;       // bf16 path, fp32 values only: v rounded to bf16 (bf16 [BHkv][n][dv])
     size_t total = 0;
 };
 
 // Hkv k/v heads (each shared by H/Hkv query heads) and dv value channels;
-// 0 means Hkv = H and dv = d.
+// 0 means Hkv = H and dv = d.  v_f32: the values come as fp32 (on the bf16
+// path they are rounded to bf16 once, into the v16 region).
 inline Layout make_layout(int64_t B, int64_t H, int64_t n, int64_t d, bool bf16_path,
-                          int64_t Hkv = 0, int64_t dv = 0) {
+                          int64_t Hkv = 0, int64_t dv = 0, bool v_f32 = false) {
     Layout L;
     L.BH = B * H;
     L.n = n;
@@ -81,8 +82,8 @@ inline Layout make_layout(int64_t B, int64_t H, int64_t n, int64_t d, bool bf16_
     off = align_up(off + per_qt, 256);
     L.counters = off;
     off = align_up(off + 2 * sizeof(uint32_t), 256);
-    L.vt = off;
-    if (bf16_path) off = align_up(off + 2 * size_t(L.BHkv) * size_t(L.dv) * size_t(L.n_pad), 256);
+    L.v16 = off;
+    if (bf16_path && v_f32) off = align_up(off + 2 * size_t(L.BHkv) * size_t(L.n) * size_t(L.dv), 256);
     L.total = off;
     return L;
 }
@@ -270,23 +271,26 @@ RESOLVENT_HD constexpr int vfrag_base(int qi, int h) {
 }
 
 // Padded bf16 tiles of the fused forward (bf16 path).  A K row of d bf16
-// values takes KSL = d/8 + 1 sixteen-byte slots in LDS and a v^T row of the BK
-// keys of a tile VSL = 2 BK/16 + 1 = 9 slots; the last slot of each row is
-// padding.  With a row stride of an odd number of slots, the 16 rows that a
-// half-wave reads at one chunk fall into 16 different bank groups, and every
-// matrix-operand read is a per-lane base plus an immediate offset.  The K
-// tile occupies slots [0, 64 KSL) of a buffer and v^T the next 9 dv slots; copy
-// instruction j of a tile (a direct global->LDS copy of 16 bytes per lane)
-// fills slots [64 j, 64 j + 64): lane L slot 64 j + L.  The padding slot of a
-// row is filled with a copy of the row's last chunk.
+// values takes KSL = d/8 + 1 sixteen-byte slots in LDS; with a row stride of
+// an odd number of slots, the 16 rows that a half-wave reads at one chunk fall
+// into 16 different bank groups.  The values of a tile are staged as they lie
+// in v, a row of dv bf16 values per key, each row taking VSL = dv/8 + 2 slots
+// (the last two are padding): the matrix product reads them with the
+// transposing 8-byte LDS read, which hands each lane four consecutive keys of
+// one channel.  Every operand read is a per-lane base plus an immediate
+// offset.  The K tile occupies slots [0, 64 KSL) of a buffer and the value
+// tile the next 64 VSL; copy instruction j of a tile (a direct global->LDS
+// copy of 16 bytes per lane) fills slots [64 j, 64 j + 64): lane L slot
+// 64 j + L.  A padding slot holds a copy of its row's last chunk.
 template <int D>
 RESOLVENT_HD constexpr int pad_kslots() { return D / 8 + 1; }
-constexpr int PAD_VSLOTS = BK * 2 / 16 + 1;
+template <int DV>
+RESOLVENT_HD constexpr int pad_vslots() { return DV / 8 + 2; }
 template <int D>
 RESOLVENT_HD constexpr int pad_kcopies() { return pad_kslots<D>(); }  // BK rows x KSL slots / 64
 template <int DV>
-RESOLVENT_HD constexpr int pad_vcopies() { return DV * PAD_VSLOTS / 64; }
-// The NC = KSL + 9 dv / 64 copy instructions of a tile are shared by waves
+RESOLVENT_HD constexpr int pad_vcopies() { return pad_vslots<DV>(); }  // BK rows x VSL slots / 64
+// The NC = KSL + VSL copy instructions of a tile are shared by waves
 // 1..NWAVES-1 (wave 0 copies the gate data): copying wave w issues, as its
 // i-th of pad_copies_per_wave, instruction j = w - 1 + (NWAVES - 1) i, the
 // last one repeated past NC (the same bytes to the same slots).
@@ -301,21 +305,21 @@ RESOLVENT_HD inline int pad_copy_j(int w, int i) {
     const int j = w - 1 + (NWAVES - 1) * i;
     return j < pad_copies<D, DV>() ? j : pad_copies<D, DV>() - 1;
 }
-// Source byte offset of copy instruction j, lane `lane`: for j < KSL inside
-// the K rows of the tile, relative to the tile's first key row (rows of 2d
-// bytes); otherwise inside v^T [dv][n_pad] bf16, relative to the tile's first
-// column of row 0.  (The whole tile inside the sequence; see pad_kcopy_src_ragged.)
-template <int D>
-RESOLVENT_HD inline uint32_t pad_copy_src(int j, int lane, int64_t n_pad) {
-    constexpr int KSL = pad_kslots<D>();
+// Source byte offset of copy instruction j, lane `lane`, relative to the
+// tile's first key row: for j < KSL inside the K rows of the tile (rows of 2d
+// bytes), otherwise inside its value rows (2 dv bytes).  (The whole tile
+// inside the sequence; see the ragged forms below.)
+template <int D, int DV>
+RESOLVENT_HD inline uint32_t pad_copy_src(int j, int lane) {
+    constexpr int KSL = pad_kslots<D>(), VSL = pad_vslots<DV>();
     if (j < KSL) {
         const int p = 64 * j + lane, r = p / KSL;
         const int c = p % KSL < KSL - 1 ? p % KSL : KSL - 2;
         return uint32_t(r * D * 2 + 16 * c);
     }
-    const int p = 64 * (j - KSL) + lane, r = p / PAD_VSLOTS;
-    const int c = p % PAD_VSLOTS < PAD_VSLOTS - 1 ? p % PAD_VSLOTS : PAD_VSLOTS - 2;
-    return uint32_t(int64_t(r) * n_pad * 2 + 16 * c);
+    const int p = 64 * (j - KSL) + lane, r = p / VSL;
+    const int c = p % VSL < DV / 8 ? p % VSL : DV / 8 - 1;
+    return uint32_t(r * DV * 2 + 16 * c);
 }
 // The K copy source of tile t when the tile reaches past key n - 1 (or lies
 // wholly past it, as own tiles of the last query tile can): rows past it
@@ -329,17 +333,35 @@ RESOLVENT_HD inline uint32_t pad_kcopy_src_ragged(int j, int lane, int64_t n, in
     const int64_t key = t * BK + r < n ? t * BK + r : n - 1;
     return uint32_t(key * D * 2 + 16 * c);
 }
-// Byte offsets, inside a buffer, of the operand reads of lane (qi, h) of a
-// 32x32x16 bf16 product: K row kb + qi, chunk 2s + h (step s); v^T row
-// 32 db + qi, chunk kb/8 + 2 kc + h.  Each is a lane part plus a constant.
+// The same for the value copies (copy jv = j - KSL of the value tile):
+// relative to the head's first value row.
+template <int DV>
+RESOLVENT_HD inline uint32_t pad_vcopy_src_ragged(int jv, int lane, int64_t n, int64_t t) {
+    constexpr int VSL = pad_vslots<DV>();
+    const int p = 64 * jv + lane, r = p / VSL;
+    const int c = p % VSL < DV / 8 ? p % VSL : DV / 8 - 1;
+    const int64_t key = t * BK + r < n ? t * BK + r : n - 1;
+    return uint32_t(key * DV * 2 + 16 * c);
+}
+// Byte offsets, inside a buffer, of the operand reads of a 32x32x16 bf16
+// product.  K: lane (qi, h) reads row kb + qi, chunk 2s + h (step s).
+// Values: the A operand of O^T += V^T W~^T for channels 32 db .. 32 db + 31 and
+// the 16 keys kb + 16 kc .. of chunk kc is two transposing 8-byte reads
+// (s = 0, 1).  In the read, each group of 16 lanes addresses a 4 x 4 grid of
+// 8-byte pieces (four keys by four groups of four channels) and lane i
+// receives channel (i & 3) of the pieces of lanes (i >> 2) + 4 e, e = 0..3;
+// the addresses below hand lane l four keys kb + 16 kc + 8 s + 4 (l >> 5) + e
+// of channel 32 db + (l & 31), the keys of the W~ operand's k order (the
+// lane's eight logits are the keys 8 (e >> 2) + 4 h + (e & 3) of the chunk).
 template <int D>
 RESOLVENT_HD constexpr int pad_kread(int kb, int s, int qi, int h) {
     return (kb + qi) * 16 * pad_kslots<D>() + 16 * (2 * s + h);
 }
-template <int D>
-RESOLVENT_HD constexpr int pad_vread(int kb, int kc, int db, int qi, int h) {
-    return 16 * BK * pad_kslots<D>() + (32 * db + qi) * 16 * PAD_VSLOTS +
-           16 * (kb / 8 + 2 * kc + h);
+template <int D, int DV>
+RESOLVENT_HD constexpr int pad_vread_tr(int kb, int kc, int db, int s, int lane) {
+    return 16 * BK * pad_kslots<D>() +
+           (kb + 16 * kc + 8 * s + 4 * (lane >> 5) + ((lane & 15) >> 2)) * 16 * pad_vslots<DV>() +
+           2 * (32 * db + 16 * ((lane >> 4) & 1) + 4 * (lane & 3));
 }
 
 // Float index, inside a gate plane [BH][n_pad], of the datum lane `lane`

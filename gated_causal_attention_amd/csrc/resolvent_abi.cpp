@@ -50,7 +50,8 @@ size_t workspace_grouped(int64_t B, int64_t H, int64_t Hkv, int64_t n, int64_t d
     if (B <= 0 || H <= 0 || Hkv <= 0 || n <= 0 || d <= 0 || dv <= 0 || H % Hkv != 0) return 0;
     if (!supported(d, qk_dtype, v_dtype) || !supported_dv(dv) || !within_limits(B, H, n))
         return 0;
-    return make_layout(B, H, n, d, qk_dtype == RESOLVENT_BF16, Hkv, dv).total;
+    return make_layout(B, H, n, d, qk_dtype == RESOLVENT_BF16, Hkv, dv, v_dtype == RESOLVENT_F32)
+        .total;
 }
 
 int32_t forward_impl(const void *q, const void *k, const float *u, const float *theta,
@@ -72,7 +73,8 @@ int32_t forward_impl(const void *q, const void *k, const float *u, const float *
         !aligned(o_im, 16) || !aligned(u, 4) || !aligned(theta, 4) || !aligned(status_dev, 4) ||
         !aligned(workspace, 256))
         return RESOLVENT_BAD_ARG;
-    const Layout L = make_layout(B, H, n, d, qk_dtype == RESOLVENT_BF16, Hkv, dv);
+    const Layout L =
+        make_layout(B, H, n, d, qk_dtype == RESOLVENT_BF16, Hkv, dv, v_dtype == RESOLVENT_F32);
     if (workspace_bytes < L.total) return RESOLVENT_BAD_ARG;
 
     // logit scale in log2 units; the device computes logits in float32
@@ -108,13 +110,14 @@ size_t resolvent_workspace_bytes(int64_t B, int64_t H, int64_t n, int64_t d, int
                                  int32_t v_dtype) {
     if (B <= 0 || H <= 0 || n <= 0 || d <= 0) return 0;
     if (!supported(d, qk_dtype, v_dtype) || !within_limits(B, H, n)) return 0;
-    return make_layout(B, H, n, d, qk_dtype == RESOLVENT_BF16).total;
+    return make_layout(B, H, n, d, qk_dtype == RESOLVENT_BF16, 0, 0, v_dtype == RESOLVENT_F32).total;
 }
 
 size_t resolvent_counters_offset(int64_t B, int64_t H, int64_t n, int64_t d, int32_t qk_dtype,
                                  int32_t v_dtype) {
     if (resolvent_workspace_bytes(B, H, n, d, qk_dtype, v_dtype) == 0) return SIZE_MAX;
-    return make_layout(B, H, n, d, qk_dtype == RESOLVENT_BF16).counters;
+    return make_layout(B, H, n, d, qk_dtype == RESOLVENT_BF16, 0, 0, v_dtype == RESOLVENT_F32)
+        .counters;
 }
 
 void resolvent_tile_shape(int32_t *bq, int32_t *bk) {

@@ -21,11 +21,12 @@
 //
 // Kernels, in launch order on the caller's stream:
 //   prep_kernel                      status := OK; blend + gate in f64 and the
-//                                    in-tile scans; (bf16 path) v -> bf16 v^T
-//   schedule_kernel                  key tiles each query tile visits, and
-//                                    the carried product C_t of each visit
-//   fwd_kernel                       the fused forward (MFMA)
-//   logit_check_kernel               exact logit-overflow refusal, only for
+//                                    in-tile scans; fp32 values on the bf16
+//                                    path rounded to bf16
+//   schedule_kernel                  key tiles each query tile visits
+//   fwd_pad_kernel / fwd_kernel      the fused forward (bf16 / fp32 MFMA); the
+//                                    carried products C_t are formed in it
+//   logit_check_(pad_)kernel         exact logit-overflow refusal, only for
 //                                    heads whose |q|,|k| extrema allow one
 #include <hip/hip_runtime.h>
 
@@ -85,64 +86,22 @@ __global__ void clear_status_kernel(int32_t *status, uint32_t *counters) {
     if (threadIdx.x < 2) counters[threadIdx.x] = 0;
 }
 
-// --------------------------------------------------------------------------
-// v [BH][n][D] (bf16 or fp32) -> v^T [BH][D][n_pad] bf16, keys stored in
-// perm16 order inside each group of 16 and zero past n.  A thread moves an
-// 8 x 8 block through its registers: the 8 keys of slots 8so..8so+7 (slot p
-// holds key perm64(p)) at the 8 channels of chunk c, read as 8 16-byte key
-// rows and written as 8 16-byte channel rows.  A wave reads 8 whole 128-byte
-// row halves and writes 8 whole 128-byte row segments per instruction; no LDS.
-// D threads per key tile, 256 / D tiles per 256-thread block (index blk).
-template <int D, bool VF32>
-__device__ __forceinline__ void vt_tiles(const void *__restrict__ v, uint16_t *__restrict__ vt,
-                                         int64_t n, int64_t n_pad, int n_kt, int64_t blk) {
-    const int tid = threadIdx.x;
-    const int64_t tl = blk * (256 / D) + tid / D;  // key tile over all k/v heads
-    const int r = tid % D;
-    const int so = r & 7, c = r >> 3;
-    const int64_t bh = tl / n_kt, kt = tl % n_kt;
-    uint32_t in[8][4];
+// fp32 values on the bf16 path: v rounded to bf16 once, row-major as v
+// ([k/v head][key][channel]), eight values a thread (index i of count8).
+__device__ __forceinline__ void v16_convert(const float *__restrict__ v, uint16_t *__restrict__ v16,
+                                            int64_t count8, int64_t i) {
+    if (i >= count8) return;
+    const float4 f0 = *reinterpret_cast<const float4 *>(v + 8 * i);
+    const float4 f1 = *reinterpret_cast<const float4 *>(v + 8 * i + 4);
+    const float fs[8] = {f0.x, f0.y, f0.z, f0.w, f1.x, f1.y, f1.z, f1.w};
+    uint32_t o[4];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-        const int64_t p = kt * BK + perm64(8 * so + i);
-        if (p < n) {
-            if constexpr (VF32) {
-                const float *src = static_cast<const float *>(v) + (bh * n + p) * D + 8 * c;
-                const float4 f0 = *reinterpret_cast<const float4 *>(src);
-                const float4 f1 = *reinterpret_cast<const float4 *>(src + 4);
-                const float fs[8] = {f0.x, f0.y, f0.z, f0.w, f1.x, f1.y, f1.z, f1.w};
-#pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    const uint32_t lo = __builtin_bit_cast(uint16_t, (__bf16)fs[2 * e]);
-                    const uint32_t hi = __builtin_bit_cast(uint16_t, (__bf16)fs[2 * e + 1]);
-                    in[i][e] = lo | (hi << 16);
-                }
-            } else {
-                const uint4 raw = *reinterpret_cast<const uint4 *>(
-                    static_cast<const uint16_t *>(v) + (bh * n + p) * D + 8 * c);
-                in[i][0] = raw.x;
-                in[i][1] = raw.y;
-                in[i][2] = raw.z;
-                in[i][3] = raw.w;
-            }
-        } else {
-#pragma unroll
-            for (int e = 0; e < 4; ++e) in[i][e] = 0u;
-        }
+    for (int e = 0; e < 4; ++e) {
+        const uint32_t lo = __builtin_bit_cast(uint16_t, (__bf16)fs[2 * e]);
+        const uint32_t hi = __builtin_bit_cast(uint16_t, (__bf16)fs[2 * e + 1]);
+        o[e] = lo | (hi << 16);
     }
-    uint16_t *dst = vt + (bh * D + 8 * c) * n_pad + kt * BK + 8 * so;
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-        // channel 8c+e of slots 8so..8so+7: the 16-bit half e%2 of word e/2
-        // of each key, two keys per word
-        const uint32_t sel = (e & 1) ? 0x07060302u : 0x05040100u;
-        uint4 o;
-        o.x = __builtin_amdgcn_perm(in[1][e / 2], in[0][e / 2], sel);
-        o.y = __builtin_amdgcn_perm(in[3][e / 2], in[2][e / 2], sel);
-        o.z = __builtin_amdgcn_perm(in[5][e / 2], in[4][e / 2], sel);
-        o.w = __builtin_amdgcn_perm(in[7][e / 2], in[6][e / 2], sel);
-        *reinterpret_cast<uint4 *>(dst + int64_t(e) * n_pad) = o;
-    }
+    *reinterpret_cast<uint4 *>(v16 + 8 * i) = make_uint4(o[0], o[1], o[2], o[3]);
 }
 
 // --------------------------------------------------------------------------
@@ -303,13 +262,12 @@ __global__ __launch_bounds__(64) void gates_kernel(GatesArgs A) {
 // The forward pass's first launch: clears the status word and the counters
 // (block 0), runs the gates of four query tiles per block in blocks
 // [0, ngb) -- a refusal is noted in gbad[query tile], always written, which
-// schedule_kernel folds into the status word -- and (bf16 path) the v^T tiles
-// in the blocks after them, so that the latency-bound gate scans overlap the
-// bandwidth-bound transpose.
-template <int D, bool VF32, bool VT>
+// schedule_kernel folds into the status word -- and (bf16 path, fp32 values)
+// rounds v to bf16 in the blocks after them, 2048 values a block.
+template <bool VCONV>
 __global__ __launch_bounds__(256) void prep_kernel(GatesArgs G, int ngb, int32_t *__restrict__ gbad,
-                                                   const void *__restrict__ v,
-                                                   uint16_t *__restrict__ vt, int n_kt,
+                                                   const float *__restrict__ v,
+                                                   uint16_t *__restrict__ v16, int64_t count8,
                                                    uint32_t *__restrict__ counters) {
     const int tid = threadIdx.x;
     if (blockIdx.x == 0 && tid == 0) G.status[0] = 0;
@@ -321,8 +279,8 @@ __global__ __launch_bounds__(256) void prep_kernel(GatesArgs G, int ngb, int32_t
             const bool any_bad = __any(bad);
             if ((tid & 63) == 0) gbad[tq] = any_bad ? 1 : 0;
         }
-    } else if constexpr (VT) {
-        vt_tiles<D, VF32>(v, vt, G.n, G.n_pad, n_kt, int64_t(blockIdx.x) - ngb);
+    } else if constexpr (VCONV) {
+        v16_convert(v, v16, count8, 256 * (int64_t(blockIdx.x) - ngb) + tid);
     }
 }
 
@@ -330,7 +288,7 @@ __global__ __launch_bounds__(256) void prep_kernel(GatesArgs G, int ngb, int32_t
 // Fused forward.
 struct FwdArgs {
     const void *q, *k, *v;
-    const uint16_t *vt;
+    const uint16_t *v16;  // bf16 path: the values in bf16, row-major as v
     const float *a_re, *a_im, *a_m, *s_re, *s_im, *s_m, *p_re, *p_im, *p_m;
     const double *t_re, *t_im, *t_m;
     const double *t4;     // (A_re, A_im, A_m, 0) per key tile [BH][n_kt]
@@ -601,14 +559,14 @@ __device__ __forceinline__ void stage_async(const FwdArgs &A, uint32_t buf,
 }
 
 // Bases of the tile copies for k/v head kvh (wave-uniform): its rows of k,
-// and of v^T (bf16 path) or v (fp32 path).
+// and of the bf16 values (bf16 path) or v (fp32 path).
 template <bool F32, int D, int DV>
 __device__ __forceinline__ void head_bases(const FwdArgs &A, int64_t kvh,
                                            const unsigned char *&kh, const unsigned char *&vh) {
     constexpr int64_t ROWB = D * Smem<F32, D>::ESZ;
     kh = uniform_ptr(static_cast<const unsigned char *>(A.k) + kvh * A.n * ROWB);
     if constexpr (!F32)
-        vh = uniform_ptr(reinterpret_cast<const unsigned char *>(A.vt) + kvh * DV * A.n_pad * 2);
+        vh = uniform_ptr(reinterpret_cast<const unsigned char *>(A.v16) + kvh * A.n * (DV * 2));
     else
         vh = uniform_ptr(static_cast<const unsigned char *>(A.v) + kvh * A.n * (DV * 4));
 }
@@ -1641,9 +1599,9 @@ template <int D, int DV>
 struct PSmem {
     static constexpr int KSL = pad_kslots<D>();
     static constexpr int KROW = 16 * KSL;          // bytes per K row
-    static constexpr int VROW = 16 * PAD_VSLOTS;   // bytes per v^T row
+    static constexpr int VSTR = 16 * pad_vslots<DV>();  // bytes per value row
     static constexpr int NKC = pad_kcopies<D>();   // copy instructions of a K tile
-    static constexpr int NVC = pad_vcopies<DV>();  // of a v^T tile
+    static constexpr int NVC = pad_vcopies<DV>();  // of a value tile
     static constexpr int NC = NKC + NVC;
     static constexpr int CPW = pad_copies_per_wave<D, DV>();  // per copying wave and tile
     static constexpr size_t k_bytes = size_t(1024) * NKC;
@@ -1665,7 +1623,7 @@ struct PSmem {
     static constexpr int NKHI = (NKC + NWAVES - 2) / (NWAVES - 1);
     static constexpr int WSPLIT = NKC - (NWAVES - 1) * (NKHI - 1);
     static_assert(bytes <= 160 * 1024, "LDS");
-    static_assert(size_t(BK) * KROW == k_bytes && size_t(DV) * VROW == v_bytes, "whole copies");
+    static_assert(size_t(BK) * KROW == k_bytes && size_t(BK) * VSTR == v_bytes, "whole copies");
     static_assert(CPW <= 5, "copy batch");
 };
 
@@ -1769,7 +1727,22 @@ struct G2LBatch<5> {
 };
 #undef RESOLVENT_G2L
 
-// Matrix step on padded tiles: O^T += V^T W~^T for the block whose v^T rows
+// The A operand of O^T += V^T W~^T for one (16-key chunk, 32-channel group)
+// from the value rows: two transposing 8-byte reads at the lane's address p
+// and eight rows further on (keys +8).
+template <int DV>
+__device__ __forceinline__ bf16x8 vread_tr(const unsigned char *p) {
+    typedef short v4s __attribute__((ext_vector_type(4)));
+    typedef __attribute__((address_space(3))) v4s lds_v4s;
+    const v4s a = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s *)(lds_void *)(p));
+    const v4s b = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (lds_v4s *)(lds_void *)(p + 8 * 16 * pad_vslots<DV>()));
+    typedef short v8s __attribute__((ext_vector_type(8)));
+    const v8s ab = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+    return __builtin_bit_cast(bf16x8, ab);
+}
+
+// Matrix step on padded tiles: O^T += V^T W~^T for the block whose value rows
 // start at vb (lane part included) at key offset KBV (PV), and S^T = K Q^T for
 // the block at K offset KBS of the K tile at kb (lane part included) (S).
 // Operand fragments stream four deep through pf; NPRE of each kind were
@@ -1783,8 +1756,7 @@ __device__ __forceinline__ void pstep_prefetch(const unsigned char *vb, const un
     for (int i = I0; i < I1; ++i) {
         if (i < NV) {
             const int kc = i / (DV / 32), db = i % (DV / 32);
-            pf.vf[i] = *reinterpret_cast<const bf16x8 *>(vb + 2 * KBV + 32 * kc +
-                                                        db * 32 * (16 * PAD_VSLOTS));
+            pf.vf[i] = vread_tr<DV>(vb + (KBV + 16 * kc) * (16 * pad_vslots<DV>()) + 64 * db);
         }
         if (i < NK)
             pf.kf[i] = *reinterpret_cast<const bf16x8 *>(kb + KBS * 16 * pad_kslots<D>() + 32 * i);
@@ -1810,8 +1782,8 @@ __device__ __forceinline__ void pstep(const unsigned char *vb, const unsigned ch
             oim[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, wi[kc], oim[db], 0, 0, 0);
             if (i + MDEPTH < NV) {
                 const int kc2 = (i + MDEPTH) / NDB, db2 = (i + MDEPTH) % NDB;
-                pf.vf[i % MDEPTH] = *reinterpret_cast<const bf16x8 *>(
-                    vb + 2 * KBV + 32 * kc2 + db2 * 32 * (16 * PAD_VSLOTS));
+                pf.vf[i % MDEPTH] =
+                    vread_tr<DV>(vb + (KBV + 16 * kc2) * (16 * pad_vslots<DV>()) + 64 * db2);
             }
         }
         if (i < NK) {
@@ -1832,7 +1804,7 @@ __global__ __launch_bounds__(NTHREADS, 1) void fwd_pad_kernel(FwdArgs A) {
     constexpr int NDIAG = BQ / BK;  // key tiles inside the query tile
     constexpr int NDB = 2 * NDIAG;  // 32-key blocks inside the query tile
     constexpr int CPW = SM::CPW;
-    constexpr int KROW = SM::KROW, VROW = SM::VROW;
+    constexpr int KROW = SM::KROW, VSTR = SM::VSTR;
     extern __shared__ __align__(16) unsigned char smem[];
     uint32_t *misc = reinterpret_cast<uint32_t *>(smem + SM::misc_off);
     // misc[2]: largest |q|; misc[3]: largest |k|
@@ -1884,7 +1856,7 @@ __global__ __launch_bounds__(NTHREADS, 1) void fwd_pad_kernel(FwdArgs A) {
 #pragma unroll
         for (int i = 0; i < CPW; ++i)
             coffs[((w - 1) * CPW + i) * 64 + lane] =
-                pad_copy_src<D>(pad_copy_j<D, DV>(w, i), lane, A.n_pad);
+                pad_copy_src<D, DV>(pad_copy_j<D, DV>(w, i), lane);
     }
     const double *t4 = uniform_ptr(A.t4 + 4 * bh * A.n_kt);
     const float *gS = uniform_ptr(A.gates + 3 * A.plane + bh * A.n_pad);
@@ -1899,7 +1871,8 @@ __global__ __launch_bounds__(NTHREADS, 1) void fwd_pad_kernel(FwdArgs A) {
             const bool ragged = (t + 1) * BK > n32;
             const unsigned char *kt =
                 uniform_ptr(ragged ? kh : kh + int64_t(t) * (BK * D * 2));
-            const unsigned char *vt = uniform_ptr(vh + int64_t(t) * (BK * 2));
+            const unsigned char *vt =
+                uniform_ptr(ragged ? vh : vh + int64_t(t) * (BK * DV * 2));
             const uint32_t *co = coffs + (w - 1) * CPW * 64 + fresh_lane();
             uint32_t o[CPW];
 #pragma unroll
@@ -1908,7 +1881,9 @@ __global__ __launch_bounds__(NTHREADS, 1) void fwd_pad_kernel(FwdArgs A) {
 #pragma unroll
                 for (int i = 0; i < CPW; ++i) {
                     const int j = pad_copy_j<D, DV>(w, i);
-                    if (j < SM::NKC) o[i] = pad_kcopy_src_ragged<D>(j, fresh_lane(), A.n, t);
+                    o[i] = j < SM::NKC
+                               ? pad_kcopy_src_ragged<D>(j, fresh_lane(), A.n, t)
+                               : pad_vcopy_src_ragged<DV>(j - SM::NKC, fresh_lane(), A.n, t);
                 }
             }
             if constexpr (SM::EXACT && CPW == 5) {
@@ -2090,7 +2065,7 @@ __global__ __launch_bounds__(NTHREADS, 1) void fwd_pad_kernel(FwdArgs A) {
 
     // per-lane parts of the operand and side-data reads
     const int klane = qi * KROW + 16 * h;
-    const int vlane = int(SM::k_bytes) + qi * VROW + 16 * h;
+    const int vlane = pad_vread_tr<D, DV>(0, 0, 0, 0, lane);
     const int slane = int(SM::side_off) + 32 * h;
 
     auto block_shift = [&]() __attribute__((always_inline)) -> float {
@@ -2411,7 +2386,7 @@ __global__ __launch_bounds__(NTHREADS, 1) void fwd_pad_kernel(FwdArgs A) {
         lds_barrier();
         vstep_off(bufm + slane, 32, wave_dead_rows || __builtin_amdgcn_readfirstlane(kflag1) != 0u);
         settle_weights();
-        vprev = vb_ + 2 * 32;
+        vprev = vb_ + 32 * VSTR;
         if (m + 1 < n_off)
             pstep_prefetch<D, DV, 0, 0, true, !QKZ, 0, NPRE>(vprev, tile_buf(m + 1) + klane, pf);
         else
@@ -2455,7 +2430,7 @@ __global__ __launch_bounds__(NTHREADS, 1) void fwd_pad_kernel(FwdArgs A) {
             pstep_prefetch<D, DV, 0, 32, true, !QKZ, 0, NPRE>(vprev, kb_, pf);
             pstep<D, DV, 0, 32, true, !QKZ, NPRE>(vprev, kb_, pf, wk.r, wk.i, qf, ore, oim, x);
             vstep_own(bufm, 32, __builtin_amdgcn_readfirstlane(32 * w - (tl * BK + 32)) < 32);
-            vprev = vb_ + 2 * 32;
+            vprev = vb_ + 32 * VSTR;
         }
         if (own_active(2 * mm + 1)) {  // keys 0..31 of the tile
             pstep_prefetch<D, DV, 0, 0, true, !QKZ, 0, NPRE>(vprev, kb_, pf);
@@ -2610,24 +2585,20 @@ int launch_typed(const Problem &P, hipStream_t st, hipEvent_t const *marks) {
     if (marks) (void)hipEventRecord(marks[0], st);
     const int BH = (int)L.BH;
 
-    // gates (four query tiles per block) and, on the bf16 path, v^T (256/dv
-    // key tiles per block; the key tiles of a head are a multiple of 4) in
-    // one launch
+    // gates (four query tiles per block) and, on the bf16 path with fp32
+    // values, their rounding to bf16 (2048 values per block) in one launch
     const GatesArgs G = gates_args(L, P.u, P.theta, P.g, ws, P.status);
     int32_t *gbad = reinterpret_cast<int32_t *>(ws + L.gbad);
     const int ngb = (int)((BH * L.n_qt + 3) / 4);
-    uint16_t *vt = reinterpret_cast<uint16_t *>(ws + L.vt);
-    if constexpr (!F32) {
-        const unsigned blocks = (unsigned)(ngb + L.BHkv * L.n_kt * DV / 256);
-        if (P.v_f32)
-            hipLaunchKernelGGL((prep_kernel<DV, true, true>), dim3(blocks), dim3(256), 0, st, G,
-                               ngb, gbad, P.v, vt, (int)L.n_kt, counters);
-        else
-            hipLaunchKernelGGL((prep_kernel<DV, false, true>), dim3(blocks), dim3(256), 0, st, G,
-                               ngb, gbad, P.v, vt, (int)L.n_kt, counters);
+    uint16_t *v16 = reinterpret_cast<uint16_t *>(ws + L.v16);
+    const int64_t count8 = L.BHkv * L.n * DV / 8;
+    if (!F32 && P.v_f32) {
+        const unsigned blocks = (unsigned)(ngb + (count8 + 255) / 256);
+        hipLaunchKernelGGL(prep_kernel<true>, dim3(blocks), dim3(256), 0, st, G, ngb, gbad,
+                           static_cast<const float *>(P.v), v16, count8, counters);
     } else {
-        hipLaunchKernelGGL((prep_kernel<DV, true, false>), dim3(ngb), dim3(256), 0, st, G, ngb,
-                           gbad, P.v, vt, (int)L.n_kt, counters);
+        hipLaunchKernelGGL(prep_kernel<false>, dim3(ngb), dim3(256), 0, st, G, ngb, gbad,
+                           static_cast<const float *>(P.v), v16, count8, counters);
     }
     int32_t *noff = reinterpret_cast<int32_t *>(ws + L.noff);
     hipLaunchKernelGGL(schedule_kernel, dim3(BH * L.n_qt), dim3(64), 0, st, G.t_re, G.t_im,
@@ -2639,7 +2610,8 @@ int launch_typed(const Problem &P, hipStream_t st, hipEvent_t const *marks) {
     F.q = P.q;
     F.k = P.k;
     F.v = P.v;
-    F.vt = reinterpret_cast<const uint16_t *>(ws + L.vt);
+    F.v16 = P.v_f32 ? reinterpret_cast<const uint16_t *>(ws + L.v16)
+                    : static_cast<const uint16_t *>(P.v);
     F.a_re = G.a_re;
     F.a_im = G.a_im;
     F.a_m = G.a_m;

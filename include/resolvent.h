@@ -59,8 +59,8 @@ enum resolvent_dtype { RESOLVENT_BF16 = 0, RESOLVENT_F32 = 1 };
  * for this shape and these storage types (0 for an empty problem, and also 0
  * for an invalid or unsupported one, which resolvent_forward rejects).
  * The workspace holds the gates, their in-tile scans, the tile products, the
- * per-tile extrema of q and k and, on the bf16 path, a transposed bf16 copy of
- * v; it grows linearly with n.  Its contents are scratch between calls.
+ * per-tile extrema of q and k and, only when fp32 values meet bf16 q and k, a
+ * bf16 copy of v; it grows linearly with n.  Its contents are scratch between calls.
  */
 size_t resolvent_workspace_bytes(int64_t B, int64_t H, int64_t n, int64_t d,
                                  int32_t qk_dtype, int32_t v_dtype);

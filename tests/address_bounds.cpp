@@ -25,7 +25,6 @@ static int check(int64_t B, int64_t H, int64_t n, int64_t d, int esz, bool bf16_
     const int64_t row_bytes = d * esz;
     const int kch = int(row_bytes / 16);
     const int64_t tensor = L.BHkv * n * row_bytes;
-    const int64_t vt_bytes = L.BHkv * dv * L.n_pad * 2;
     const int64_t vrow_bytes = dv * esz;
     const int64_t vtensor = L.BHkv * n * vrow_bytes;
     int bad = 0;
@@ -63,97 +62,46 @@ static int check(int64_t B, int64_t H, int64_t n, int64_t d, int esz, bool bf16_
                             std::printf("v out of range: n=%lld dv=%lld t=%lld r=%d\n",
                                         (long long)n, (long long)dv, (long long)t, r);
                     }
-            if (bf16_path)
-                for (int dd = 0; dd < dv; ++dd)
-                    for (int c = 0; c < BK * 2 / 16; ++c) {
-                        const int64_t off = vt_src(bh, dv, L.n_pad, t, dd, c);
-                        const int64_t alt =
-                            bh * dv * L.n_pad * 2 + int64_t(vt_row_off(L.n_pad, t, dd)) + 16 * c;
-                        if (alt != off && bad++ < 5)
-                            std::printf("v^T 32-bit offset mismatch: n=%lld t=%lld d=%d\n",
-                                        (long long)n, (long long)t, dd);
-                        if (off < 0 || off + 16 > vt_bytes) {
-                            if (bad++ < 5)
-                                std::printf("v^T out of range: n=%lld t=%lld d=%d c=%d\n",
-                                            (long long)n, (long long)t, dd, c);
-                        }
-                    }
-            // the padded copies of fwd_pad_kernel, lane by lane: a tile reaching
-            // past key n-1 takes head-relative, clamped K offsets
+            // the padded copies of fwd_pad_kernel, lane by lane: K rows from k and
+            // value rows from the bf16 values (v itself, or v rounded to bf16 in
+            // the workspace when it comes as fp32: both [BHkv][n][dv]); a tile
+            // reaching past key n-1 takes head-relative, clamped offsets
             if (bf16_path) {
-                const int64_t head_k = bh * n * row_bytes, head_vt = bh * dv * L.n_pad * 2;
+                const int64_t head_k = bh * n * row_bytes, head_v = bh * n * dv * 2;
                 const int ksl = d == 128 ? pad_kslots<128>() : pad_kslots<64>();
-                const int nc = ksl + int(dv) * PAD_VSLOTS / 64;
-                for (int j = 0; j < nc; ++j)
+                const int vsl = dv == 128 ? pad_vslots<128>() : pad_vslots<64>();
+                const bool ragged = (t + 1) * BK > n;
+                auto src = [&](int j, int lane) -> int64_t {
+                    if (d == 128)
+                        return dv == 128 ? pad_copy_src<128, 128>(j, lane) : pad_copy_src<128, 64>(j, lane);
+                    return dv == 128 ? pad_copy_src<64, 128>(j, lane) : pad_copy_src<64, 64>(j, lane);
+                };
+                for (int j = 0; j < ksl + vsl; ++j)
                     for (int lane = 0; lane < 64; ++lane) {
                         int64_t lo, hi, off;
                         if (j < ksl) {
                             lo = head_k;
                             hi = head_k + n * row_bytes;
-                            if ((t + 1) * BK > n)
+                            if (ragged)
                                 off = head_k + (d == 128 ? pad_kcopy_src_ragged<128>(j, lane, n, t)
                                                          : pad_kcopy_src_ragged<64>(j, lane, n, t));
                             else
-                                off = head_k + t * BK * row_bytes +
-                                      (d == 128 ? pad_copy_src<128>(j, lane, L.n_pad)
-                                                : pad_copy_src<64>(j, lane, L.n_pad));
+                                off = head_k + t * BK * row_bytes + src(j, lane);
                         } else {
-                            lo = head_vt;
-                            hi = head_vt + dv * L.n_pad * 2;
-                            off = head_vt + t * BK * 2 +
-                                  (d == 128 ? pad_copy_src<128>(j, lane, L.n_pad)
-                                            : pad_copy_src<64>(j, lane, L.n_pad));
+                            lo = head_v;
+                            hi = head_v + n * dv * 2;
+                            if (ragged)
+                                off = head_v + (dv == 128 ? pad_vcopy_src_ragged<128>(j - ksl, lane, n, t)
+                                                          : pad_vcopy_src_ragged<64>(j - ksl, lane, n, t));
+                            else
+                                off = head_v + t * BK * dv * 2 + src(j, lane);
                         }
                         if ((off < lo || off + 16 > hi) && bad++ < 5)
                             std::printf("padded copy out of its head: n=%lld d=%lld dv=%lld t=%lld "
                                         "j=%d lane=%d\n", (long long)n, (long long)d, (long long)dv,
                                         (long long)t, j, lane);
-                    }
-            }
-            // the bf16 copy instructions, lane by lane (kernel helpers)
-            if (bf16_path) {
-                const int64_t head_k = bh * n * row_bytes, head_vt = bh * dv * L.n_pad * 2;
-                for (int j = 0; j < kch; ++j)
-                    for (int lane = 0; lane < 64; ++lane) {
-                        const int64_t ko = head_k + int64_t(d == 128 ? k_copy_off<16>(n, t, j, lane)
-                                                                     : k_copy_off<8>(n, t, j, lane));
-                        if ((ko < head_k || ko + 16 > head_k + n * row_bytes) && bad++ < 5)
-                            std::printf("k copy out of the head: n=%lld t=%lld j=%d lane=%d\n",
-                                        (long long)n, (long long)t, j, lane);
-                    }
-                // the kernels' split into per-lane and uniform parts (NC copy waves)
-                const bool inside = (t + 1) * BK <= n;
-                for (int NC = 4; NC <= 8; NC += 4) {
-                    for (int j = 0; j < kch; ++j)
-                        for (int lane = 0; lane < 64; ++lane) {
-                            const int j0 = j % NC, i = j / NC;
-                            const uint32_t full = d == 128 ? k_copy_off<16>(n, t, j, lane)
-                                                           : k_copy_off<8>(n, t, j, lane);
-                            const uint32_t split = uint32_t(t * BK * 2 * d) +
-                                                   uint32_t(1024 * NC * i) +
-                                                   (d == 128 ? k_lane_off<16>(j0, lane)
-                                                             : k_lane_off<8>(j0, lane));
-                            if (inside && full != split && bad++ < 5)
-                                std::printf("k copy split mismatch: n=%lld t=%lld j=%d lane=%d\n",
-                                            (long long)n, (long long)t, j, lane);
-                        }
-                    for (int j = 0; j < int(dv) / 8; ++j)
-                        for (int lane = 0; lane < 64; ++lane) {
-                            const int j0 = j % NC, i = j / NC;
-                            const uint32_t split = uint32_t(2 * BK * t) +
-                                                   uint32_t(16 * NC * L.n_pad * i) +
-                                                   vt_lane_off(L.n_pad, j0, lane);
-                            if (split != vt_copy_off(L.n_pad, t, j, lane) && bad++ < 5)
-                                std::printf("v^T copy split mismatch: n=%lld t=%lld j=%d lane=%d\n",
-                                            (long long)n, (long long)t, j, lane);
-                        }
-                }
-                for (int j = 0; j < int(dv) / 8; ++j)
-                    for (int lane = 0; lane < 64; ++lane) {
-                        const int64_t vo = head_vt + int64_t(vt_copy_off(L.n_pad, t, j, lane));
-                        if ((vo < head_vt || vo + 16 > head_vt + dv * L.n_pad * 2) && bad++ < 5)
-                            std::printf("v^T copy out of the head: n=%lld t=%lld j=%d lane=%d\n",
-                                        (long long)n, (long long)t, j, lane);
+                        if (bh * n * dv * 2 + n * dv * 2 > L.BHkv * n * dv * 2 && bad++ < 5)
+                            std::printf("value head past the tensor: bh=%lld\n", (long long)bh);
                     }
             }
         }
@@ -268,16 +216,23 @@ static int check_v_reads(int d) {
 
 // The padded bf16 tiles of fwd_pad_kernel (d = D, value width DV), independent
 // of the shape: every copy instruction j < NC is issued by some copying wave;
-// the 64 slots of instruction j (lane L -> slot 64 j + L) hold, for a K slot
-// (row r, chunk c < KSL - 1) exactly the chunk the operand read of (row r,
-// chunk c) addresses, every (row, chunk) of the K and v^T tiles is held by
-// exactly one non-padding slot, every operand read stays inside the K or
-// v^T tile, and each 16-lane group of an operand read touches 16 distinct
-// bank groups (16-byte units modulo 16).
+// the 64 slots of instruction j (lane L -> slot 64 j + L) hold, for a
+// non-padding slot, exactly the (row, chunk) the slot stands for, every
+// (row, chunk) of the K and value tiles is held by exactly one non-padding
+// slot, every K operand read stays inside the K tile and each of its 16-lane
+// groups touches 16 distinct bank groups (16-byte units modulo 16).  The value
+// reads are simulated with the transposing read's lane exchange (lane i of a
+// 16-lane group receives element i & 3 of the 8-byte pieces that lanes
+// (i >> 2) + 4 e address): lane l must receive the keys
+// kb + 16 kc + 8 s + 4 (l >> 5) + e of channel 32 db + (l & 31), from
+// non-padding slots inside the value tile, with at most two lanes of a half
+// wave on one bank.
 template <int D, int DV>
 static int check_pad_layout() {
-    constexpr int KSL = pad_kslots<D>(), NC = pad_copies<D, DV>(), CPW = pad_copies_per_wave<D, DV>();
+    constexpr int KSL = pad_kslots<D>(), VSL = pad_vslots<DV>(), NC = pad_copies<D, DV>();
+    constexpr int CPW = pad_copies_per_wave<D, DV>();
     constexpr int kbytes = 1024 * pad_kcopies<D>(), vbytes = 1024 * pad_vcopies<DV>();
+    constexpr int VSTR = 16 * VSL;
     int bad = 0;
     auto fail = [&](const char *what, int a, int b) {
         if (bad++ < 10) std::printf("pad layout d=%d dv=%d: %s (%d, %d)\n", D, DV, what, a, b);
@@ -292,13 +247,13 @@ static int check_pad_layout() {
     for (int j = 0; j < NC; ++j)
         if (!issued[j]) fail("copy never issued", j, 0);
     if (1024 * NC != kbytes + vbytes) fail("copies do not tile the buffer", NC, 0);
+    if (BK * VSTR != vbytes) fail("value rows do not fill the value tile", VSTR, vbytes);
     // which slot holds (row, chunk): from the copies (source side)
-    std::vector<int> kslot(BK * (D / 8), -1), vslot(DV * 8, -1);
-    const int64_t n_pad = 4096;  // any v^T row stride
+    std::vector<int> kslot(BK * (D / 8), -1), vslot(BK * (DV / 8), -1);
     for (int j = 0; j < NC; ++j)
         for (int lane = 0; lane < 64; ++lane) {
             const int p = 64 * j + lane;
-            const uint32_t src = pad_copy_src<D>(j, lane, n_pad);
+            const uint32_t src = pad_copy_src<D, DV>(j, lane);
             if (j < KSL) {
                 const int r = int(src / (D * 2)), c = int(src % (D * 2)) / 16;
                 if (r < 0 || r >= BK || c < 0 || c >= D / 8) { fail("K copy source", j, lane); continue; }
@@ -309,21 +264,21 @@ static int check_pad_layout() {
                 }
             } else {
                 const int q = p - 64 * KSL;
-                const int r = int(src / (n_pad * 2)), c = int(src % (n_pad * 2)) / 16;
-                if (r < 0 || r >= DV || c < 0 || c >= 8) { fail("v^T copy source", j, lane); continue; }
-                if (q % PAD_VSLOTS != PAD_VSLOTS - 1) {
-                    if (vslot[r * 8 + c] != -1) fail("v^T chunk copied twice", r, c);
-                    vslot[r * 8 + c] = p;
-                    if (q / PAD_VSLOTS != r || q % PAD_VSLOTS != c) fail("v^T slot holds another chunk", r, c);
+                const int r = int(src / (DV * 2)), c = int(src % (DV * 2)) / 16;
+                if (r < 0 || r >= BK || c < 0 || c >= DV / 8) { fail("value copy source", j, lane); continue; }
+                if (q % VSL < DV / 8) {  // not a padding slot
+                    if (vslot[r * (DV / 8) + c] != -1) fail("value chunk copied twice", r, c);
+                    vslot[r * (DV / 8) + c] = p;
+                    if (q / VSL != r || q % VSL != c) fail("value slot holds another chunk", r, c);
                 }
             }
         }
     for (size_t x = 0; x < kslot.size(); ++x)
         if (kslot[x] < 0) fail("K chunk never copied", int(x / (D / 8)), int(x % (D / 8)));
     for (size_t x = 0; x < vslot.size(); ++x)
-        if (vslot[x] < 0) fail("v^T chunk never copied", int(x / 8), int(x % 8));
-    // operand reads (reader side)
-    for (int kb = 0; kb < BK; kb += 32) {
+        if (vslot[x] < 0) fail("value chunk never copied", int(x / (DV / 8)), int(x % (DV / 8)));
+    // K operand reads (reader side)
+    for (int kb = 0; kb < BK; kb += 32)
         for (int st = 0; st < D / 16; ++st)
             for (int g = 0; g < 4; ++g) {
                 const int h = g >> 1;
@@ -338,22 +293,46 @@ static int check_pad_layout() {
                 }
                 if (used != 0xFFFFu) fail("K read bank groups", kb, int(used));
             }
+    // value operand reads: the transposing 8-byte reads, simulated
+    int worst_bank = 0;
+    for (int kb = 0; kb < BK; kb += 32)
         for (int kc = 0; kc < 2; ++kc)
             for (int db = 0; db < DV / 32; ++db)
-                for (int g = 0; g < 4; ++g) {
-                    const int h = g >> 1;
-                    unsigned used = 0;
-                    for (int q = 0; q < 16; ++q) {
-                        const int qi = 16 * (g & 1) + q;
-                        const int off = pad_vread<D>(kb, kc, db, qi, h);
-                        if (off < kbytes || off + 16 > kbytes + vbytes) fail("v^T read outside the tile", kb, kc);
-                        else if (off != 16 * vslot[(32 * db + qi) * 8 + kb / 8 + 2 * kc + h])
-                            fail("v^T read misses its chunk", 32 * db + qi, kb / 8 + 2 * kc + h);
-                        used |= 1u << ((off / 16) % 16);
+                for (int s = 0; s < 2; ++s) {
+                    int row[64], ch[64];
+                    for (int lane = 0; lane < 64; ++lane) {
+                        const int off = pad_vread_tr<D, DV>(kb, kc, db, s, lane);
+                        row[lane] = ch[lane] = -1;
+                        if (off < kbytes || off + 8 > kbytes + vbytes || off % 8) {
+                            fail("value read outside the value tile", kb, lane);
+                            continue;
+                        }
+                        const int o = off - kbytes, r = o / VSTR, cb = o % VSTR;
+                        if (cb + 8 > DV * 2) { fail("value read in a padding slot", r, cb); continue; }
+                        if (o / 16 != vslot[r * (DV / 8) + cb / 16] - 64 * KSL)
+                            fail("value read misses its chunk", r, cb / 16);
+                        row[lane] = r;
+                        ch[lane] = cb / 2;
                     }
-                    if (used != 0xFFFFu) fail("v^T read bank groups", kb, int(used));
+                    for (int half = 0; half < 2; ++half) {
+                        std::vector<int> bank(64, 0);
+                        for (int lane = 32 * half; lane < 32 * half + 32; ++lane) {
+                            const int off = pad_vread_tr<D, DV>(kb, kc, db, s, lane);
+                            for (int b = 0; b < 2; ++b) worst_bank = std::max(worst_bank, ++bank[(off / 4 + b) % 64]);
+                        }
+                    }
+                    for (int lane = 0; lane < 64; ++lane) {
+                        const int g = lane >> 4, i = lane & 15;
+                        for (int e = 0; e < 4; ++e) {
+                            const int srcl = 16 * g + (i >> 2) + 4 * e;
+                            const int key = row[srcl], chan = ch[srcl] < 0 ? -1 : ch[srcl] + (i & 3);
+                            const int want_key = kb + 16 * kc + 8 * s + 4 * (lane >> 5) + e;
+                            const int want_ch = 32 * db + (lane & 31);
+                            if (key != want_key || chan != want_ch) fail("value lane gets another element", lane, e);
+                        }
+                    }
                 }
-    }
+    if (worst_bank > 2) fail("value read: lanes of a half wave on one bank", worst_bank, 0);
     return bad;
 }
 

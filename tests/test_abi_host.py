@@ -83,7 +83,10 @@ def test_workspace_sizes():
     assert bq % bk == 0 and bq % 32 == 0 and bk % 32 == 0
     a, b = ws(1, 1, bq, 64), ws(1, 1, bq + 1, 64)  # one more query tile
     assert 0 < a < b
-    assert ws(1, 1, bq, 64, 1, 1) < a  # the fp32 path keeps no v^T copy
+    # values are read where they lie; only fp32 values on the bf16 path need
+    # a bf16 copy (n x d_v x 2 bytes per key/value head)
+    assert ws(1, 1, bq, 64, binding.F32, binding.F32) <= a
+    assert ws(1, 1, bq, 64, binding.BF16, binding.F32) >= a + bq * 64 * 2
     off = binding.resolvent_counters_offset(4, 16, 8192, 128)
     assert 0 < off < ws(4, 16, 8192, 128)
     assert binding.resolvent_counters_offset(1, 1, 0, 64) == 2 ** 64 - 1
@@ -104,8 +107,10 @@ def test_noalloc_host_checks():
                                              n, d, 0, 0, FAKE, FAKE, FAKE, None)
 
     # refused on the host before the scratch array is looked up
-    assert lib.resolvent_workspace_bytes(4, 16, 8192, 128, 0, 0) > 64 << 20
-    assert na(B=4, H=16, n=8192, d=128) == S.TOO_LARGE
+    assert lib.resolvent_workspace_bytes(4, 16, 65536, 128, 0, 0) > 64 << 20
+    assert na(B=4, H=16, n=65536, d=128) == S.TOO_LARGE
+    # fp32 values on the bf16 path add a bf16 copy of V to the workspace
+    assert lib.resolvent_workspace_bytes(4, 16, 8192, 128, 0, 1) > 64 << 20
     assert na(B=-1) == S.BAD_SHAPE
     assert na(n=0) == S.OK
     assert na(d=0) == S.BAD_SHAPE
@@ -174,10 +179,16 @@ def test_grouped_host_checks():
     assert grouped_call(ws_bytes=64) == S.BAD_ARG
     ws = binding.resolvent_workspace_bytes_grouped
     assert ws(1, 4, 3, 128, 64, 64) == 0 and ws(1, 4, 2, 128, 64, 96) == 0
-    # fewer k/v heads: a smaller v^T copy; the same call as resolvent_forward at Hkv = H, dv = d
-    assert ws(2, 8, 2, 512, 128, 128) < ws(2, 8, 8, 512, 128, 128)
+    # bf16 values are read where they lie: the workspace does not depend on Hkv or dv;
+    # the same call as resolvent_forward at Hkv = H, dv = d
+    assert ws(2, 8, 2, 512, 128, 128) == ws(2, 8, 8, 512, 128, 128)
     assert ws(2, 8, 8, 512, 128, 128) == binding.resolvent_workspace_bytes(2, 8, 512, 128)
-    assert ws(1, 2, 2, 256, 64, 128) > ws(1, 2, 2, 256, 64, 64)
+    assert ws(1, 2, 2, 256, 64, 128) == ws(1, 2, 2, 256, 64, 64)
+    # fp32 values on the bf16 path: a bf16 copy of V, Hkv x n x dv per sequence
+    f = lambda Hkv, dv: ws(2, 8, Hkv, 512, 128, dv, binding.BF16, binding.F32)
+    assert f(2, 128) < f(8, 128)
+    assert f(8, 128) - f(2, 128) >= 2 * 6 * 512 * 128 * 2
+    assert f(2, 128) > f(2, 64)
 
 
 def decode_call(B=1, H=4, Hkv=2, n=130, cap=None, d=64, dv=128, beta=1.0, qk=1.0, g=1.0, qdt=0,
