@@ -178,7 +178,7 @@ inline OperatorLayout make_operator_layout(int64_t B, int64_t H, int64_t n, int6
 }
 
 // Source byte offsets of the direct global->LDS tile copies, relative to the
-// start of the tensor (q/k/v, or the v^T region for the bf16 path).  Row `r`
+// start of the tensor (q, k or v).  Row `r`
 // of key tile `t` is key t*BK + r, clamped into [0, n-1] so that a tile
 // reaching past the sequence end still reads inside the tensor; `chunk` is a
 // 16-byte chunk of that row.
@@ -188,11 +188,6 @@ RESOLVENT_HD inline int64_t tile_row_src(int64_t bh, int64_t n, int64_t t, int r
     key = key < n ? key : n - 1;
     return (bh * n + key) * row_bytes + int64_t(chunk) * 16;
 }
-// v^T [BH][d][n_pad] bf16: row `dd` of key tile t, chunk `chunk` (8 keys).
-RESOLVENT_HD inline int64_t vt_src(int64_t bh, int64_t d, int64_t n_pad, int64_t t, int dd,
-                                   int chunk) {
-    return ((bh * d + dd) * n_pad + t * BK) * 2 + int64_t(chunk) * 16;
-}
 
 // The same as 32-bit offsets inside one head (the kernels add them to a
 // wave-uniform head base; every offset fits 32 bits for n <= 2^22, d <= 128).
@@ -200,74 +195,6 @@ RESOLVENT_HD inline uint32_t tile_row_off(int64_t n, int64_t t, int r, int64_t r
     int64_t key = t * BK + r;
     key = key < n ? key : n - 1;
     return uint32_t(key * row_bytes);
-}
-RESOLVENT_HD inline uint32_t vt_row_off(int64_t n_pad, int64_t t, int dd) {
-    return uint32_t((dd * n_pad + t * BK) * 2);
-}
-
-// bf16-path tiles in LDS are row-major -- K: BK rows of 2d bytes; v^T: d
-// rows of 2BK bytes -- with the 16-byte chunks of row r stored in the order
-// c ^ chunk_swz(r).  With CPR chunks per row (8 or 16), any 16 consecutive
-// rows then hold a given chunk in 16 different 16-byte bank groups of the
-// 256-byte bank cycle, so a half-wave reading one chunk of 16 rows has no
-// bank conflict, while one direct global->LDS wave instruction still copies
-// 1 KiB of whole, consecutive rows (lane L writes 16 bytes at 16 L).
-template <int CPR>
-RESOLVENT_HD constexpr int chunk_swz(int r) {
-    static_assert(CPR == 8 || CPR == 16, "8 or 16 chunks per row");
-    return (r >> (CPR == 16 ? 0 : 1)) & (CPR - 1);
-}
-// Copy instruction j of a tile with CPR chunks per row: lane `lane` fetches
-// chunk copy_chunk of row copy_row (and writes LDS offset 1024 j + 16 lane).
-template <int CPR>
-RESOLVENT_HD constexpr int copy_row(int j, int lane) {
-    return (64 / CPR) * j + lane / CPR;
-}
-template <int CPR>
-RESOLVENT_HD constexpr int copy_chunk(int j, int lane) {
-    return (lane % CPR) ^ chunk_swz<CPR>(copy_row<CPR>(j, lane));
-}
-// Source offsets (inside one head, 32 bits) of copy instruction j, lane
-// `lane`, of key tile t: the K copy (row_bytes = 16 CPR, rows past n clamped
-// to key n-1) and the v^T copy (8 chunks of 8 keys per row).
-template <int CPR>
-RESOLVENT_HD inline uint32_t k_copy_off(int64_t n, int64_t t, int j, int lane) {
-    return tile_row_off(n, t, copy_row<CPR>(j, lane), 16 * CPR) +
-           uint32_t(16 * copy_chunk<CPR>(j, lane));
-}
-RESOLVENT_HD inline uint32_t vt_copy_off(int64_t n_pad, int64_t t, int j, int lane) {
-    return vt_row_off(n_pad, t, copy_row<8>(j, lane)) + uint32_t(16 * copy_chunk<8>(j, lane));
-}
-// The per-lane parts of those offsets for copy instruction j (wave-uniform
-// parts excluded).  A wave that issues instructions j0, j0 + NC, j0 + 2 NC,
-// ... (NC a multiple of 4 rows' worth of instructions, so that every step
-// moves 16 rows and keeps the swizzle) adds only uniform terms:
-//   k_copy_off(n, t, j0 + NC i, lane)
-//       = t BK 16 CPR + 1024 NC i + k_lane_off(j0, lane)   (tile t inside n)
-//   vt_copy_off(n_pad, t, j0 + NC i, lane)
-//       = 2 BK t + 16 NC n_pad i + vt_lane_off(n_pad, j0, lane)
-template <int CPR>
-RESOLVENT_HD constexpr uint32_t k_lane_off(int j, int lane) {
-    return uint32_t(copy_row<CPR>(j, lane) * 16 * CPR + 16 * copy_chunk<CPR>(j, lane));
-}
-RESOLVENT_HD inline uint32_t vt_lane_off(int64_t n_pad, int j, int lane) {
-    return uint32_t(copy_row<8>(j, lane) * n_pad * 2 + 16 * copy_chunk<8>(j, lane));
-}
-// Byte offset inside a tile of the 16-byte chunk `c` of row `r`.
-template <int CPR>
-RESOLVENT_HD constexpr int tile_chunk_off(int r, int c) {
-    return r * CPR * 16 + 16 * (c ^ chunk_swz<CPR>(r));
-}
-// Matrix-operand reads.  Lane (qi, h) of a 32x32x16 bf16 product reads, for
-// step s, chunk 2s+h of K row kb+qi (kb a multiple of 32); its offset is
-// kfrag_base ^ (32 s).  For v^T it reads chunk kb/8 + 2kc + h of row
-// 32db + qi: offset (vfrag_base ^ (2kb + 32kc)) + 4096 db.
-template <int CPR>
-RESOLVENT_HD constexpr int kfrag_base(int kb, int qi, int h) {
-    return (kb + qi) * CPR * 16 + 16 * (h ^ chunk_swz<CPR>(qi));
-}
-RESOLVENT_HD constexpr int vfrag_base(int qi, int h) {
-    return qi * 128 + 16 * (h ^ chunk_swz<8>(qi));
 }
 
 // Padded bf16 tiles of the fused forward (bf16 path).  A K row of d bf16

@@ -310,26 +310,19 @@ __device__ __forceinline__ int64_t kv_head(const FwdArgs &A, int64_t bh) {
     return (bh / A.H) * (A.H / A.group) + (bh % A.H) / A.group;
 }
 
-// Shared-memory plan: NBUF buffers, each holding one key tile K [BK][D], its
-// values (bf16 path: v^T [DV][BK] in perm16 key order; fp32 path: V [BK][DV]),
-// per-key side data (the carried gate factor T_j = C*S_j with its modulus
-// for tiles before the query tile; the gates a_{j+1} for the query tile's
-// own keys) and the raw in-tile suffix products S_j it is formed from.
-// bf16 tiles are row-major with the 16-byte chunks of each row in a
-// row-dependent XOR order (chunk_swz): a direct global->LDS wave instruction
-// copies 1 KiB of whole consecutive rows (8 cache lines) and the MFMA
-// operand reads stay free of bank conflicts.  fp32 tiles are 16-byte-chunk-
-// major: chunk c of row r sits at (c * rows + r) * 16 (one wave instruction
-// copies one chunk of 64 rows).  Buffers start on 256-byte boundaries.
-template <bool F32, int D, int DV = D>
+// Shared-memory plan of the fp32 path: NBUF buffers, each holding one key
+// tile K [BK][D] and its values V [BK][DV], per-key side data (the carried
+// gate factor T_j = C*S_j with its modulus for tiles before the query tile;
+// the gates a_{j+1} for the query tile's own keys) and the raw in-tile suffix
+// products S_j it is formed from.  Tiles are 16-byte-chunk-major: chunk c of
+// row r sits at (c * BK + r) * 16 (one wave instruction copies one chunk of
+// the 64 rows).  Buffers start on 256-byte boundaries.
+template <int D, int DV = D>
 struct Smem {
-    static constexpr int ESZ = F32 ? 4 : 2;
-    static constexpr int KCH = D * ESZ / 16;    // 16-byte chunks per K row
-    static constexpr int VKCH = DV * 4 / 16;    // chunks per V row (fp32 path)
-    static constexpr int VCH = BK * 2 / 16;     // chunks per v^T row (bf16 path)
-    static constexpr int VINS = F32 ? VKCH : VCH * DV / 64;  // V copy instructions per tile
+    static constexpr int KCH = D * 4 / 16;    // 16-byte chunks per K row
+    static constexpr int VINS = DV * 4 / 16;  // chunks per V row = V copy instructions per tile
     static constexpr size_t k_bytes = size_t(KCH) * BK * 16;
-    static constexpr size_t v_bytes = F32 ? size_t(VKCH) * BK * 16 : size_t(VCH) * DV * 16;
+    static constexpr size_t v_bytes = size_t(VINS) * BK * 16;
     static constexpr size_t side_off = k_bytes + v_bytes;
     // side data: 3 x BK floats; raw: S_j as 3 x BK floats and the product of
     // the tile's gates (A_re, A_im, A_m, 0) as doubles; then 2 flag words
@@ -339,7 +332,7 @@ struct Smem {
     static constexpr size_t flag_off = tprod_off + 4 * sizeof(double);
     static constexpr size_t buf_bytes = (flag_off + 16 + 255) / 256 * 256;
     // four buffers keep two tiles in flight while two are read, when they
-    // fit into the 160 KB of LDS (not the larger fp32 tiles)
+    // fit into the 160 KB of LDS (d = dv = 128 takes two)
     static constexpr int NBUF = 4 * buf_bytes + 64 <= 160 * 1024 ? 4 : 2;
     static constexpr size_t misc_off = NBUF * buf_bytes;
     // the running carried product of the landings (3 doubles)
@@ -373,18 +366,6 @@ __device__ __forceinline__ int fresh_lane() {
     int l;
     asm volatile("v_mbcnt_lo_u32_b32 %0, -1, 0\n\tv_mbcnt_hi_u32_b32 %0, -1, %0" : "=v"(l));
     return l;
-}
-
-// A wave-uniform value the compiler must treat as new at each use, so that
-// values derived from it are recomputed there instead of held in scalar
-// registers through the loop.
-__device__ __forceinline__ int launder_s(int x) {
-    asm volatile("" : "+s"(x));
-    return x;
-}
-__device__ __forceinline__ int64_t launder_s64(int64_t x) {
-    asm volatile("" : "+s"(x));
-    return x;
 }
 
 // LDS byte address of a pointer into the workgroup's shared memory.
@@ -511,50 +492,29 @@ __device__ __forceinline__ uint32_t load_q(const FwdArgs &A, int64_t bh, int64_t
 }
 
 // Start the asynchronous copy of key tile t (K, and the values unless
-// k_only) into buffer buf (an LDS byte address).  Wave w < NCOPY copies
-// chunks w, w+NCOPY, ...: lane L fetches 16 bytes of row L; other waves copy
-// nothing.  Keys past n repeat key n-1 (their entries are
-// masked); the v^T copy is zero there.  kh, vh: this head's rows of k and of
-// v^T (bf16 path) or v (fp32 path), wave-uniform.
-template <bool F32, int D, int DV>
+// k_only) into buffer buf (an LDS byte address), fp32 path.  Wave w < NCOPY
+// copies chunks w, w+NCOPY, ...: lane L fetches 16 bytes of row L; other
+// waves copy nothing.  Keys past n repeat key n-1 (their entries are masked).
+// kh, vh: this head's rows of k and of v, wave-uniform.
+template <int D, int DV>
 __device__ __forceinline__ void stage_async(const FwdArgs &A, uint32_t buf,
                                             const unsigned char *kh, const unsigned char *vh,
                                             int t, bool k_only, int w) {
-    using SM = Smem<F32, D, DV>;
+    using SM = Smem<D, DV>;
     const int lane = fresh_lane();
     if (w >= NCOPY) return;
-    constexpr int ROWB = D * SM::ESZ;  // bytes per q/k/v row in memory
-    if constexpr (!F32) {
-        // K: instruction j copies whole rows (64/CPR) j, ... of the tile
-        constexpr int CPR = D / 8;
+    const uint32_t koff = tile_row_off(A.n, t, lane, D * 4);
 #pragma unroll
-        for (int i = 0; i < SM::KCH / NCOPY; ++i) {
-            const int j = w + NCOPY * i;
-            g2lds16(kh, k_copy_off<CPR>(A.n, t, j, lane), buf + uint32_t(j * 1024));
-        }
-        if (k_only) return;
-        // v^T: instruction j copies rows d = 8 j, ..., 8 j + 7 (keys of tile t)
-        constexpr int NI = SM::VINS / NCOPY;
+    for (int i = 0; i < SM::KCH / NCOPY; ++i) {
+        const int c = w + NCOPY * i;
+        g2lds16(kh, koff + uint32_t(c * 16), buf + uint32_t(c * 1024));
+    }
+    if (k_only) return;
+    const uint32_t voff = tile_row_off(A.n, t, lane, DV * 4);
 #pragma unroll
-        for (int i = 0; i < NI; ++i) {
-            const int j = w + NCOPY * i;
-            g2lds16(vh, vt_copy_off(A.n_pad, t, j, lane),
-                    buf + uint32_t(SM::k_bytes + j * 1024));
-        }
-    } else {
-        const uint32_t koff = tile_row_off(A.n, t, lane, ROWB);
-#pragma unroll
-        for (int i = 0; i < SM::KCH / NCOPY; ++i) {
-            const int c = w + NCOPY * i;
-            g2lds16(kh, koff + uint32_t(c * 16), buf + uint32_t(c * 1024));
-        }
-        if (k_only) return;
-        const uint32_t voff = tile_row_off(A.n, t, lane, DV * 4);
-#pragma unroll
-        for (int i = 0; i < SM::VINS / NCOPY; ++i) {
-            const int c = w + NCOPY * i;
-            g2lds16(vh, voff + uint32_t(c * 16), buf + uint32_t(SM::k_bytes + c * 1024));
-        }
+    for (int i = 0; i < SM::VINS / NCOPY; ++i) {
+        const int c = w + NCOPY * i;
+        g2lds16(vh, voff + uint32_t(c * 16), buf + uint32_t(SM::k_bytes + c * 1024));
     }
 }
 
@@ -563,7 +523,7 @@ __device__ __forceinline__ void stage_async(const FwdArgs &A, uint32_t buf,
 template <bool F32, int D, int DV>
 __device__ __forceinline__ void head_bases(const FwdArgs &A, int64_t kvh,
                                            const unsigned char *&kh, const unsigned char *&vh) {
-    constexpr int64_t ROWB = D * Smem<F32, D>::ESZ;
+    constexpr int64_t ROWB = D * (F32 ? 4 : 2);
     kh = uniform_ptr(static_cast<const unsigned char *>(A.k) + kvh * A.n * ROWB);
     if constexpr (!F32)
         vh = uniform_ptr(reinterpret_cast<const unsigned char *>(A.v16) + kvh * A.n * (DV * 2));
@@ -575,82 +535,49 @@ __device__ __forceinline__ void head_bases(const FwdArgs &A, int64_t kvh,
 // itself (stage_async: its copy instructions j = w, w+NCOPY, ... wrote LDS
 // offset 1024 j + 16 lane).  A row past the sequence end holds a copy of key
 // n-1.  Valid once the wave's own copies have landed.
-template <bool F32, int D>
-__device__ __forceinline__ uint32_t own_kbits(const FwdArgs &A, const unsigned char *buf,
-                                              int64_t t, int w) {
-    using SM = Smem<F32, D>;
+template <int D>
+__device__ __forceinline__ uint32_t own_kbits(const unsigned char *buf, int w) {
+    using SM = Smem<D>;
     uint32_t bits = 0;
     if (w < NCOPY) {
 #pragma unroll
         for (int i = 0; i < SM::KCH / NCOPY; ++i) {
             const int j = w + NCOPY * i;
             const uint4 v = *reinterpret_cast<const uint4 *>(buf + (j * 64 + fresh_lane()) * 16);
-            if constexpr (F32)
-                bits = max(bits, absbits_f4(__builtin_bit_cast(float4, v)));
-            else
-                bits = max(bits, absbits_u4_bf16(v));
+            bits = max(bits, absbits_f4(__builtin_bit_cast(float4, v)));
         }
     }
     return bits;
 }
 
-// S^T for keys kb..kb+31 of the staged tile against the wave's 32 queries.
-// Lane (qi, h), register r holds key kb + 8(r/4) + 4h + r%4 of query qi.
-template <bool F32, int D>
+// S^T for keys kb..kb+31 of the staged tile against the wave's 32 queries
+// (fp32 path).  Lane (qi, h), register r holds key kb + 8(r/4) + 4h + r%4 of
+// query qi.
+template <int D>
 __device__ __forceinline__ f32x16 s_block(const unsigned char *buf, int kb, int qi, int h,
-                                          const typename Frag<F32, D>::type (&qf)[Frag<F32, D>::count]) {
+                                          const float (&qf)[D / 2]) {
     f32x16 acc;
 #pragma unroll
     for (int r = 0; r < 16; ++r) acc[r] = 0.f;
-    if constexpr (!F32) {
-        const int kf = kfrag_base<D / 8>(kb, qi, h);  // chunk 2s+h of row kb+qi: kf ^ 32s
+    const unsigned char *kp = buf + (h * (D / 8) * BK + kb + qi) * 16;
 #pragma unroll
-        for (int s = 0; s < D / 16; ++s) {
-            const bf16x8 a = *reinterpret_cast<const bf16x8 *>(buf + (kf ^ (32 * s)));
-            acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[s], acc, 0, 0, 0);
-        }
-    } else {
-        const unsigned char *kp = buf + (h * (D / 8) * BK + kb + qi) * 16;
-#pragma unroll
-        for (int t = 0; t < D / 8; ++t) {
-            const float4 a = *reinterpret_cast<const float4 *>(kp + t * BK * 16);
-            acc = __builtin_amdgcn_mfma_f32_32x32x2f32(a.x, qf[4 * t + 0], acc, 0, 0, 0);
-            acc = __builtin_amdgcn_mfma_f32_32x32x2f32(a.y, qf[4 * t + 1], acc, 0, 0, 0);
-            acc = __builtin_amdgcn_mfma_f32_32x32x2f32(a.z, qf[4 * t + 2], acc, 0, 0, 0);
-            acc = __builtin_amdgcn_mfma_f32_32x32x2f32(a.w, qf[4 * t + 3], acc, 0, 0, 0);
-        }
+    for (int t = 0; t < D / 8; ++t) {
+        const float4 a = *reinterpret_cast<const float4 *>(kp + t * BK * 16);
+        acc = __builtin_amdgcn_mfma_f32_32x32x2f32(a.x, qf[4 * t + 0], acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_32x32x2f32(a.y, qf[4 * t + 1], acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_32x32x2f32(a.z, qf[4 * t + 2], acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_32x32x2f32(a.w, qf[4 * t + 3], acc, 0, 0, 0);
     }
     return acc;
 }
 
-// O^T += V^T W~^T for one 32-key block at kb (bf16 path), W~ packed per
-// 16-key chunk kc as the B operand (registers 8kc..8kc+7 of the S^T block):
-// two accumulators, one for Re W~ and one for Im W~, share the V operand.
-template <int D, int DV>
-__device__ __forceinline__ void pv_block_bf16(const unsigned char *buf, int kb, int qi, int h,
-                                              const bf16x8 (&wr)[2], const bf16x8 (&wi)[2],
-                                              f32x16 (&ore)[DV / 32], f32x16 (&oim)[DV / 32]) {
-    const unsigned char *vb = buf + Smem<false, D>::k_bytes;
-    const int vf = vfrag_base(qi, h);
-#pragma unroll
-    for (int kc = 0; kc < 2; ++kc) {
-        // chunk (kb/8 + 2kc + h) of v^T row 32db + qi
-        const unsigned char *vp = vb + (vf ^ (2 * kb + 32 * kc));
-#pragma unroll
-        for (int db = 0; db < DV / 32; ++db) {
-            const bf16x8 a = *reinterpret_cast<const bf16x8 *>(vp + 32 * db * 128);
-            ore[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, wr[kc], ore[db], 0, 0, 0);
-            oim[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, wi[kc], oim[db], 0, 0, 0);
-        }
-    }
-}
-
-// The same for the 16 keys of chunk kc on the fp32 path (fp32 V rows).
+// O^T += V^T W~^T for the 16 keys of chunk kc of the 32-key block at kb
+// (fp32 path), W~ as 8 floats per lane.
 template <int D, int DV>
 __device__ __forceinline__ void pv_chunk_f32(const unsigned char *buf, int kb, int kc, int qi,
                                              int h, const float (&wre)[8], const float (&wim)[8],
                                              f32x16 (&ore)[DV / 32], f32x16 (&oim)[DV / 32]) {
-    const unsigned char *vb = buf + Smem<true, D>::k_bytes;
+    const unsigned char *vb = buf + Smem<D>::k_bytes;
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
         const int s = 8 * kc + e;
@@ -664,80 +591,6 @@ __device__ __forceinline__ void pv_chunk_f32(const unsigned char *buf, int kb, i
             oim[db] = __builtin_amdgcn_mfma_f32_32x32x2f32(a, wim[e], oim[db], 0, 0, 0);
         }
     }
-}
-
-// Matrix step of the bf16 path: O^T += V^T W~^T for the block at (bv, kbv)
-// (PV) and S^T = K Q^T for the block at (bs, kbs) into sacc (S).  The S
-// products form one accumulation chain, so each sits between two W~ V
-// products (a dependent matrix instruction then never waits on the one
-// before).  K and v^T fragments stream through four-deep pipelines (LDS
-// latency under load is a few hundred cycles); scheduling fences keep the
-// order.
-constexpr int MDEPTH = 4;
-struct MPrefetch {
-    bf16x8 vf[MDEPTH], kf[MDEPTH];
-};
-template <int D, int DV>
-__device__ __forceinline__ bf16x8 mstep_vload(const unsigned char *bv, int vf, int kbv, int i) {
-    // chunk (kbv/8 + 2kc + h) of v^T row 32db + qi, fragment i = (kc, db)
-    const int kc = i / (DV / 32), db = i % (DV / 32);
-    return *reinterpret_cast<const bf16x8 *>(bv + Smem<false, D>::k_bytes + 4096 * db +
-                                             (vf ^ (2 * kbv + 32 * kc)));
-}
-__device__ __forceinline__ bf16x8 mstep_kload(const unsigned char *bs, int kf, int i) {
-    // chunk 2i+h of K row kbs+qi
-    return *reinterpret_cast<const bf16x8 *>(bs + (kf ^ (32 * i)));
-}
-// Operand fragments [I0, I1) of each kind of a matrix step (mstep_bf16 with
-// NPRE = I1 then starts from the first NPRE of them).
-template <int D, int DV, bool PV, bool S, int I0, int I1>
-__device__ __forceinline__ void mstep_prefetch(const unsigned char *bv, int kbv,
-                                               const unsigned char *bs, int kbs, int qi, int h,
-                                               MPrefetch &pf) {
-    constexpr int NV = PV ? 2 * (DV / 32) : 0;
-    constexpr int NK = S ? D / 16 : 0;
-    const int vf = vfrag_base(qi, h);
-    const int kf = kfrag_base<D / 8>(kbs, qi, h);
-#pragma unroll
-    for (int i = I0; i < I1; ++i) {
-        if (i < NV) pf.vf[i] = mstep_vload<D, DV>(bv, vf, kbv, i);
-        if (i < NK) pf.kf[i] = mstep_kload(bs, kf, i);
-    }
-}
-template <int D, int DV, bool PV, bool S, int NPRE>
-__device__ __forceinline__ void mstep_bf16(const unsigned char *bv, int kbv,
-                                           const unsigned char *bs, int kbs, int qi, int h,
-                                           MPrefetch &pf, const bf16x8 (&wr)[2],
-                                           const bf16x8 (&wi)[2], const bf16x8 (&qf)[D / 16],
-                                           f32x16 (&ore)[DV / 32], f32x16 (&oim)[DV / 32],
-                                           f32x16 &sacc) {
-    constexpr int NDB = DV / 32;
-    constexpr int NV = PV ? 2 * NDB : 0;  // v^T fragments: chunk kc, row block db
-    constexpr int NK = S ? D / 16 : 0;    // K fragments
-    constexpr int NSTEP = NV > NK ? NV : NK;
-    const int vf = vfrag_base(qi, h);
-    const int kf = kfrag_base<D / 8>(kbs, qi, h);
-    mstep_prefetch<D, DV, PV, S, NPRE, MDEPTH>(bv, kbv, bs, kbs, qi, h, pf);
-    if constexpr (S) {
-#pragma unroll
-        for (int r = 0; r < 16; ++r) sacc[r] = 0.f;
-    }
-#pragma unroll
-    for (int i = 0; i < NSTEP; ++i) {
-        __builtin_amdgcn_sched_barrier(0);
-        if (i < NV) {
-            const int kc = i / NDB, db = i % NDB;
-            const bf16x8 a = pf.vf[i % MDEPTH];
-            ore[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, wr[kc], ore[db], 0, 0, 0);
-            oim[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, wi[kc], oim[db], 0, 0, 0);
-            if (i + MDEPTH < NV) pf.vf[i % MDEPTH] = mstep_vload<D, DV>(bv, vf, kbv, i + MDEPTH);
-        }
-        if (i < NK) {
-            sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(pf.kf[i % MDEPTH], qf[i], sacc, 0, 0, 0);
-            if (i + MDEPTH < NK) pf.kf[i % MDEPTH] = mstep_kload(bs, kf, i + MDEPTH);
-        }
-    }
-    __builtin_amdgcn_sched_barrier(0);
 }
 
 // Lazy rescaling: the shift M only moves when a logit exceeds it by more than
@@ -812,41 +665,16 @@ __global__ __launch_bounds__(64) void schedule_kernel(const double *__restrict__
     }
 }
 
-// Weights W~ of one 32-key block as the B operand of O^T += V^T W~^T, per
-// 16-key chunk kc (bf16: packed; fp32: 8 floats per lane).
-template <bool F32>
-struct BlockW {
-    bf16x8 r[2], i[2];
-};
-template <>
-struct BlockW<true> {
-    float r[2][8], i[2][8];
-};
-
-// O^T += V^T W~^T for the 32-key block at kb of a staged tile.
-template <bool F32, int D, int DV>
-__device__ __forceinline__ void pv_block(const unsigned char *buf, int kb, int qi, int h,
-                                         const BlockW<F32> &wb, f32x16 (&ore)[DV / 32],
-                                         f32x16 (&oim)[DV / 32]) {
-    if constexpr (F32) {
-#pragma unroll
-        for (int kc = 0; kc < 2; ++kc)
-            pv_chunk_f32<D, DV>(buf, kb, kc, qi, h, wb.r[kc], wb.i[kc], ore, oim);
-    } else {
-        pv_block_bf16<D, DV>(buf, kb, qi, h, wb.r, wb.i, ore, oim);
-    }
-}
-
-// Fused forward.  A workgroup owns the BQ queries [i0, i0+BQ) of one head;
+// Fused forward, fp32 path (fp32 q, k, v; the bf16 path runs
+// fwd_pad_kernel).  A workgroup owns the BQ queries [i0, i0+BQ) of one head;
 // wave w owns rows i0+32w .. i0+32w+31.  Keys go in 32-key blocks, tile by
 // tile: the n_off key tiles before the query tile that the visit count
 // allows, last to first, then the query tile's own NDIAG tiles, last to first.
 //
 // Each block k passes through two steps of a wave:
-//   M(k)  matrix step: O += W~(k-1) V(k-1) and S(k) = K(k) Q^T;
+//   M(k)  matrix step: S(k) = K(k) Q^T;
 //   V(k)  vector step: masks, shift, exponentials and gate factors of block
-//         k, giving W~(k) packed as the next B operand (the fp32 path adds
-//         W~(k) V(k) right there).
+//         k, giving W~(k), and O += W~(k) V(k).
 // The workgroup advances in phases separated by LDS-only barriers.  Waves
 // 0..3 run step p in phase p and waves 4..7 one phase later, so the two
 // waves that share a SIMD (w and w+4) alternate between matrix and vector
@@ -855,11 +683,10 @@ __device__ __forceinline__ void pv_block(const unsigned char *buf, int kb, int q
 // copied and landed in a phase is a function of the phase number alone, and
 // every vector-memory operation in the phase loops is such a copy, waited
 // for with exact counts.
-template <bool F32, int D, int DV, bool QKZ>
+template <int D, int DV, bool QKZ>
 __global__ __launch_bounds__(NTHREADS, 1) void fwd_kernel(FwdArgs A) {
-    using SM = Smem<F32, D, DV>;
-    using FR = Frag<F32, D>;
-    using WB = BlockW<F32>;
+    using SM = Smem<D, DV>;
+    using FR = Frag<true, D>;
     constexpr int NBUF = SM::NBUF;
     constexpr int NDIAG = BQ / BK;    // key tiles inside the query tile
     constexpr int NDB = 2 * NDIAG;    // 32-key blocks inside the query tile
@@ -896,7 +723,7 @@ __global__ __launch_bounds__(NTHREADS, 1) void fwd_kernel(FwdArgs A) {
     const int n_off = __builtin_amdgcn_readfirstlane(A.noff[bh * A.n_qt + qt]);
     const int n_tiles = n_off + NDIAG;
     const unsigned char *kh, *vh;
-    head_bases<F32, D, DV>(A, kv_head(A, bh), kh, vh);
+    head_bases<true, D, DV>(A, kv_head(A, bh), kh, vh);
 
     if (tid == 0) {
         misc[2] = 0;
@@ -916,19 +743,8 @@ __global__ __launch_bounds__(NTHREADS, 1) void fwd_kernel(FwdArgs A) {
     // raw area for a tile before the query tile, a_{j+1} straight into the
     // side area for an own tile (the gate planes hold the identity gate past
     // n, and a_{j+1} past the head's last position is only ever multiplied
-    // into an entry above the diagonal) -- and the tile's product.  On the
-    // bf16 path every copy of a tile inside the sequence adds only uniform
-    // terms to the wave's two per-lane offsets (recomputed per tile rather
-    // than held in registers through the loop); the ragged last tile (rows
-    // clamped to key n-1) takes the general K copy.
+    // into an entry above the diagonal) -- and the tile's product.
     const uint32_t smem_lds = lds_addr(smem);
-    static_assert(F32 || (64 / (D / 8)) * NCOPY % 16 == 0, "a copy step keeps the swizzle");
-    const int n32 = int(A.n);  // n <= 2^22 (checked on the host)
-    uint32_t k_lane = 0, v_lane = 0;
-    if constexpr (!F32) {
-        k_lane = k_lane_off<D / 8>(w, lane);
-        v_lane = vt_lane_off(A.n_pad, w, lane);
-    }
     // this head's S_j planes, a_{j+1} planes and tile products
     const double *t4 = uniform_ptr(A.t4 + 4 * bh * A.n_kt);
     const float *gS = uniform_ptr(A.gates + 3 * A.plane + bh * A.n_pad);
@@ -937,28 +753,7 @@ __global__ __launch_bounds__(NTHREADS, 1) void fwd_kernel(FwdArgs A) {
         if (sg >= n_tiles) return;
         const int t = tile_of(sg);
         const uint32_t buf = smem_lds + uint32_t((sg % NBUF) * SM::buf_bytes);
-        if constexpr (!F32) {
-            if (w < NCOPY) {
-                const int wl = launder_s(w);
-                if ((t + 1) * BK <= n32) {
-                    const unsigned char *kt = kh + int64_t(t) * (BK * D * 2);
-#pragma unroll
-                    for (int i = 0; i < SM::KCH / NCOPY; ++i)
-                        g2lds16(kt + 1024 * NCOPY * i, k_lane,
-                                buf + uint32_t((wl + NCOPY * i) * 1024));
-                } else {
-                    stage_async<F32, D, DV>(A, buf, kh, vh, t, true, wl);
-                }
-                const unsigned char *vt = vh + int64_t(t) * (BK * 2);
-                const int64_t np = launder_s64(A.n_pad);
-#pragma unroll
-                for (int i = 0; i < SM::VINS / NCOPY; ++i)
-                    g2lds16(vt + int64_t(16 * NCOPY * i) * np, v_lane,
-                            buf + uint32_t(SM::k_bytes + (wl + NCOPY * i) * 1024));
-            }
-        } else {
-            stage_async<F32, D, DV>(A, buf, kh, vh, t, false, w);
-        }
+        stage_async<D, DV>(A, buf, kh, vh, t, false, w);
         if (w == 0) {
             const bool off = sg < n_off;
             const uint32_t lo = uint32_t(fresh_lane() * 4);
@@ -1028,7 +823,7 @@ __global__ __launch_bounds__(NTHREADS, 1) void fwd_kernel(FwdArgs A) {
                 }
             }
         } else {
-            kbits = max(kbits, own_kbits<F32, D>(A, buf, tile_of(sg), w));
+            kbits = max(kbits, own_kbits<D>(buf, w));
         }
     };
     // wait until this wave's copies of the tile landing now are in, leaving
@@ -1096,7 +891,7 @@ __global__ __launch_bounds__(NTHREADS, 1) void fwd_kernel(FwdArgs A) {
 #pragma unroll
     for (int sg = 0; sg < NBUF / 2; ++sg) issue(sg);
     typename FR::type qf[FR::count];
-    const uint32_t qbits = load_q<F32, D>(A, bh, row, row_ok, h, qf);
+    const uint32_t qbits = load_q<true, D>(A, bh, row, row_ok, h, qf);
     // a row whose prefix inside the query tile holds a closed gate sees no
     // key before the query tile
     const float prow_re = A.p_re[gbase + row], prow_im = A.p_im[gbase + row];
@@ -1124,7 +919,6 @@ __global__ __launch_bounds__(NTHREADS, 1) void fwd_kernel(FwdArgs A) {
     f32x16 x;                              // scores of the block between M and V
 #pragma unroll
     for (int r = 0; r < 16; ++r) x[r] = 0.f;
-    WB wk;  // W~ of the block between V and M (bf16 path)
     // Logits are c*S in log2 units; c = qk log2(e)/sqrt(d) may be negative.
     const bool cpos = A.c > 0.0f;
     const float dead_s = cpos ? -INFINITY : INFINITY;  // a score whose logit is -inf
@@ -1176,8 +970,7 @@ __global__ __launch_bounds__(NTHREADS, 1) void fwd_kernel(FwdArgs A) {
         }
     };
     // exponentials e = 2^(c S - M) of one 16-key chunk, the normaliser, and
-    // W~ = e * gate factor: packed for the next matrix step (bf16 path) or
-    // multiplied into O right away (fp32 path).  QKZ: e is 1 on live entries
+    // W~ = e * gate factor, multiplied into O right away.  QKZ: e is 1 on live entries
     // (all_live, or a non-zero modulus on a live row), else 0.
     // own: the exponent is formed as the rounded logit c*S minus the shift,
     // the shift being the rounded logit of the row's maximum when it was set,
@@ -1203,114 +996,42 @@ __global__ __launch_bounds__(NTHREADS, 1) void fwd_kernel(FwdArgs A) {
             wre[e] = ex * fre[e];
             wim[e] = ex * fim[e];
         }
-        if constexpr (F32) {
-            pv_chunk_f32<D, DV>(buf, kb, kc, qi, h, wre, wim, ore, oim);
-        } else {
-#pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                wk.r[kc][e] = (__bf16)wre[e];
-                wk.i[kc][e] = (__bf16)wim[e];
-            }
-        }
+        pv_chunk_f32<D, DV>(buf, kb, kc, qi, h, wre, wim, ore, oim);
     };
     // vector step of a block of a tile before the query tile: G = S_j C_t P_i
     // (P_i applied to O once, when the query tile's own keys begin); masked:
     // the block holds a dead column or the wave a dead row
     auto vstep_off = [&](const unsigned char *buf, int kb, bool masked) __attribute__((always_inline)) {
         const float *side = reinterpret_cast<const float *>(buf + SM::side_off);
-        if constexpr (F32) {
-            if (!QKZ && masked) {
-#pragma unroll
-                for (int kc = 0; kc < 2; ++kc) {
-                    const float4 m0 =
-                        *reinterpret_cast<const float4 *>(side + 2 * BK + kb + 16 * kc + 8 * h);
-                    const float4 m1 =
-                        *reinterpret_cast<const float4 *>(side + 2 * BK + kb + 16 * kc + 8 * h + 4);
-                    const float mm[8] = {m0.x, m0.y, m0.z, m0.w, m1.x, m1.y, m1.z, m1.w};
-#pragma unroll
-                    for (int e = 0; e < 8; ++e)
-                        x[8 * kc + e] = (mm[e] > 0.0f && row_live) ? x[8 * kc + e] : dead_s;
-                }
-            }
-            const float msub = block_shift();
+        if (!QKZ && masked) {
 #pragma unroll
             for (int kc = 0; kc < 2; ++kc) {
-                float fre[8], fim[8], fm[8];
-                const int s0 = kb + 16 * kc + 8 * h;
+                const float4 m0 =
+                    *reinterpret_cast<const float4 *>(side + 2 * BK + kb + 16 * kc + 8 * h);
+                const float4 m1 =
+                    *reinterpret_cast<const float4 *>(side + 2 * BK + kb + 16 * kc + 8 * h + 4);
+                const float mm[8] = {m0.x, m0.y, m0.z, m0.w, m1.x, m1.y, m1.z, m1.w};
 #pragma unroll
-                for (int e = 0; e < 8; e += 4) {
-                    const float4 a = *reinterpret_cast<const float4 *>(side + s0 + e);
-                    const float4 b = *reinterpret_cast<const float4 *>(side + BK + s0 + e);
-                    const float4 c = *reinterpret_cast<const float4 *>(side + 2 * BK + s0 + e);
-                    fre[e] = a.x; fre[e + 1] = a.y; fre[e + 2] = a.z; fre[e + 3] = a.w;
-                    fim[e] = b.x; fim[e + 1] = b.y; fim[e + 2] = b.z; fim[e + 3] = b.w;
-                    fm[e] = c.x; fm[e + 1] = c.y; fm[e + 2] = c.z; fm[e + 3] = c.w;
-                }
-                weights(buf, kb, kc, msub, fre, fim, fm, !masked, row_live, false);
-                __builtin_amdgcn_sched_barrier(0);  // one chunk's side data at a time
+                for (int e = 0; e < 8; ++e)
+                    x[8 * kc + e] = (mm[e] > 0.0f && row_live) ? x[8 * kc + e] : dead_s;
             }
-        } else {
-            // The side data of the lane's keys (T_re, T_im, R_T; planes BK floats
-            // apart; chunk kc at float 16 kc), the first chunk's requested before
-            // the shift and the second's while the first chunk's weights form, so
-            // that their LDS latency overlaps arithmetic.  (Volatile 16-byte
-            // reads: the compiler would otherwise split them and wait for each.)
-            typedef float v4f __attribute__((ext_vector_type(4)));
-            typedef __attribute__((address_space(3))) const v4f lds_v4f;
-            lds_v4f *sv = (lds_v4f *)(lds_void *)(side + kb + 8 * h);
-#define RD128(r, off) r = __builtin_nontemporal_load(sv + (off) / 16)
-            auto unpack = [](const v4f &a, const v4f &b, float (&o)[8]) __attribute__((always_inline)) {
-                o[0] = a.x; o[1] = a.y; o[2] = a.z; o[3] = a.w;
-                o[4] = b.x; o[5] = b.y; o[6] = b.z; o[7] = b.w;
-            };
-            v4f a0, a1, b0, b1, c0, c1;
-            __builtin_amdgcn_sched_barrier(0);
-            RD128(a0, 0); RD128(a1, 16); RD128(b0, 4 * BK); RD128(b1, 4 * BK + 16); RD128(c0, 8 * BK); RD128(c1, 8 * BK + 16);
-            __builtin_amdgcn_sched_barrier(0);
-            if (!QKZ && masked) {
-                v4f m0, m1;
-                RD128(m0, 8 * BK + 64); RD128(m1, 8 * BK + 80);
-                float fm0[8], fm1[8];
-                unpack(c0, c1, fm0);
-                unpack(m0, m1, fm1);
+        }
+        const float msub = block_shift();
 #pragma unroll
-                for (int e = 0; e < 8; ++e) {
-                    x[e] = (fm0[e] > 0.0f && row_live) ? x[e] : dead_s;
-                    x[8 + e] = (fm1[e] > 0.0f && row_live) ? x[8 + e] : dead_s;
-                }
-            }
-            const float msub = block_shift();
-            __builtin_amdgcn_sched_barrier(0);
+        for (int kc = 0; kc < 2; ++kc) {
             float fre[8], fim[8], fm[8];
-            unpack(a0, a1, fre);
-            unpack(b0, b1, fim);
-            unpack(c0, c1, fm);
-            float ex[8];
+            const int s0 = kb + 16 * kc + 8 * h;
 #pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                if constexpr (QKZ)
-                    ex[e] = (!masked || (fm[e] > 0.0f && row_live)) ? 1.0f : 0.0f;
-                else
-                    ex[e] = __builtin_amdgcn_exp2f(fmaf(x[e], A.c, -msub));
-                z += ex[e] * fm[e];
+            for (int e = 0; e < 8; e += 4) {
+                const float4 a = *reinterpret_cast<const float4 *>(side + s0 + e);
+                const float4 b = *reinterpret_cast<const float4 *>(side + BK + s0 + e);
+                const float4 c = *reinterpret_cast<const float4 *>(side + 2 * BK + s0 + e);
+                fre[e] = a.x; fre[e + 1] = a.y; fre[e + 2] = a.z; fre[e + 3] = a.w;
+                fim[e] = b.x; fim[e + 1] = b.y; fim[e + 2] = b.z; fim[e + 3] = b.w;
+                fm[e] = c.x; fm[e + 1] = c.y; fm[e + 2] = c.z; fm[e + 3] = c.w;
             }
-            __builtin_amdgcn_sched_barrier(0);
-            RD128(a0, 64); RD128(a1, 80); RD128(b0, 4 * BK + 64); RD128(b1, 4 * BK + 80);
-            __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                wk.r[0][e] = (__bf16)(ex[e] * fre[e]);
-                wk.i[0][e] = (__bf16)(ex[e] * fim[e]);
-            }
-            __builtin_amdgcn_sched_barrier(0);
-            RD128(c0, 8 * BK + 64); RD128(c1, 8 * BK + 80);
-            __builtin_amdgcn_sched_barrier(0);
-            unpack(a0, a1, fre);
-            unpack(b0, b1, fim);
-            unpack(c0, c1, fm);
-            weights(buf, kb, 1, msub, fre, fim, fm, !masked, row_live, false);
-            __builtin_amdgcn_sched_barrier(0);
-#undef RD128
+            weights(buf, kb, kc, msub, fre, fim, fm, !masked, row_live, false);
+            __builtin_amdgcn_sched_barrier(0);  // one chunk's side data at a time
         }
     };
     // vector step of a block of the query tile's own keys: explicit G_ij by a
@@ -1382,68 +1103,26 @@ __global__ __launch_bounds__(NTHREADS, 1) void fwd_kernel(FwdArgs A) {
     // latency hides behind the matrix instructions)
     uint32_t kflag = 0;
     // matrix step of block k when blocks k-1 and k both lie before the query
-    // tile (bf16 path: its first operands were requested by m_prefetch_off at
-    // the end of the vector step of block k-1)
-    MPrefetch pf;
-    constexpr int NPRE_OFF = 2;  // fragments of each kind requested early
-    auto m_prefetch_off = [&](int k) __attribute__((always_inline)) {
-        if constexpr (!F32)
-            mstep_prefetch<D, DV, true, !QKZ, 0, NPRE_OFF>(block_buf(k - 1), block_kb(k - 1, true),
-                                                      block_buf(k), block_kb(k, true), qi, h, pf);
-    };
+    // tile
     auto m_step_off = [&](int k) __attribute__((always_inline)) {
         kflag = reinterpret_cast<const uint32_t *>(block_buf(k) + SM::flag_off)[k & 1];
-        if constexpr (!F32) {
-            if (k >= 1)
-                mstep_bf16<D, DV, true, !QKZ, NPRE_OFF>(block_buf(k - 1), block_kb(k - 1, true),
-                                                block_buf(k), block_kb(k, true), qi, h, pf, wk.r,
-                                                wk.i, qf, ore, oim, x);
-            else
-                mstep_bf16<D, DV, false, !QKZ, 0>(block_buf(k), 0, block_buf(k),
-                                                  block_kb(k, true), qi, h, pf, wk.r, wk.i, qf, ore,
-                                                  oim, x);
-        } else if constexpr (!QKZ) {
-            x = s_block<F32, D>(block_buf(k), block_kb(k, true), qi, h, qf);
-        }
+        if constexpr (!QKZ) x = s_block<D>(block_buf(k), block_kb(k, true), qi, h, qf);
     };
     auto m_step = [&](int k) __attribute__((always_inline)) {
-        if constexpr (!F32) {
-            if (k >= 1) {
-                const int kp = k - 1;
-                const bool offp = (kp >> 1) < n_off;
-                if (block_active(kp, offp))
-                    pv_block<F32, D, DV>(block_buf(kp), block_kb(kp, offp), qi, h, wk, ore, oim);
-            }
-        }
         if constexpr (!QKZ) {
             if ((k >> 1) < n_tiles) {
                 const bool off = (k >> 1) < n_off;
-                if (block_active(k, off)) x = s_block<F32, D>(block_buf(k), block_kb(k, off), qi, h, qf);
+                if (block_active(k, off)) x = s_block<D>(block_buf(k), block_kb(k, off), qi, h, qf);
             }
         }
     };
-    // the vector step's results stay in its own phase (the bf16 path's W~ is
-    // first used by the next matrix step, after a barrier)
-    auto settle_weights = [&]() __attribute__((always_inline)) {
-        if constexpr (!F32) {
-            settle(wk.r[0]);
-            settle(wk.r[1]);
-            settle(wk.i[0]);
-            settle(wk.i[1]);
-        }
-        settle(z);
-    };
-    // vector step of block k of a tile before the query tile; block k+1 is
-    // one too when k + 1 < 2 n_off, and its matrix step's first operands are
-    // requested here (the vector step ends well before its partner's matrix
-    // step, so the LDS latency hides in the wait at the barrier).  Block k+1's
-    // tile has landed: the landing of a tile is two phases before the first
-    // vector step that reaches it.
+    // the vector step's results stay in its own phase
+    auto settle_weights = [&]() __attribute__((always_inline)) { settle(z); };
+    // vector step of block k of a tile before the query tile
     auto v_step_off = [&](int k) __attribute__((always_inline)) {
         vstep_off(block_buf(k), block_kb(k, true),
                   wave_dead_rows || __builtin_amdgcn_readfirstlane(kflag) != 0u);
         settle_weights();
-        if (k + 1 < 2 * n_off) m_prefetch_off(k + 1);
     };
     // vector step of block k of the query tile's own tiles
     auto v_step_own = [&](int k) __attribute__((always_inline)) {
@@ -1488,7 +1167,7 @@ __global__ __launch_bounds__(NTHREADS, 1) void fwd_kernel(FwdArgs A) {
         after_v(k);
         lds_barrier();
     }
-    m_step(k);  // the last block's W~ V
+    m_step(k);  // (no block left: keeps the phase count)
     after_m(k);
     lds_barrier();
     if (!lag) lds_barrier();
@@ -1536,13 +1215,14 @@ __global__ __launch_bounds__(NTHREADS, 1) void fwd_kernel(FwdArgs A) {
 
 // --------------------------------------------------------------------------
 // Refusal of an overflowing logit (section "Evaluation and refusals").  The
-// per-head extrema of |q| and |k| that fwd_kernel folded in bound every logit by
-// |c| d max|q| max|k|; only a head where that bound reaches the float32 range
-// recomputes its logits (with the same MFMA code and scale as fwd_kernel) and
-// checks every j <= i.
-template <bool F32, int D>
+// per-head extrema of |q| and |k| that the fused forward folded in bound every
+// logit by |c| d max|q| max|k|; only a head where that bound reaches the
+// float32 range recomputes its logits (with the same MFMA code and scale as
+// the fused forward) and checks every j <= i.  fp32 path; the bf16 path runs
+// logit_check_pad_kernel.
+template <int D>
 __global__ __launch_bounds__(NTHREADS) void logit_check_kernel(FwdArgs A) {
-    using FR = Frag<F32, D>;
+    using FR = Frag<true, D>;
     extern __shared__ __align__(16) unsigned char smem[];
     __shared__ int go;
     const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, h = lane >> 5, qi = lane & 31;
@@ -1561,19 +1241,19 @@ __global__ __launch_bounds__(NTHREADS) void logit_check_kernel(FwdArgs A) {
     const int64_t row = i0 + 32 * w + qi;
     const bool row_ok = row < A.n;
     typename FR::type qf[FR::count];
-    load_q<F32, D>(A, bh, row, row_ok, h, qf);
+    load_q<true, D>(A, bh, row, row_ok, h, qf);
     const unsigned char *kh, *vh;
-    head_bases<F32, D, D>(A, kv_head(A, bh), kh, vh);
+    head_bases<true, D, D>(A, kv_head(A, bh), kh, vh);
     bool bad = false;
     for (int64_t t = 0; t < (i0 + BQ) / BK; ++t) {
         __syncthreads();
-        stage_async<F32, D, D>(A, lds_addr(smem), kh, vh, int(t), true,
+        stage_async<D, D>(A, lds_addr(smem), kh, vh, int(t), true,
                             __builtin_amdgcn_readfirstlane(w));
         __builtin_amdgcn_s_waitcnt(0);
         __syncthreads();
 #pragma unroll
         for (int blk = 0; blk < 2; ++blk) {
-            const f32x16 s = s_block<F32, D>(smem, 32 * blk, qi, h, qf);
+            const f32x16 s = s_block<D>(smem, 32 * blk, qi, h, qf);
             {
 #pragma clang fp contract(off)
 #pragma unroll
@@ -1593,7 +1273,7 @@ __global__ __launch_bounds__(NTHREADS) void logit_check_kernel(FwdArgs A) {
 // 16-byte slots, so every matrix-operand read is a per-lane base plus an
 // immediate offset and a half-wave's rows fall into distinct bank groups),
 // and a phase loop unrolled per key tile, so that the step of each block is
-// fixed at compile time.  Waves 1..7 copy the K and v^T tiles; wave 0 copies
+// fixed at compile time.  Waves 1..7 copy the K and value tiles; wave 0 copies
 // the gate planes and the tile products and lands the tiles.
 template <int D, int DV>
 struct PSmem {
@@ -1629,7 +1309,7 @@ struct PSmem {
 
 // The copies of one wave for one tile when every copying wave issues CPW = 5
 // distinct ones (j = w - 1 + 7 i): the first NK read K rows (base kb), the
-// others v^T rows (base vb); copy i writes at LDS address l0 + 7168 i.  m0 is
+// others value rows (base vb); copy i writes at LDS address l0 + 7168 i.  m0 is
 // saved once, set before each direct global->LDS load (lane L reads base +
 // o[i], writes 16 bytes at m0 + 16 L) and restored at the end.
 #define RESOLVENT_G2LS(v, s, imm) \
@@ -1742,6 +1422,18 @@ __device__ __forceinline__ bf16x8 vread_tr(const unsigned char *p) {
     return __builtin_bit_cast(bf16x8, ab);
 }
 
+// Operand fragments of a matrix step stream through four-deep pipelines (LDS
+// latency under load is a few hundred cycles).
+constexpr int MDEPTH = 4;
+struct MPrefetch {
+    bf16x8 vf[MDEPTH], kf[MDEPTH];
+};
+// Weights W~ of one 32-key block as the B operand of O^T += V^T W~^T, per
+// 16-key chunk kc, packed bf16.
+struct BlockW {
+    bf16x8 r[2], i[2];
+};
+
 // Matrix step on padded tiles: O^T += V^T W~^T for the block whose value rows
 // start at vb (lane part included) at key offset KBV (PV), and S^T = K Q^T for
 // the block at K offset KBS of the K tile at kb (lane part included) (S).
@@ -1846,7 +1538,7 @@ __global__ __launch_bounds__(NTHREADS, 1) void fwd_pad_kernel(FwdArgs A) {
     const uint32_t smem_lds = lds_addr(smem);
     const int n32 = int(A.n);  // n <= 2^22 (checked on the host)
 
-    // ---- copies: waves 1..7 copy K and v^T, CPW instructions each per tile,
+    // ---- copies: waves 1..7 copy K and V, CPW instructions each per tile,
     // with per-lane source offsets computed once; wave 0 copies the three gate
     // planes of the tile's 64 keys (S_j into the raw area for a tile before
     // the query tile, a_{j+1} into the side area for an own tile) and the tile
@@ -2060,7 +1752,7 @@ __global__ __launch_bounds__(NTHREADS, 1) void fwd_pad_kernel(FwdArgs A) {
     f32x16 x;
 #pragma unroll
     for (int r = 0; r < 16; ++r) x[r] = 0.f;
-    BlockW<false> wk;
+    BlockW wk;
     constexpr float dead_s = -INFINITY;
 
     // per-lane parts of the operand and side-data reads
@@ -2356,7 +2048,7 @@ __global__ __launch_bounds__(NTHREADS, 1) void fwd_pad_kernel(FwdArgs A) {
     // before the first block and after a block a wave skips, so that it adds
     // exact zeros) and the scores of its own block (ignored by a wave that
     // skips the block), one instruction sequence for every block: vb below
-    // points at the v^T columns of the previous block.  The first operand
+    // points at the value rows of the previous block.  The first operand
     // fragments of a matrix step are requested at the end of the vector step
     // before it.
     zero_w();
@@ -2417,7 +2109,7 @@ __global__ __launch_bounds__(NTHREADS, 1) void fwd_pad_kernel(FwdArgs A) {
         z *= prow_m;
     }
     // until a wave's first active block its W~ is zero and the W~ V of the
-    // step before that block reads the first own tile's v^T (never rewritten)
+    // step before that block reads the first own tile's values (never rewritten)
     zero_w();
     vprev = tile_buf(m) + vlane;
     for (int mm = 0; mm < NDIAG; ++mm, ++m) {
@@ -2578,7 +2270,6 @@ GatesArgs gates_args(const Layout &L, const float *u, const float *theta, double
 
 template <bool F32, int D, int DV>
 int launch_typed(const Problem &P, hipStream_t st, hipEvent_t const *marks) {
-    using SM = Smem<F32, D, DV>;
     const Layout &L = P.L;
     unsigned char *ws = P.ws;
     uint32_t *counters = reinterpret_cast<uint32_t *>(ws + L.counters);
@@ -2647,25 +2338,25 @@ int launch_typed(const Problem &P, hipStream_t st, hipEvent_t const *marks) {
     F.beta_mode = P.beta_mode;
     F.qk_zero = P.qk_zero ? 1 : 0;
     if constexpr (F32) {
-        const size_t shm = SM::bytes;
+        const size_t shm = Smem<D, DV>::bytes;
         if (shm > 65536) {
-            (void)hipFuncSetAttribute(reinterpret_cast<const void *>(&fwd_kernel<F32, D, DV, false>),
+            (void)hipFuncSetAttribute(reinterpret_cast<const void *>(&fwd_kernel<D, DV, false>),
                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)shm);
-            (void)hipFuncSetAttribute(reinterpret_cast<const void *>(&fwd_kernel<F32, D, DV, true>),
+            (void)hipFuncSetAttribute(reinterpret_cast<const void *>(&fwd_kernel<D, DV, true>),
                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)shm);
-            (void)hipFuncSetAttribute(reinterpret_cast<const void *>(&logit_check_kernel<F32, D>),
+            (void)hipFuncSetAttribute(reinterpret_cast<const void *>(&logit_check_kernel<D>),
                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)shm);
         }
         if (marks) (void)hipEventRecord(marks[1], st);
         if (P.qk_zero)
-            hipLaunchKernelGGL((fwd_kernel<F32, D, DV, true>), dim3(BH * L.n_qt), dim3(NTHREADS),
+            hipLaunchKernelGGL((fwd_kernel<D, DV, true>), dim3(BH * L.n_qt), dim3(NTHREADS),
                                shm, st, F);
         else
-            hipLaunchKernelGGL((fwd_kernel<F32, D, DV, false>), dim3(BH * L.n_qt), dim3(NTHREADS),
+            hipLaunchKernelGGL((fwd_kernel<D, DV, false>), dim3(BH * L.n_qt), dim3(NTHREADS),
                                shm, st, F);
         if (marks) (void)hipEventRecord(marks[2], st);
         if (!P.qk_zero)
-            hipLaunchKernelGGL((logit_check_kernel<F32, D>), dim3(BH * L.n_qt), dim3(NTHREADS),
+            hipLaunchKernelGGL((logit_check_kernel<D>), dim3(BH * L.n_qt), dim3(NTHREADS),
                                shm, st, F);
     } else {
         const size_t shm = PSmem<D, DV>::bytes;

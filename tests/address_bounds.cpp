@@ -1,5 +1,5 @@
 // Host check of the fused kernel's direct global->LDS copies: every source
-// range that a workgroup can ask for lies inside its tensor (K, V, v^T) or
+// range that a workgroup can ask for lies inside its tensor (K, V) or
 // inside the workspace (the gate planes).  It walks
 // every key tile of every shape given on the command line (all tiles a
 // workgroup of any query tile stages, the logit check included), every row
@@ -132,85 +132,6 @@ static int check(int64_t B, int64_t H, int64_t n, int64_t d, int esz, bool bf16_
                     std::printf("tile product out of range: n=%lld t=%lld lane=%d\n",
                                 (long long)n, (long long)t, lane);
             }
-    return bad;
-}
-
-// The swizzled bf16 tile layout with CPR chunks per row (K: CPR = d/8;
-// v^T: CPR = 8), independent of the shape.
-template <int CPR>
-static int check_tile_layout(const char *what) {
-    int bad = 0;
-    // copies: instruction j, lane -> LDS offset 1024 j + 16 lane holds chunk
-    // copy_chunk of row copy_row.  CPR 16: the K tile of d = 128 (64 rows);
-    // CPR 8: the v^T tile of d = 128 (128 rows; its first 64 are the K tile of
-    // d = 64 and the v^T tile of d = 64).
-    const int rows = (CPR == 16) ? 64 : 128;
-    std::vector<int> seen(size_t(rows) * CPR, 0);
-    for (int j = 0; j < rows * CPR / 64; ++j)
-        for (int lane = 0; lane < 64; ++lane) {
-            const int r = copy_row<CPR>(j, lane), c = copy_chunk<CPR>(j, lane);
-            if (r < 0 || r >= rows || c < 0 || c >= CPR) {
-                if (bad++ < 5) std::printf("%s: copy j=%d lane=%d out of tile\n", what, j, lane);
-                continue;
-            }
-            ++seen[size_t(r) * CPR + c];
-            if (tile_chunk_off<CPR>(r, c) != 1024 * j + 16 * lane && bad++ < 5)
-                std::printf("%s: chunk (%d,%d) copied to %d, read at %d\n", what, r, c,
-                            1024 * j + 16 * lane, tile_chunk_off<CPR>(r, c));
-        }
-    for (size_t i = 0; i < seen.size(); ++i)
-        if (seen[i] != 1 && bad++ < 5)
-            std::printf("%s: (row %zu, chunk %zu) copied %d times\n", what, i / CPR, i % CPR,
-                        seen[i]);
-    return bad;
-}
-
-// Operand reads of the bf16 matrix steps: lane (qi, h), step s reads chunk
-// 2s+h of K row kb+qi; PV reads chunk kb/8+2kc+h of v^T row 32db+qi.
-template <int CPR>
-static int check_operand_reads() {
-    int bad = 0;
-    for (int kb = 0; kb < 64; kb += 32)
-        for (int s = 0; s < CPR / 2; ++s)
-            for (int g = 0; g < 4; ++g) {  // 16-lane groups: (h, qi / 16)
-                const int h = g >> 1;
-                unsigned used = 0;
-                for (int q = 0; q < 16; ++q) {
-                    const int qi = 16 * (g & 1) + q;
-                    const int off = kfrag_base<CPR>(kb, qi, h) ^ (32 * s);
-                    if (off != tile_chunk_off<CPR>(kb + qi, 2 * s + h) && bad++ < 5)
-                        std::printf("K read (kb %d s %d qi %d h %d) at %d, chunk at %d\n", kb, s,
-                                    qi, h, off, tile_chunk_off<CPR>(kb + qi, 2 * s + h));
-                    used |= 1u << ((off % 256) / 16);
-                }
-                if (used != 0xFFFFu && bad++ < 5)
-                    std::printf("K read (CPR %d kb %d s %d group %d): bank groups %04x\n", CPR, kb,
-                                s, g, used);
-            }
-    return bad;
-}
-
-static int check_v_reads(int d) {
-    int bad = 0;
-    for (int kb = 0; kb < 64; kb += 32)
-        for (int kc = 0; kc < 2; ++kc)
-            for (int db = 0; db < d / 32; ++db)
-                for (int g = 0; g < 4; ++g) {
-                    const int h = g >> 1;
-                    unsigned used = 0;
-                    for (int q = 0; q < 16; ++q) {
-                        const int qi = 16 * (g & 1) + q;
-                        const int off = 4096 * db + (vfrag_base(qi, h) ^ (2 * kb + 32 * kc));
-                        const int want = tile_chunk_off<8>(32 * db + qi, kb / 8 + 2 * kc + h);
-                        if (off != want && bad++ < 5)
-                            std::printf("v^T read (kb %d kc %d db %d qi %d h %d) at %d, chunk at %d\n",
-                                        kb, kc, db, qi, h, off, want);
-                        used |= 1u << ((off % 256) / 16);
-                    }
-                    if (used != 0xFFFFu && bad++ < 5)
-                        std::printf("v^T read (kb %d kc %d db %d group %d): bank groups %04x\n", kb,
-                                    kc, db, g, used);
-                }
     return bad;
 }
 
@@ -531,16 +452,13 @@ static int check_chain(int64_t B, int64_t H, int64_t n, int64_t dv, int esz) {
 int main(int argc, char **argv) {
     int bad = check_pad_layout<128, 128>() + check_pad_layout<128, 64>() +
               check_pad_layout<64, 128>() + check_pad_layout<64, 64>();
-    bad += check_tile_layout<16>("K d=128") + check_tile_layout<8>("K d=64 / v^T") +
-              check_operand_reads<16>() + check_operand_reads<8>() + check_v_reads(64) +
-              check_v_reads(128);
     int cases = 0;
     for (int a = 1; a + 3 < argc; a += 4) {
         const int64_t B = std::atoll(argv[a]), H = std::atoll(argv[a + 1]);
         const int64_t n = std::atoll(argv[a + 2]), d = std::atoll(argv[a + 3]);
         for (int64_t dv = 64; dv <= 128; dv += 64)
             for (int64_t Hkv : {H, int64_t(1)}) {
-                bad += check(B, H, n, d, 2, true, Hkv, dv);   // bf16 q, k; bf16 v^T copy
+                bad += check(B, H, n, d, 2, true, Hkv, dv);   // bf16 q, k, v
                 bad += check(B, H, n, d, 4, false, Hkv, dv);  // fp32 q, k, v
                 if (H % Hkv == 0 && n <= 40000) {
                     bad += check_decode(B, H, Hkv, n, n, d, dv, 2, 2);
