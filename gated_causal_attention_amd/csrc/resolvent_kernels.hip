@@ -1272,9 +1272,10 @@ __global__ __launch_bounds__(NTHREADS) void logit_check_kernel(FwdArgs A) {
 // Fused forward, bf16 path: padded tiles (row strides of an odd number of
 // 16-byte slots, so every matrix-operand read is a per-lane base plus an
 // immediate offset and a half-wave's rows fall into distinct bank groups),
-// and a phase loop unrolled per key tile, so that the step of each block is
-// fixed at compile time.  Waves 1..7 copy the K and value tiles; wave 0 copies
-// the gate planes and the tile products and lands the tiles.
+// and a loop unrolled per key tile, so that the step of each block is fixed
+// at compile time, with one workgroup barrier per key tile.  Waves 1..7 copy
+// the K and value tiles; wave 0 copies the gate planes and the tile products
+// and lands the tiles.
 template <int D, int DV>
 struct PSmem {
     static constexpr int KSL = pad_kslots<D>();
@@ -2037,63 +2038,61 @@ __global__ __launch_bounds__(NTHREADS, 1) void fwd_pad_kernel(FwdArgs A) {
                 wk.i[kc][e] = (__bf16)0.0f;
             }
     };
-    // ---- the phases.  Block k has its matrix step in phase 2k + lag and its
-    // vector step in phase 2k + 1 + lag; a barrier ends every phase.  Tile m
-    // holds blocks 2m and 2m+1.  Every wave issues its copies of tile m+2
-    // after its matrix step of block 2m and waits for its copies of tile m+1
-    // in phase 4m+2 (the leading waves after their matrix step of block 2m+1,
-    // where wave 0 also lands the tile; the trailing ones after their vector
-    // step of block 2m), so that the barrier closing phase 4m+2 publishes
-    // tile m+1.  Every matrix step runs the W~ V of the block before it (W~ = 0
-    // before the first block and after a block a wave skips, so that it adds
-    // exact zeros) and the scores of its own block (ignored by a wave that
-    // skips the block), one instruction sequence for every block: vb below
-    // points at the value rows of the previous block.  The first operand
-    // fragments of a matrix step are requested at the end of the vector step
-    // before it.
+    // ---- the key tiles before the query tile.  Tile m holds blocks 2m and
+    // 2m+1.  Every wave runs its steps back to back, with one barrier per
+    // tile: the leading waves (0..3) run M(2m) V(2m) M(2m+1) V(2m+1) before
+    // it, the trailing ones (4..7) run V(2m+1) after it, so that the two
+    // waves of a SIMD stay one step apart and alternate between matrix and
+    // vector work.  Every wave issues its copies of tile m+2 after its matrix
+    // step of block 2m (into the buffer of tile m-2, which every wave has
+    // finished before the barrier closing tile m-1) and waits for its copies
+    // of tile m+1 after its matrix step of block 2m+1, where wave 0 also lands
+    // tile m+1; the barrier closing tile m publishes it.  The K fragments of
+    // tile m+1 are therefore requested after that barrier (the leading waves
+    // at the start of the next tile), the value fragments of the block before
+    // at the end of the vector step.  Every matrix step runs the W~ V of the
+    // block before it (W~ = 0 before the first block and after a block a wave
+    // skips, so that it adds exact zeros) and the scores of its own block
+    // (ignored by a wave that skips the block), one instruction sequence for
+    // every block: vprev points at the value rows of the previous block.
     zero_w();
     const unsigned char *vprev = tile_buf(0) + vlane;
     if (n_off > 0)
         pstep_prefetch<D, DV, 0, 0, true, !QKZ, 0, NPRE>(vprev, tile_buf(0) + klane, pf);
-    if (lag) lds_barrier();
     int m = 0;
     for (; m < n_off; ++m) {
         const unsigned char *bufm = tile_buf(m);
         const unsigned char *kb_ = bufm + klane;
         const unsigned char *vb_ = bufm + vlane;
+        if (m > 0 && !lag) pstep_prefetch<D, DV, 0, 0, false, !QKZ, 0, NPRE>(vprev, kb_, pf);
         // block 2m (keys 0..31 of tile m)
         const uint32_t kflag0 = flag_of(bufm, 0);
         pstep<D, DV, 0, 0, true, !QKZ, NPRE>(vprev, kb_, pf, wk.r, wk.i, qf, ore, oim, x);
         issue(m + 2);
-        lds_barrier();
         vstep_off(bufm + slane, 0, wave_dead_rows || __builtin_amdgcn_readfirstlane(kflag0) != 0u);
         settle_weights();
         pstep_prefetch<D, DV, 0, 32, true, !QKZ, 0, NPRE>(vb_, kb_, pf);
-        if (lag) land_wait(m);
-        lds_barrier();
         // block 2m+1 (keys 32..63)
         const uint32_t kflag1 = flag_of(bufm, 1);
         pstep<D, DV, 0, 32, true, !QKZ, NPRE>(vb_, kb_, pf, wk.r, wk.i, qf, ore, oim, x);
-        if (!lag) land_wait(m);
-        lds_barrier();
+        vprev = vb_ + 32 * VSTR;
+        land_wait(m);
+        if (lag) lds_barrier();
         vstep_off(bufm + slane, 32, wave_dead_rows || __builtin_amdgcn_readfirstlane(kflag1) != 0u);
         settle_weights();
-        vprev = vb_ + 32 * VSTR;
-        if (m + 1 < n_off)
+        if (lag && m + 1 < n_off)
             pstep_prefetch<D, DV, 0, 0, true, !QKZ, 0, NPRE>(vprev, tile_buf(m + 1) + klane, pf);
         else
             pstep_prefetch<D, DV, 0, 0, true, false, 0, NPRE>(vprev, vprev, pf);
-        lds_barrier();
+        if (!lag) lds_barrier();
     }
     // ---- the query tile's own tiles: blocks visited highest keys first
     // (keys 32..63 of a tile, then 0..31); the block of visit index kk of the
-    // NDB is active for wave w when kk >= NDB-1-w.  Once the trailing waves
-    // have finished the last vector step before the query tile, every wave
-    // runs its active blocks back to back, without a barrier between steps:
-    // no buffer is written while a tile's blocks run (the copies of the tile
-    // two ahead go to a buffer every wave has finished), and one barrier per
-    // own tile publishes the next one, landed by the copy waits before it.
-    if (!lag) lds_barrier();
+    // NDB is active for wave w when kk >= NDB-1-w.  Every wave runs its active
+    // blocks back to back: no buffer is written while a tile's blocks run
+    // (the copies of the tile two ahead go to a buffer every wave has
+    // finished), and one barrier per own tile publishes the next one, landed
+    // by the copy waits before it.
     if (n_off > 0) {
         // the W~ V of the last block before the query tile; then the blocks
         // before the query tile are in O: rotate by P_i
