@@ -36,7 +36,8 @@ struct Layout {
     size_t qstat = 0, kstat = 0;  // per head max |q|, max |k| bits (uint32 [BH])
     size_t noff = 0;  // per query tile: key tiles before it that the forward visits (int32 [BH][n_qt])
     size_t gbad = 0;  // per query tile: 1 if its gates saw a refused input (int32 [BH][n_qt])
-    size_t counters = 0;  // uint32 [2]: key tiles processed before the query tiles; spare
+    size_t counters = 0;  // uint32 [16]: key tiles processed before the query tiles; spare;
+                          // [8..15] the bf16 forward's work queues
     size_t v16 = 0;       // bf16 path, fp32 values only: v rounded to bf16 (bf16 [BHkv][n][dv])
     size_t total = 0;
 };
@@ -81,7 +82,7 @@ inline Layout make_layout(int64_t B, int64_t H, int64_t n, int64_t d, bool bf16_
     L.gbad = off;
     off = align_up(off + per_qt, 256);
     L.counters = off;
-    off = align_up(off + 2 * sizeof(uint32_t), 256);
+    off = align_up(off + 16 * sizeof(uint32_t), 256);
     L.v16 = off;
     if (bf16_path && v_f32) off = align_up(off + 2 * size_t(L.BHkv) * size_t(L.n) * size_t(L.dv), 256);
     L.total = off;
@@ -195,6 +196,27 @@ RESOLVENT_HD inline uint32_t tile_row_off(int64_t n, int64_t t, int r, int64_t r
     int64_t key = t * BK + r;
     key = key < n ? key : n - 1;
     return uint32_t(key * row_bytes);
+}
+
+// Work queues of the bf16 forward: queue x (of nq, nq dividing BH) holds the
+// query tiles of heads x, x + nq, x + 2 nq, ..., hx = BH / nq heads with n_qt
+// query tiles each.  Entry k of the queue is the query tile bh * n_qt + qt
+// (-1 past the queue's end): order 0 takes the heaviest query tile (the last)
+// of every head of the queue first, then the next ones; order 1 takes one
+// head at a time, heaviest query tile first.
+RESOLVENT_HD inline int64_t queue_item(int x, uint32_t k, int nq, int64_t BH, int64_t n_qt,
+                                       int order) {
+    const int64_t hx = BH / nq;
+    if (int64_t(k) >= hx * n_qt) return -1;
+    int64_t hj, qt;
+    if (order == 0) {
+        hj = int64_t(k) % hx;
+        qt = n_qt - 1 - int64_t(k) / hx;
+    } else {
+        hj = int64_t(k) / n_qt;
+        qt = n_qt - 1 - int64_t(k) % n_qt;
+    }
+    return (x + nq * hj) * n_qt + qt;
 }
 
 // Padded bf16 tiles of the fused forward (bf16 path).  A K row of d bf16

@@ -30,6 +30,8 @@
 //                                    heads whose |q|,|k| extrema allow one
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
+#include <atomic>
 #include <cmath>
 #include <cstdint>
 #include <type_traits>
@@ -271,7 +273,7 @@ __global__ __launch_bounds__(256) void prep_kernel(GatesArgs G, int ngb, int32_t
                                                    uint32_t *__restrict__ counters) {
     const int tid = threadIdx.x;
     if (blockIdx.x == 0 && tid == 0) G.status[0] = 0;
-    if (blockIdx.x == 0 && tid < 2) counters[tid] = 0;
+    if (blockIdx.x == 0 && tid < 16) counters[tid] = 0;
     if ((int)blockIdx.x < ngb) {
         const int64_t tq = 4 * int64_t(blockIdx.x) + (tid >> 6);  // query tile, all heads
         if (tq < G.BH * G.n_qt) {
@@ -296,6 +298,8 @@ struct FwdArgs {
     int64_t plane;
     float *o_re, *o_im;
     uint32_t *qstat, *kstat, *counters;
+    uint32_t *queues;  // bf16 path: the work queues' counters (cleared by prep_kernel)
+    int nq, order;     // number of queues (1 or 8), item order inside a queue (queue_item)
     const int32_t *noff;
     int32_t *status;
     int64_t n, n_pad;
@@ -306,7 +310,9 @@ struct FwdArgs {
 };
 
 // The k/v head that query head bh (= b H + h) reads: b H/group + h/group.
-__device__ __forceinline__ int64_t kv_head(const FwdArgs &A, int64_t bh) {
+// (Args: FwdArgs, or FwdArgs read in place from the argument segment.)
+template <typename Args>
+__device__ __forceinline__ int64_t kv_head(const Args &A, int64_t bh) {
     return (bh / A.H) * (A.H / A.group) + (bh % A.H) / A.group;
 }
 
@@ -462,8 +468,8 @@ __device__ __forceinline__ void lds_barrier() {
 
 // Query fragment (B operand of S^T = K Q^T) for the lane's row; returns the
 // largest |q| as float bits.
-template <bool F32, int D>
-__device__ __forceinline__ uint32_t load_q(const FwdArgs &A, int64_t bh, int64_t row, bool row_ok,
+template <bool F32, int D, typename Args>
+__device__ __forceinline__ uint32_t load_q(const Args &A, int64_t bh, int64_t row, bool row_ok,
                                            int h, typename Frag<F32, D>::type (&qf)[Frag<F32, D>::count]) {
     uint32_t bits = 0;
     if constexpr (!F32) {
@@ -520,8 +526,8 @@ __device__ __forceinline__ void stage_async(const FwdArgs &A, uint32_t buf,
 
 // Bases of the tile copies for k/v head kvh (wave-uniform): its rows of k,
 // and of the bf16 values (bf16 path) or v (fp32 path).
-template <bool F32, int D, int DV>
-__device__ __forceinline__ void head_bases(const FwdArgs &A, int64_t kvh,
+template <bool F32, int D, int DV, typename Args>
+__device__ __forceinline__ void head_bases(const Args &A, int64_t kvh,
                                            const unsigned char *&kh, const unsigned char *&vh) {
     constexpr int64_t ROWB = D * (F32 ? 4 : 2);
     kh = uniform_ptr(static_cast<const unsigned char *>(A.k) + kvh * A.n * ROWB);
@@ -1490,8 +1496,8 @@ __device__ __forceinline__ void pstep(const unsigned char *vb, const unsigned ch
     __builtin_amdgcn_sched_barrier(0);
 }
 
-template <int D, int DV, bool QKZ>
-__global__ __launch_bounds__(NTHREADS, 1) void fwd_pad_kernel(FwdArgs A) {
+template <int D, int DV, bool QKZ, typename Args>
+__device__ __forceinline__ void fwd_pad_item(const Args &A, int64_t bh, int64_t qt) {
     using SM = PSmem<D, DV>;
     constexpr int NBUF = SM::NBUF;
     constexpr int NDIAG = BQ / BK;  // key tiles inside the query tile
@@ -1500,23 +1506,11 @@ __global__ __launch_bounds__(NTHREADS, 1) void fwd_pad_kernel(FwdArgs A) {
     constexpr int KROW = SM::KROW, VSTR = SM::VSTR;
     extern __shared__ __align__(16) unsigned char smem[];
     uint32_t *misc = reinterpret_cast<uint32_t *>(smem + SM::misc_off);
-    // misc[2]: largest |q|; misc[3]: largest |k|
+    // misc[2]: largest |q|; misc[3]: largest |k|; misc[4]: the work item
 
     const int tid = threadIdx.x, lane = tid & 63, h = lane >> 5, qi = lane & 31;
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int lag = w / (NWAVES / 2);  // 0: leading waves, 1: trailing waves
-    // work item (as fwd_kernel): round-robin over the XCDs, one head at a
-    // time per XCD when the heads split evenly, heaviest query tile first
-    const int L = blockIdx.x;
-    int64_t qt, bh;
-    if ((A.BH & 7) == 0) {
-        const int x = L & 7, j = L >> 3;
-        bh = x + 8 * (j / A.n_qt);
-        qt = A.n_qt - 1 - (j % A.n_qt);
-    } else {
-        qt = A.n_qt - 1 - L / A.BH;
-        bh = L % A.BH;
-    }
     const int64_t i0 = qt * BQ;
     const int64_t row = i0 + 32 * w + qi;
     const bool row_ok = row < A.n;
@@ -1526,7 +1520,7 @@ __global__ __launch_bounds__(NTHREADS, 1) void fwd_pad_kernel(FwdArgs A) {
     const int n_tiles = n_off + NDIAG;
     const unsigned char *kh, *vh;
     head_bases<false, D, DV>(A, kv_head(A, bh), kh, vh);
-    if (tid == 0) {
+    if (w == 0) {  // whole wave: no divergent branch in the workgroup's loop
         misc[2] = 0;
         misc[3] = 0;
     }
@@ -1659,12 +1653,12 @@ __global__ __launch_bounds__(NTHREADS, 1) void fwd_pad_kernel(FwdArgs A) {
                     ni = ar * c_im + ai * c_re;
                     nm = am * c_m;
                 }
-                if (ln == 0) {
-                    cst[0] = nr;
-                    cst[1] = ni;
-                    cst[2] = nm;
-                    *reinterpret_cast<uint64_t *>(buf + SM::flag_off) = dead;
-                }
+                // (every lane holds the same values and writes them: no
+                // divergent branch in the workgroup's loop)
+                cst[0] = nr;
+                cst[1] = ni;
+                cst[2] = nm;
+                *reinterpret_cast<uint64_t *>(buf + SM::flag_off) = dead;
             }
         } else if (w == 0) {
             // an own tile: the inclusive suffix products of its gate factors
@@ -2168,12 +2162,63 @@ __global__ __launch_bounds__(NTHREADS, 1) void fwd_pad_kernel(FwdArgs A) {
             }
     }
     __syncthreads();
-    if (tid == 0) {
-        const uint32_t qb = misc[2], kb = misc[3];
+    if (w == 0) {  // whole wave (the maxima are idempotent; lane 0 counts)
+        const uint32_t qb = __builtin_amdgcn_readfirstlane(misc[2]);
+        const uint32_t kb = __builtin_amdgcn_readfirstlane(misc[3]);
         atomicMax(&A.qstat[bh], qb);
         atomicMax(&A.kstat[bh], kb);
         if (qb >= kInfBits || kb >= kInfBits) A.status[0] = kNonFinite;
-        atomicAdd(&A.counters[0], uint32_t(n_off));
+        atomicAdd(&A.counters[0], lane == 0 ? uint32_t(n_off) : 0u);
+    }
+}
+
+// The next work item of a workgroup whose home queue is `home` (the query
+// tile bh * n_qt + qt, queue_item), or -1 when every queue is empty: a
+// workgroup takes items from its home queue and, once that is empty, from the
+// others in turn.  Called by every lane of one wave, with
+// no divergent branch: lane 0 adds 1 to the queue's counter and the other
+// lanes 0, and every lane takes lane 0's result.  (A branch on the thread
+// index here, inside the workgroup's loop, let the compiler run the lanes of
+// the fetching wave through different loop paths with different barrier
+// sequences.)
+__device__ __forceinline__ int next_item(const FwdArgs &A, int home) {
+    const uint32_t inc = (threadIdx.x & 63) == 0 ? 1u : 0u;
+    for (int i = 0; i < A.nq; ++i) {
+        const int x = home + i < A.nq ? home + i : home + i - A.nq;
+        const uint32_t k = __builtin_amdgcn_readfirstlane(atomicAdd(&A.queues[x], inc));
+        const int64_t it = queue_item(x, k, A.nq, A.BH, A.n_qt, A.order);
+        if (it >= 0) return int(it);
+    }
+    return -1;
+}
+
+// Fused forward, bf16 path: one workgroup per compute unit (the grid is at
+// most the number of compute units), each taking query tiles from the work
+// queues until they are empty.  Workgroup g starts on queue g mod nq: with
+// nq = 8, the XCD that round-robin placement puts it on.
+template <int D, int DV, bool QKZ>
+__global__ __launch_bounds__(NTHREADS, 1) void fwd_pad_kernel(FwdArgs A) {
+    using SM = PSmem<D, DV>;
+    extern __shared__ __align__(16) unsigned char smem[];
+    uint32_t *misc = reinterpret_cast<uint32_t *>(smem + SM::misc_off);
+    const int home = int(blockIdx.x) % A.nq;
+    const int w = __builtin_amdgcn_readfirstlane(int(threadIdx.x) >> 6);
+    typedef __attribute__((address_space(4))) const FwdArgs cfwd;
+    // Every branch in this loop is uniform across each wave (wave 0 fetches
+    // with all its lanes, and the item body's per-item bookkeeping runs in
+    // whole waves too), so that every wave passes the same barriers.
+    for (;;) {
+        if (w == 0) misc[4] = uint32_t(next_item(A, home));  // every lane, one value
+        __syncthreads();
+        const int it = __builtin_amdgcn_readfirstlane(int(misc[4]));
+        if (it < 0) break;
+        // the arguments are read afresh for every item, from the kernel's
+        // argument segment (A is its only argument) through a pointer the
+        // compiler cannot prove loop-invariant, instead of held in registers
+        // across the loop
+        cfwd *ap = (cfwd *)__builtin_amdgcn_kernarg_segment_ptr();
+        asm volatile("" : "+s"(ap));
+        fwd_pad_item<D, DV, QKZ>(*ap, it / A.n_qt, it % A.n_qt);
     }
 }
 
@@ -2267,6 +2312,21 @@ GatesArgs gates_args(const Layout &L, const float *u, const float *theta, double
     return G;
 }
 
+// Compute units of the current device, looked up once per device.
+int compute_units() {
+    static std::atomic<int> cache[64];
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+    int c = cache[dev].load(std::memory_order_relaxed);
+    if (c <= 0) {
+        if (hipDeviceGetAttribute(&c, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+            c <= 0)
+            c = 256;
+        cache[dev].store(c, std::memory_order_relaxed);
+    }
+    return c;
+}
+
 template <bool F32, int D, int DV>
 int launch_typed(const Problem &P, hipStream_t st, hipEvent_t const *marks) {
     const Layout &L = P.L;
@@ -2322,6 +2382,13 @@ int launch_typed(const Problem &P, hipStream_t st, hipEvent_t const *marks) {
     F.qstat = reinterpret_cast<uint32_t *>(ws + L.qstat);
     F.kstat = reinterpret_cast<uint32_t *>(ws + L.kstat);
     F.counters = counters;
+    F.queues = counters + 8;
+    F.nq = (BH & 7) == 0 ? 8 : 1;
+    // one head at a time per queue: the 32 compute units of an XCD then read
+    // one head's keys and values, which its L2 holds (heaviest query tile
+    // first across the queue's heads balances the end better but reads more
+    // from HBM: 5% slower at B=4 H=16 n=8192)
+    F.order = 1;
     F.noff = noff;
     F.status = P.status;
     F.n = L.n;
@@ -2368,12 +2435,15 @@ int launch_typed(const Problem &P, hipStream_t st, hipEvent_t const *marks) {
                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)shm);
         }
         if (marks) (void)hipEventRecord(marks[1], st);
+        // one workgroup per compute unit (fewer when there are fewer query tiles)
+        const int64_t items = int64_t(BH) * L.n_qt;
+        const unsigned grid = (unsigned)std::min<int64_t>(items, compute_units());
         if (P.qk_zero)
-            hipLaunchKernelGGL((fwd_pad_kernel<D, DV, true>), dim3(BH * L.n_qt), dim3(NTHREADS),
-                               shm, st, F);
+            hipLaunchKernelGGL((fwd_pad_kernel<D, DV, true>), dim3(grid), dim3(NTHREADS), shm, st,
+                               F);
         else
-            hipLaunchKernelGGL((fwd_pad_kernel<D, DV, false>), dim3(BH * L.n_qt), dim3(NTHREADS),
-                               shm, st, F);
+            hipLaunchKernelGGL((fwd_pad_kernel<D, DV, false>), dim3(grid), dim3(NTHREADS), shm,
+                               st, F);
         if (marks) (void)hipEventRecord(marks[2], st);
         if (!P.qk_zero)
             hipLaunchKernelGGL((logit_check_pad_kernel<D>), dim3(BH * L.n_qt), dim3(NTHREADS),

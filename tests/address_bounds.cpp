@@ -449,6 +449,48 @@ static int check_chain(int64_t B, int64_t H, int64_t n, int64_t dv, int esz) {
     return bad;
 }
 
+// The work queues of the bf16 forward (queue_item): for either item order
+// and either queue count, the entries of all queues up to their ends are
+// every query tile exactly once, heaviest first inside a queue under order 0,
+// and the first entry past a queue's end is -1.
+static int check_queues(int64_t B, int64_t H, int64_t n) {
+    const Layout L = make_layout(B, H, n, 64, true);
+    const int64_t BH = L.BH, n_qt = L.n_qt;
+    int bad = 0;
+    for (int nq : {1, 8}) {
+        if (BH % nq != 0) continue;
+        for (int order = 0; order < 2; ++order) {
+            std::vector<int> seen(size_t(BH * n_qt), 0);
+            for (int x = 0; x < nq; ++x) {
+                int64_t prev_qt = n_qt;
+                for (uint32_t k = 0;; ++k) {
+                    const int64_t it = queue_item(x, k, nq, BH, n_qt, order);
+                    if (it < 0) {
+                        if (int64_t(k) != BH / nq * n_qt && bad++ < 5)
+                            std::printf("queue %d of %d ends at %u\n", x, nq, k);
+                        break;
+                    }
+                    if ((it >= BH * n_qt || (it / n_qt) % nq != x) && bad++ < 5) {
+                        std::printf("queue %d entry %u: item %lld\n", x, k, (long long)it);
+                        break;
+                    }
+                    ++seen[size_t(it)];
+                    if (order == 0) {
+                        if (it % n_qt > prev_qt && bad++ < 5)
+                            std::printf("queue %d entry %u not heaviest first\n", x, k);
+                        prev_qt = it % n_qt;
+                    }
+                }
+            }
+            for (int64_t i = 0; i < BH * n_qt; ++i)
+                if (seen[size_t(i)] != 1 && bad++ < 5)
+                    std::printf("query tile %lld queued %d times (nq %d order %d)\n",
+                                (long long)i, seen[size_t(i)], nq, order);
+        }
+    }
+    return bad;
+}
+
 int main(int argc, char **argv) {
     int bad = check_pad_layout<128, 128>() + check_pad_layout<128, 64>() +
               check_pad_layout<64, 128>() + check_pad_layout<64, 64>();
@@ -470,6 +512,7 @@ int main(int argc, char **argv) {
             bad += check_chain(B, H, n, cdv, 2);
             if (cdv <= 128) bad += check_chain(B, H, n, cdv, 4);
         }
+        bad += check_queues(B, H, n);
         if (n <= 1100) {
             bad += check_exports(B, H, n, d, 2);
             bad += check_exports(B, H, n, d, 4);

@@ -17,6 +17,7 @@ def test_tile_copies_stay_in_bounds(tmp_path):
         for d in (64, 128):
             shapes += [2, 2, n, d]
     shapes += [1, 1, 8192, 128, 1, 1, 32768, 128]
+    shapes += [2, 8, 1000, 64]  # 16 heads: eight work queues of the bf16 forward
     shapes += [1, 1, 1 << 22, 128]  # the longest sequence the boundary accepts
     out = subprocess.run([exe, *map(str, shapes)], capture_output=True, text=True)
     print(out.stdout)
