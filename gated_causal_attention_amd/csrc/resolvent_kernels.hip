@@ -1496,8 +1496,29 @@ __device__ __forceinline__ void pstep(const unsigned char *vb, const unsigned ch
     __builtin_amdgcn_sched_barrier(0);
 }
 
+// The next work item of a workgroup whose home queue is `home` (the query
+// tile bh * n_qt + qt, queue_item), or -1 when every queue is empty: a
+// workgroup takes items from its home queue and, once that is empty, from the
+// others in turn.  Called by every lane of one wave, with
+// no divergent branch: lane 0 adds 1 to the queue's counter and the other
+// lanes 0, and every lane takes lane 0's result.  (A branch on the thread
+// index here, inside the workgroup's loop, let the compiler run the lanes of
+// the fetching wave through different loop paths with different barrier
+// sequences.)
+template <typename Args>
+__device__ __forceinline__ int next_item(const Args &A, int home) {
+    const uint32_t inc = (threadIdx.x & 63) == 0 ? 1u : 0u;
+    for (int i = 0; i < A.nq; ++i) {
+        const int x = home + i < A.nq ? home + i : home + i - A.nq;
+        const uint32_t k = __builtin_amdgcn_readfirstlane(atomicAdd(&A.queues[x], inc));
+        const int64_t it = queue_item(x, k, A.nq, A.BH, A.n_qt, A.order);
+        if (it >= 0) return int(it);
+    }
+    return -1;
+}
+
 template <int D, int DV, bool QKZ, typename Args>
-__device__ __forceinline__ void fwd_pad_item(const Args &A, int64_t bh, int64_t qt) {
+__device__ __forceinline__ void fwd_pad_item(const Args &A, int64_t bh, int64_t qt, int home) {
     using SM = PSmem<D, DV>;
     constexpr int NBUF = SM::NBUF;
     constexpr int NDIAG = BQ / BK;  // key tiles inside the query tile
@@ -1506,7 +1527,8 @@ __device__ __forceinline__ void fwd_pad_item(const Args &A, int64_t bh, int64_t 
     constexpr int KROW = SM::KROW, VSTR = SM::VSTR;
     extern __shared__ __align__(16) unsigned char smem[];
     uint32_t *misc = reinterpret_cast<uint32_t *>(smem + SM::misc_off);
-    // misc[2]: largest |q|; misc[3]: largest |k|; misc[4]: the work item
+    // misc[2]: largest |q|; misc[3]: largest |k|; misc[4]: the first work
+    // item, misc[5]: the next one
 
     const int tid = threadIdx.x, lane = tid & 63, h = lane >> 5, qi = lane & 31;
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -2124,6 +2146,10 @@ __device__ __forceinline__ void fwd_pad_item(const Args &A, int64_t bh, int64_t 
             vprev = vb_;
         }
         land_wait(m);
+        // wave 0 (whose rows see only the last own block) fetches the
+        // workgroup's next item here, where its copies are in and it has
+        // nothing else to do; the barrier publishes it
+        if (mm == 0 && w == 0) misc[5] = uint32_t(next_item(A, home));
         lds_barrier();
     }
     // the last block's W~ V (keys 0..31 of the lowest own tile: every wave)
@@ -2172,25 +2198,6 @@ __device__ __forceinline__ void fwd_pad_item(const Args &A, int64_t bh, int64_t 
     }
 }
 
-// The next work item of a workgroup whose home queue is `home` (the query
-// tile bh * n_qt + qt, queue_item), or -1 when every queue is empty: a
-// workgroup takes items from its home queue and, once that is empty, from the
-// others in turn.  Called by every lane of one wave, with
-// no divergent branch: lane 0 adds 1 to the queue's counter and the other
-// lanes 0, and every lane takes lane 0's result.  (A branch on the thread
-// index here, inside the workgroup's loop, let the compiler run the lanes of
-// the fetching wave through different loop paths with different barrier
-// sequences.)
-__device__ __forceinline__ int next_item(const FwdArgs &A, int home) {
-    const uint32_t inc = (threadIdx.x & 63) == 0 ? 1u : 0u;
-    for (int i = 0; i < A.nq; ++i) {
-        const int x = home + i < A.nq ? home + i : home + i - A.nq;
-        const uint32_t k = __builtin_amdgcn_readfirstlane(atomicAdd(&A.queues[x], inc));
-        const int64_t it = queue_item(x, k, A.nq, A.BH, A.n_qt, A.order);
-        if (it >= 0) return int(it);
-    }
-    return -1;
-}
 
 // Fused forward, bf16 path: one workgroup per compute unit (the grid is at
 // most the number of compute units), each taking query tiles from the work
@@ -2207,18 +2214,20 @@ __global__ __launch_bounds__(NTHREADS, 1) void fwd_pad_kernel(FwdArgs A) {
     // Every branch in this loop is uniform across each wave (wave 0 fetches
     // with all its lanes, and the item body's per-item bookkeeping runs in
     // whole waves too), so that every wave passes the same barriers.
-    for (;;) {
-        if (w == 0) misc[4] = uint32_t(next_item(A, home));  // every lane, one value
-        __syncthreads();
-        const int it = __builtin_amdgcn_readfirstlane(int(misc[4]));
-        if (it < 0) break;
+    // the first item; each item's wave 0 fetches the next one during the
+    // item (misc[5], published by the item's barriers)
+    if (w == 0) misc[4] = uint32_t(next_item(A, home));  // every lane, one value
+    __syncthreads();
+    int it = __builtin_amdgcn_readfirstlane(int(misc[4]));
+    while (it >= 0) {
         // the arguments are read afresh for every item, from the kernel's
         // argument segment (A is its only argument) through a pointer the
         // compiler cannot prove loop-invariant, instead of held in registers
         // across the loop
         cfwd *ap = (cfwd *)__builtin_amdgcn_kernarg_segment_ptr();
         asm volatile("" : "+s"(ap));
-        fwd_pad_item<D, DV, QKZ>(*ap, it / A.n_qt, it % A.n_qt);
+        fwd_pad_item<D, DV, QKZ>(*ap, it / A.n_qt, it % A.n_qt, home);
+        it = __builtin_amdgcn_readfirstlane(int(misc[5]));
     }
 }
 
