@@ -2166,27 +2166,49 @@ __device__ __forceinline__ void fwd_pad_item(const Args &A, int64_t bh, int64_t 
         f = exp2f(M);
     else
         f = exp2f(A.one_minus_beta * M - A.beta * log2f(zt));
-    if (row_ok) {
-        float *orp = A.o_re + (bh * A.n + row) * DV;
-        float *oip = A.o_im + (bh * A.n + row) * DV;
+    // Stored through LDS: a lane holds 4-channel groups of its row, so stores
+    // straight from the accumulators write 32 bytes in each of 32 rows per
+    // instruction.  Once every wave has finished reading the tiles, each wave
+    // stages its 32 rows, 64 channels at a time (rows of SROW floats, padded so
+    // that the writes spread over the banks), and stores 16 lanes per row:
+    // four rows of 256 contiguous bytes per instruction.
+    lds_barrier();
+    constexpr int SROW = 64 + 8;
+    static_assert(size_t(NWAVES) * 32 * SROW * sizeof(float) <= SM::misc_off,
+                  "staging fits the tile buffers");
+    float *stg = reinterpret_cast<float *>(smem) + w * (32 * SROW);
 #pragma unroll
-        for (int db = 0; db < DV / 32; ++db)
+    for (int part = 0; part < 2; ++part) {
+        float *op = part ? A.o_im : A.o_re;
 #pragma unroll
-            for (int g4 = 0; g4 < 4; ++g4) {
-                const int d0 = 32 * db + 8 * g4 + 4 * h;
-                float4 vr, vi;
-                vr.x = scale_keep_zero(ore[db][4 * g4 + 0], f);
-                vr.y = scale_keep_zero(ore[db][4 * g4 + 1], f);
-                vr.z = scale_keep_zero(ore[db][4 * g4 + 2], f);
-                vr.w = scale_keep_zero(ore[db][4 * g4 + 3], f);
-                vi.x = scale_keep_zero(oim[db][4 * g4 + 0], f);
-                vi.y = scale_keep_zero(oim[db][4 * g4 + 1], f);
-                vi.z = scale_keep_zero(oim[db][4 * g4 + 2], f);
-                vi.w = scale_keep_zero(oim[db][4 * g4 + 3], f);
-                *reinterpret_cast<float4 *>(orp + d0) = vr;
-                *reinterpret_cast<float4 *>(oip + d0) = vi;
+        for (int half = 0; half < DV / 64; ++half) {
+#pragma unroll
+            for (int dd = 0; dd < 2; ++dd)
+#pragma unroll
+                for (int g4 = 0; g4 < 4; ++g4) {
+                    // channels 64 half + 32 dd + 8 g4 + 4 h .. +3 of row qi
+                    const f32x16 &acc = part ? oim[2 * half + dd] : ore[2 * half + dd];
+                    float4 v;
+                    v.x = scale_keep_zero(acc[4 * g4 + 0], f);
+                    v.y = scale_keep_zero(acc[4 * g4 + 1], f);
+                    v.z = scale_keep_zero(acc[4 * g4 + 2], f);
+                    v.w = scale_keep_zero(acc[4 * g4 + 3], f);
+                    *reinterpret_cast<float4 *>(stg + qi * SROW + 32 * dd + 8 * g4 + 4 * h) = v;
+                }
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                const int r = 4 * i + (lane >> 4);  // row of the wave
+                const float4 v =
+                    *reinterpret_cast<const float4 *>(stg + r * SROW + 4 * (lane & 15));
+                const int64_t grow = i0 + 32 * w + r;
+                if (grow < A.n)
+                    *reinterpret_cast<float4 *>(op + (bh * A.n + grow) * DV + 64 * half +
+                                                4 * (lane & 15)) = v;
             }
+        }
     }
+    // (every wave's staged rows are read before the next item's copies
+    // overwrite the buffers)
     __syncthreads();
     if (w == 0) {  // whole wave (the maxima are idempotent; lane 0 counts)
         const uint32_t qb = __builtin_amdgcn_readfirstlane(misc[2]);
