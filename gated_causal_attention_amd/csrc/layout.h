@@ -201,20 +201,32 @@ RESOLVENT_HD inline uint32_t tile_row_off(int64_t n, int64_t t, int r, int64_t r
 // Work queues of the bf16 forward: queue x (of nq, nq dividing BH) holds the
 // query tiles of heads x, x + nq, x + 2 nq, ..., hx = BH / nq heads with n_qt
 // query tiles each.  Entry k of the queue is the query tile bh * n_qt + qt
-// (-1 past the queue's end): order 0 takes the heaviest query tile (the last)
-// of every head of the queue first, then the next ones; order 1 takes one
-// head at a time, heaviest query tile first.
+// (-1 past the queue's end).  order 0 takes the heaviest query tile (the
+// last) of every head of the queue first, then the next ones; order 1 takes
+// one head at a time, heaviest query tile first; order 2 takes the query
+// tiles qt >= q0 of one head at a time, heaviest first, and then the light
+// ones (qt < q0) of every head, heaviest first across the heads.
 RESOLVENT_HD inline int64_t queue_item(int x, uint32_t k, int nq, int64_t BH, int64_t n_qt,
-                                       int order) {
+                                       int order, int64_t q0 = 0) {
     const int64_t hx = BH / nq;
     if (int64_t(k) >= hx * n_qt) return -1;
     int64_t hj, qt;
     if (order == 0) {
         hj = int64_t(k) % hx;
         qt = n_qt - 1 - int64_t(k) / hx;
-    } else {
+    } else if (order == 1 || q0 <= 0 || q0 >= n_qt) {
         hj = int64_t(k) / n_qt;
         qt = n_qt - 1 - int64_t(k) % n_qt;
+    } else {
+        const int64_t heavy = n_qt - q0;  // per head
+        if (int64_t(k) < hx * heavy) {
+            hj = int64_t(k) / heavy;
+            qt = n_qt - 1 - int64_t(k) % heavy;
+        } else {
+            const int64_t kk = int64_t(k) - hx * heavy;
+            hj = kk % hx;
+            qt = q0 - 1 - kk / hx;
+        }
     }
     return (x + nq * hj) * n_qt + qt;
 }

@@ -300,6 +300,7 @@ struct FwdArgs {
     uint32_t *qstat, *kstat, *counters;
     uint32_t *queues;  // bf16 path: the work queues' counters (cleared by prep_kernel)
     int nq, order;     // number of queues (1 or 8), item order inside a queue (queue_item)
+    int q0;            // order 2: the light query tiles, qt < q0
     const int32_t *noff;
     int32_t *status;
     int64_t n, n_pad;
@@ -1511,7 +1512,7 @@ __device__ __forceinline__ int next_item(const Args &A, int home) {
     for (int i = 0; i < A.nq; ++i) {
         const int x = home + i < A.nq ? home + i : home + i - A.nq;
         const uint32_t k = __builtin_amdgcn_readfirstlane(atomicAdd(&A.queues[x], inc));
-        const int64_t it = queue_item(x, k, A.nq, A.BH, A.n_qt, A.order);
+        const int64_t it = queue_item(x, k, A.nq, A.BH, A.n_qt, A.order, A.q0);
         if (it >= 0) return int(it);
     }
     return -1;
@@ -2415,11 +2416,15 @@ int launch_typed(const Problem &P, hipStream_t st, hipEvent_t const *marks) {
     F.counters = counters;
     F.queues = counters + 8;
     F.nq = (BH & 7) == 0 ? 8 : 1;
-    // one head at a time per queue: the 32 compute units of an XCD then read
-    // one head's keys and values, which its L2 holds (heaviest query tile
-    // first across the queue's heads balances the end better but reads more
-    // from HBM: 5% slower at B=4 H=16 n=8192)
-    F.order = 1;
+    // one head at a time per queue, so that the 32 compute units of an XCD
+    // read one head's keys and values, which its L2 holds (heaviest query
+    // tile first across the queue's heads balances the end better but reads
+    // more from HBM: every item 5% slower at B=4 H=16 n=8192); the light
+    // query tiles (the lowest sixth) of every head come last, heaviest first,
+    // to fill the end (1.317 -> 1.292 ms there; a quarter or an eighth of the
+    // query tiles does as well, a half does not)
+    F.order = 2;
+    F.q0 = (int)(L.n_qt / 6);
     F.noff = noff;
     F.status = P.status;
     F.n = L.n;

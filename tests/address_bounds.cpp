@@ -449,22 +449,23 @@ static int check_chain(int64_t B, int64_t H, int64_t n, int64_t dv, int esz) {
     return bad;
 }
 
-// The work queues of the bf16 forward (queue_item): for either item order
-// and either queue count, the entries of all queues up to their ends are
-// every query tile exactly once, heaviest first inside a queue under order 0,
-// and the first entry past a queue's end is -1.
+// The work queues of the bf16 forward (queue_item): for every item order and
+// either queue count, the entries of all queues up to their ends are every
+// query tile exactly once, heaviest first inside a queue under order 0, and
+// the first entry past a queue's end is -1.
 static int check_queues(int64_t B, int64_t H, int64_t n) {
     const Layout L = make_layout(B, H, n, 64, true);
     const int64_t BH = L.BH, n_qt = L.n_qt;
     int bad = 0;
     for (int nq : {1, 8}) {
         if (BH % nq != 0) continue;
-        for (int order = 0; order < 2; ++order) {
+        for (int order = 0; order < 3; ++order) {
+            const int64_t q0 = order == 2 ? n_qt / 4 : 0;
             std::vector<int> seen(size_t(BH * n_qt), 0);
             for (int x = 0; x < nq; ++x) {
                 int64_t prev_qt = n_qt;
                 for (uint32_t k = 0;; ++k) {
-                    const int64_t it = queue_item(x, k, nq, BH, n_qt, order);
+                    const int64_t it = queue_item(x, k, nq, BH, n_qt, order, q0);
                     if (it < 0) {
                         if (int64_t(k) != BH / nq * n_qt && bad++ < 5)
                             std::printf("queue %d of %d ends at %u\n", x, nq, k);
