@@ -1508,9 +1508,16 @@ __device__ __forceinline__ void pstep(const unsigned char *vb, const unsigned ch
 // sequences.)
 template <typename Args>
 __device__ __forceinline__ int next_item(const Args &A, int home) {
-    const uint32_t inc = (threadIdx.x & 63) == 0 ? 1u : 0u;
+    const int lane = threadIdx.x & 63;
+    const uint32_t inc = lane == 0 ? 1u : 0u;
+    const uint32_t count = uint32_t(A.BH / A.nq) * uint32_t(A.n_qt);  // items per queue
+    // every queue's counter at once (lane x reads queue x): a counter only
+    // grows, so one at or past the end proves its queue empty without an
+    // atomic (a workgroup's last fetch would otherwise take nq atomics in turn)
+    const uint32_t seen = lane < A.nq ? __atomic_load_n(&A.queues[lane], __ATOMIC_RELAXED) : count;
     for (int i = 0; i < A.nq; ++i) {
         const int x = home + i < A.nq ? home + i : home + i - A.nq;
+        if (uint32_t(__builtin_amdgcn_readlane(int(seen), x)) >= count) continue;
         const uint32_t k = __builtin_amdgcn_readfirstlane(atomicAdd(&A.queues[x], inc));
         const int64_t it = queue_item(x, k, A.nq, A.BH, A.n_qt, A.order, A.q0);
         if (it >= 0) return int(it);
