@@ -266,10 +266,16 @@ RESOLVENT_HD inline int pad_copy_j(int w, int i) {
     const int j = w - 1 + (NWAVES - 1) * i;
     return j < pad_copies<D, DV>() ? j : pad_copies<D, DV>() - 1;
 }
+// The key whose values row q of a value tile holds: inside each group of 8
+// rows, rows 2e and 2e + 1 hold keys e and 4 + e.  A half-wave's transposing
+// read then takes four rows two apart (4 x 64 bytes at a stride of two rows),
+// which fall into distinct bank groups for the row stride of dv/8 + 2 slots.
+RESOLVENT_HD constexpr int pad_vrow_key(int q) { return (q & ~7) | ((q & 1) << 2) | ((q & 7) >> 1); }
 // Source byte offset of copy instruction j, lane `lane`, relative to the
 // tile's first key row: for j < KSL inside the K rows of the tile (rows of 2d
-// bytes), otherwise inside its value rows (2 dv bytes).  (The whole tile
-// inside the sequence; see the ragged forms below.)
+// bytes), otherwise inside its value rows (2 dv bytes; value row r of the
+// tile takes key pad_vrow_key(r)).  (The whole tile inside the sequence; see
+// the ragged forms below.)
 template <int D, int DV>
 RESOLVENT_HD inline uint32_t pad_copy_src(int j, int lane) {
     constexpr int KSL = pad_kslots<D>(), VSL = pad_vslots<DV>();
@@ -280,7 +286,7 @@ RESOLVENT_HD inline uint32_t pad_copy_src(int j, int lane) {
     }
     const int p = 64 * (j - KSL) + lane, r = p / VSL;
     const int c = p % VSL < DV / 8 ? p % VSL : DV / 8 - 1;
-    return uint32_t(r * DV * 2 + 16 * c);
+    return uint32_t(pad_vrow_key(r) * DV * 2 + 16 * c);
 }
 // The K copy source of tile t when the tile reaches past key n - 1 (or lies
 // wholly past it, as own tiles of the last query tile can): rows past it
@@ -299,7 +305,7 @@ RESOLVENT_HD inline uint32_t pad_kcopy_src_ragged(int j, int lane, int64_t n, in
 template <int DV>
 RESOLVENT_HD inline uint32_t pad_vcopy_src_ragged(int jv, int lane, int64_t n, int64_t t) {
     constexpr int VSL = pad_vslots<DV>();
-    const int p = 64 * jv + lane, r = p / VSL;
+    const int p = 64 * jv + lane, r = pad_vrow_key(p / VSL);
     const int c = p % VSL < DV / 8 ? p % VSL : DV / 8 - 1;
     const int64_t key = t * BK + r < n ? t * BK + r : n - 1;
     return uint32_t(key * DV * 2 + 16 * c);
@@ -313,7 +319,9 @@ RESOLVENT_HD inline uint32_t pad_vcopy_src_ragged(int jv, int lane, int64_t n, i
 // receives channel (i & 3) of the pieces of lanes (i >> 2) + 4 e, e = 0..3;
 // the addresses below hand lane l four keys kb + 16 kc + 8 s + 4 (l >> 5) + e
 // of channel 32 db + (l & 31), the keys of the W~ operand's k order (the
-// lane's eight logits are the keys 8 (e >> 2) + 4 h + (e & 3) of the chunk).
+// lane's eight logits are the keys 8 (e >> 2) + 4 h + (e & 3) of the chunk),
+// from the value rows that hold them (pad_vrow_key: rows kb + 16 kc + 8 s +
+// (l >> 5) + 2 e).
 template <int D>
 RESOLVENT_HD constexpr int pad_kread(int kb, int s, int qi, int h) {
     return (kb + qi) * 16 * pad_kslots<D>() + 16 * (2 * s + h);
@@ -321,7 +329,7 @@ RESOLVENT_HD constexpr int pad_kread(int kb, int s, int qi, int h) {
 template <int D, int DV>
 RESOLVENT_HD constexpr int pad_vread_tr(int kb, int kc, int db, int s, int lane) {
     return 16 * BK * pad_kslots<D>() +
-           (kb + 16 * kc + 8 * s + 4 * (lane >> 5) + ((lane & 15) >> 2)) * 16 * pad_vslots<DV>() +
+           (kb + 16 * kc + 8 * s + (lane >> 5) + 2 * ((lane & 15) >> 2)) * 16 * pad_vslots<DV>() +
            2 * (32 * db + 16 * ((lane >> 4) & 1) + 4 * (lane & 3));
 }
 
