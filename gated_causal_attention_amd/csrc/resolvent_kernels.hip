@@ -74,6 +74,21 @@ __device__ __forceinline__ uint32_t absbits_u4_bf16(uint4 v) {
 // zero when f overflows to inf (a zero lane of G stays 0, never NaN).
 __device__ __forceinline__ float scale_keep_zero(float x, float f) { return x == 0.0f ? x : x * f; }
 
+// Largest value over the wave, returned uniform: four DPP steps give every
+// row of 16 lanes its maximum, four lane reads combine the rows.  (An LDS
+// atomic of a per-lane value otherwise becomes a 64-step scalar loop.)
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
+    v = max(v, uint32_t(__builtin_amdgcn_update_dpp(int(v), int(v), 0xB1, 0xF, 0xF, false)));
+    v = max(v, uint32_t(__builtin_amdgcn_update_dpp(int(v), int(v), 0x4E, 0xF, 0xF, false)));
+    v = max(v, uint32_t(__builtin_amdgcn_update_dpp(int(v), int(v), 0x124, 0xF, 0xF, false)));
+    v = max(v, uint32_t(__builtin_amdgcn_update_dpp(int(v), int(v), 0x128, 0xF, 0xF, false)));
+    const uint32_t a = max(uint32_t(__builtin_amdgcn_readlane(int(v), 0)),
+                           uint32_t(__builtin_amdgcn_readlane(int(v), 16)));
+    const uint32_t b = max(uint32_t(__builtin_amdgcn_readlane(int(v), 32)),
+                           uint32_t(__builtin_amdgcn_readlane(int(v), 48)));
+    return max(a, b);
+}
+
 __device__ __forceinline__ uint32_t absbits_f4(float4 v) {
     uint32_t a = max(__float_as_uint(v.x) & 0x7FFFFFFFu, __float_as_uint(v.y) & 0x7FFFFFFFu);
     uint32_t b = max(__float_as_uint(v.z) & 0x7FFFFFFFu, __float_as_uint(v.w) & 0x7FFFFFFFu);
@@ -908,7 +923,7 @@ __global__ __launch_bounds__(NTHREADS, 1) void fwd_kernel(FwdArgs A) {
     wait_vmcnt<0>();
     land(0);
     lds_barrier();
-    atomicMax(&misc[2], qbits);
+    atomicMax(&misc[2], wave_max_u32(qbits));
 
     f32x16 ore[DV / 32], oim[DV / 32];
 #pragma unroll
@@ -1178,7 +1193,7 @@ __global__ __launch_bounds__(NTHREADS, 1) void fwd_kernel(FwdArgs A) {
     after_m(k);
     lds_barrier();
     if (!lag) lds_barrier();
-    atomicMax(&misc[3], kbits);
+    atomicMax(&misc[3], wave_max_u32(kbits));
 
     // ---- epilogue: O *= exp2((1-beta) M) z^-beta -------------------------
     const float zt = z + __shfl_xor(z, 32);
@@ -1761,7 +1776,7 @@ __device__ __forceinline__ void fwd_pad_item(const Args &A, int64_t bh, int64_t 
     wait_vmcnt<0>();
     land(0);
     lds_barrier();
-    atomicMax(&misc[2], qbits);
+    atomicMax(&misc[2], wave_max_u32(qbits));
 
     f32x16 ore[DV / 32], oim[DV / 32];
 #pragma unroll
@@ -2163,7 +2178,7 @@ __device__ __forceinline__ void fwd_pad_item(const Args &A, int64_t bh, int64_t 
     // the last block's W~ V (keys 0..31 of the lowest own tile: every wave)
     pstep_prefetch<D, DV, 0, 0, true, false, 0, NPRE>(vprev, vprev, pf);
     pstep<D, DV, 0, 0, true, false, NPRE>(vprev, vprev, pf, wk.r, wk.i, qf, ore, oim, x);
-    atomicMax(&misc[3], kbits);
+    atomicMax(&misc[3], wave_max_u32(kbits));
 
     // ---- epilogue: O *= exp2((1-beta) M) z^-beta -------------------------
     const float zt = z + __shfl_xor(z, 32);
